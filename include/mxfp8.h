@@ -1,0 +1,178 @@
+/*
+ * mxfp8.h -- C ABI of the MI355X (gfx950) MXFP8 training cast and MXFP8 scaled
+ * grouped GEMM.
+ *
+ * The operations are the ones the pages turn on:
+ *   - the MXFP8 training cast: bf16 in, 1x32 blocks, an E8M0 scale per block
+ *     rounded up ("RCEIL"), E4M3 data, with scales written straight into the
+ *     layout the GEMM reads ("blocked E8M0 scales", no rearrange pass)
+ *     [torchtitan PR 5334, body; ao fork PR 10 "[moe training] Add
+ *     backward_override to the MXFP8 grouped GEMM", Design notes];
+ *     a rowwise (dim0) and a columnwise (dim1) form [same ao page, Summary and
+ *     Test plan] and a 32x32 weight-scale form [torchtitan PR 5334, body and
+ *     review];
+ *   - the MXFP8 scaled grouped GEMM over per-group row offsets `offs`, with
+ *     offs = NULL for a dense layer ("a single API for dense and grouped",
+ *     "offs=None") [torchtitan PR 5334, body], in forward, dgrad and wgrad
+ *     [ao fork PR 10, Summary; pytorch/ao PR 4705 "Wire MoE and MXFP8Linear
+ *     training paths to CuTeDSL by default", body].
+ * The numerics follow the OCP Microscaling (MX) definition:
+ *   scale exponent s = ceil(log2(amax / 448)) clamped to [-127, 127], stored as
+ *   the byte s + 127; each element is encoded as E4M3 (OCP E4M3FN: bias 7, max
+ *   448, NaN = S.1111.111) of x / 2^s, round-to-nearest-even, saturating. A zero
+ *   block gets scale byte 0. The sign of zero is kept.
+ *
+ * CONVENTIONS (every entry point)
+ *   - Pointers are device pointers unless stated; the caller allocates and frees
+ *     every buffer. The library allocates no device memory and keeps no state
+ *     beyond a per-device architecture check.
+ *   - bf16 data is passed as uint16_t bit patterns; E4M3 codes and E8M0 scales
+ *     as uint8_t; `stream` is a hipStream_t (NULL = the default stream).
+ *   - Work is enqueued asynchronously on `stream`. No call synchronises the host,
+ *     copies device memory to the host or reads `offs` on the host, so sequences
+ *     of calls can be captured into a HIP graph.
+ *   - Arguments are validated on the host before anything is launched. On any
+ *     error nothing is launched, a negative status is returned and
+ *     mx_last_error() describes the problem (thread-local string).
+ *   - Inputs must be finite. NaN or Inf input gives unspecified codes/scales.
+ *   - All pointers must be 16-byte aligned; all row pitches are in elements and
+ *     must make every row 16-byte aligned.
+ *
+ * SCALE LAYOUT ("MFMA-blocked"), used by every scale buffer below
+ *   A quantized matrix Q [R x C] (C = the blocked, contiguous axis, a multiple
+ *   of 32) has logical scales S [R x KB], KB = C / 32. Physically they are stored
+ *   in tiles of 32 rows x 8 blocks, 256 bytes per tile, tiles ordered row-band
+ *   major:
+ *       KT     = ceil(KB / 8)
+ *       offset(r, kb) = ((r / 32) * KT + kb / 8) * 256
+ *                       + (kb % 2) * 128 + (r % 32) * 4 + (kb % 8) / 2
+ *   Buffer size = mx_scale_bytes(R, C) = ceil(R / 32) * KT * 256 bytes. Bytes
+ *   that no (r, kb) maps to are written as 0x7F (scale 1.0) by the casts.
+ *   Why: the gfx950 block-scaled MFMA (32x32x64, fp8) takes the scale of output
+ *   row r and of the k-block b (0 or 1) of one 64-wide k-step from lane r + 32*b,
+ *   and a byte selector picks one byte of that lane's 32-bit scale register. With
+ *   this layout lane l loads the dword at tile offset 4*l and it serves four
+ *   consecutive k-steps (256 contraction elements) through bytes 0..3.
+ */
+#ifndef MXFP8_H_
+#define MXFP8_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int mx_status;
+
+#define MX_OK 0
+#define MX_E_NULL (-1)    /* a required pointer is NULL */
+#define MX_E_SHAPE (-2)   /* a size is negative, too large, or not a required multiple */
+#define MX_E_ALIGN (-3)   /* a pointer or row pitch breaks the 16-byte alignment rule */
+#define MX_E_LAYOUT (-4)  /* a row pitch is smaller than the row length */
+#define MX_E_DTYPE (-5)   /* unknown output dtype */
+#define MX_E_DEVICE (-6)  /* no HIP device, or the current device is not gfx950 */
+#define MX_E_LAUNCH (-7)  /* the kernel launch failed (see mx_last_error) */
+
+#define MX_OUT_F32 0  /* GEMM output as float32 */
+#define MX_OUT_BF16 1 /* GEMM output as bf16 (round-to-nearest-even of the fp32 sum) */
+
+/* Bytes of the MFMA-blocked scale buffer for a [rows x cols] quantized matrix
+ * (cols = the blocked axis). Returns -1 if rows < 0 or cols is not a
+ * non-negative multiple of 32. Host function, no device access. */
+int64_t mx_scale_bytes(int64_t rows, int64_t cols);
+
+/* Status code as text, e.g. "MX_E_SHAPE". */
+const char* mx_status_string(mx_status s);
+
+/* Description of the last error raised on the calling thread ("" if none). */
+const char* mx_last_error(void);
+
+/* 1x32 rowwise ("dim0") cast [torchtitan PR 5334, body: 1x32 RCEIL casts
+ * with blocked E8M0 scales; ao fork PR 10, Design notes].
+ *   x      [rows x cols] bf16, row pitch ld_x elements (ld_x >= cols, ld_x % 8 == 0)
+ *   q      [rows x cols] E4M3 codes, row pitch cols (written)
+ *   scale  mx_scale_bytes(rows, cols) bytes, MFMA-blocked layout (written)
+ * Blocks are 32 consecutive elements of a row. cols % 32 == 0; rows >= 0 (any
+ * value). A 3D tensor [G, N, K] is cast as rows = G*N. */
+mx_status mx_quantize_dim0(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, uint8_t* q,
+                           uint8_t* scale, void* stream);
+
+/* 32x1 columnwise ("dim1") cast, written transposed [ao fork PR 10, Summary
+ * and Test plan: dim1-cast wgrad operands; pytorch/ao PR 4705, ghstack list:
+ * 32x1 quantization].
+ *   x        batch x [rows x cols] bf16; batch b starts at x + b*rows*ld_x;
+ *            row pitch ld_x (ld_x >= cols, ld_x % 8 == 0)
+ *   q_t      batch x [cols x rows] E4M3 codes (the transpose: blocks of 32
+ *            consecutive input rows become 32 contiguous bytes), written
+ *   scale_t  mx_scale_bytes(batch*cols, rows) bytes: the scales of the stacked
+ *            [batch*cols x rows] matrix q_t, MFMA-blocked (written)
+ * rows % 32 == 0, cols % 32 == 0, batch >= 1. Identity: dim1(X) == dim0(X^T). */
+mx_status mx_quantize_dim1(const uint16_t* x, int64_t batch, int64_t rows, int64_t cols, int64_t ld_x,
+                           uint8_t* q_t, uint8_t* scale_t, void* stream);
+
+/* 32x32 weight cast: one scale per 32x32 tile [torchtitan PR 5334, body
+ * ("32x32 RCEIL weight-scale policy") and review (the square weight kernel is
+ * RCEIL-only)]. One set of codes, quantized with the tile scale, is written
+ * in both orientations (the rowwise and columnwise copies of one weight).
+ *   w          batch x [n x k] bf16, row pitch ld_w (ld_w >= k, ld_w % 8 == 0)
+ *   q          batch x [n x k] codes (written)
+ *   q_t        batch x [k x n] the same codes transposed (written; may be NULL)
+ *   scale_row  mx_scale_bytes(batch*n, k): scales of q, tile byte repeated over
+ *              the tile's 32 rows (written)
+ *   scale_col  mx_scale_bytes(batch*k, n): scales of q_t (written; NULL iff q_t
+ *              is NULL)
+ * n % 32 == 0, k % 32 == 0, batch >= 1. */
+mx_status mx_quantize_weight_32x32(const uint16_t* w, int64_t batch, int64_t n, int64_t k, int64_t ld_w,
+                                   uint8_t* q, uint8_t* q_t, uint8_t* scale_row, uint8_t* scale_col,
+                                   void* stream);
+
+/* Grouped GEMM forward: out[r, :] = deq(a)[r, :] . deq(b_g)^T for r in group g
+ * [ao fork PR 10, Summary (the MXFP8 grouped GEMM); torchtitan PR 5334, body
+ * (offs=None for dense)].
+ *   a, a_s    [m x k] codes + mx_scale_bytes(m, k) scales (dim0 of the tokens)
+ *   b, b_s    [groups*n x k] codes (group g's [n x k] weight at rows g*n) +
+ *             mx_scale_bytes(groups*n, k) scales
+ *   offs      device int32[groups]: inclusive cumulative group ends; group g is
+ *             rows [offs[g-1], offs[g]) with offs[-1] = 0. NULL = one dense group
+ *             (groups must be 1). Caller precondition (not checked, offs stays on
+ *             the device): non-decreasing, every entry % 32 == 0, offs[G-1] == m.
+ *             Rows past offs[G-1] are left unwritten.
+ *   out       [m x n], float32 or bf16 per out_dtype, row pitch n (written)
+ * k % 32 == 0 (k need not be a multiple of 128: the tail is zero-padded inside
+ * the kernel); m >= 0; n >= 1; if groups > 1, n % 32 == 0. fp32 accumulation. */
+mx_status mx_grouped_mm_fwd(const uint8_t* a, const uint8_t* a_s, const uint8_t* b, const uint8_t* b_s,
+                            const int32_t* offs, int32_t groups, int64_t m, int64_t n, int64_t k, void* out,
+                            int out_dtype, void* stream);
+
+/* Grouped GEMM dgrad: dx[r, :] = deq(dy)[r, :] . deq(W_g) for r in group g
+ * [ao fork PR 10, Summary: dgrad from the dim0-cast grad_out].
+ *   dy, dy_s     [m x n] codes + mx_scale_bytes(m, n) (dim0 of grad_out)
+ *   w_t, w_t_s   [groups*k x n]: W_g^T per group (the dim1 cast of the
+ *                [groups, n, k] weight, or q_t of the 32x32 cast) +
+ *                mx_scale_bytes(groups*k, n)
+ *   offs, groups as for mx_grouped_mm_fwd
+ *   dx           [m x k] (written)
+ * n % 32 == 0 (the contraction); if groups > 1, k % 32 == 0. */
+mx_status mx_grouped_mm_dgrad(const uint8_t* dy, const uint8_t* dy_s, const uint8_t* w_t, const uint8_t* w_t_s,
+                              const int32_t* offs, int32_t groups, int64_t m, int64_t n, int64_t k, void* dx,
+                              int out_dtype, void* stream);
+
+/* Grouped GEMM wgrad: dw[g] = deq(dy_t)[:, rows_g] . deq(x_t)[:, rows_g]^T; an
+ * empty group gives zeros [ao fork PR 10, Summary and Test plan: wgrad from
+ * dim1 casts of grad_out and input; pytorch/ao PR 4705, ghstack list: K-groups].
+ *   dy_t, dy_t_s  [n x m] codes (dim1 of grad_out) + mx_scale_bytes(n, m)
+ *   x_t, x_t_s    [k x m] codes (dim1 of the input) + mx_scale_bytes(k, m)
+ *   offs, groups  group g contracts over rows [offs[g-1], offs[g]) of m; NULL =
+ *                 one group over all m. Same caller preconditions as fwd.
+ *   dw            [groups x n x k] (written, every element)
+ * m % 32 == 0 (the contraction), n >= 1, k >= 1. */
+mx_status mx_grouped_mm_wgrad(const uint8_t* dy_t, const uint8_t* dy_t_s, const uint8_t* x_t, const uint8_t* x_t_s,
+                              const int32_t* offs, int32_t groups, int64_t m, int64_t n, int64_t k, void* dw,
+                              int out_dtype, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MXFP8_H_ */

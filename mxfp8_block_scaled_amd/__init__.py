@@ -1,0 +1,170 @@
+"""MXFP8 training cast and MXFP8 scaled grouped GEMM for AMD MI355X (gfx950).
+
+Thin Python binding over the C ABI in include/mxfp8.h: each function below has the
+name of its C entry point, checks nothing the library checks itself, allocates the
+outputs with torch on the input's device and calls the library on the current HIP
+stream. Every step of the computation runs in the library's HIP kernels.
+
+Tensors: bf16 inputs may be torch.bfloat16 or int16/uint16 bit patterns; E4M3
+codes and E8M0 scales are uint8 tensors; scales are in the library's MFMA-blocked
+layout (see `mx_scale_bytes`).
+"""
+
+import torch
+
+from . import _lib
+from ._lib import MX_OUT_BF16, MX_OUT_F32, MXError  # noqa: F401
+
+__all__ = [
+    "mx_scale_bytes",
+    "mx_quantize_dim0",
+    "mx_quantize_dim1",
+    "mx_quantize_weight_32x32",
+    "mx_grouped_mm_fwd",
+    "mx_grouped_mm_dgrad",
+    "mx_grouped_mm_wgrad",
+    "MXError",
+    "library_path",
+]
+
+
+def library_path():
+    return _lib.LIB_PATH
+
+
+def _stream(t):
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _bf16_bits(x):
+    if x.dtype == torch.bfloat16:
+        return x
+    if x.dtype in (torch.int16, torch.uint16):
+        return x
+    raise TypeError(f"expected bf16 data (torch.bfloat16 or 16-bit bit patterns), got {x.dtype}")
+
+
+def mx_scale_bytes(rows, cols):
+    """Bytes of the MFMA-blocked scale buffer of a [rows x cols] quantized matrix."""
+    n = _lib.load().mx_scale_bytes(int(rows), int(cols))
+    if n < 0:
+        raise ValueError(f"mx_scale_bytes({rows}, {cols}): cols must be a non-negative multiple of 32")
+    return n
+
+
+def _u8(n, device):
+    return torch.empty(int(n), dtype=torch.uint8, device=device)
+
+
+def mx_quantize_dim0(x, q=None, scale=None):
+    """1x32 rowwise cast of x [rows, cols] (row pitch x.stride(0)) -> (q [rows, cols], scale)."""
+    x = _bf16_bits(x)
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be a 2D tensor with unit inner stride")
+    rows, cols = x.shape
+    if q is None:
+        q = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
+    if scale is None:
+        scale = _u8(mx_scale_bytes(rows, cols), x.device)
+    _lib.call("mx_quantize_dim0", _ptr(x), rows, cols, x.stride(0), _ptr(q), _ptr(scale), _stream(x))
+    return q, scale
+
+
+def mx_quantize_dim1(x, q_t=None, scale_t=None):
+    """32x1 columnwise cast, written transposed.
+
+    x [rows, cols] or [batch, rows, cols] (batches contiguous) -> q_t [.., cols, rows]
+    and the scales of the stacked [batch*cols, rows] matrix.
+    """
+    x = _bf16_bits(x)
+    if x.dim() == 2:
+        batch, (rows, cols) = 1, x.shape
+    elif x.dim() == 3:
+        batch, rows, cols = x.shape
+        if x.stride(0) != rows * x.stride(1):
+            raise ValueError("batches of x must be contiguous with the row pitch")
+    else:
+        raise ValueError("x must be 2D or 3D")
+    if x.stride(-1) != 1:
+        raise ValueError("x must have unit inner stride")
+    if q_t is None:
+        shape = (cols, rows) if x.dim() == 2 else (batch, cols, rows)
+        q_t = torch.empty(shape, dtype=torch.uint8, device=x.device)
+    if scale_t is None:
+        scale_t = _u8(mx_scale_bytes(batch * cols, rows), x.device)
+    _lib.call("mx_quantize_dim1", _ptr(x), batch, rows, cols, x.stride(-2), _ptr(q_t), _ptr(scale_t), _stream(x))
+    return q_t, scale_t
+
+
+def mx_quantize_weight_32x32(w, transposed=True):
+    """32x32 weight cast of w [n, k] or [batch, n, k] -> (q, q_t, scale_row, scale_col).
+
+    q_t and scale_col are None when transposed=False.
+    """
+    w = _bf16_bits(w)
+    if w.dim() == 2:
+        batch, (n, k) = 1, w.shape
+    elif w.dim() == 3:
+        batch, n, k = w.shape
+        if w.stride(0) != n * w.stride(1):
+            raise ValueError("batches of w must be contiguous with the row pitch")
+    else:
+        raise ValueError("w must be 2D or 3D")
+    if w.stride(-1) != 1:
+        raise ValueError("w must have unit inner stride")
+    lead = () if w.dim() == 2 else (batch,)
+    q = torch.empty(lead + (n, k), dtype=torch.uint8, device=w.device)
+    s_row = _u8(mx_scale_bytes(batch * n, k), w.device)
+    q_t = s_col = None
+    if transposed:
+        q_t = torch.empty(lead + (k, n), dtype=torch.uint8, device=w.device)
+        s_col = _u8(mx_scale_bytes(batch * k, n), w.device)
+    _lib.call("mx_quantize_weight_32x32", _ptr(w), batch, n, k, w.stride(-2), _ptr(q), _ptr(q_t), _ptr(s_row),
+              _ptr(s_col), _stream(w))
+    return q, q_t, s_row, s_col
+
+
+def _out(shape, out_dtype, device, out):
+    if out is not None:
+        return out
+    dt = torch.float32 if out_dtype == MX_OUT_F32 else torch.bfloat16
+    return torch.empty(shape, dtype=dt, device=device)
+
+
+def _groups(offs, groups):
+    if offs is None:
+        return 1 if groups is None else groups
+    if offs.dtype != torch.int32:
+        raise TypeError("offs must be int32")
+    return offs.numel() if groups is None else groups
+
+
+def mx_grouped_mm_fwd(a, a_s, b, b_s, offs, m, n, k, groups=None, out_dtype=MX_OUT_BF16, out=None):
+    """out [m, n] = a [m, k] . b_g [n, k]^T per row group (offs None = dense)."""
+    G = _groups(offs, groups)
+    out = _out((m, n), out_dtype, a.device, out)
+    _lib.call("mx_grouped_mm_fwd", _ptr(a), _ptr(a_s), _ptr(b), _ptr(b_s), _ptr(offs), G, m, n, k, _ptr(out),
+              out_dtype, _stream(a))
+    return out
+
+
+def mx_grouped_mm_dgrad(dy, dy_s, w_t, w_t_s, offs, m, n, k, groups=None, out_dtype=MX_OUT_BF16, out=None):
+    """dx [m, k] = dy [m, n] . W_g [n, k] per row group, with W_g^T given as w_t [G*k, n]."""
+    G = _groups(offs, groups)
+    out = _out((m, k), out_dtype, dy.device, out)
+    _lib.call("mx_grouped_mm_dgrad", _ptr(dy), _ptr(dy_s), _ptr(w_t), _ptr(w_t_s), _ptr(offs), G, m, n, k, _ptr(out),
+              out_dtype, _stream(dy))
+    return out
+
+
+def mx_grouped_mm_wgrad(dy_t, dy_t_s, x_t, x_t_s, offs, m, n, k, groups=None, out_dtype=MX_OUT_F32, out=None):
+    """dw [G, n, k]: dw[g] = dy_t[:, rows_g] . x_t[:, rows_g]^T (empty group -> zeros)."""
+    G = _groups(offs, groups)
+    out = _out((G, n, k), out_dtype, dy_t.device, out)
+    _lib.call("mx_grouped_mm_wgrad", _ptr(dy_t), _ptr(dy_t_s), _ptr(x_t), _ptr(x_t_s), _ptr(offs), G, m, n, k,
+              _ptr(out), out_dtype, _stream(dy_t))
+    return out

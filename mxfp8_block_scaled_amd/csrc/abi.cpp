@@ -1,0 +1,234 @@
+// C ABI: argument validation, error reporting and dispatch to the HIP kernels.
+// Every check runs on the host before anything is launched; the device is only
+// queried (once per device, for its architecture) after the arguments pass.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <mutex>
+
+#include "../../include/mxfp8.h"
+
+hipError_t mx_launch_dim0(const uint16_t*, int64_t, int64_t, int64_t, uint8_t*, uint8_t*, hipStream_t);
+hipError_t mx_launch_dim1(const uint16_t*, int64_t, int64_t, int64_t, int64_t, uint8_t*, uint8_t*, hipStream_t);
+hipError_t mx_launch_w32(const uint16_t*, int64_t, int64_t, int64_t, int64_t, uint8_t*, uint8_t*, uint8_t*, uint8_t*,
+                         hipStream_t);
+hipError_t mx_launch_gemm_mgroup(const uint8_t*, const uint8_t*, const uint8_t*, const uint8_t*, const int32_t*, int,
+                                 int64_t, int64_t, int64_t, void*, int, hipStream_t);
+hipError_t mx_launch_gemm_kgroup(const uint8_t*, const uint8_t*, const uint8_t*, const uint8_t*, const int32_t*, int,
+                                 int64_t, int64_t, int64_t, void*, int, hipStream_t);
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+// Largest size accepted for any dimension: keeps every byte offset far inside int64.
+constexpr int64_t kMaxDim = (int64_t)1 << 31;
+
+mx_status fail(mx_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+mx_status fail(mx_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
+// Architecture check, cached per device ordinal.
+mx_status check_device() {
+  static std::mutex mu;
+  static int state[64] = {0};  // 0 unknown, 1 ok, -1 not gfx950
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return fail(MX_E_DEVICE, "no HIP device is available");
+  if (dev >= 64) return fail(MX_E_DEVICE, "device ordinal %d out of range", dev);
+  std::lock_guard<std::mutex> lock(mu);
+  if (state[dev] == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return fail(MX_E_DEVICE, "cannot query device %d", dev);
+    state[dev] = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
+    if (state[dev] < 0) return fail(MX_E_DEVICE, "device %d is %s; this library runs on gfx950 only", dev, prop.gcnArchName);
+  }
+  if (state[dev] < 0) return fail(MX_E_DEVICE, "device %d is not gfx950", dev);
+  return MX_OK;
+}
+
+mx_status launched(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(MX_E_LAUNCH, "%s: launch failed: %s", what, hipGetErrorString(e));
+  g_err[0] = 0;
+  return MX_OK;
+}
+
+mx_status check_dim(const char* name, int64_t v, int64_t lo) {
+  if (v < lo || v > kMaxDim) return fail(MX_E_SHAPE, "%s = %lld is outside [%lld, 2^31]", name, (long long)v, (long long)lo);
+  return MX_OK;
+}
+
+#define TRY(x)                  \
+  do {                          \
+    mx_status _s = (x);         \
+    if (_s != MX_OK) return _s; \
+  } while (0)
+
+mx_status check_ptr(const char* name, const void* p) {
+  if (!p) return fail(MX_E_NULL, "%s is NULL", name);
+  if (!aligned16(p)) return fail(MX_E_ALIGN, "%s is not 16-byte aligned", name);
+  return MX_OK;
+}
+
+mx_status check_pitch(const char* name, int64_t ld, int64_t cols) {
+  if (ld < cols) return fail(MX_E_LAYOUT, "%s = %lld is smaller than the row length %lld", name, (long long)ld, (long long)cols);
+  if (ld % 8 != 0) return fail(MX_E_ALIGN, "%s = %lld: bf16 rows must start 16-byte aligned (pitch %% 8 == 0)", name, (long long)ld);
+  if (ld > kMaxDim) return fail(MX_E_SHAPE, "%s = %lld is too large", name, (long long)ld);
+  return MX_OK;
+}
+
+mx_status check_mul32(const char* name, int64_t v) {
+  if (v % 32 != 0) return fail(MX_E_SHAPE, "%s = %lld must be a multiple of 32 (one MX block)", name, (long long)v);
+  return MX_OK;
+}
+
+mx_status check_gemm_common(const void* a, const void* a_s, const void* b, const void* b_s, const void* out,
+                            int out_dtype, int32_t groups, const int32_t* offs) {
+  TRY(check_ptr("a", a));
+  TRY(check_ptr("a_scale", a_s));
+  TRY(check_ptr("b", b));
+  TRY(check_ptr("b_scale", b_s));
+  TRY(check_ptr("out", out));
+  if (out_dtype != MX_OUT_F32 && out_dtype != MX_OUT_BF16)
+    return fail(MX_E_DTYPE, "out_dtype = %d is neither MX_OUT_F32 (0) nor MX_OUT_BF16 (1)", out_dtype);
+  if (groups < 1 || groups > 65536) return fail(MX_E_SHAPE, "groups = %d is outside [1, 65536]", groups);
+  if (!offs && groups != 1) return fail(MX_E_SHAPE, "offs is NULL (dense) but groups = %d", groups);
+  if (offs && ((uintptr_t)offs & 3)) return fail(MX_E_ALIGN, "offs is not 4-byte aligned");
+  return MX_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t mx_scale_bytes(int64_t rows, int64_t cols) {
+  if (rows < 0 || cols < 0 || cols % 32 != 0) return -1;
+  const int64_t kb = cols / 32;
+  return ((rows + 31) / 32) * ((kb + 7) / 8) * 256;
+}
+
+const char* mx_status_string(mx_status s) {
+  switch (s) {
+    case MX_OK: return "MX_OK";
+    case MX_E_NULL: return "MX_E_NULL";
+    case MX_E_SHAPE: return "MX_E_SHAPE";
+    case MX_E_ALIGN: return "MX_E_ALIGN";
+    case MX_E_LAYOUT: return "MX_E_LAYOUT";
+    case MX_E_DTYPE: return "MX_E_DTYPE";
+    case MX_E_DEVICE: return "MX_E_DEVICE";
+    case MX_E_LAUNCH: return "MX_E_LAUNCH";
+    default: return "MX_E_UNKNOWN";
+  }
+}
+
+const char* mx_last_error(void) { return g_err; }
+
+mx_status mx_quantize_dim0(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, uint8_t* q, uint8_t* scale,
+                           void* stream) {
+  TRY(check_dim("rows", rows, 0));
+  TRY(check_dim("cols", cols, 32));
+  TRY(check_mul32("cols", cols));
+  TRY(check_pitch("ld_x", ld_x, cols));
+  TRY(check_ptr("x", x));
+  TRY(check_ptr("q", q));
+  TRY(check_ptr("scale", scale));
+  TRY(check_device());
+  return launched(mx_launch_dim0(x, rows, cols, ld_x, q, scale, (hipStream_t)stream), "mx_quantize_dim0");
+}
+
+mx_status mx_quantize_dim1(const uint16_t* x, int64_t batch, int64_t rows, int64_t cols, int64_t ld_x, uint8_t* q_t,
+                           uint8_t* scale_t, void* stream) {
+  TRY(check_dim("batch", batch, 1));
+  TRY(check_dim("rows", rows, 32));
+  TRY(check_dim("cols", cols, 32));
+  TRY(check_mul32("rows", rows));
+  TRY(check_mul32("cols", cols));
+  TRY(check_pitch("ld_x", ld_x, cols));
+  if (batch * rows > kMaxDim || batch * cols > kMaxDim) return fail(MX_E_SHAPE, "batch * rows or batch * cols exceeds 2^31");
+  TRY(check_ptr("x", x));
+  TRY(check_ptr("q_t", q_t));
+  TRY(check_ptr("scale_t", scale_t));
+  TRY(check_device());
+  return launched(mx_launch_dim1(x, batch, rows, cols, ld_x, q_t, scale_t, (hipStream_t)stream), "mx_quantize_dim1");
+}
+
+mx_status mx_quantize_weight_32x32(const uint16_t* w, int64_t batch, int64_t n, int64_t k, int64_t ld_w, uint8_t* q,
+                                   uint8_t* q_t, uint8_t* scale_row, uint8_t* scale_col, void* stream) {
+  TRY(check_dim("batch", batch, 1));
+  TRY(check_dim("n", n, 32));
+  TRY(check_dim("k", k, 32));
+  TRY(check_mul32("n", n));
+  TRY(check_mul32("k", k));
+  TRY(check_pitch("ld_w", ld_w, k));
+  if (batch * n > kMaxDim || batch * k > kMaxDim) return fail(MX_E_SHAPE, "batch * n or batch * k exceeds 2^31");
+  TRY(check_ptr("w", w));
+  TRY(check_ptr("q", q));
+  TRY(check_ptr("scale_row", scale_row));
+  if ((q_t == nullptr) != (scale_col == nullptr))
+    return fail(MX_E_NULL, "q_t and scale_col must both be given or both be NULL");
+  if (q_t) {
+    TRY(check_ptr("q_t", q_t));
+    TRY(check_ptr("scale_col", scale_col));
+  }
+  TRY(check_device());
+  return launched(mx_launch_w32(w, batch, n, k, ld_w, q, q_t, scale_row, scale_col, (hipStream_t)stream),
+                  "mx_quantize_weight_32x32");
+}
+
+mx_status mx_grouped_mm_fwd(const uint8_t* a, const uint8_t* a_s, const uint8_t* b, const uint8_t* b_s,
+                            const int32_t* offs, int32_t groups, int64_t m, int64_t n, int64_t k, void* out,
+                            int out_dtype, void* stream) {
+  TRY(check_gemm_common(a, a_s, b, b_s, out, out_dtype, groups, offs));
+  TRY(check_dim("m", m, 0));
+  TRY(check_dim("n", n, 1));
+  TRY(check_dim("k", k, 32));
+  TRY(check_mul32("k", k));
+  if (groups > 1 && n % 32 != 0) return fail(MX_E_SHAPE, "n = %lld must be a multiple of 32 when groups > 1", (long long)n);
+  if ((int64_t)groups * n > kMaxDim) return fail(MX_E_SHAPE, "groups * n exceeds 2^31");
+  TRY(check_device());
+  return launched(mx_launch_gemm_mgroup(a, a_s, b, b_s, offs, groups, m, n, k, out, out_dtype, (hipStream_t)stream),
+                  "mx_grouped_mm_fwd");
+}
+
+mx_status mx_grouped_mm_dgrad(const uint8_t* dy, const uint8_t* dy_s, const uint8_t* w_t, const uint8_t* w_t_s,
+                              const int32_t* offs, int32_t groups, int64_t m, int64_t n, int64_t k, void* dx,
+                              int out_dtype, void* stream) {
+  TRY(check_gemm_common(dy, dy_s, w_t, w_t_s, dx, out_dtype, groups, offs));
+  TRY(check_dim("m", m, 0));
+  TRY(check_dim("n", n, 32));
+  TRY(check_dim("k", k, 1));
+  TRY(check_mul32("n", n));
+  if (groups > 1 && k % 32 != 0) return fail(MX_E_SHAPE, "k = %lld must be a multiple of 32 when groups > 1", (long long)k);
+  if ((int64_t)groups * k > kMaxDim) return fail(MX_E_SHAPE, "groups * k exceeds 2^31");
+  TRY(check_device());
+  // dX[m x k] = dY[m x n] . (W_g^T [k x n])^T : the M-grouped core with contraction n
+  return launched(mx_launch_gemm_mgroup(dy, dy_s, w_t, w_t_s, offs, groups, m, k, n, dx, out_dtype, (hipStream_t)stream),
+                  "mx_grouped_mm_dgrad");
+}
+
+mx_status mx_grouped_mm_wgrad(const uint8_t* dy_t, const uint8_t* dy_t_s, const uint8_t* x_t, const uint8_t* x_t_s,
+                              const int32_t* offs, int32_t groups, int64_t m, int64_t n, int64_t k, void* dw,
+                              int out_dtype, void* stream) {
+  TRY(check_gemm_common(dy_t, dy_t_s, x_t, x_t_s, dw, out_dtype, groups, offs));
+  TRY(check_dim("m", m, 0));
+  TRY(check_dim("n", n, 1));
+  TRY(check_dim("k", k, 1));
+  TRY(check_mul32("m", m));
+  if ((int64_t)groups * n > kMaxDim) return fail(MX_E_SHAPE, "groups * n exceeds 2^31");
+  TRY(check_device());
+  // dW_g[n x k] = dY^T[n x m] . (X^T[k x m])^T over group g's range of m
+  return launched(mx_launch_gemm_kgroup(dy_t, dy_t_s, x_t, x_t_s, offs, groups, n, k, m, dw, out_dtype, (hipStream_t)stream),
+                  "mx_grouped_mm_wgrad");
+}
+
+}  // extern "C"

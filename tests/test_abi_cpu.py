@@ -1,0 +1,108 @@
+"""The C-ABI library loads, exports every declared entry point and validates its
+arguments on the host (no GPU needed: nothing here launches a kernel)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from mxfp8_block_scaled_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mxfp8.h")
+
+MX_E_NULL, MX_E_SHAPE, MX_E_ALIGN, MX_E_LAYOUT, MX_E_DTYPE, MX_E_DEVICE = -1, -2, -3, -4, -5, -6
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mx_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert len(names) >= 9
+    for n in names:
+        assert hasattr(lib, n), n
+        assert n in _lib.SIGNATURES, n
+
+
+def test_scale_bytes(lib):
+    assert lib.mx_scale_bytes(32, 256) == 256
+    assert lib.mx_scale_bytes(33, 256) == 512
+    assert lib.mx_scale_bytes(32, 288) == 512
+    assert lib.mx_scale_bytes(576, 4096) == 18 * 16 * 256
+    assert lib.mx_scale_bytes(0, 64) == 0
+    assert lib.mx_scale_bytes(32, 48) == -1
+    assert lib.mx_scale_bytes(-1, 32) == -1
+
+
+def test_status_strings(lib):
+    assert lib.mx_status_string(0) == b"MX_OK"
+    assert lib.mx_status_string(-2) == b"MX_E_SHAPE"
+    assert lib.mx_status_string(-99) == b"MX_E_UNKNOWN"
+
+
+# fake, aligned, never dereferenced device addresses: validation fails before any launch
+P = 0x10000
+P2 = 0x20000
+
+
+@pytest.mark.parametrize(
+    "args,status",
+    [
+        ((P, 4, 48, 48, P2, P2, None), MX_E_SHAPE),  # cols not a multiple of 32
+        ((P, -1, 32, 32, P2, P2, None), MX_E_SHAPE),
+        ((P, 4, 64, 32, P2, P2, None), MX_E_LAYOUT),  # pitch < cols
+        ((P, 4, 64, 68, P2, P2, None), MX_E_ALIGN),  # pitch breaks 16-byte rows
+        ((None, 4, 64, 64, P2, P2, None), MX_E_NULL),
+        ((P + 2, 4, 64, 64, P2, P2, None), MX_E_ALIGN),
+        ((P, 4, 64, 64, P2, None, None), MX_E_NULL),
+    ],
+)
+def test_dim0_validation(lib, args, status):
+    assert lib.mx_quantize_dim0(*args) == status
+    assert len(lib.mx_last_error()) > 0
+
+
+def test_dim1_and_w32_validation(lib):
+    assert lib.mx_quantize_dim1(P, 1, 48, 64, 64, P2, P2, None) == MX_E_SHAPE  # rows % 32
+    assert lib.mx_quantize_dim1(P, 0, 64, 64, 64, P2, P2, None) == MX_E_SHAPE  # batch
+    assert lib.mx_quantize_weight_32x32(P, 1, 40, 64, 64, P2, None, P2, None, None) == MX_E_SHAPE
+    assert lib.mx_quantize_weight_32x32(P, 1, 64, 64, 64, P2, P2, P2, None, None) == MX_E_NULL  # q_t without scale_col
+
+
+def test_gemm_validation(lib):
+    f = lib.mx_grouped_mm_fwd
+    assert f(P, P, P, P, None, 1, 64, 64, 48, P2, 0, None) == MX_E_SHAPE  # k % 32
+    assert f(P, P, P, P, None, 2, 64, 64, 64, P2, 0, None) == MX_E_SHAPE  # dense with groups > 1
+    assert f(P, P, P, P, P, 2, 64, 40, 64, P2, 0, None) == MX_E_SHAPE  # grouped n % 32
+    assert f(P, P, P, P, None, 1, 64, 64, 64, P2, 7, None) == MX_E_DTYPE
+    assert f(P, P, P, P, P + 2, 1, 64, 64, 64, P2, 0, None) == MX_E_ALIGN
+    assert lib.mx_grouped_mm_dgrad(P, P, P, P, None, 1, 64, 40, 64, P2, 0, None) == MX_E_SHAPE  # n % 32
+    assert lib.mx_grouped_mm_wgrad(P, P, P, P, None, 1, 40, 64, 64, P2, 0, None) == MX_E_SHAPE  # m % 32
+
+
+def test_valid_arguments_without_a_gpu_report_device(lib):
+    """With valid arguments and no GPU the library says so instead of launching."""
+    import torch
+
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert lib.mx_quantize_dim0(P, 4, 64, 64, P2, P2, None) == MX_E_DEVICE
+    assert b"device" in lib.mx_last_error()
+
+
+def test_python_binding_raises(lib):
+    from mxfp8_block_scaled_amd import mx_scale_bytes
+
+    with pytest.raises(ValueError):
+        mx_scale_bytes(32, 40)
+    assert mx_scale_bytes(64, 512) == 2 * 2 * 256
