@@ -1,0 +1,257 @@
+"""Benchmark: one MXFP8 MoE training step (casts + grouped GEMM forward, dgrad,
+wgrad) on one MI355X, printed as one JSON line.
+
+Workload (the pages' grouped-GEMM benchmark shape, pytorch/ao PR 4705 "Wire MoE
+and MXFP8Linear training paths to CuTeDSL by default", grouped benchmark command:
+K=N=4096, G=8, M=16384): tokens X [16384, 4096] ~ N(0,1), expert weights
+W [8, 4096, 4096] ~ N(0,0.02), grad_out dY [16384, 4096] ~ N(0,1e-2), multinomial
+group sizes in multiples of 32; plus the unaligned dense layer of the 576-wide
+gradient (torchtitan PR 5334, body): W' [576, 4096] with 32x32 weight scales and
+dY' [16384, 576]. Synthetic, seeded data; inputs resident in HBM before timing.
+
+One step runs, in order:
+  dim0 X, dim0 W (3D as rows), grouped fwd           -> Y  [16384, 4096] bf16
+  dim0 dY, dim1 W (3D batched), grouped dgrad         -> dX [16384, 4096] bf16
+  dim1 dY, dim1 X, grouped wgrad                      -> dW [8, 4096, 4096] bf16
+  32x32 W', dense fwd (reuses dim0 X)                 -> Y' [16384, 576] bf16
+  dim0 dY', dense dgrad over the 576-wide contraction -> dX' [16384, 4096] bf16
+  dim1 dY', dense wgrad (reuses dim1 X)               -> dW' [576, 4096] bf16
+`value` = all GEMM flops of the step / step time (casts included).
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MXFP8 grouped GEMM TFLOP/s (fwd+bwd) and cast GB/s vs roofline, 1 GPU"
+PEAK_FP8_TFLOPS = 5000.0  # MI355X dense fp8 / MXFP8 MFMA
+PEAK_HBM_GBPS = 8000.0
+CAST_BYTES_PER_ELEM = 2 + 1 + 1 / 32  # read bf16, write e4m3 + one scale byte per 32
+W32_BYTES_PER_ELEM = 2 + 1 + 1 + 2 / 32  # both orientations, row and column scales
+M, K, N, G, NARROW = 16384, 4096, 4096, 8, 576
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def src_hash():
+    h = hashlib.sha256()
+    for f in ("gemm.hip", "cast.hip", "common.h"):
+        with open(os.path.join(ROOT, "mxfp8_block_scaled_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel_key, units_per_launch):
+    """HBM bytes per launch from the committed counter summary, if still current."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        d = json.load(fh)
+    e = d.get(kernel_key)
+    if not e or e.get("source_hash") != src_hash():
+        return None
+    return e.get("hbm_bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); "
+              "there is no multi-GPU path. Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import mxfp8_block_scaled_amd as mx
+    from mxfp8_block_scaled_amd import synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+
+    def to_dev(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    d = synth.moe_g8(0, with_backward=True)
+    offs_np = d["offs"]
+    X, W, dY = to_dev(d["x"]), to_dev(d["w"]), to_dev(d["dy"])
+    Wn, dYn = to_dev(d["w_narrow"]), to_dev(d["dy_narrow"])
+    offs = torch.from_numpy(offs_np).to(dev)
+    del d
+
+    u8 = lambda *s: torch.empty(s, dtype=torch.uint8, device=dev)  # noqa: E731
+    sb = mx.mx_scale_bytes
+    bf = lambda *s: torch.empty(s, dtype=torch.bfloat16, device=dev)  # noqa: E731
+    buf = {
+        "xq": u8(M, K), "xs": u8(sb(M, K)),
+        "wq": u8(G * N, K), "ws": u8(sb(G * N, K)),
+        "dyq": u8(M, N), "dys": u8(sb(M, N)),
+        "wtq": u8(G, K, N), "wts": u8(sb(G * K, N)),
+        "dytq": u8(N, M), "dyts": u8(sb(N, M)),
+        "xtq": u8(K, M), "xts": u8(sb(K, M)),
+        "y": bf(M, N), "dx": bf(M, K), "dw": bf(G, N, K),
+        "dynq": u8(M, NARROW), "dyns": u8(sb(M, NARROW)),
+        "dyntq": u8(NARROW, M), "dynts": u8(sb(NARROW, M)),
+        "yn": bf(M, NARROW), "dxn": bf(M, K), "dwn": bf(1, NARROW, K),
+    }
+    Wflat = W.view(G * N, K)
+
+    # (name, kind, work units, fn) ; kind "gemm": units = flops, "cast": units = bytes
+    cast0 = lambda n_elem: n_elem * CAST_BYTES_PER_ELEM  # noqa: E731
+    ops = [
+        ("cast_dim0 X", "cast", cast0(M * K), lambda: mx.mx_quantize_dim0(X, buf["xq"], buf["xs"])),
+        ("cast_dim0 W", "cast", cast0(G * N * K), lambda: mx.mx_quantize_dim0(Wflat, buf["wq"], buf["ws"])),
+        ("gemm_fwd grouped", "gemm", 2 * M * N * K,
+         lambda: mx.mx_grouped_mm_fwd(buf["xq"], buf["xs"], buf["wq"], buf["ws"], offs, M, N, K, out=buf["y"])),
+        ("cast_dim0 dY", "cast", cast0(M * N), lambda: mx.mx_quantize_dim0(dY, buf["dyq"], buf["dys"])),
+        ("cast_dim1 W", "cast", cast0(G * N * K), lambda: mx.mx_quantize_dim1(W, buf["wtq"], buf["wts"])),
+        ("gemm_dgrad grouped", "gemm", 2 * M * N * K,
+         lambda: mx.mx_grouped_mm_dgrad(buf["dyq"], buf["dys"], buf["wtq"], buf["wts"], offs, M, N, K, out=buf["dx"])),
+        ("cast_dim1 dY", "cast", cast0(M * N), lambda: mx.mx_quantize_dim1(dY, buf["dytq"], buf["dyts"])),
+        ("cast_dim1 X", "cast", cast0(M * K), lambda: mx.mx_quantize_dim1(X, buf["xtq"], buf["xts"])),
+        ("gemm_wgrad grouped", "gemm", 2 * M * N * K,
+         lambda: mx.mx_grouped_mm_wgrad(buf["dytq"], buf["dyts"], buf["xtq"], buf["xts"], offs, M, N, K,
+                                        out=buf["dw"], out_dtype=mx.MX_OUT_BF16)),
+        ("cast_w32 W'", "cast", NARROW * K * W32_BYTES_PER_ELEM, None),  # set below (returns buffers)
+        ("gemm_fwd dense576", "gemm", 2 * M * NARROW * K, None),
+        ("cast_dim0 dY'", "cast", cast0(M * NARROW), lambda: mx.mx_quantize_dim0(dYn, buf["dynq"], buf["dyns"])),
+        ("gemm_dgrad dense576", "gemm", 2 * M * NARROW * K, None),
+        ("cast_dim1 dY'", "cast", cast0(M * NARROW), lambda: mx.mx_quantize_dim1(dYn, buf["dyntq"], buf["dynts"])),
+        ("gemm_wgrad dense576", "gemm", 2 * M * NARROW * K,
+         lambda: mx.mx_grouped_mm_wgrad(buf["dyntq"], buf["dynts"], buf["xtq"], buf["xts"], None, M, NARROW, K,
+                                        out=buf["dwn"], out_dtype=mx.MX_OUT_BF16)),
+    ]
+    w32 = {}
+
+    def cast_w32():
+        w32["q"], w32["qt"], w32["sr"], w32["sc"] = mx.mx_quantize_weight_32x32(Wn)
+
+    ops[9] = (ops[9][0], ops[9][1], ops[9][2], cast_w32)
+    ops[10] = (ops[10][0], ops[10][1], ops[10][2],
+               lambda: mx.mx_grouped_mm_fwd(buf["xq"], buf["xs"], w32["q"], w32["sr"], None, M, NARROW, K,
+                                            out=buf["yn"]))
+    ops[12] = (ops[12][0], ops[12][1], ops[12][2],
+               lambda: mx.mx_grouped_mm_dgrad(buf["dynq"], buf["dyns"], w32["qt"], w32["sc"], None, M, NARROW, K,
+                                              out=buf["dxn"]))
+
+    def step(events=None):
+        for i, (_, _, _, fn) in enumerate(ops):
+            if events is not None:
+                events[i][0].record()
+            fn()
+            if events is not None:
+                events[i][1].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region: exactly `steps` steps, events around every launch on the current stream
+    ev = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)] for _ in ops]
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(ev[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+
+    per_op = {}
+    for i, (name, kind, units, _) in enumerate(ops):
+        ms = float(np.mean([ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(args.steps)]))
+        rate = units / (ms * 1e-3) / (1e12 if kind == "gemm" else 1e9)
+        peak = PEAK_FP8_TFLOPS if kind == "gemm" else PEAK_HBM_GBPS
+        per_op[name] = {"us": round(ms * 1e3, 2), ("tflops" if kind == "gemm" else "gbps"): round(rate, 1),
+                        "frac": round(rate / peak, 4)}
+
+    gemm_flops = sum(u for _, k, u, _ in ops if k == "gemm")
+    cast_bytes = sum(u for _, k, u, _ in ops if k == "cast")
+    gemm_us = sum(per_op[n]["us"] for n, k, _, _ in ops if k == "gemm")
+    cast_us = sum(per_op[n]["us"] for n, k, _, _ in ops if k == "cast")
+    value = gemm_flops / (ms_per_step * 1e-3) / 1e12
+
+    # dominant kernel: the longest launch of the step
+    dom_name, dom_kind, dom_units, _ = max(ops, key=lambda o: per_op[o[0]]["us"])
+    dom = per_op[dom_name]
+    achieved = dom_units / (dom["us"] * 1e-6) / 1e12
+    traffic = load_traffic(dom_name, dom_units)
+    roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_FP8_TFLOPS, 4), "traffic": traffic, "kernel": dom_name,
+                "flops_per_launch": dom_units, "avg_launch_us": dom["us"]}
+
+    cpu = None if args.no_cpu_baseline else cpu_baseline()
+
+    line = {
+        "metric": METRIC, "value": round(value, 1), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "mxfp8 (e4m3 x e4m3, e8m0 block scales, fp32 accumulate)",
+        "data": "synthetic (seeded N(0,sigma) bf16, multinomial group sizes)",
+        "config": {"workload": "moe_g8 fwd+dgrad+wgrad: G=8 experts, M=16384 tokens, K=N=4096, "
+                               "grad_out 16384x4096, plus dense 576x4096 layer (32x32 weight scales, "
+                               "576-wide contraction in dgrad)",
+                   "M": M, "K": K, "N": N, "G": G, "narrow": NARROW, "offs": offs_np.tolist(),
+                   "parallelism": "none (1 GPU)"},
+        "gemm_tflops": round(gemm_flops / (gemm_us * 1e-6) / 1e12, 1),
+        "gemm_frac_of_peak": round(gemm_flops / (gemm_us * 1e-6) / 1e12 / PEAK_FP8_TFLOPS, 4),
+        "cast_gbps": round(cast_bytes / (cast_us * 1e-6) / 1e9, 1),
+        "cast_frac_of_hbm": round(cast_bytes / (cast_us * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4),
+        "step_gemm_gflop": round(gemm_flops / 1e9, 2), "step_cast_gb": round(cast_bytes / 1e9, 4),
+        "roofline": roofline, "cpu_baseline": cpu, "kernels": per_op, "source_hash": src_hash(),
+    }
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline():
+    """The CPU oracle on a bounded slice of the same step, in the same unit.
+
+    Slice: expert 0's weight [4096, 4096] and 2048 token rows routed to it (with
+    their grad_out rows): oracle dim0 and dim1 casts of all three operands, then
+    the float64 forward, dgrad and wgrad. value = GEMM flops / total time.
+    """
+    import threadpoolctl
+
+    from mxfp8_block_scaled_amd import synth
+    from oracle import mx as orc
+
+    r = synth.spawn(0, 6)
+    rows = 2048
+    x = synth.normal_bf16(r[1], (rows, K), 1.0)
+    w = synth.normal_bf16(r[2], (N, K), 0.02)
+    dy = synth.normal_bf16(r[3], (rows, N), 1e-2)
+    t0 = time.perf_counter()
+    xq, xs = orc.quantize_dim0(x)
+    wq, ws = orc.quantize_dim0(w)
+    orc.mx_grouped_mm_fwd(xq, xs, wq, ws, None, 1)
+    dyq, dys = orc.quantize_dim0(dy)
+    wtq, wts = orc.quantize_dim1(w)
+    orc.mx_grouped_mm_fwd(dyq, dys, wtq, wts, None, 1)
+    dytq, dyts = orc.quantize_dim1(dy)
+    xtq, xts = orc.quantize_dim1(x)
+    orc.mx_grouped_mm_wgrad(dytq, dyts, xtq, xts, None, 1)
+    dt = time.perf_counter() - t0
+    flops = 3 * 2 * rows * N * K
+    threads = max([i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()] or [1])
+    return {"value": round(flops / dt / 1e12, 5), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "seconds": round(dt, 2),
+            "sample": f"expert-0 slice: {rows} token rows x W[{N},{K}]; oracle dim0+dim1 casts of X, W, dY and "
+                      "float64 fwd+dgrad+wgrad (numpy; casts single-threaded, BLAS matmul multi-threaded)"}
+
+
+if __name__ == "__main__":
+    main()

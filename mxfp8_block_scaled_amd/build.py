@@ -41,6 +41,12 @@ def build(verbose=False):
         raise RuntimeError("hipcc failed:\n" + out)
     if verbose and out.strip():
         print(out)
+    # every kernel launched from host code must have its host stub defined in the
+    # library; a template whose host-side instantiation failed leaves it undefined
+    nm = subprocess.run(["nm", "-D", "--undefined-only", tmp], capture_output=True, text=True)
+    missing = [ln.split()[-1] for ln in nm.stdout.splitlines() if "_ZN2mx" in ln]
+    if missing:
+        raise RuntimeError("libmxfp8.so would have undefined kernel symbols: " + ", ".join(missing))
     os.replace(tmp, LIB)
     return LIB
 

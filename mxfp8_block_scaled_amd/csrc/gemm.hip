@@ -38,250 +38,424 @@ struct GemmArgs {
                     // K-grouped: M = rows of A, N = rows of B, K = contraction (tokens)
   int64_t ldo;      // output row pitch (elements)
   int64_t mt_total, nt;  // tile grid: m-tiles (upper bound for M-grouped), n-tiles
+  int64_t tiles;         // logical tiles (some M-grouped ones may be empty)
   int groups;
 };
 
-template <int BM, int BN, int BK, int WAVES_M, int WAVES_N>
+// Block tile BM x BN, 4 waves as 2 x 2, each wave (BM/2) x (BN/2) in 32x32 MFMA
+// tiles; the contraction advances 64 elements (one MFMA k-step) per pipeline stage.
+template <int BM, int BN>
 struct Cfg {
-  static constexpr int THREADS = 64 * WAVES_M * WAVES_N;
-  static constexpr int WM = BM / WAVES_M;  // rows per wave
-  static constexpr int WN = BN / WAVES_N;
-  static constexpr int TM = WM / 32;  // 32x32 MFMA tiles per wave
-  static constexpr int TN = WN / 32;
-  static constexpr int KSTEPS = BK / 64;
-  static constexpr int CHUNKS_ROW = BK / 16;
-  static constexpr int A_CHUNKS = BM * CHUNKS_ROW / THREADS;  // 16-byte chunks per thread
-  static constexpr int B_CHUNKS = BN * CHUNKS_ROW / THREADS;
-  static constexpr int A_BYTES = BM * BK;
-  static constexpr int B_BYTES = BN * BK;
-  static_assert(BK == 128, "scale handling assumes two 128-wide k-tiles per 256-wide scale tile");
-  static_assert(A_CHUNKS * THREADS == BM * CHUNKS_ROW && B_CHUNKS * THREADS == BN * CHUNKS_ROW, "");
+  static constexpr int THREADS = 256;
+  static constexpr int BK = 64;
+  static constexpr int NST = 4;  // LDS ring depth: stages in flight
+  static constexpr int WM = BM / 2, WN = BN / 2;
+  static constexpr int TM = WM / 32, TN = WN / 32;
+  static constexpr int A_BYTES = BM * BK, B_BYTES = BN * BK;
+  static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
+  // scale tiles of one 256-wide window: A bands then B bands, 256 B each; two
+  // windows are resident (the one in use and the next)
+  static constexpr int BANDS = (BM + BN) / 32;
+  static constexpr int SC_BYTES = BANDS * 256;
+  static constexpr int LDS_BYTES = NST * STAGE_BYTES + 2 * SC_BYTES;
+  // per wave and stage: A and B rows in 1 KB loads (16 rows x 64 B); per window:
+  // one 1 KB load (four 256-byte scale tiles) by each of the first SC_WAVES waves
+  static constexpr int A_LOADS = BM / 64, B_LOADS = BN / 64;
+  static constexpr int AB_LOADS = A_LOADS + B_LOADS;
+  static constexpr int SC_WAVES = BANDS / 4;
+  // epilogue staging: each wave owns STAGE_BYTES / 4 of the ring slot NST - 1
+  static constexpr int EPI_WAVE_BYTES = STAGE_BYTES / 4;
+  static_assert(BM == BN && BANDS % 8 == 0 && SC_WAVES <= 4, "scale loads assume square tiles");
+  static_assert(TM % 2 == 0 && 2 * AB_LOADS + 2 < 64, "");
+  static_assert(EPI_WAVE_BYTES >= 4096, "an fp32 32x32 tile must fit the wave's staging area");
 };
 
-// XOR swizzle of the 16-byte chunk within a row (8 chunks per 128-byte row).
-__device__ inline int lds_off(int row, int kc) { return row * 128 + ((kc ^ (row & 7)) << 4); }
+// LDS holds each 64-byte row (four 16-byte chunks of one k-step) with chunk c of
+// row r at slot c ^ ((r >> 2) & 3): sixteen consecutive rows reading the same chunk
+// then hit sixteen different 16-byte bank groups.
 
 __device__ inline int32_t group_start(const int32_t* offs, int g) { return g == 0 ? 0 : offs[g - 1]; }
 
-template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int MODE, int OUT_BF16>
-__global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm(GemmArgs p) {
-  using C = Cfg<BM, BN, BK, WAVES_M, WAVES_N>;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2][C::A_BYTES + C::B_BYTES];
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
+// vmcnt bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]).
+#define MX_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (((n) >> 4) << 14) | (0x7 << 4) | (0xF << 8))
 
-  const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63, h = l >> 5;
-  const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-  // ---- tile id: spread consecutive tiles over one XCD (blocks are dealt
-  // round-robin to the 8 XCDs), then a grouped raster of 8 m-tiles.
-  const int64_t nblk = gridDim.x, bid = blockIdx.x;
-  const int64_t per_xcd = nblk / 8;
-  const int64_t lid = bid < per_xcd * 8 ? (bid % 8) * per_xcd + bid / 8 : bid;
+// One output tile: where it sits and what it contracts over.
+struct Tile {
+  int64_t a_row0, a_row_end, b_row0, b_row_end, k_beg, k_end, col0;
+  uint8_t* out_base;
+  bool valid;
+};
 
+// Persistent blocks (one per compute unit) walk the logical tiles. Blocks are dealt
+// round-robin to the 8 XCDs, so XCD x takes the contiguous tile range
+// [x * per_xcd, (x+1) * per_xcd) and its blocks advance through it together; with
+// a raster of GM m-tiles by all n-tiles, the ~32 tiles in flight on one XCD share
+// their A and B slices in its L2.
+template <int BM, int BN, int MODE, int OUT_BF16>
+__device__ inline Tile tile_at(const GemmArgs& p, int64_t t) {
+  constexpr int64_t GM = 4;
+  constexpr int out_es = OUT_BF16 ? 2 : 4;
+  Tile T{};
+  T.out_base = (uint8_t*)p.out;
+  const int64_t per_g = p.mt_total * p.nt;
+  int64_t r = t;
   int g = 0;
-  int64_t m_tile, n_tile;
-  int64_t a_row0, a_row_end, b_row0, b_row_end, k_beg, k_end, out_row0;
-  uint8_t* out_base = (uint8_t*)p.out;
-  const int out_es = OUT_BF16 ? 2 : 4;
+  if (MODE == MODE_KGROUP) {
+    g = (int)(t / per_g);
+    r = t % per_g;
+  }
+  const int64_t band = r / (GM * p.nt);
+  const int64_t first_m = band * GM;
+  const int64_t gm = p.mt_total - first_m < GM ? p.mt_total - first_m : GM;
+  const int64_t in_band = r % (GM * p.nt);
+  const int64_t mt = first_m + in_band % gm;
+  const int64_t n_tile = in_band / gm;
+  T.col0 = n_tile * BN;
   if (MODE == MODE_MGROUP) {
-    const int64_t GM = 8;
-    const int64_t band = lid / (GM * p.nt);
-    const int64_t first_m = band * GM;
-    const int64_t gm = p.mt_total - first_m < GM ? p.mt_total - first_m : GM;
-    const int64_t in_band = lid % (GM * p.nt);
-    const int64_t mt_glob = first_m + in_band % gm;
-    n_tile = in_band / gm;
-    // find the group that owns this m-tile
+    // find the group owning m-tile `mt` of the concatenated per-group tile lists
     int64_t cum = 0;
     int found = -1;
-    int64_t local = 0;
     const int G = p.offs ? p.groups : 1;
     for (int gg = 0; gg < G; ++gg) {
       const int64_t s = p.offs ? group_start(p.offs, gg) : 0;
       const int64_t e = p.offs ? p.offs[gg] : p.M;
       const int64_t tiles = (e - s + BM - 1) / BM;
-      if (mt_glob < cum + tiles) {
+      if (mt < cum + tiles) {
         found = gg;
-        local = mt_glob - cum;
-        a_row0 = s + local * BM;
-        a_row_end = e;
+        T.a_row0 = s + (mt - cum) * BM;
+        T.a_row_end = e;
         break;
       }
       cum += tiles;
     }
-    if (found < 0) return;
-    g = found;
-    m_tile = local;
-    b_row0 = (int64_t)g * p.N + n_tile * BN;
-    b_row_end = (int64_t)g * p.N + p.N;
-    k_beg = 0;
-    k_end = p.K;
-    out_row0 = a_row0;
+    T.valid = found >= 0;
+    g = found < 0 ? 0 : found;
+    T.b_row0 = (int64_t)g * p.N + n_tile * BN;
+    T.b_row_end = (int64_t)g * p.N + p.N;
+    T.k_beg = 0;
+    T.k_end = p.K;
   } else {
-    const int64_t per_g = p.mt_total * p.nt;
-    g = (int)(lid / per_g);
-    const int64_t r = lid % per_g;
-    const int64_t GM = 8;
-    const int64_t band = r / (GM * p.nt);
-    const int64_t first_m = band * GM;
-    const int64_t gm = p.mt_total - first_m < GM ? p.mt_total - first_m : GM;
-    const int64_t in_band = r % (GM * p.nt);
-    m_tile = first_m + in_band % gm;
-    n_tile = in_band / gm;
-    a_row0 = m_tile * BM;
-    a_row_end = p.M;
-    b_row0 = n_tile * BN;
-    b_row_end = p.N;
-    k_beg = p.offs ? group_start(p.offs, g) : 0;
-    k_end = p.offs ? p.offs[g] : p.K;
-    out_row0 = a_row0;
-    out_base += (int64_t)g * p.M * p.ldo * out_es;
+    T.valid = true;
+    T.a_row0 = mt * BM;
+    T.a_row_end = p.M;
+    T.b_row0 = n_tile * BN;
+    T.b_row_end = p.N;
+    T.k_beg = p.offs ? group_start(p.offs, g) : 0;
+    T.k_end = p.offs ? p.offs[g] : p.K;
+    T.out_base += (int64_t)g * p.M * p.ldo * out_es;
   }
-  const int64_t col0 = n_tile * BN;                            // output column of the tile
-  const int64_t n_limit = MODE == MODE_MGROUP ? p.N : p.N;     // columns per output row
+  return T;
+}
 
-  // ---- global -> register staging (16-byte chunks) --------------------------------
-  u32x4 ra[C::A_CHUNKS], rb[C::B_CHUNKS];
-  auto load_tile = [&](int64_t k0) {
-#pragma unroll
-    for (int i = 0; i < C::A_CHUNKS; ++i) {
-      const int id = tid + i * C::THREADS;
-      const int row = id / C::CHUNKS_ROW, kc = id % C::CHUNKS_ROW;
-      const int64_t gr = a_row0 + row, kk = k0 + kc * 16;
-      ra[i] = (u32x4){0, 0, 0, 0};
-      if (gr < a_row_end && gr < p.a_rows && kk >= k_beg && kk < k_end) ra[i] = *(const u32x4*)(p.a + gr * p.lda + kk);
-    }
-#pragma unroll
-    for (int i = 0; i < C::B_CHUNKS; ++i) {
-      const int id = tid + i * C::THREADS;
-      const int row = id / C::CHUNKS_ROW, kc = id % C::CHUNKS_ROW;
-      const int64_t gr = b_row0 + row, kk = k0 + kc * 16;
-      rb[i] = (u32x4){0, 0, 0, 0};
-      if (gr < b_row_end && gr < p.b_rows && kk >= k_beg && kk < k_end) rb[i] = *(const u32x4*)(p.b + gr * p.ldb + kk);
-    }
-  };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < C::A_CHUNKS; ++i) {
-      const int id = tid + i * C::THREADS;
-      const int row = id / C::CHUNKS_ROW, kc = id % C::CHUNKS_ROW;
-      *(u32x4*)(&lds[buf][lds_off(row, kc)]) = ra[i];
-    }
-#pragma unroll
-    for (int i = 0; i < C::B_CHUNKS; ++i) {
-      const int id = tid + i * C::THREADS;
-      const int row = id / C::CHUNKS_ROW, kc = id % C::CHUNKS_ROW;
-      *(u32x4*)(&lds[buf][C::A_BYTES + lds_off(row, kc)]) = rb[i];
-    }
-  };
+// Tile order: blocks are dealt round-robin to the 8 XCDs, so the remap gives each
+// XCD a contiguous range of logical tiles; with the GM-band raster of tile_at, the
+// ~32 tiles resident on one XCD share their A and B slices in its L2.
+__device__ inline int64_t xcd_remap(int64_t bid, int64_t nblk) {
+  const int64_t per_xcd = nblk / 8;
+  return bid < per_xcd * 8 ? (bid % 8) * per_xcd + bid / 8 : bid;
+}
 
-  // ---- scales: one dword per lane per 32-row tile per 256-wide k window ----------
+template <int BM, int BN, int MODE, int OUT_BF16>
+__global__ __launch_bounds__(256) void k_gemm(GemmArgs p) {
+  using C = Cfg<BM, BN>;
+  constexpr int NST = C::NST, BK = C::BK;
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+
+  const int tid = threadIdx.x, l = tid & 63, h = l >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+  const int wm = wave >> 1, wn = wave & 1;
+  const Tile T = tile_at<BM, BN, MODE, OUT_BF16>(p, xcd_remap(blockIdx.x, gridDim.x));
+  if (!T.valid) return;
+
   const int64_t a_bands = (p.a_rows + 31) / 32, b_bands = (p.b_rows + 31) / 32;
-  auto load_scale = [&](const uint8_t* s, int64_t row0, int64_t bands, int64_t ktiles, int64_t kwin) -> unsigned {
-    const int64_t band = row0 / 32;
-    if (band >= bands) return 0x7f7f7f7fu;
-    return *(const unsigned*)(s + scale_tile_base(band, kwin, ktiles) + 4 * l);
+  const __amdgpu_buffer_rsrc_t as_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)p.a_s, (short)0, (int)(a_bands * p.a_ktiles * 256), 0x00020000);
+  const __amdgpu_buffer_rsrc_t bs_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)p.b_s, (short)0, (int)(b_bands * p.b_ktiles * 256), 0x00020000);
+  const int kc_l = (l & 3) ^ (l >> 4);
+  const int a_row_l = wave * (BM / 4) + (l >> 2), b_row_l = wave * (BN / 4) + (l >> 2);
+  // Per-lane offsets are fixed for a tile (row and chunk); the contraction position
+  // goes in the scalar offset. Lanes whose chunk lies outside [k_beg, k_end) in a
+  // given stage switch to an out-of-range offset, which reads as zero.
+  const unsigned a_off0 = (unsigned)(a_row_l * p.lda + kc_l * 16), a_offq = (unsigned)(16 * p.lda);
+  const unsigned b_off0 = (unsigned)(b_row_l * p.ldb + kc_l * 16), b_offq = (unsigned)(16 * p.ldb);
+  const bool has_sc = wave < C::SC_WAVES;  // this wave loads four scale tiles per window
+  const int sc_band = wave * 4 + (l >> 4);  // index in the A-then-B band list
+  const bool sc_is_a = wave < C::SC_WAVES / 2;  // square tiles: the first half of the list is A's
+
+  // contraction steps of BK from the 256-aligned position at or below k_beg (a scale
+  // window boundary: every fourth stage opens a window; stages before k_beg are
+  // masked to zero)
+  const int64_t k_first = (T.k_beg / 256) * 256;
+  const int64_t n_iter = T.k_end > T.k_beg ? (T.k_end - k_first + BK - 1) / BK : 0;
+  const int kb32 = (int)T.k_beg, ke32 = (int)T.k_end;  // contraction lengths are < 2^31
+  // Raw buffer descriptors span exactly the valid rows of the tile, so rows past the
+  // group / matrix end read as zero.
+  const int64_t a_lim = T.a_row_end < p.a_rows ? T.a_row_end : p.a_rows;
+  const int64_t b_lim = T.b_row_end < p.b_rows ? T.b_row_end : p.b_rows;
+  const int64_t a_valid = a_lim > T.a_row0 ? (a_lim - T.a_row0 < BM ? a_lim - T.a_row0 : BM) : 0;
+  const int64_t b_valid = b_lim > T.b_row0 ? (b_lim - T.b_row0 < BN ? b_lim - T.b_row0 : BN) : 0;
+  const __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(p.a + T.a_row0 * p.lda), (short)0, (int)(a_valid * p.lda), 0x00020000);
+  const __amdgpu_buffer_rsrc_t b_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(p.b + T.b_row0 * p.ldb), (short)0, (int)(b_valid * p.ldb), 0x00020000);
+  const int64_t sc_row_band = sc_is_a ? T.a_row0 / 32 + sc_band : T.b_row0 / 32 + (sc_band - BM / 32);
+  const int64_t sc_ktiles = sc_is_a ? p.a_ktiles : p.b_ktiles;
+  const unsigned sc_off = sc_row_band < (sc_is_a ? a_bands : b_bands)
+                              ? (unsigned)(sc_row_band * sc_ktiles * 256 + (l & 15) * 16)
+                              : 0x80000000u;
+
+  // Every step issues the A/B loads of one stage (C::AB_LOADS per wave) plus, when
+  // that stage opens a 256-wide scale window, one scale load by each of the first
+  // C::SC_WAVES waves. A stage past the end of the contraction (`live` false)
+  // issues the same loads out of range: they read nothing and only fill LDS that is
+  // never consumed, so the counter arithmetic is the same on every step.
+  auto opens_window = [&](int64_t s_idx) -> bool { return (s_idx & 3) == 0; };  // k_first is 256-aligned
+  auto issue_stage = [&](int64_t s_idx, bool live) {
+    const int64_t k0 = k_first + s_idx * BK;
+    uint8_t* st = lds + (int)(s_idx % NST) * C::STAGE_BYTES;
+    const int kk = (int)k0 + kc_l * 16;
+    const bool drop = !live || kk < kb32 || kk >= ke32;  // this lane's chunk is masked
+    const int soff = live ? (int)k0 : 0;
+#pragma unroll
+    for (int q = 0; q < C::A_LOADS; ++q)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, (lds_ptr_t)(st + wave * (BM / 4) * 64 + q * 1024), 16,
+                                               drop ? 0x80000000u : a_off0 + q * a_offq, soff, 0, 0);
+#pragma unroll
+    for (int q = 0; q < C::B_LOADS; ++q)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(b_rsrc, (lds_ptr_t)(st + C::A_BYTES + wave * (BN / 4) * 64 + q * 1024),
+                                               16, drop ? 0x80000000u : b_off0 + q * b_offq, soff, 0, 0);
+    if (has_sc && opens_window(s_idx)) {
+      const int64_t kwin = k0 / 256;
+      uint8_t* dst = lds + NST * C::STAGE_BYTES + (int)(kwin & 1) * C::SC_BYTES + wave * 1024;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(sc_is_a ? as_rsrc : bs_rsrc, (lds_ptr_t)dst, 16,
+                                               live ? sc_off : 0x80000000u, live ? (int)(kwin * 256) : 0, 0, 0);
+    }
+  };
+  // loads this wave issues for stages s_idx+1 .. last (all issued)
+  auto loads_after = [&](int64_t s_idx, int64_t last) -> int {
+    int n = 0;
+    for (int64_t q = s_idx + 1; q <= last; ++q) n += C::AB_LOADS + (has_sc && opens_window(q) ? 1 : 0);
+    return n;
+  };
+  auto wait_n = [&](int n) {  // s_waitcnt needs an immediate; n takes one of a few values
+    if (n >= 2 * C::AB_LOADS + 1) MX_WAIT_VMCNT(2 * C::AB_LOADS + 1);
+    else if (n == 2 * C::AB_LOADS) MX_WAIT_VMCNT(2 * C::AB_LOADS);
+    else if (n == C::AB_LOADS + 1) MX_WAIT_VMCNT(C::AB_LOADS + 1);
+    else if (n == C::AB_LOADS) MX_WAIT_VMCNT(C::AB_LOADS);
+    else MX_WAIT_VMCNT(0);
+  };
+
+  // ---- fragments: lane reads chunks h and h+2 of its row (32 bytes) ---------------
+  const int frow = l & 31;
+  const int sw = (frow >> 2) & 3;
+  const int off_lo = frow * 64 + ((h ^ sw) << 4), off_hi = frow * 64 + (((h + 2) ^ sw) << 4);
+  struct Frag {
+    v8i a[C::TM], b[C::TN];
+    unsigned sa[C::TM], sb[C::TN];
+  };
+  auto read_frags = [&](Frag& f, int buf, int64_t k0) {
+    const uint8_t* st = lds + buf * C::STAGE_BYTES;
+    const uint8_t* sc = lds + NST * C::STAGE_BYTES + (int)((k0 >> 8) & 1) * C::SC_BYTES;
+    const uint8_t* la = st + wm * C::WM * 64;
+    const uint8_t* lb = st + C::A_BYTES + wn * C::WN * 64;
+    const int sh = (int)((k0 >> 6) & 3) * 8;  // byte of the window dword for this k-step
+#pragma unroll
+    for (int j = 0; j < C::TN; ++j) {
+      u32x4 lo = *(const u32x4*)(lb + j * 2048 + off_lo);
+      u32x4 hi = *(const u32x4*)(lb + j * 2048 + off_hi);
+      f.b[j] = (v8i){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      f.sb[j] = *(const unsigned*)(sc + (BM / 32 + wn * C::TN + j) * 256 + 4 * l) >> sh;
+    }
+#pragma unroll
+    for (int i = 0; i < C::TM; ++i) {
+      u32x4 lo = *(const u32x4*)(la + i * 2048 + off_lo);
+      u32x4 hi = *(const u32x4*)(la + i * 2048 + off_hi);
+      f.a[i] = (v8i){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      f.sa[i] = *(const unsigned*)(sc + (wm * C::TM + i) * 256 + 4 * l) >> sh;
+    }
   };
 
   v16f acc[C::TM][C::TN];
+  auto mfma_rows = [&](const Frag& f, int i0, int i1) {
+#pragma unroll
+    for (int i = i0; i < i1; ++i)
+#pragma unroll
+      for (int j = 0; j < C::TN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.a[i], f.b[j], acc[i][j], 0, 0, 0, (int)f.sa[i],
+                                                                    0, (int)f.sb[j]);
+  };
+
+  // One pipeline step over an NST-deep LDS ring. Step `it` issues stage it+NST-1,
+  // runs the first half of stage it's MFMAs, waits for its own loads of stage it+1
+  // (at most NST-2 later stages stay in flight), meets the other waves at a barrier
+  // (so stage it+1 is complete in LDS and every wave is past stage it-1, whose slot
+  // the next issue overwrites), then reads stage it+1's fragments interleaved with
+  // the second half of stage it's MFMAs.
+  auto step = [&](int64_t it, int slot, const Frag& cur, Frag& nxt) {
+    issue_stage(it + NST - 1, it + NST - 1 < n_iter);
+    mfma_rows(cur, 0, C::TM / 2);
+    // spread the loads over the MFMAs so no load waits in front of an idle matrix core
+#pragma unroll
+    for (int q = 0; q < C::TM / 2 * C::TN; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // VALU (load offsets)
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    wait_n(loads_after(it + 1, it + NST - 1));
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    read_frags(nxt, (slot + 1) % NST, k_first + (it + 1) * BK);
+    mfma_rows(cur, C::TM / 2, C::TM);
+    // interleave: one MFMA, then three LDS reads
+#pragma unroll
+    for (int q = 0; q < C::TM / 2 * C::TN; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // ---- epilogue: stage each 32x32 tile through LDS, write 16 bytes per lane --------
+  // Lane l holds column l % 32 of each MFMA tile, rows 8*(v/4) + 4*h + v%4.
+  uint8_t* epi = lds + (NST - 1) * C::STAGE_BYTES + wave * C::EPI_WAVE_BYTES;
+  auto epilogue = [&]() {
+    const int64_t row_limit = MODE == MODE_MGROUP ? T.a_row_end : p.M;
+    constexpr int ES = OUT_BF16 ? 2 : 4;
+    constexpr int TILE_BYTES = 32 * 32 * ES;
+    constexpr int NBUF = C::EPI_WAVE_BYTES / TILE_BYTES;
+    constexpr int ROW_BYTES = 32 * ES;          // one row of a 32x32 tile
+    constexpr int LPR = ROW_BYTES / 16;         // lanes per row (16 bytes each)
+    constexpr int ROWS_PER_PASS = 64 / LPR;
+#pragma unroll
+    for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+      for (int j = 0; j < C::TN; ++j) {
+        uint8_t* buf = epi + ((i * C::TN + j) % NBUF) * TILE_BYTES;
+        if (OUT_BF16) {
+          // lanes 2c, 2c+1 swap values so each writes two adjacent columns of one row
+          const int odd = l & 1;
+#pragma unroll
+          for (int v = 0; v < 16; v += 2) {
+            const float m0 = acc[i][j][v], m1 = acc[i][j][v + 1];
+            const float send = odd ? m0 : m1;
+            const float recv = __builtin_bit_cast(float, dpp_xor1(__builtin_bit_cast(unsigned, send)));
+            const float lo = odd ? recv : m0, hi = odd ? m1 : recv;
+            const unsigned packed = (unsigned)f32_to_bf16_rne(lo) | ((unsigned)f32_to_bf16_rne(hi) << 16);
+            const int row = 8 * (v >> 2) + 4 * h + (v & 3) + odd;
+            *(unsigned*)(buf + row * ROW_BYTES + ((l & 31) & ~1) * 2) = packed;
+          }
+        } else {
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int row = 8 * (v >> 2) + 4 * h + (v & 3);
+            *(float*)(buf + row * ROW_BYTES + (l & 31) * 4) = acc[i][j][v];
+          }
+        }
+        const int64_t trow = T.a_row0 + wm * C::WM + 32 * i;
+        const int64_t tcol = T.col0 + wn * C::WN + 32 * j;
+        const int cl = (l % LPR) * (16 / ES);  // first column of this lane's 16 bytes
+#pragma unroll
+        for (int pass = 0; pass < 32 / ROWS_PER_PASS; ++pass) {
+          const int r = pass * ROWS_PER_PASS + l / LPR;
+          const u32x4 d = *(const u32x4*)(buf + r * ROW_BYTES + (l % LPR) * 16);
+          const int64_t row = trow + r, col = tcol + cl;
+          uint8_t* dst = T.out_base + (row * p.ldo + col) * ES;
+          if (row < row_limit) {
+            if (col + 16 / ES <= p.N && ((p.ldo * ES) & 15) == 0) {
+              *(u32x4*)dst = d;
+            } else {
+              const unsigned w4[4] = {d.x, d.y, d.z, d.w};
+#pragma unroll
+              for (int e = 0; e < 16 / ES; ++e)
+                if (col + e < p.N) {
+                  if (OUT_BF16)
+                    ((uint16_t*)dst)[e] = (uint16_t)(w4[e / 2] >> (16 * (e & 1)));
+                  else
+                    ((unsigned*)dst)[e] = w4[e];
+                }
+            }
+          }
+        }
+      }
+  };
+
+  // ---- main loop -------------------------------------------------------------------
 #pragma unroll
   for (int i = 0; i < C::TM; ++i)
 #pragma unroll
     for (int j = 0; j < C::TN; ++j) acc[i][j] = (v16f){};
-
-  const int64_t k_first = (k_beg / BK) * BK;
-  const int64_t n_iter = k_end > k_beg ? (k_end - k_first + BK - 1) / BK : 0;
-
   if (n_iter > 0) {
-    load_tile(k_first);
-    store_tile(0);
-  }
-  __syncthreads();
-  unsigned sa[C::TM], sb[C::TN];
-  for (int64_t it = 0; it < n_iter; ++it) {
-    const int buf = (int)(it & 1);
-    const int64_t k0 = k_first + it * BK;
-    if (it + 1 < n_iter) load_tile(k0 + BK);
-    const int64_t kwin = k0 / 256;
-    const int shift = (k0 & 255) ? 16 : 0;
-#pragma unroll
-    for (int i = 0; i < C::TM; ++i)
-      sa[i] = load_scale(p.a_s, a_row0 + wm * C::WM + 32 * i, a_bands, p.a_ktiles, kwin) >> shift;
-#pragma unroll
-    for (int j = 0; j < C::TN; ++j)
-      sb[j] = load_scale(p.b_s, b_row0 + wn * C::WN + 32 * j, b_bands, p.b_ktiles, kwin) >> shift;
-
-    const uint8_t* la = &lds[buf][0];
-    const uint8_t* lb = &lds[buf][C::A_BYTES];
-#pragma unroll
-    for (int s = 0; s < C::KSTEPS; ++s) {
-      v8i fa[C::TM], fb[C::TN];
-#pragma unroll
-      for (int i = 0; i < C::TM; ++i) {
-        const int row = wm * C::WM + 32 * i + (l & 31);
-        u32x4 lo = *(const u32x4*)(la + lds_off(row, 4 * s + h));
-        u32x4 hi = *(const u32x4*)(la + lds_off(row, 4 * s + 2 + h));
-        fa[i] = (v8i){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-      }
-#pragma unroll
-      for (int j = 0; j < C::TN; ++j) {
-        const int row = wn * C::WN + 32 * j + (l & 31);
-        u32x4 lo = *(const u32x4*)(lb + lds_off(row, 4 * s + h));
-        u32x4 hi = *(const u32x4*)(lb + lds_off(row, 4 * s + 2 + h));
-        fb[j] = (v8i){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-      }
-#pragma unroll
-      for (int i = 0; i < C::TM; ++i)
-#pragma unroll
-        for (int j = 0; j < C::TN; ++j) {
-          if (s == 0)
-            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[i], fb[j], acc[i][j], 0, 0, 0, (int)sa[i], 0,
-                                                                        (int)sb[j]);
-          else
-            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[i], fb[j], acc[i][j], 0, 0, 1, (int)sa[i], 1,
-                                                                        (int)sb[j]);
-        }
+    for (int s = 0; s < NST - 1; ++s) issue_stage(s, s < n_iter);
+    wait_n(loads_after(0, NST - 2));
+    __builtin_amdgcn_s_barrier();
+    // The main loop is unrolled by the ring depth, so ring slots are compile-time
+    // constants, and alternates two register sets, so no fragment is ever copied.
+    Frag f0, f1;
+    read_frags(f0, 0, k_first);
+    int64_t it = 0;
+    for (; it + NST <= n_iter; it += NST) {
+      step(it, 0, f0, f1);
+      step(it + 1, 1, f1, f0);
+      step(it + 2, 2, f0, f1);
+      step(it + 3, 3, f1, f0);
     }
-    if (it + 1 < n_iter) store_tile(buf ^ 1);
-    __syncthreads();
-  }
-
-  // ---- epilogue --------------------------------------------------------------------
-  const int64_t row_limit = MODE == MODE_MGROUP ? a_row_end : p.M;
-#pragma unroll
-  for (int i = 0; i < C::TM; ++i)
-#pragma unroll
-    for (int j = 0; j < C::TN; ++j) {
-      const int64_t col = col0 + wn * C::WN + 32 * j + (l & 31);
-      if (col >= n_limit) continue;
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int64_t row = out_row0 + wm * C::WM + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3);
-        if (row >= row_limit) continue;
-        if (OUT_BF16)
-          ((uint16_t*)out_base)[row * p.ldo + col] = f32_to_bf16_rne(acc[i][j][v]);
-        else
-          ((float*)out_base)[row * p.ldo + col] = acc[i][j][v];
-      }
+    for (; it < n_iter; ++it) {  // 0 to 3 remaining steps
+      step(it, (int)(it % NST), f0, f1);
+      f0 = f1;
     }
+    MX_WAIT_VMCNT(0);  // every load has landed
+    __builtin_amdgcn_s_barrier();  // every wave is done with the ring
+  }
+  epilogue();
 }
 
 }  // namespace mx
 
 namespace {
-constexpr int BM = 128, BN = 128, BK = 128, WAVES_M = 2, WAVES_N = 2;
+
+// Tile configurations: 256x256 for large problems; 128x128 where 256x256 tiles
+// would leave most compute units idle.
+template <int BM, int BN, int MODE>
+hipError_t launch_cfg(mx::GemmArgs p, int out_bf16, hipStream_t stream) {
+  using C = mx::Cfg<BM, BN>;
+  const int64_t mt_extra = (MODE == mx::MODE_MGROUP && p.offs) ? p.groups : 0;
+  p.mt_total = (p.M + BM - 1) / BM + mt_extra;
+  p.nt = (p.N + BN - 1) / BN;
+  p.tiles = MODE == mx::MODE_MGROUP ? p.mt_total * p.nt : (int64_t)p.groups * p.mt_total * p.nt;
+  if (p.tiles == 0) return hipSuccess;
+  const int64_t blocks = p.tiles;
+  const size_t lds = (size_t)C::LDS_BYTES;
+  static bool attr_set[2] = {false, false};
+  hipError_t e = hipSuccess;
+  if (out_bf16) {
+    if (!attr_set[1])
+      e = hipFuncSetAttribute((const void*)mx::k_gemm<BM, BN, MODE, 1>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)lds);
+    if (e != hipSuccess) return e;
+    attr_set[1] = true;
+    hipLaunchKernelGGL((mx::k_gemm<BM, BN, MODE, 1>), dim3((unsigned)blocks), dim3(C::THREADS), lds, stream, p);
+  } else {
+    if (!attr_set[0])
+      e = hipFuncSetAttribute((const void*)mx::k_gemm<BM, BN, MODE, 0>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)lds);
+    if (e != hipSuccess) return e;
+    attr_set[0] = true;
+    hipLaunchKernelGGL((mx::k_gemm<BM, BN, MODE, 0>), dim3((unsigned)blocks), dim3(C::THREADS), lds, stream, p);
+  }
+  return hipGetLastError();
+}
 
 template <int MODE>
 hipError_t launch(mx::GemmArgs& p, int out_bf16, hipStream_t stream) {
-  const int64_t blocks = MODE == mx::MODE_MGROUP ? p.mt_total * p.nt : (int64_t)p.groups * p.mt_total * p.nt;
-  if (blocks == 0) return hipSuccess;
-  const int threads = 64 * WAVES_M * WAVES_N;
-  if (out_bf16)
-    hipLaunchKernelGGL((mx::k_gemm<BM, BN, BK, WAVES_M, WAVES_N, MODE, 1>), dim3((unsigned)blocks), dim3(threads), 0,
-                       stream, p);
-  else
-    hipLaunchKernelGGL((mx::k_gemm<BM, BN, BK, WAVES_M, WAVES_N, MODE, 0>), dim3((unsigned)blocks), dim3(threads), 0,
-                       stream, p);
-  return hipGetLastError();
+  const int64_t groups_tiles = MODE == mx::MODE_KGROUP ? p.groups : 1;
+  const int64_t big_tiles = groups_tiles * ((p.M + 255) / 256) * ((p.N + 255) / 256);
+  if (big_tiles >= 512) return launch_cfg<256, 256, MODE>(p, out_bf16, stream);
+  return launch_cfg<128, 128, MODE>(p, out_bf16, stream);
 }
 }  // namespace
 
@@ -296,8 +470,6 @@ hipError_t mx_launch_gemm_mgroup(const uint8_t* a, const uint8_t* a_s, const uin
   p.a_ktiles = p.b_ktiles = mx::scale_tiles_k(k / 32);
   p.M = m; p.N = n; p.K = k; p.ldo = n;
   p.groups = groups;
-  p.mt_total = (m + BM - 1) / BM + (offs ? groups : 0);
-  p.nt = (n + BN - 1) / BN;
   return launch<mx::MODE_MGROUP>(p, out_bf16, stream);
 }
 
@@ -312,7 +484,5 @@ hipError_t mx_launch_gemm_kgroup(const uint8_t* a, const uint8_t* a_s, const uin
   p.a_ktiles = p.b_ktiles = mx::scale_tiles_k(k / 32);
   p.M = m; p.N = n; p.K = k; p.ldo = n;
   p.groups = groups;
-  p.mt_total = (m + BM - 1) / BM;
-  p.nt = (n + BN - 1) / BN;
   return launch<mx::MODE_KGROUP>(p, out_bf16, stream);
 }
