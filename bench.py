@@ -45,6 +45,10 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", default=None,
+                    help="run only the ops of the step whose name contains this text (for counter runs)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run a 1 GiB device-to-device copy instead (reference for HBM byte counters)")
     return ap.parse_args()
 
 
@@ -83,6 +87,15 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(args.warmup + args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_each_way": 1 << 30, "copies": args.warmup + args.steps}))
+        return
 
     def to_dev(bits):
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
@@ -148,6 +161,20 @@ def main():
     ops[12] = (ops[12][0], ops[12][1], ops[12][2],
                lambda: mx.mx_grouped_mm_dgrad(buf["dynq"], buf["dyns"], w32["qt"], w32["sc"], None, M, NARROW, K,
                                               out=buf["dxn"]))
+
+    if args.only:
+        # the casts an op depends on still run once, untimed, so its inputs exist
+        for _, _, _, fn in ops:
+            fn()
+        torch.cuda.synchronize()
+        sel = [o for o in ops if args.only in o[0]]
+        assert sel, f"no op matches {args.only!r}"
+        for _ in range(args.warmup + args.steps):
+            for _, _, _, fn in sel:
+                fn()
+        torch.cuda.synchronize()
+        print(json.dumps({"only": [o[0] for o in sel], "launches": args.warmup + args.steps}))
+        return
 
     def step(events=None):
         for i, (_, _, _, fn) in enumerate(ops):
