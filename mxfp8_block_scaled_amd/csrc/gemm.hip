@@ -56,16 +56,17 @@ struct Cfg {
   // scale tiles of one 256-wide window: A bands then B bands, 256 B each; two
   // windows are resident (the one in use and the next)
   static constexpr int BANDS = (BM + BN) / 32;
-  static constexpr int SC_BYTES = BANDS * 256;
+  static constexpr int SC_BYTES = 4096;  // 4 waves x 1 KB; waves past BANDS/4 fill theirs with zeros
   static constexpr int LDS_BYTES = NST * STAGE_BYTES + 2 * SC_BYTES;
   // per wave and stage: A and B rows in 1 KB loads (16 rows x 64 B); per window:
-  // one 1 KB load (four 256-byte scale tiles) by each of the first SC_WAVES waves
+  // one 1 KB load (four 256-byte scale tiles) by every wave (out of range, i.e.
+  // zeros, for waves past SC_WAVES, so every wave issues the same loads)
   static constexpr int A_LOADS = BM / 64, B_LOADS = BN / 64;
   static constexpr int AB_LOADS = A_LOADS + B_LOADS;
   static constexpr int SC_WAVES = BANDS / 4;
   // epilogue staging: each wave owns STAGE_BYTES / 4 of the ring slot NST - 1
   static constexpr int EPI_WAVE_BYTES = STAGE_BYTES / 4;
-  static_assert(BM == BN && BANDS % 8 == 0 && SC_WAVES <= 4, "scale loads assume square tiles");
+  static_assert(BM == BN && BANDS % 8 == 0 && SC_WAVES <= 4 && BANDS * 256 <= SC_BYTES, "square tiles");
   static_assert(TM % 2 == 0 && 2 * AB_LOADS + 2 < 64, "");
   static_assert(EPI_WAVE_BYTES >= 4096, "an fp32 32x32 tile must fit the wave's staging area");
 };
@@ -182,7 +183,6 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs p) {
   // given stage switch to an out-of-range offset, which reads as zero.
   const unsigned a_off0 = (unsigned)(a_row_l * p.lda + kc_l * 16), a_offq = (unsigned)(16 * p.lda);
   const unsigned b_off0 = (unsigned)(b_row_l * p.ldb + kc_l * 16), b_offq = (unsigned)(16 * p.ldb);
-  const bool has_sc = wave < C::SC_WAVES;  // this wave loads four scale tiles per window
   const int sc_band = wave * 4 + (l >> 4);  // index in the A-then-B band list
   const bool sc_is_a = wave < C::SC_WAVES / 2;  // square tiles: the first half of the list is A's
 
@@ -204,7 +204,7 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs p) {
       (void*)(p.b + T.b_row0 * p.ldb), (short)0, (int)(b_valid * p.ldb), 0x00020000);
   const int64_t sc_row_band = sc_is_a ? T.a_row0 / 32 + sc_band : T.b_row0 / 32 + (sc_band - BM / 32);
   const int64_t sc_ktiles = sc_is_a ? p.a_ktiles : p.b_ktiles;
-  const unsigned sc_off = sc_row_band < (sc_is_a ? a_bands : b_bands)
+  const unsigned sc_off = wave < C::SC_WAVES && sc_row_band < (sc_is_a ? a_bands : b_bands)
                               ? (unsigned)(sc_row_band * sc_ktiles * 256 + (l & 15) * 16)
                               : 0x80000000u;
 
@@ -213,8 +213,9 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs p) {
   // C::SC_WAVES waves. A stage past the end of the contraction (`live` false)
   // issues the same loads out of range: they read nothing and only fill LDS that is
   // never consumed, so the counter arithmetic is the same on every step.
-  auto opens_window = [&](int64_t s_idx) -> bool { return (s_idx & 3) == 0; };  // k_first is 256-aligned
-  auto issue_stage = [&](int64_t s_idx, bool live) {
+  // k_first is 256-aligned, so stage s opens a scale window iff s % 4 == 0; callers
+  // pass s % 4 as a compile-time constant where they can (the unrolled steps)
+  auto issue_stage = [&](int64_t s_idx, int s_mod4, bool live) {
     const int64_t k0 = k_first + s_idx * BK;
     uint8_t* st = lds + (int)(s_idx % NST) * C::STAGE_BYTES;
     const int kk = (int)k0 + kc_l * 16;
@@ -228,17 +229,17 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs p) {
     for (int q = 0; q < C::B_LOADS; ++q)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(b_rsrc, (lds_ptr_t)(st + C::A_BYTES + wave * (BN / 4) * 64 + q * 1024),
                                                16, drop ? 0x80000000u : b_off0 + q * b_offq, soff, 0, 0);
-    if (has_sc && opens_window(s_idx)) {
+    if (s_mod4 == 0) {
       const int64_t kwin = k0 / 256;
       uint8_t* dst = lds + NST * C::STAGE_BYTES + (int)(kwin & 1) * C::SC_BYTES + wave * 1024;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(sc_is_a ? as_rsrc : bs_rsrc, (lds_ptr_t)dst, 16,
                                                live ? sc_off : 0x80000000u, live ? (int)(kwin * 256) : 0, 0, 0);
     }
   };
-  // loads this wave issues for stages s_idx+1 .. last (all issued)
-  auto loads_after = [&](int64_t s_idx, int64_t last) -> int {
+  // loads this wave issues for the `count` stages following a stage with s % 4 == s_mod4
+  auto loads_after = [&](int s_mod4, int count) -> int {
     int n = 0;
-    for (int64_t q = s_idx + 1; q <= last; ++q) n += C::AB_LOADS + (has_sc && opens_window(q) ? 1 : 0);
+    for (int q = 1; q <= count; ++q) n += C::AB_LOADS + (((s_mod4 + q) & 3) == 0 ? 1 : 0);
     return n;
   };
   auto wait_n = [&](int n) {  // s_waitcnt needs an immediate; n takes one of a few values
@@ -296,7 +297,7 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs p) {
   // the next issue overwrites), then reads stage it+1's fragments interleaved with
   // the second half of stage it's MFMAs.
   auto step = [&](int64_t it, int slot, const Frag& cur, Frag& nxt) {
-    issue_stage(it + NST - 1, it + NST - 1 < n_iter);
+    issue_stage(it + NST - 1, (slot + NST - 1) & 3, it + NST - 1 < n_iter);
     mfma_rows(cur, 0, C::TM / 2);
     // spread the loads over the MFMAs so no load waits in front of an idle matrix core
 #pragma unroll
@@ -306,7 +307,7 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs p) {
       __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read
     }
     __builtin_amdgcn_sched_barrier(0);
-    wait_n(loads_after(it + 1, it + NST - 1));
+    wait_n(loads_after((slot + 1) & 3, NST - 2));
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
     read_frags(nxt, (slot + 1) % NST, k_first + (it + 1) * BK);
@@ -390,7 +391,7 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs p) {
 #pragma unroll
     for (int j = 0; j < C::TN; ++j) acc[i][j] = (v16f){};
   if (n_iter > 0) {
-    for (int s = 0; s < NST - 1; ++s) issue_stage(s, s < n_iter);
+    for (int s = 0; s < NST - 1; ++s) issue_stage(s, s & 3, s < n_iter);
     wait_n(loads_after(0, NST - 2));
     __builtin_amdgcn_s_barrier();
     // The main loop is unrolled by the ring depth, so ring slots are compile-time
