@@ -13,6 +13,8 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef short s16x2 __attribute__((ext_vector_type(2)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v2f __attribute__((ext_vector_type(2)));
 
 // MFMA-blocked scale layout: tiles of 32 rows x 8 blocks (256 B), row-band major.
 __host__ __device__ inline int64_t scale_tiles_k(int64_t kb) { return (kb + 7) / 8; }
@@ -86,11 +88,10 @@ __device__ inline unsigned dpp_xor2(unsigned v) {
 
 __device__ inline unsigned umax(unsigned a, unsigned b) { return a > b ? a : b; }
 
-// float -> bf16 bits, round-to-nearest-even (finite input).
-__device__ inline unsigned short f32_to_bf16_rne(float f) {
-  unsigned u = __builtin_bit_cast(unsigned, f);
-  u += 0x7fff + ((u >> 16) & 1);
-  return (unsigned short)(u >> 16);
+// Two floats -> two bf16 (round to nearest even; NaN stays NaN), packed a | b << 16:
+// one v_cvt_pk_bf16_f32.
+__device__ inline unsigned bf16x2_rne(float a, float b) {
+  return __builtin_bit_cast(unsigned, __builtin_convertvector((v2f){a, b}, bf16x2));
 }
 
 }  // namespace mx

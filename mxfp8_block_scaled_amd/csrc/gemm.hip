@@ -16,7 +16,10 @@
 // operand tile; its 32 bytes are the contraction elements [16h, 16h+16) and
 // [32+16h, 32+16h+16) of the 64-wide k-step, h = l / 32. The scale of row r and
 // k-block b (0/1) of the step comes from lane r + 32b, byte `opsel`. The output
-// 32x32 tile: lane l, register v -> row 8*(v/4) + 4*h + v%4, column l % 32.
+// 32x32 tile: lane l, register v -> row 8*(v/4) + 4*h + v%4 (of the first
+// operand), column l % 32 (of the second). The kernel passes B first, so each
+// lane accumulates four consecutive output columns of one output row per v/4:
+// C[row l % 32][col 8*(v/4) + 4*h + v%4], which it stores directly.
 
 #include "common.h"
 
@@ -64,11 +67,8 @@ struct Cfg {
   static constexpr int A_LOADS = BM / 64, B_LOADS = BN / 64;
   static constexpr int AB_LOADS = A_LOADS + B_LOADS;
   static constexpr int SC_WAVES = BANDS / 4;
-  // epilogue staging: each wave owns STAGE_BYTES / 4 of the ring slot NST - 1
-  static constexpr int EPI_WAVE_BYTES = STAGE_BYTES / 4;
   static_assert(BM == BN && BANDS % 8 == 0 && SC_WAVES <= 4 && BANDS * 256 <= SC_BYTES, "square tiles");
   static_assert(TM % 2 == 0 && 2 * AB_LOADS + 2 < 64, "");
-  static_assert(EPI_WAVE_BYTES >= 4096, "an fp32 32x32 tile must fit the wave's staging area");
 };
 
 // LDS holds each 64-byte row (four 16-byte chunks of one k-step) with chunk c of
@@ -151,6 +151,15 @@ __device__ inline Tile tile_at(const GemmArgs& p, int64_t t) {
   return T;
 }
 
+// A block-uniform value computed in vector registers (a 64-bit division, a load
+// through a vector address) is not known to be uniform; reading lane 0 makes it a
+// scalar again, so buffer offsets and descriptors built from it need no per-lane loop.
+__device__ inline int64_t uniform(int64_t v) {
+  const unsigned lo = (unsigned)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+  const unsigned hi = (unsigned)__builtin_amdgcn_readfirstlane((int)(uint32_t)((uint64_t)v >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
 // Tile order: blocks are dealt round-robin to the 8 XCDs, so the remap gives each
 // XCD a contiguous range of logical tiles; with the GM-band raster of tile_at, the
 // ~32 tiles resident on one XCD share their A and B slices in its L2.
@@ -168,8 +177,12 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs p) {
   const int tid = threadIdx.x, l = tid & 63, h = l >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int wm = wave >> 1, wn = wave & 1;
-  const Tile T = tile_at<BM, BN, MODE, OUT_BF16>(p, xcd_remap(blockIdx.x, gridDim.x));
-  if (!T.valid) return;
+  Tile T = tile_at<BM, BN, MODE, OUT_BF16>(p, xcd_remap(blockIdx.x, gridDim.x));
+  if (!__builtin_amdgcn_readfirstlane((int)T.valid)) return;
+  T.a_row0 = uniform(T.a_row0); T.a_row_end = uniform(T.a_row_end);
+  T.b_row0 = uniform(T.b_row0); T.b_row_end = uniform(T.b_row_end);
+  T.k_beg = uniform(T.k_beg); T.k_end = uniform(T.k_end); T.col0 = uniform(T.col0);
+  T.out_base = (uint8_t*)uniform((int64_t)T.out_base);
 
   const int64_t a_bands = (p.a_rows + 31) / 32, b_bands = (p.b_rows + 31) / 32;
   const __amdgpu_buffer_rsrc_t as_rsrc = __builtin_amdgcn_make_buffer_rsrc(
@@ -286,8 +299,8 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs p) {
     for (int i = i0; i < i1; ++i)
 #pragma unroll
       for (int j = 0; j < C::TN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.a[i], f.b[j], acc[i][j], 0, 0, 0, (int)f.sa[i],
-                                                                    0, (int)f.sb[j]);
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.b[j], f.a[i], acc[i][j], 0, 0, 0, (int)f.sb[j],
+                                                                    0, (int)f.sa[i]);
   };
 
   // One pipeline step over an NST-deep LDS ring. Step `it` issues stage it+NST-1,
@@ -321,68 +334,79 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs p) {
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  // ---- epilogue: stage each 32x32 tile through LDS, write 16 bytes per lane --------
-  // Lane l holds column l % 32 of each MFMA tile, rows 8*(v/4) + 4*h + v%4.
-  uint8_t* epi = lds + (NST - 1) * C::STAGE_BYTES + wave * C::EPI_WAVE_BYTES;
+  // ---- epilogue ------------------------------------------------------------------
+  // Each lane holds four consecutive columns of one row per v/4. In the common case
+  // (the wave's columns inside N, rows 16-byte aligned) each wave stages its whole
+  // WM x WN output, or half of it for fp32 at 256x256, in its quarter of the idle
+  // ring: 8- or 16-byte LDS writes, 16-byte chunks of a row XOR-swizzled by the row
+  // so neither the writes (32 rows, one chunk) nor the reads (whole rows) collide in
+  // banks. It then writes whole row segments (WN * ES bytes) with 16-byte stores.
+  // Otherwise (the ragged right edge) lanes store elements with a bounds check.
   auto epilogue = [&]() {
     const int64_t row_limit = MODE == MODE_MGROUP ? T.a_row_end : p.M;
     constexpr int ES = OUT_BF16 ? 2 : 4;
-    constexpr int TILE_BYTES = 32 * 32 * ES;
-    constexpr int NBUF = C::EPI_WAVE_BYTES / TILE_BYTES;
-    constexpr int ROW_BYTES = 32 * ES;          // one row of a 32x32 tile
-    constexpr int LPR = ROW_BYTES / 16;         // lanes per row (16 bytes each)
-    constexpr int ROWS_PER_PASS = 64 / LPR;
+    constexpr int ROW_BYTES = C::WN * ES;
+    constexpr int CPR = ROW_BYTES / 16;                      // 16-byte chunks per row
+    constexpr int EPI_BYTES = NST * C::STAGE_BYTES / 4;      // staging bytes per wave
+    constexpr int RP = EPI_BYTES / ROW_BYTES < C::WM ? EPI_BYTES / ROW_BYTES : C::WM;  // rows per pass
+    constexpr int RPI = 64 / CPR;                            // rows per 16-byte read / store
+    static_assert(RP % 32 == 0 && RP % RPI == 0 && C::WM % RP == 0, "epilogue staging shape");
+    const int64_t wrow0 = T.a_row0 + wm * C::WM;
+    const int64_t wcol0 = T.col0 + wn * C::WN;
+    if (((p.ldo * ES) & 15) == 0 && wcol0 + C::WN <= p.N) {
+      uint8_t* stg = lds + wave * EPI_BYTES;
+      const int ch = l % CPR;
 #pragma unroll
-    for (int i = 0; i < C::TM; ++i)
+      for (int pass = 0; pass < C::WM / RP; ++pass) {
 #pragma unroll
-      for (int j = 0; j < C::TN; ++j) {
-        uint8_t* buf = epi + ((i * C::TN + j) % NBUF) * TILE_BYTES;
-        if (OUT_BF16) {
-          // lanes 2c, 2c+1 swap values so each writes two adjacent columns of one row
-          const int odd = l & 1;
+        for (int ii = 0; ii < RP / 32; ++ii) {
+          const int i = pass * (RP / 32) + ii;
+          const int r = 32 * ii + (l & 31);
+          uint8_t* srow = stg + r * ROW_BYTES;
 #pragma unroll
-          for (int v = 0; v < 16; v += 2) {
-            const float m0 = acc[i][j][v], m1 = acc[i][j][v + 1];
-            const float send = odd ? m0 : m1;
-            const float recv = __builtin_bit_cast(float, dpp_xor1(__builtin_bit_cast(unsigned, send)));
-            const float lo = odd ? recv : m0, hi = odd ? m1 : recv;
-            const unsigned packed = (unsigned)f32_to_bf16_rne(lo) | ((unsigned)f32_to_bf16_rne(hi) << 16);
-            const int row = 8 * (v >> 2) + 4 * h + (v & 3) + odd;
-            *(unsigned*)(buf + row * ROW_BYTES + ((l & 31) & ~1) * 2) = packed;
-          }
-        } else {
+          for (int j = 0; j < C::TN; ++j)
 #pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int row = 8 * (v >> 2) + 4 * h + (v & 3);
-            *(float*)(buf + row * ROW_BYTES + (l & 31) * 4) = acc[i][j][v];
-          }
-        }
-        const int64_t trow = T.a_row0 + wm * C::WM + 32 * i;
-        const int64_t tcol = T.col0 + wn * C::WN + 32 * j;
-        const int cl = (l % LPR) * (16 / ES);  // first column of this lane's 16 bytes
-#pragma unroll
-        for (int pass = 0; pass < 32 / ROWS_PER_PASS; ++pass) {
-          const int r = pass * ROWS_PER_PASS + l / LPR;
-          const u32x4 d = *(const u32x4*)(buf + r * ROW_BYTES + (l % LPR) * 16);
-          const int64_t row = trow + r, col = tcol + cl;
-          uint8_t* dst = T.out_base + (row * p.ldo + col) * ES;
-          if (row < row_limit) {
-            if (col + 16 / ES <= p.N && ((p.ldo * ES) & 15) == 0) {
-              *(u32x4*)dst = d;
-            } else {
-              const unsigned w4[4] = {d.x, d.y, d.z, d.w};
-#pragma unroll
-              for (int e = 0; e < 16 / ES; ++e)
-                if (col + e < p.N) {
-                  if (OUT_BF16)
-                    ((uint16_t*)dst)[e] = (uint16_t)(w4[e / 2] >> (16 * (e & 1)));
-                  else
-                    ((unsigned*)dst)[e] = w4[e];
-                }
+            for (int q = 0; q < 4; ++q) {
+              const int lb = (32 * j + 8 * q + 4 * h) * ES;  // byte of the lane's first column
+              uint8_t* dst = srow + ((((lb >> 4) ^ r) & (CPR - 1)) << 4) + (lb & 15);
+              const v16f& c = acc[i][j];
+              if (OUT_BF16)
+                *(u32x2*)dst = (u32x2){bf16x2_rne(c[4 * q], c[4 * q + 1]), bf16x2_rne(c[4 * q + 2], c[4 * q + 3])};
+              else
+                *(v4f*)dst = (v4f){c[4 * q], c[4 * q + 1], c[4 * q + 2], c[4 * q + 3]};
             }
-          }
+        }
+#pragma unroll
+        for (int k = 0; k < RP / RPI; ++k) {
+          const int r = k * RPI + l / CPR;
+          const u32x4 d = *(const u32x4*)(stg + r * ROW_BYTES + (((ch ^ r) & (CPR - 1)) << 4));
+          const int64_t row = wrow0 + pass * RP + r;
+          if (row < row_limit) *(u32x4*)(T.out_base + (row * p.ldo + wcol0) * ES + ch * 16) = d;
         }
       }
+    } else {
+#pragma unroll
+      for (int i = 0; i < C::TM; ++i) {
+        const int64_t row = wrow0 + 32 * i + (l & 31);
+        if (row >= row_limit) continue;
+        uint8_t* dst_row = T.out_base + (row * p.ldo + wcol0 + 4 * h) * ES;
+        const int cols_left = (int)(p.N - wcol0 - 4 * h);  // valid columns from this lane's first
+#pragma unroll
+        for (int j = 0; j < C::TN; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int c = 32 * j + 8 * q + e;
+              if (c < cols_left) {
+                if (OUT_BF16)
+                  *(uint16_t*)(dst_row + c * 2) = (uint16_t)bf16x2_rne(acc[i][j][4 * q + e], 0.f);
+                else
+                  *(float*)(dst_row + c * 4) = acc[i][j][4 * q + e];
+              }
+            }
+      }
+    }
   };
 
   // ---- main loop -------------------------------------------------------------------
