@@ -140,7 +140,11 @@ mx_status mx_quantize_weight_32x32(const uint16_t* w, int64_t batch, int64_t n, 
  *             Rows past offs[G-1] are left unwritten.
  *   out       [m x n], float32 or bf16 per out_dtype, row pitch n (written)
  * k % 32 == 0 (k need not be a multiple of 128: the tail is zero-padded inside
- * the kernel); m >= 0; n >= 1; if groups > 1, n % 32 == 0. fp32 accumulation. */
+ * the kernel); m >= 0; n >= 1; if groups > 1, n % 32 == 0. fp32 accumulation.
+ * Extent limits (all three GEMM calls, MX_E_SHAPE otherwise): the contraction
+ * length (k here, n for dgrad, m for wgrad) is at most 2^22, and each operand's
+ * scale buffer (mx_scale_bytes of its rows and the contraction) is below 2^31
+ * bytes; the kernels address operands with 32-bit buffer offsets. */
 mx_status mx_grouped_mm_fwd(const uint8_t* a, const uint8_t* a_s, const uint8_t* b, const uint8_t* b_s,
                             const int32_t* offs, int32_t groups, int64_t m, int64_t n, int64_t k, void* out,
                             int out_dtype, void* stream);

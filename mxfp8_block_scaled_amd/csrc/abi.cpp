@@ -27,6 +27,7 @@ thread_local char g_err[512] = "";
 
 // Largest size accepted for any dimension: keeps every byte offset far inside int64.
 constexpr int64_t kMaxDim = (int64_t)1 << 31;
+constexpr int64_t kMaxContraction = (int64_t)1 << 22;
 
 mx_status fail(mx_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
 mx_status fail(mx_status s, const char* fmt, ...) {
@@ -185,6 +186,17 @@ mx_status mx_quantize_weight_32x32(const uint16_t* w, int64_t batch, int64_t n, 
                   "mx_quantize_weight_32x32");
 }
 
+// The GEMM addresses a 256-row window of an operand and a whole scale buffer
+// through 32-bit buffer offsets, so the contraction is capped at 2^22 bytes per
+// row and each operand's scale buffer below 2^31 bytes.
+mx_status check_gemm_extent(const char* name, int64_t contraction, int64_t a_rows, int64_t b_rows) {
+  if (contraction > kMaxContraction)
+    return fail(MX_E_SHAPE, "%s = %lld exceeds the contraction limit 2^22", name, (long long)contraction);
+  if (mx_scale_bytes(a_rows, contraction) >= kMaxDim || mx_scale_bytes(b_rows, contraction) >= kMaxDim)
+    return fail(MX_E_SHAPE, "an operand's scale buffer would reach 2^31 bytes");
+  return MX_OK;
+}
+
 mx_status mx_grouped_mm_fwd(const uint8_t* a, const uint8_t* a_s, const uint8_t* b, const uint8_t* b_s,
                             const int32_t* offs, int32_t groups, int64_t m, int64_t n, int64_t k, void* out,
                             int out_dtype, void* stream) {
@@ -195,6 +207,7 @@ mx_status mx_grouped_mm_fwd(const uint8_t* a, const uint8_t* a_s, const uint8_t*
   TRY(check_mul32("k", k));
   if (groups > 1 && n % 32 != 0) return fail(MX_E_SHAPE, "n = %lld must be a multiple of 32 when groups > 1", (long long)n);
   if ((int64_t)groups * n > kMaxDim) return fail(MX_E_SHAPE, "groups * n exceeds 2^31");
+  TRY(check_gemm_extent("k", k, m, (int64_t)groups * n));
   TRY(check_device());
   return launched(mx_launch_gemm_mgroup(a, a_s, b, b_s, offs, groups, m, n, k, out, out_dtype, (hipStream_t)stream),
                   "mx_grouped_mm_fwd");
@@ -210,6 +223,7 @@ mx_status mx_grouped_mm_dgrad(const uint8_t* dy, const uint8_t* dy_s, const uint
   TRY(check_mul32("n", n));
   if (groups > 1 && k % 32 != 0) return fail(MX_E_SHAPE, "k = %lld must be a multiple of 32 when groups > 1", (long long)k);
   if ((int64_t)groups * k > kMaxDim) return fail(MX_E_SHAPE, "groups * k exceeds 2^31");
+  TRY(check_gemm_extent("n", n, m, (int64_t)groups * k));
   TRY(check_device());
   // dX[m x k] = dY[m x n] . (W_g^T [k x n])^T : the M-grouped core with contraction n
   return launched(mx_launch_gemm_mgroup(dy, dy_s, w_t, w_t_s, offs, groups, m, k, n, dx, out_dtype, (hipStream_t)stream),
@@ -225,6 +239,7 @@ mx_status mx_grouped_mm_wgrad(const uint8_t* dy_t, const uint8_t* dy_t_s, const 
   TRY(check_dim("k", k, 1));
   TRY(check_mul32("m", m));
   if ((int64_t)groups * n > kMaxDim) return fail(MX_E_SHAPE, "groups * n exceeds 2^31");
+  TRY(check_gemm_extent("m", m, n, k));
   TRY(check_device());
   // dW_g[n x k] = dY^T[n x m] . (X^T[k x m])^T over group g's range of m
   return launched(mx_launch_gemm_kgroup(dy_t, dy_t_s, x_t, x_t_s, offs, groups, n, k, m, dw, out_dtype, (hipStream_t)stream),

@@ -88,6 +88,17 @@ def test_gemm_validation(lib):
     assert f(P, P, P, P, P + 2, 1, 64, 64, 64, P2, 0, None) == MX_E_ALIGN
     assert lib.mx_grouped_mm_dgrad(P, P, P, P, None, 1, 64, 40, 64, P2, 0, None) == MX_E_SHAPE  # n % 32
     assert lib.mx_grouped_mm_wgrad(P, P, P, P, None, 1, 40, 64, 64, P2, 0, None) == MX_E_SHAPE  # m % 32
+    # extent limits: contraction above 2^22, or a scale buffer reaching 2^31 bytes
+    big = (1 << 22) + 32
+    assert f(P, P, P, P, None, 1, 64, 64, big, P2, 0, None) == MX_E_SHAPE
+    assert b"2^22" in lib.mx_last_error()
+    assert lib.mx_grouped_mm_dgrad(P, P, P, P, None, 1, 64, big, 64, P2, 0, None) == MX_E_SHAPE
+    assert lib.mx_grouped_mm_wgrad(P, P, P, P, None, 1, big, 64, 64, P2, 0, None) == MX_E_SHAPE
+    assert f(P, P, P, P, None, 1, 1 << 30, 64, 1 << 22, P2, 0, None) == MX_E_SHAPE  # a's scales: 2^47 bytes
+    assert b"2^31" in lib.mx_last_error()
+    assert lib.mx_grouped_mm_wgrad(P, P, P, P, None, 1, 1 << 22, 1 << 16, 64, P2, 0, None) == MX_E_SHAPE  # 2^33
+    # at the limit the shapes are accepted (no GPU here: the device check answers)
+    assert f(P, P, P, P, None, 1, 64, 64, 1 << 22, P2, 0, None) in (MX_E_DEVICE, 0)
 
 
 def test_valid_arguments_without_a_gpu_report_device(lib):
