@@ -8,7 +8,8 @@ Recipe (shared by every workload):
   * one numpy Generator per tensor, spawned in a fixed order from
     SeedSequence(seed), so adding a tensor never changes the others;
   * "N(0, sigma)" means a normal with standard deviation sigma, drawn in float32,
-    scaled, then rounded to bf16 with round-to-nearest-even;
+    scaled, then rounded to bf16 with round-to-nearest-even; a tensor's rows are
+    drawn in ~4M-element chunks, each from its own child of the tensor's generator;
   * group sizes are multiples of 32 rows (the grouped GEMM's alignment) and sum to
     the token count; offs holds their inclusive cumulative sums (group ends).
 
@@ -19,32 +20,66 @@ command), the 576-wide gradient (torchtitan PR 5334 body) and a DeepSeek-V3-like
 one-GPU expert share (32 experts, hidden 7168, expert width 2048, top-8 routing).
 """
 
+import os
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 
 
 def f32_to_bf16_bits(x):
-    """Round float32 values to bf16 (nearest, ties to even) and return uint16 bits."""
-    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
-    nan = np.isnan(np.asarray(x, dtype=np.float32))
-    r = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
-    r = np.where(nan, 0x7FC0, r)
-    return r.astype(np.uint16)
+    """Round float32 values to bf16 (nearest, ties to even) and return uint16 bits.
+
+    In uint32 arithmetic: a non-NaN pattern plus 0x7FFF plus its bit 16 stays below
+    2^32 (the largest, -inf's 0xFF800000, gains at most 0x8000); NaNs map to 0x7FC0.
+    """
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32)
+    r = u + np.uint32(0x7FFF)
+    r += (u >> 16) & np.uint32(1)
+    r >>= 16
+    out = r.astype(np.uint16)
+    nan = np.isnan(x)
+    if nan.any():
+        out[nan] = 0x7FC0
+    return out
 
 
 def bf16_bits_to_f32(bits):
     return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
 
 
-def normal_bf16(rng, shape, std, chunk_rows=4096):
-    """bf16 patterns of N(0, std) draws; generated in row chunks to bound memory."""
+_CHUNK_ELEMS = 1 << 22
+_THREADS = max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def normal_bf16(rng, shape, std):
+    """bf16 patterns of N(0, std) draws.
+
+    The rows are cut into chunks of about 4M elements; chunk i draws from the i-th
+    child generator spawned from `rng`, so the values depend only on the seed and
+    the shape, and the chunks can be drawn on several threads (numpy releases the
+    GIL while filling).
+    """
     shape = tuple(int(s) for s in shape)
     out = np.empty(shape, dtype=np.uint16)
     flat = out.reshape(-1, shape[-1]) if len(shape) > 1 else out.reshape(1, -1)
-    for r0 in range(0, flat.shape[0], chunk_rows):
-        r1 = min(flat.shape[0], r0 + chunk_rows)
-        x = rng.standard_normal((r1 - r0, flat.shape[1]), dtype=np.float32)
+    rows, cols = flat.shape
+    chunk_rows = max(1, _CHUNK_ELEMS // max(cols, 1))
+    starts = list(range(0, rows, chunk_rows))
+    kids = rng.spawn(len(starts))
+
+    def fill(i):
+        r0 = starts[i]
+        r1 = min(rows, r0 + chunk_rows)
+        x = kids[i].standard_normal((r1 - r0, cols), dtype=np.float32)
         x *= np.float32(std)
         flat[r0:r1] = f32_to_bf16_bits(x)
+
+    if len(starts) == 1:
+        fill(0)
+    else:
+        with ThreadPoolExecutor(_THREADS) as ex:
+            list(ex.map(fill, range(len(starts))))
     return out
 
 

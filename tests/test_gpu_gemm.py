@@ -1,16 +1,9 @@
 """GPU parity of the MXFP8 grouped GEMM (forward, dgrad, wgrad) against the oracle.
 
-Bars, all against the float64 product of the same dequantized operands:
-  * bit-exact fp32 output where every partial sum is exactly representable
-    (codes in {0, +-0.5, +-1, +-2}, scales 2^-1..2^1);
-  * every fp32 output within HW_REL * sum_k |a_k b_k| (+ the fp32 accumulation
-    bound). The gfx950 block-scaled MFMA does not round each addition to fp32:
-    inside one 64-element dot product it drops product bits below about 2^-14 of
-    the largest product (measured on adversarial random codes: worst error
-    3.2e-4 = 2^-11.6 of sum |a b| per instruction). HW_REL = 2^-11 covers that;
-  * relative Frobenius error reported for every case and held to REL_FRO_HW;
-  * bf16 output within 1 bf16 ulp of the correctly rounded value, or inside the
-    per-element bound above plus half a bf16 ulp.
+Bit-exact fp32 output where every partial sum is exactly representable (codes in
+{0, +-0.5, +-1, +-2}, scales 2^-1..2^1); otherwise the bars of gemm_check (per
+element within the MFMA's accumulation bound, relative Frobenius error, bf16
+within one ulp of the correctly rounded value or inside the bound).
 """
 
 import numpy as np
@@ -20,13 +13,10 @@ import torch
 import mxfp8_block_scaled_amd as mx
 from mxfp8_block_scaled_amd import synth
 
+from gemm_check import REL_FRO_HW, check_bf16, check_f32  # noqa: F401
 from gpu_util import dev_bf16, dev_i32, dev_u8, host, require_gpu, say
 
 pytestmark = pytest.mark.gpu
-
-REL_FRO = 1e-5  # the bound an IEEE fp32 accumulation would meet (reported, not gated)
-REL_FRO_HW = 5e-5  # gate: measured 1.5e-5 on N(0,1) x N(0,0.02) data, K = 512
-HW_REL = 2.0**-11
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -36,33 +26,6 @@ def gpu():
 
 def phys(oracle, logical):
     return dev_u8(oracle.scales_to_physical(logical))
-
-
-def check_f32(oracle, got, ref, name, absprod=None, K=None):
-    err = oracle.rel_frobenius(got, ref)
-    say(f"    {name}: rel frobenius {err:.3e} (IEEE-fp32 bar {REL_FRO:g}: {'met' if err <= REL_FRO else 'not met'})")
-    assert err <= REL_FRO_HW, f"{name}: relative Frobenius error {err:.3e} > {REL_FRO_HW}"
-    if absprod is not None:
-        u = 2.0**-24
-        bound = (HW_REL + K * u / (1 - K * u)) * absprod + 1e-30
-        worst = np.max(np.abs(got - ref) / bound)
-        say(f"    {name}: worst |err| / per-element bound = {worst:.3f}")
-        assert worst <= 1.0, f"{name}: per-element bound exceeded ({worst:.3f})"
-
-
-def check_bf16(oracle, got_bits, ref, absprod, K, name):
-    """R13 rule: ordinal distance <= 1 from RNE_bf16(ref), else |err| within gamma_K * sum|a||b|."""
-    ref_bits = oracle.round_to_bf16_bits(ref)
-    d = np.abs(oracle.bf16_ordinal(got_bits) - oracle.bf16_ordinal(ref_bits))
-    bad = d > 1
-    if bad.any():
-        got = oracle.bf16_to_f64(got_bits[bad])
-        u = 2.0**-24
-        gamma = K * u / (1 - K * u)
-        # the bf16 rounding of the fp32 result adds half a bf16 ulp
-        bound = (HW_REL + gamma) * absprod[bad] + np.abs(ref[bad]) * 2.0**-8
-        assert np.all(np.abs(got - ref[bad]) <= bound), f"{name}: {np.sum(np.abs(got - ref[bad]) > bound)} outside bound"
-    say(f"    {name}: {bad.sum()} of {d.size} outputs needed the fp32-bound branch")
 
 
 def exact_operands(rng, rows, k):
