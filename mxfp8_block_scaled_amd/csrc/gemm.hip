@@ -45,29 +45,36 @@ struct GemmArgs {
   int groups;
 };
 
-// Block tile BM x BN, 4 waves as 2 x 2, each wave (BM/2) x (BN/2) in 32x32 MFMA
-// tiles; the contraction advances 64 elements (one MFMA k-step) per pipeline stage.
-template <int BM, int BN>
+// Block tile BM x BN over a WGM x WGN grid of waves, each wave (BM/WGM) x (BN/WGN)
+// in 32x32 MFMA tiles; the contraction advances 64 elements (one MFMA k-step) per
+// pipeline stage.
+template <int BM, int BN, int WGM, int WGN>
 struct Cfg {
-  static constexpr int THREADS = 256;
+  static constexpr int WAVES = WGM * WGN;
+  static constexpr int THREADS = 64 * WAVES;
   static constexpr int BK = 64;
   static constexpr int NST = 4;  // LDS ring depth: stages in flight
-  static constexpr int WM = BM / 2, WN = BN / 2;
+  static constexpr int WM = BM / WGM, WN = BN / WGN;
   static constexpr int TM = WM / 32, TN = WN / 32;
   static constexpr int A_BYTES = BM * BK, B_BYTES = BN * BK;
   static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
   // scale tiles of one 256-wide window: A bands then B bands, 256 B each; two
   // windows are resident (the one in use and the next)
   static constexpr int BANDS = (BM + BN) / 32;
-  static constexpr int SC_BYTES = 4096;  // 4 waves x 1 KB; waves past BANDS/4 fill theirs with zeros
+  static constexpr int SC_BYTES = WAVES * 1024;  // 1 KB per wave; waves past BANDS/4 fill theirs with zeros
   static constexpr int LDS_BYTES = NST * STAGE_BYTES + 2 * SC_BYTES;
-  // per wave and stage: A and B rows in 1 KB loads (16 rows x 64 B); per window:
-  // one 1 KB load (four 256-byte scale tiles) by every wave (out of range, i.e.
-  // zeros, for waves past SC_WAVES, so every wave issues the same loads)
-  static constexpr int A_LOADS = BM / 64, B_LOADS = BN / 64;
+  // per wave and stage: its share of A and B rows in 1 KB loads (16 rows x 64 B);
+  // per window: one 1 KB load (four 256-byte scale tiles) by every wave (out of
+  // range, i.e. zeros, for waves past SC_WAVES, so every wave issues the same loads)
+  static constexpr int A_ROWS_W = BM / WAVES, B_ROWS_W = BN / WAVES;
+  static constexpr int A_LOADS = A_ROWS_W / 16, B_LOADS = B_ROWS_W / 16;
   static constexpr int AB_LOADS = A_LOADS + B_LOADS;
   static constexpr int SC_WAVES = BANDS / 4;
-  static_assert(BM == BN && BANDS % 8 == 0 && SC_WAVES <= 4 && BANDS * 256 <= SC_BYTES, "square tiles");
+  // LDS reads per k-step (two 16-byte fragment halves and one scale dword per tile)
+  // spread over the second half's MFMAs
+  static constexpr int HALF_MFMAS = TM / 2 * TN;
+  static constexpr int DS_PER_MFMA = (3 * (TM + TN) + HALF_MFMAS - 1) / HALF_MFMAS;
+  static_assert(BM == BN && BANDS % 8 == 0 && SC_WAVES <= WAVES && A_ROWS_W % 16 == 0, "tile shape");
   static_assert(TM % 2 == 0 && 2 * AB_LOADS + 2 < 64, "");
 };
 
@@ -168,15 +175,15 @@ __device__ inline int64_t xcd_remap(int64_t bid, int64_t nblk) {
   return bid < per_xcd * 8 ? (bid % 8) * per_xcd + bid / 8 : bid;
 }
 
-template <int BM, int BN, int MODE, int OUT_BF16>
-__global__ __launch_bounds__(256) void k_gemm(GemmArgs p) {
-  using C = Cfg<BM, BN>;
+template <int BM, int BN, int WGM, int WGN, int MODE, int OUT_BF16>
+__global__ __launch_bounds__(64 * WGM * WGN) void k_gemm(GemmArgs p) {
+  using C = Cfg<BM, BN, WGM, WGN>;
   constexpr int NST = C::NST, BK = C::BK;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
 
   const int tid = threadIdx.x, l = tid & 63, h = l >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WGN, wn = wave % WGN;
   Tile T = tile_at<BM, BN, MODE, OUT_BF16>(p, xcd_remap(blockIdx.x, gridDim.x));
   if (!__builtin_amdgcn_readfirstlane((int)T.valid)) return;
   T.a_row0 = uniform(T.a_row0); T.a_row_end = uniform(T.a_row_end);
@@ -190,7 +197,7 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs p) {
   const __amdgpu_buffer_rsrc_t bs_rsrc = __builtin_amdgcn_make_buffer_rsrc(
       (void*)p.b_s, (short)0, (int)(b_bands * p.b_ktiles * 256), 0x00020000);
   const int kc_l = (l & 3) ^ (l >> 4);
-  const int a_row_l = wave * (BM / 4) + (l >> 2), b_row_l = wave * (BN / 4) + (l >> 2);
+  const int a_row_l = wave * C::A_ROWS_W + (l >> 2), b_row_l = wave * C::B_ROWS_W + (l >> 2);
   // Per-lane offsets are fixed for a tile (row and chunk); the contraction position
   // goes in the scalar offset. Lanes whose chunk lies outside [k_beg, k_end) in a
   // given stage switch to an out-of-range offset, which reads as zero.
@@ -236,11 +243,11 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs p) {
     const int soff = live ? (int)k0 : 0;
 #pragma unroll
     for (int q = 0; q < C::A_LOADS; ++q)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, (lds_ptr_t)(st + wave * (BM / 4) * 64 + q * 1024), 16,
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, (lds_ptr_t)(st + wave * C::A_ROWS_W * 64 + q * 1024), 16,
                                                drop ? 0x80000000u : a_off0 + q * a_offq, soff, 0, 0);
 #pragma unroll
     for (int q = 0; q < C::B_LOADS; ++q)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(b_rsrc, (lds_ptr_t)(st + C::A_BYTES + wave * (BN / 4) * 64 + q * 1024),
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(b_rsrc, (lds_ptr_t)(st + C::A_BYTES + wave * C::B_ROWS_W * 64 + q * 1024),
                                                16, drop ? 0x80000000u : b_off0 + q * b_offq, soff, 0, 0);
     if (s_mod4 == 0) {
       const int64_t kwin = k0 / 256;
@@ -325,11 +332,11 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs p) {
     __builtin_amdgcn_sched_barrier(0);
     read_frags(nxt, (slot + 1) % NST, k_first + (it + 1) * BK);
     mfma_rows(cur, C::TM / 2, C::TM);
-    // interleave: one MFMA, then three LDS reads
+    // interleave: one MFMA, then a share of the LDS reads
 #pragma unroll
-    for (int q = 0; q < C::TM / 2 * C::TN; ++q) {
+    for (int q = 0; q < C::HALF_MFMAS; ++q) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, C::DS_PER_MFMA, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
   };
@@ -347,7 +354,7 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs p) {
     constexpr int ES = OUT_BF16 ? 2 : 4;
     constexpr int ROW_BYTES = C::WN * ES;
     constexpr int CPR = ROW_BYTES / 16;                      // 16-byte chunks per row
-    constexpr int EPI_BYTES = NST * C::STAGE_BYTES / 4;      // staging bytes per wave
+    constexpr int EPI_BYTES = NST * C::STAGE_BYTES / C::WAVES;  // staging bytes per wave
     constexpr int RP = EPI_BYTES / ROW_BYTES < C::WM ? EPI_BYTES / ROW_BYTES : C::WM;  // rows per pass
     constexpr int RPI = 64 / CPR;                            // rows per 16-byte read / store
     static_assert(RP % 32 == 0 && RP % RPI == 0 && C::WM % RP == 0, "epilogue staging shape");
@@ -445,9 +452,9 @@ namespace {
 
 // Tile configurations: 256x256 for large problems; 128x128 where 256x256 tiles
 // would leave most compute units idle.
-template <int BM, int BN, int MODE>
+template <int BM, int BN, int WGM, int WGN, int MODE>
 hipError_t launch_cfg(mx::GemmArgs p, int out_bf16, hipStream_t stream) {
-  using C = mx::Cfg<BM, BN>;
+  using C = mx::Cfg<BM, BN, WGM, WGN>;
   const int64_t mt_extra = (MODE == mx::MODE_MGROUP && p.offs) ? p.groups : 0;
   p.mt_total = (p.M + BM - 1) / BM + mt_extra;
   p.nt = (p.N + BN - 1) / BN;
@@ -459,18 +466,18 @@ hipError_t launch_cfg(mx::GemmArgs p, int out_bf16, hipStream_t stream) {
   hipError_t e = hipSuccess;
   if (out_bf16) {
     if (!attr_set[1])
-      e = hipFuncSetAttribute((const void*)mx::k_gemm<BM, BN, MODE, 1>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                              (int)lds);
+      e = hipFuncSetAttribute((const void*)mx::k_gemm<BM, BN, WGM, WGN, MODE, 1>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     attr_set[1] = true;
-    hipLaunchKernelGGL((mx::k_gemm<BM, BN, MODE, 1>), dim3((unsigned)blocks), dim3(C::THREADS), lds, stream, p);
+    hipLaunchKernelGGL((mx::k_gemm<BM, BN, WGM, WGN, MODE, 1>), dim3((unsigned)blocks), dim3(C::THREADS), lds, stream, p);
   } else {
     if (!attr_set[0])
-      e = hipFuncSetAttribute((const void*)mx::k_gemm<BM, BN, MODE, 0>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                              (int)lds);
+      e = hipFuncSetAttribute((const void*)mx::k_gemm<BM, BN, WGM, WGN, MODE, 0>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     attr_set[0] = true;
-    hipLaunchKernelGGL((mx::k_gemm<BM, BN, MODE, 0>), dim3((unsigned)blocks), dim3(C::THREADS), lds, stream, p);
+    hipLaunchKernelGGL((mx::k_gemm<BM, BN, WGM, WGN, MODE, 0>), dim3((unsigned)blocks), dim3(C::THREADS), lds, stream, p);
   }
   return hipGetLastError();
 }
@@ -479,8 +486,10 @@ template <int MODE>
 hipError_t launch(mx::GemmArgs& p, int out_bf16, hipStream_t stream) {
   const int64_t groups_tiles = MODE == mx::MODE_KGROUP ? p.groups : 1;
   const int64_t big_tiles = groups_tiles * ((p.M + 255) / 256) * ((p.N + 255) / 256);
-  if (big_tiles >= 512) return launch_cfg<256, 256, MODE>(p, out_bf16, stream);
-  return launch_cfg<128, 128, MODE>(p, out_bf16, stream);
+  // 2 x 2 waves of 128 x 128 (256 accumulators each, one wave per SIMD); 8-wave
+  // grids of 128 x 64 per wave (two per SIMD) measured the same on the MoE shapes
+  if (big_tiles >= 512) return launch_cfg<256, 256, 2, 2, MODE>(p, out_bf16, stream);
+  return launch_cfg<128, 128, 2, 2, MODE>(p, out_bf16, stream);
 }
 }  // namespace
 

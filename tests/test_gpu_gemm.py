@@ -197,3 +197,41 @@ def test_gemm_deterministic():
     a = host(mx.mx_grouped_mm_fwd(xq, xs, wq, ws, doffs, 512, 256, 512, out_dtype=mx.MX_OUT_F32))
     b = host(mx.mx_grouped_mm_fwd(xq, xs, wq, ws, doffs, 512, 256, 512, out_dtype=mx.MX_OUT_F32))
     assert np.array_equal(a, b)
+
+
+def test_fwd_two_rounds_ragged_groups(oracle):
+    """M=8192, N=4096 in 4 ragged groups (every group ends mid-tile), full output compared."""
+    m, n, k, G = 8192, 4096, 256, 4
+    rng = np.random.default_rng(21)
+    sizes = np.array([2080, 1984, 2112, 2016])  # ragged: every group ends mid-tile
+    offs = synth.offs_from_sizes(sizes)
+    x = synth.normal_bf16(rng, (m, k), 1.0)
+    w = synth.normal_bf16(rng, (G, n, k), 0.02)
+    say(f"[gemm 2-round fwd] offs={offs.tolist()}")
+    xq, xs = mx.mx_quantize_dim0(dev_bf16(x))
+    wq, ws = mx.mx_quantize_dim0(dev_bf16(w.reshape(G * n, k)))
+    y = host(mx.mx_grouped_mm_fwd(xq, xs, wq, ws, dev_i32(offs), m, n, k, out_dtype=mx.MX_OUT_F32))
+    oxq, oxs = oracle.quantize_dim0(x)
+    owq, ows = oracle.quantize_dim0(w.reshape(G * n, k))
+    ref = oracle.mx_grouped_mm_fwd(oxq, oxs, owq, ows, offs, G)
+    absprod = oracle.grouped_mm(np.abs(oracle.dequantize(oxq, oxs)), np.abs(oracle.dequantize(owq, ows)), offs, G)
+    check_f32(oracle, y, ref, "2-round fwd f32", absprod, k)
+
+
+def test_wgrad_ragged_tile_grid(oracle):
+    """K-grouped, G=4 (one empty), 2560 x 3328 outputs: partial tiles on both output edges."""
+    m, n, k, G = 256, 2560, 3328, 4
+    rng = np.random.default_rng(22)
+    offs = synth.offs_from_sizes(np.array([96, 0, 64, 96]))
+    dy = synth.normal_bf16(rng, (m, n), 1e-2)
+    x = synth.normal_bf16(rng, (m, k), 1.0)
+    say(f"[gemm ragged wgrad] offs={offs.tolist()}")
+    dytq, dyts = mx.mx_quantize_dim1(dev_bf16(dy))
+    xtq, xts = mx.mx_quantize_dim1(dev_bf16(x))
+    dw = host(mx.mx_grouped_mm_wgrad(dytq, dyts, xtq, xts, dev_i32(offs), m, n, k, out_dtype=mx.MX_OUT_F32))
+    odyt, odyts = oracle.quantize_dim1(dy)
+    oxt, oxts = oracle.quantize_dim1(x)
+    ref = oracle.mx_grouped_mm_wgrad(odyt, odyts, oxt, oxts, offs, G)
+    absw = oracle.grouped_mm_wgrad(np.abs(oracle.dequantize(odyt, odyts)), np.abs(oracle.dequantize(oxt, oxts)), offs, G)
+    check_f32(oracle, dw, ref, "ragged wgrad f32", absw, 96)
+    assert np.all(dw[1] == 0)
