@@ -10,6 +10,8 @@
 // written in the MFMA-blocked layout the grouped GEMM reads, so no rearrange pass
 // follows (torchtitan PR 5334, body: blocked E8M0 scales emitted directly).
 
+#include <algorithm>
+
 #include "common.h"
 
 namespace mx {
@@ -39,128 +41,153 @@ __device__ inline unsigned amax8(u32x4 v) {
 }
 
 // ---------------------------------------------------------------------------------
-// dim0: one wave per 32-row x 256-column tile (exactly one 256-byte scale tile).
+// dim0: a wave quantizes 32-row x 256-column tiles (each exactly one 256-byte scale
+// tile), striding over the tiles so every wave stays busy to the end and the waves
+// of a compute unit drift apart, keeping reads and writes in flight together.
 // Lane l reads 16-byte chunk (l % 32) of rows 2i + l/32, i = 0..15; the four lanes
-// of a quad hold one 32-element block, reduced with two DPP quad permutes.
+// of a quad hold one 32-element block, reduced with two DPP quad permutes. The
+// scale tile is assembled in the wave's own LDS slice (one wave's LDS accesses
+// execute in order, so no barrier is needed).
 // ---------------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_quant_dim0(const uint16_t* __restrict__ x, int64_t rows, int64_t cols,
                                                     int64_t ld, uint8_t* __restrict__ q, uint8_t* __restrict__ scale,
                                                     int64_t row_bands, int64_t ktiles) {
   __shared__ unsigned s_tile[4][64];
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63, h = l >> 5, c = l & 31;
-  const int64_t t = (int64_t)blockIdx.x * 4 + w;
-  const bool active = t < row_bands * ktiles;
-  const int64_t rb = active ? t / ktiles : 0, kt = active ? t % ktiles : 0;
-  const int64_t col0 = kt * 256 + c * 8;
-  const bool col_ok = active && col0 < cols;
-  s_tile[w][l] = 0x7f7f7f7fu;
-  __syncthreads();
-
-  u32x4 v[16];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    int64_t r = rb * 32 + 2 * i + h;
-    v[i] = (u32x4){0, 0, 0, 0};
-    if (col_ok && r < rows) v[i] = *(const u32x4*)(x + r * ld + col0);
-  }
+  const int64_t tiles = row_bands * ktiles, nwaves = (int64_t)gridDim.x * 4;
   uint8_t* st = (uint8_t*)s_tile[w];
+  for (int64_t t = (int64_t)blockIdx.x * 4 + w; t < tiles; t += nwaves) {
+    const int64_t rb = t / ktiles, kt = t % ktiles;
+    const int64_t col0 = kt * 256 + c * 8;
+    const bool col_ok = col0 < cols;
+    u32x4 v[16];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    int64_t r = rb * 32 + 2 * i + h;
-    unsigned a = amax8(v[i]);
-    a = umax(a, dpp_xor1(a));
-    a = umax(a, dpp_xor2(a));
-    int byte = rceil_byte(a);
-    u32x2 codes = encode8(v[i], byte, a);
-    if (col_ok && r < rows) {
-      *(u32x2*)(q + r * cols + col0) = codes;
-      if ((c & 3) == 0) st[scale_in_tile(2 * i + h, c >> 2)] = (uint8_t)byte;
+    for (int i = 0; i < 16; ++i) {
+      const int64_t r = rb * 32 + 2 * i + h;
+      v[i] = (u32x4){0, 0, 0, 0};
+      if (col_ok && r < rows) v[i] = *(const u32x4*)(x + r * ld + col0);
     }
+    s_tile[w][l] = 0x7f7f7f7fu;  // pad bytes of blocks past the last column
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int64_t r = rb * 32 + 2 * i + h;
+      unsigned a = amax8(v[i]);
+      a = umax(a, dpp_xor1(a));
+      a = umax(a, dpp_xor2(a));
+      const int byte = rceil_byte(a);
+      const u32x2 codes = encode8(v[i], byte, a);
+      if (col_ok && r < rows) {
+        *(u32x2*)(q + r * cols + col0) = codes;
+        if ((c & 3) == 0) st[scale_in_tile(2 * i + h, c >> 2)] = (uint8_t)byte;
+      }
+    }
+    ((unsigned*)(scale + scale_tile_base(rb, kt, ktiles)))[l] = s_tile[w][l];
   }
-  __syncthreads();
-  if (active) ((unsigned*)(scale + scale_tile_base(rb, kt, ktiles)))[l] = s_tile[w][l];
 }
 
 // ---------------------------------------------------------------------------------
-// dim1: a workgroup covers 256 input rows x 128 input columns of one batch. Wave w
-// takes rows 64w..64w+63; lane l takes the column pair (2l, 2l+1), one dword per
-// row, so every load instruction reads 256 contiguous bytes. Each lane then owns
-// two 32-row blocks of two columns and reduces them in registers; the codes of a
-// block are 32 contiguous bytes of an output row of q_t.
+// dim1: a workgroup quantizes a 256-row x 64-column tile of one batch: eight 32-row
+// blocks of each of 64 columns, which become 64 rows of q_t with 256 contiguous
+// codes each, and two full 256-byte scale tiles.
+//   Loads: lane l takes columns 8(l%8)..+7 (16 bytes); wave w, block half hb and
+//   i = 0..3 give row 64w + 32hb + 4(l/8) + i, so one load instruction reads eight
+//   rows x 128 bytes (whole lines) and a lane holds 4 consecutive rows of each of
+//   its two blocks.
+//   Amax: per column over the lane's 4 rows, then across the 8 lanes of its column
+//   group (lane bits 3..5).
+//   Encode: the same column of two rows forms one converter pair, so each column's
+//   4 rows come out as one dword of the transposed tile.
+//   Transpose: the 64 x 256-byte code tile sits in LDS with row c's bytes r XOR-ed
+//   by ((c / 8) % 8) * 32, so the dword writes (64 lanes, 64 banks) and the 16-byte
+//   row reads are both conflict-free; the stores then write 256-byte rows of q_t.
 // ---------------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_quant_dim1(const uint16_t* __restrict__ x, int64_t rows, int64_t cols,
                                                     int64_t ld, uint8_t* __restrict__ q_t,
                                                     uint8_t* __restrict__ scale_t, int64_t rtiles, int64_t ctiles) {
-  __shared__ unsigned s_tiles[4][64];
-  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+  __shared__ __attribute__((aligned(16))) uint8_t s_codes[64 * 256];
+  __shared__ unsigned s_scale[2][64];
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, cg = l & 7, g = l >> 3;
   const int64_t bid = blockIdx.x;
   const int64_t b = bid / (rtiles * ctiles);
   const int64_t rem = bid % (rtiles * ctiles);
   const int64_t ct = rem / rtiles, rt = rem % rtiles;
-  const int64_t c = ct * 128 + 2 * l;
-  const bool col_ok = c < cols;
+  const int64_t r0 = rt * 256, c0 = ct * 64;
+  const int64_t cl = c0 + 8 * cg;
+  const bool col_ok = cl < cols;  // cols % 32 == 0: a lane's 8 columns are all in or all out
   const uint16_t* xb = x + b * rows * ld;
-  uint8_t* qb = q_t + b * cols * rows;
-  s_tiles[w][l] = 0x7f7f7f7fu;
+  if (tid < 128) s_scale[tid >> 6][tid & 63] = 0x7f7f7f7fu;  // pad blocks past the last row
+
+  u32x4 v[2][4];
+#pragma unroll
+  for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t r = r0 + 64 * w + 32 * hb + 4 * g + i;
+      v[hb][i] = (u32x4){0, 0, 0, 0};
+      if (col_ok && r < rows) v[hb][i] = *(const u32x4*)(xb + r * ld + cl);
+    }
+  __syncthreads();  // pad fill of the scale tiles before the byte writes
+
+  uint8_t* ssc = (uint8_t*)s_scale;
+  const int swz = cg << 5;  // XOR applied to the row byte of code-tile rows 8cg..8cg+7
+#pragma unroll
+  for (int hb = 0; hb < 2; ++hb) {
+    const int kb = 2 * w + hb;              // block within the tile (input rows 32kb..32kb+31)
+    const int rloc = 64 * w + 32 * hb + 4 * g;  // the lane's first row within the tile
+    // packed amax of column pairs (2p, 2p+1), p = 0..3
+    unsigned am[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      unsigned a = amax_pair(0u, v[hb][0][p]);
+      a = amax_pair(a, v[hb][1][p]);
+      a = amax_pair(a, v[hb][2][p]);
+      a = amax_pair(a, v[hb][3][p]);
+      a = amax_pair(a, (unsigned)__builtin_amdgcn_mov_dpp((int)a, 0x128, 0xF, 0xF, false));  // lane ^ 8
+      a = amax_pair(a, (unsigned)__shfl_xor((int)a, 16));
+      a = amax_pair(a, (unsigned)__shfl_xor((int)a, 32));
+      am[p] = a;
+    }
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {  // column 2p + e of the lane's eight
+        const unsigned amax = e ? (am[p] >> 16) : (am[p] & 0xffff);
+        const int byte = rceil_byte(amax);
+        const bool tiny = byte == 0 && amax != 0;
+        const float sc = scale_operand(byte == 0 ? 1 : byte);
+        const unsigned sel = e ? 0x07060302u : 0x05040100u;
+        unsigned p01 = __builtin_amdgcn_perm(v[hb][1][p], v[hb][0][p], sel);  // (row 0, row 1) of the column
+        unsigned p23 = __builtin_amdgcn_perm(v[hb][3][p], v[hb][2][p], sel);
+        if (tiny) {
+          p01 = double_bf16x2(p01);
+          p23 = double_bf16x2(p23);
+        }
+        const unsigned codes = cvt2(p01, sc) | (cvt2(p23, sc) << 16);
+        const int c = 8 * cg + 2 * p + e;  // column within the tile = row of the code tile
+        *(unsigned*)(s_codes + c * 256 + (rloc ^ swz)) = codes;
+        if (g == 0 && r0 + 32 * kb < rows) ssc[(c >> 5) * 256 + scale_in_tile(c & 31, kb)] = (uint8_t)byte;
+      }
+    }
+  }
   __syncthreads();
 
-  const int64_t r0 = rt * 256 + 64 * w;
-  unsigned v[64];
+  // q_t rows c0 + 16w .. +15, four per instruction, 16 lanes x 16 bytes each
+  uint8_t* qb = q_t + b * cols * rows;
 #pragma unroll
-  for (int j = 0; j < 64; ++j) {
-    int64_t r = r0 + j;
-    v[j] = 0;
-    if (col_ok && r < rows) v[j] = *(const unsigned*)(xb + r * ld + c);
+  for (int k = 0; k < 4; ++k) {
+    const int orow = 16 * w + 4 * k + (l >> 4), chunk = l & 15;
+    const int64_t c = c0 + orow, rr = r0 + 16 * chunk;
+    const u32x4 d = *(const u32x4*)(s_codes + orow * 256 + ((chunk ^ (((orow >> 3) & 7) << 1)) << 4));
+    if (c < cols && rr < rows) *(u32x4*)(qb + c * rows + rr) = d;
   }
-  uint8_t* st = (uint8_t*)s_tiles;
-#pragma unroll
-  for (int half = 0; half < 2; ++half) {
-    const int64_t rb = r0 + 32 * half;  // first input row of the block
-    unsigned am = 0;
-#pragma unroll
-    for (int j = 0; j < 32; ++j) am = amax_pair(am, v[32 * half + j]);
-    const unsigned a_lo = am & 0xffff, a_hi = am >> 16;
-    const int b_lo = rceil_byte(a_lo), b_hi = rceil_byte(a_hi);
-    const bool tiny_lo = b_lo == 0 && a_lo != 0, tiny_hi = b_hi == 0 && a_hi != 0;
-    const float s_lo = scale_operand(b_lo == 0 ? 1 : b_lo), s_hi = scale_operand(b_hi == 0 ? 1 : b_hi);
-    unsigned o_lo[8], o_hi[8];
-#pragma unroll
-    for (int p = 0; p < 8; ++p) {
-      unsigned cl[2], ch[2];
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const unsigned v0 = v[32 * half + 4 * p + 2 * e], v1 = v[32 * half + 4 * p + 2 * e + 1];
-        unsigned lo = __builtin_amdgcn_perm(v1, v0, 0x05040100u);  // (col lo of row j, col lo of row j+1)
-        unsigned hi = __builtin_amdgcn_perm(v1, v0, 0x07060302u);  // (col hi of row j, col hi of row j+1)
-        if (tiny_lo) lo = double_bf16x2(lo);
-        if (tiny_hi) hi = double_bf16x2(hi);
-        cl[e] = cvt2(lo, s_lo);
-        ch[e] = cvt2(hi, s_hi);
-      }
-      o_lo[p] = cl[0] | (cl[1] << 16);
-      o_hi[p] = ch[0] | (ch[1] << 16);
+  if (tid < 128) {
+    const int tile = tid >> 6;
+    const int64_t out_row0 = c0 + 32 * tile;  // first q_t row of this scale tile
+    if (out_row0 < cols) {
+      const int64_t band = (b * cols + out_row0) / 32;
+      const int64_t ktiles = scale_tiles_k(rows / 32);
+      ((unsigned*)(scale_t + scale_tile_base(band, rt, ktiles)))[tid & 63] = s_scale[tile][tid & 63];
     }
-    if (col_ok && rb < rows) {
-      u32x4* d0 = (u32x4*)(qb + c * rows + rb);
-      u32x4* d1 = (u32x4*)(qb + (c + 1) * rows + rb);
-      d0[0] = (u32x4){o_lo[0], o_lo[1], o_lo[2], o_lo[3]};
-      d0[1] = (u32x4){o_lo[4], o_lo[5], o_lo[6], o_lo[7]};
-      d1[0] = (u32x4){o_hi[0], o_hi[1], o_hi[2], o_hi[3]};
-      d1[1] = (u32x4){o_hi[4], o_hi[5], o_hi[6], o_hi[7]};
-      // scale tile (l / 16) of this workgroup, rows 2l % 32 and (2l+1) % 32, block 2w + half
-      const int tile = l >> 4, kb = 2 * w + half;
-      st[tile * 256 + scale_in_tile((2 * l) & 31, kb)] = (uint8_t)b_lo;
-      st[tile * 256 + scale_in_tile((2 * l + 1) & 31, kb)] = (uint8_t)b_hi;
-    }
-  }
-  __syncthreads();
-  // thread t writes dword t % 64 of scale tile t / 64
-  const int tile = threadIdx.x >> 6;
-  const int64_t out_row0 = ct * 128 + 32 * tile;  // first output row (input column) of the tile
-  if (out_row0 < cols) {
-    const int64_t band = (b * cols + out_row0) / 32;
-    const int64_t ktiles = scale_tiles_k(rows / 32);
-    ((unsigned*)(scale_t + scale_tile_base(band, rt, ktiles)))[l] = s_tiles[tile][l];
   }
 }
 
@@ -269,12 +296,27 @@ __global__ __launch_bounds__(256) void k_quant_w32(const uint16_t* __restrict__ 
 // ---------------------------------------------------------------------------------
 // Launchers (called by the C ABI after validation)
 // ---------------------------------------------------------------------------------
+
+namespace {
+// Blocks that fill the current device once: resident blocks per compute unit for
+// this kernel (from its register and LDS use) times the compute units.
+int64_t resident_blocks(const void* kernel, int threads) {
+  int dev = 0, cus = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 1024;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess || per_cu <= 0) per_cu = 1;
+  return (int64_t)cus * per_cu;
+}
+}  // namespace
 hipError_t mx_launch_dim0(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, uint8_t* q, uint8_t* scale,
                           hipStream_t stream) {
   const int64_t row_bands = (rows + 31) / 32, ktiles = mx::scale_tiles_k(cols / 32);
   const int64_t tiles = row_bands * ktiles;
   if (tiles == 0) return hipSuccess;
-  const int64_t blocks = (tiles + 3) / 4;
+  // enough 4-wave blocks to fill the device once, each wave striding over the tiles
+  static int64_t fill = 0;  // per process; every gfx950 part has the same shape
+  if (fill == 0) fill = resident_blocks((const void*)mx::k_quant_dim0, 256);
+  const int64_t blocks = std::min<int64_t>((tiles + 3) / 4, fill);
   hipLaunchKernelGGL(mx::k_quant_dim0, dim3((unsigned)blocks), dim3(256), 0, stream, x, rows, cols, ld, q, scale,
                      row_bands, ktiles);
   return hipGetLastError();
@@ -282,7 +324,7 @@ hipError_t mx_launch_dim0(const uint16_t* x, int64_t rows, int64_t cols, int64_t
 
 hipError_t mx_launch_dim1(const uint16_t* x, int64_t batch, int64_t rows, int64_t cols, int64_t ld, uint8_t* q_t,
                           uint8_t* scale_t, hipStream_t stream) {
-  const int64_t rtiles = (rows + 255) / 256, ctiles = (cols + 127) / 128;
+  const int64_t rtiles = (rows + 255) / 256, ctiles = (cols + 63) / 64;
   const int64_t blocks = batch * rtiles * ctiles;
   if (blocks == 0) return hipSuccess;
   hipLaunchKernelGGL(mx::k_quant_dim1, dim3((unsigned)blocks), dim3(256), 0, stream, x, rows, cols, ld, q_t,
