@@ -176,32 +176,55 @@ def main():
         print(json.dumps({"only": [o[0] for o in sel], "launches": args.warmup + args.steps}))
         return
 
-    def step(events=None):
+    def step(events=None, only=None):
         for i, (_, _, _, fn) in enumerate(ops):
-            if events is not None:
+            rec = events is not None and (only is None or i == only)
+            if rec:
                 events[i][0].record()
             fn()
-            if events is not None:
+            if rec:
                 events[i][1].record()
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    def new_events(n):
+        return [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)] for _ in ops]
+                for _ in range(n)]
 
-    # timed region: exactly `steps` steps, events around every launch on the current stream
-    ev = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)] for _ in ops]
-          for _ in range(args.steps)]
+    def mean_ms(evs, i):
+        return float(np.mean([e[i][0].elapsed_time(e[i][1]) for e in evs]))
+
+    # W warm-up steps, with events around every launch: they pick the dominant
+    # (longest) kernel; without warm-up, the op with the most work is taken
+    wev = new_events(args.warmup)
+    for w in range(args.warmup):
+        step(wev[w])
+    torch.cuda.synchronize()
+    if args.warmup:
+        dom_i = max(range(len(ops)), key=lambda i: mean_ms(wev[1:] or wev, i))
+    else:
+        dom_i = max(range(len(ops)), key=lambda i: ops[i][2] if ops[i][1] == "gemm" else 0)
+
+    # timed region: exactly `steps` steps; events only around the dominant kernel's
+    # launches (on the current stream, where every op runs), for its launch duration
+    ev = new_events(args.steps)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):
-        step(ev[s])
+        step(ev[s], only=dom_i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
+    dom_ms = mean_ms(ev, dom_i)
+
+    # per-kernel breakdown: a further `steps` steps with events around every launch
+    # (reported only; not part of the timed region)
+    bev = new_events(args.steps)
+    for s in range(args.steps):
+        step(bev[s])
+    torch.cuda.synchronize()
 
     per_op = {}
     for i, (name, kind, units, _) in enumerate(ops):
-        ms = float(np.mean([ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(args.steps)]))
+        ms = dom_ms if i == dom_i else mean_ms(bev, i)
         rate = units / (ms * 1e-3) / (1e12 if kind == "gemm" else 1e9)
         peak = PEAK_FP8_TFLOPS if kind == "gemm" else PEAK_HBM_GBPS
         per_op[name] = {"us": round(ms * 1e3, 2), ("tflops" if kind == "gemm" else "gbps"): round(rate, 1),
@@ -213,8 +236,8 @@ def main():
     cast_us = sum(per_op[n]["us"] for n, k, _, _ in ops if k == "cast")
     value = gemm_flops / (ms_per_step * 1e-3) / 1e12
 
-    # dominant kernel: the longest launch of the step
-    dom_name, dom_kind, dom_units, _ = max(ops, key=lambda o: per_op[o[0]]["us"])
+    # dominant kernel: the longest launch of the step (timed inside the timed region)
+    dom_name, dom_kind, dom_units, _ = ops[dom_i]
     dom = per_op[dom_name]
     achieved = dom_units / (dom["us"] * 1e-6) / 1e12
     traffic = load_traffic(dom_name, dom_units)
