@@ -112,8 +112,19 @@ __device__ inline Tile tile_at(const GemmArgs& p, int64_t t) {
   int64_t r = t;
   int g = 0;
   if (MODE == MODE_KGROUP) {
-    g = (int)(t / per_g);
-    r = t % per_g;
+    // slice-major: each group's raster is cut into 8 slices of S tiles and the
+    // order runs slice by slice, every group's slice s before slice s+1, the groups
+    // of slice s starting at group s. The XCD remap hands XCD x about the x-th
+    // eighth of the order, i.e. slice x of every group: the XCDs share each group's
+    // (uneven) contraction length evenly, and at any moment they work on different
+    // groups, so their reads spread over different token ranges of the operands.
+    const int64_t S = (per_g + 7) / 8;
+    const int64_t G = p.groups;
+    const int64_t sl = t / (G * S);
+    const int64_t n_s = per_g - sl * S < S ? per_g - sl * S : S;  // tiles in this slice
+    const int64_t rem = t - sl * G * S;
+    g = (int)((rem / n_s + sl) % G);  // rotated by the slice: XCDs work on different groups at once
+    r = sl * S + rem % n_s;
   }
   const int64_t band = r / (GM * p.nt);
   const int64_t first_m = band * GM;
