@@ -21,6 +21,9 @@
 // lane accumulates four consecutive output columns of one output row per v/4:
 // C[row l % 32][col 8*(v/4) + 4*h + v%4], which it stores directly.
 
+#include <algorithm>
+#include <mutex>
+
 #include "common.h"
 
 namespace mx {
@@ -43,6 +46,8 @@ struct GemmArgs {
   int64_t mt_total, nt;  // tile grid: m-tiles (upper bound for M-grouped), n-tiles
   int64_t tiles;         // logical tiles (some M-grouped ones may be empty)
   int groups;
+  int splits;            // K-grouped: contraction splits (1 = none), partials in fp32 at out
+  int64_t split_stride;  // elements between the partial outputs of consecutive splits
 };
 
 // Block tile BM x BN over a WGM x WGN grid of waves, each wave (BM/WGM) x (BN/WGN)
@@ -111,7 +116,10 @@ __device__ inline Tile tile_at(const GemmArgs& p, int64_t t) {
   const int64_t per_g = p.mt_total * p.nt;
   int64_t r = t;
   int g = 0;
+  int sp = 0;  // contraction split (K-grouped only)
   if (MODE == MODE_KGROUP) {
+    sp = (int)(t / (p.groups * per_g));
+    t -= (int64_t)sp * p.groups * per_g;
     // slice-major: each group's raster is cut into 8 slices of S tiles and the
     // order runs slice by slice, every group's slice s before slice s+1, the groups
     // of slice s starting at group s. The XCD remap hands XCD x about the x-th
@@ -164,6 +172,19 @@ __device__ inline Tile tile_at(const GemmArgs& p, int64_t t) {
     T.b_row_end = p.N;
     T.k_beg = p.offs ? group_start(p.offs, g) : 0;
     T.k_end = p.offs ? p.offs[g] : p.K;
+    if (p.splits > 1) {
+      // split sp of `splits` takes a run of whole 256-wide windows (counted from the
+      // 256-aligned start of the group's range), so no split adds masked steps; it
+      // writes an fp32 partial, summed afterwards in split order
+      const int64_t k0 = (T.k_beg / 256) * 256;
+      const int64_t wins = T.k_end > T.k_beg ? (T.k_end - k0 + 255) / 256 : 0;
+      const int64_t w0 = wins * sp / p.splits, w1 = wins * (sp + 1) / p.splits;
+      const int64_t nb = k0 + 256 * w0 > T.k_beg ? k0 + 256 * w0 : T.k_beg;
+      const int64_t ne = k0 + 256 * w1 < T.k_end ? k0 + 256 * w1 : T.k_end;
+      T.k_beg = nb;
+      T.k_end = ne > nb ? ne : nb;
+      T.out_base += (int64_t)sp * p.split_stride * out_es;
+    }
     T.out_base += (int64_t)g * p.M * p.ldo * out_es;
   }
   return T;
@@ -461,6 +482,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm(GemmArgs p) {
 
 namespace {
 
+constexpr int64_t kComputeUnits = 256;
+
 // Tile configurations: 256x256 for large problems; 128x128 where 256x256 tiles
 // would leave most compute units idle.
 template <int BM, int BN, int WGM, int WGN, int MODE>
@@ -469,7 +492,7 @@ hipError_t launch_cfg(mx::GemmArgs p, int out_bf16, hipStream_t stream) {
   const int64_t mt_extra = (MODE == mx::MODE_MGROUP && p.offs) ? p.groups : 0;
   p.mt_total = (p.M + BM - 1) / BM + mt_extra;
   p.nt = (p.N + BN - 1) / BN;
-  p.tiles = MODE == mx::MODE_MGROUP ? p.mt_total * p.nt : (int64_t)p.groups * p.mt_total * p.nt;
+  p.tiles = MODE == mx::MODE_MGROUP ? p.mt_total * p.nt : (int64_t)p.splits * p.groups * p.mt_total * p.nt;
   if (p.tiles == 0) return hipSuccess;
   const int64_t blocks = p.tiles;
   const size_t lds = (size_t)C::LDS_BYTES;
@@ -493,8 +516,93 @@ hipError_t launch_cfg(mx::GemmArgs p, int out_bf16, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// Sums the fp32 partials of `splits` contraction splits (split s at ws + s * stride)
+// in split order into n outputs, fp32 or bf16. Four elements per thread.
+__global__ __launch_bounds__(256) void k_split_reduce(const float* __restrict__ ws, int splits, int64_t stride,
+                                                      int64_t n, void* __restrict__ out, int out_bf16) {
+  const int64_t step = (int64_t)gridDim.x * 256 * 4;
+  for (int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4; i < n; i += step) {
+    if (i + 4 <= n) {
+      mx::v4f acc = *(const mx::v4f*)(ws + i);
+      for (int s = 1; s < splits; ++s) acc += *(const mx::v4f*)(ws + s * stride + i);
+      if (out_bf16)
+        *(mx::u32x2*)((uint16_t*)out + i) = (mx::u32x2){mx::bf16x2_rne(acc[0], acc[1]), mx::bf16x2_rne(acc[2], acc[3])};
+      else
+        *(mx::v4f*)((float*)out + i) = acc;
+    } else {
+      for (int64_t j = i; j < n; ++j) {
+        float a = ws[j];
+        for (int s = 1; s < splits; ++s) a += ws[s * stride + j];
+        if (out_bf16)
+          ((uint16_t*)out)[j] = (uint16_t)mx::bf16x2_rne(a, 0.f);
+        else
+          ((float*)out)[j] = a;
+      }
+    }
+  }
+}
+
+// Per-device fp32 workspace for split partials, grown on demand. Growing waits for
+// the device first, so no launched kernel still uses the old buffer.
+hipError_t split_workspace(size_t bytes, float** ptr) {
+  static std::mutex mu;
+  static void* buf[64] = {};
+  static size_t cap[64] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (cap[dev] < bytes) {
+    if (buf[dev]) {
+      if ((e = hipDeviceSynchronize()) != hipSuccess) return e;
+      if ((e = hipFree(buf[dev])) != hipSuccess) return e;
+      buf[dev] = nullptr;
+      cap[dev] = 0;
+    }
+    if ((e = hipMalloc(&buf[dev], bytes)) != hipSuccess) return e;
+    cap[dev] = bytes;
+  }
+  *ptr = (float*)buf[dev];
+  return hipSuccess;
+}
+
+// K-grouped outputs with fewer 256x256 tiles than compute units, over a long
+// contraction (weight gradients of narrow layers): split each group's contraction
+// so the splits fill about one round of the chip. Returns 1 for no split.
+int choose_splits(const mx::GemmArgs& p) {
+  const int64_t tiles = (int64_t)p.groups * ((p.M + 255) / 256) * ((p.N + 255) / 256);
+  if (tiles >= kComputeUnits || tiles == 0) return 1;
+  const int64_t wins_per_group = (p.K + 255) / 256 / p.groups;  // 256-wide windows per group, on average
+  int64_t s = kComputeUnits / tiles;
+  s = std::min<int64_t>(s, wins_per_group / 2);  // at least two windows (8 k-steps) per split
+  s = std::min<int64_t>(s, 16);
+  return s >= 2 ? (int)s : 1;
+}
+
 template <int MODE>
 hipError_t launch(mx::GemmArgs& p, int out_bf16, hipStream_t stream) {
+  p.splits = 1;
+  if (MODE == mx::MODE_KGROUP) {
+    const int splits = choose_splits(p);
+    if (splits > 1) {
+      const int64_t n_out = (int64_t)p.groups * p.M * p.N;
+      const int64_t stride = (n_out + 3) / 4 * 4;  // keeps every partial 16-byte aligned
+      float* ws = nullptr;
+      hipError_t e = split_workspace((size_t)stride * splits * sizeof(float), &ws);
+      if (e != hipSuccess) return e;
+      mx::GemmArgs q = p;
+      q.splits = splits;
+      q.split_stride = stride;
+      q.out = ws;
+      e = launch_cfg<256, 256, 2, 2, MODE>(q, 0, stream);
+      if (e != hipSuccess) return e;
+      const int64_t blocks = std::min<int64_t>((n_out + 1023) / 1024, 4096);
+      hipLaunchKernelGGL(k_split_reduce, dim3((unsigned)std::max<int64_t>(blocks, 1)), dim3(256), 0, stream, ws,
+                         splits, stride, n_out, p.out, out_bf16);
+      return hipGetLastError();
+    }
+  }
   const int64_t groups_tiles = MODE == mx::MODE_KGROUP ? p.groups : 1;
   const int64_t big_tiles = groups_tiles * ((p.M + 255) / 256) * ((p.N + 255) / 256);
   // 2 x 2 waves of 128 x 128 (256 accumulators each, one wave per SIMD); 8-wave

@@ -235,3 +235,34 @@ def test_wgrad_ragged_tile_grid(oracle):
     absw = oracle.grouped_mm_wgrad(np.abs(oracle.dequantize(odyt, odyts)), np.abs(oracle.dequantize(oxt, oxts)), offs, G)
     check_f32(oracle, dw, ref, "ragged wgrad f32", absw, 96)
     assert np.all(dw[1] == 0)
+
+
+@pytest.mark.parametrize("out_dtype", [mx.MX_OUT_F32, mx.MX_OUT_BF16])
+def test_wgrad_split_contraction(oracle, out_dtype):
+    """576 x 512 outputs per group over 8192 tokens: few output tiles, so the contraction
+    is split (fp32 partials summed in order); group 0 ends off a 256 boundary, group 1 is empty."""
+    m, n, k = 8192, 576, 512
+    sizes = np.array([2080, 0, 6112])
+    G = len(sizes)
+    offs = synth.offs_from_sizes(sizes)
+    rng = np.random.default_rng(23)
+    dy = synth.normal_bf16(rng, (m, n), 1e-2)
+    x = synth.normal_bf16(rng, (m, k), 1.0)
+    say(f"[gemm split wgrad] offs={offs.tolist()} out={'bf16' if out_dtype else 'f32'}")
+    dytq, dyts = mx.mx_quantize_dim1(dev_bf16(dy))
+    xtq, xts = mx.mx_quantize_dim1(dev_bf16(x))
+    dw = mx.mx_grouped_mm_wgrad(dytq, dyts, xtq, xts, dev_i32(offs), m, n, k, out_dtype=out_dtype)
+    again = mx.mx_grouped_mm_wgrad(dytq, dyts, xtq, xts, dev_i32(offs), m, n, k, out_dtype=out_dtype)
+    got, got2 = host(dw), host(again)
+    assert np.array_equal(got, got2), "split reduction must be deterministic"
+    odyt, odyts = oracle.quantize_dim1(dy)
+    oxt, oxts = oracle.quantize_dim1(x)
+    da, db = oracle.dequantize(odyt, odyts), oracle.dequantize(oxt, oxts)
+    ref = oracle.grouped_mm_wgrad(da, db, offs, G)
+    absw = oracle.grouped_mm_wgrad(np.abs(da), np.abs(db), offs, G)
+    if out_dtype == mx.MX_OUT_F32:
+        check_f32(oracle, got, ref, "split wgrad f32", absw, int(sizes.max()))
+        assert np.all(got[1] == 0)
+    else:
+        check_bf16(oracle, got, ref, absw, int(sizes.max()), "split wgrad bf16")
+        assert np.all(got[1] == 0)
