@@ -270,37 +270,38 @@ def main():
 def cpu_baseline():
     """The CPU oracle on a bounded slice of the same step, in the same unit.
 
-    Slice: expert 0's weight [4096, 4096] and 2048 token rows routed to it (with
-    their grad_out rows): oracle dim0 and dim1 casts of all three operands, then
-    the float64 forward, dgrad and wgrad. value = GEMM flops / total time.
+    Slice: three experts, each a weight [4096, 4096] with 2048 token rows routed to
+    it (and their grad_out rows), drawn like the benchmark's tensors: oracle dim0
+    and dim1 casts of all three operands, then the float64 forward, dgrad and
+    wgrad. About 10-15 s of host time. value = GEMM flops / total time.
     """
     import threadpoolctl
 
     from mxfp8_block_scaled_amd import synth
     from oracle import mx as orc
 
-    r = synth.spawn(0, 6)
-    rows = 2048
-    x = synth.normal_bf16(r[1], (rows, K), 1.0)
-    w = synth.normal_bf16(r[2], (N, K), 0.02)
-    dy = synth.normal_bf16(r[3], (rows, N), 1e-2)
+    experts, rows = 3, 2048
+    r = synth.spawn(0, 3 * experts)
+    data = [(synth.normal_bf16(r[3 * e], (rows, K), 1.0), synth.normal_bf16(r[3 * e + 1], (N, K), 0.02),
+             synth.normal_bf16(r[3 * e + 2], (rows, N), 1e-2)) for e in range(experts)]
     t0 = time.perf_counter()
-    xq, xs = orc.quantize_dim0(x)
-    wq, ws = orc.quantize_dim0(w)
-    orc.mx_grouped_mm_fwd(xq, xs, wq, ws, None, 1)
-    dyq, dys = orc.quantize_dim0(dy)
-    wtq, wts = orc.quantize_dim1(w)
-    orc.mx_grouped_mm_fwd(dyq, dys, wtq, wts, None, 1)
-    dytq, dyts = orc.quantize_dim1(dy)
-    xtq, xts = orc.quantize_dim1(x)
-    orc.mx_grouped_mm_wgrad(dytq, dyts, xtq, xts, None, 1)
+    for x, w, dy in data:
+        xq, xs = orc.quantize_dim0(x)
+        wq, ws = orc.quantize_dim0(w)
+        orc.mx_grouped_mm_fwd(xq, xs, wq, ws, None, 1)
+        dyq, dys = orc.quantize_dim0(dy)
+        wtq, wts = orc.quantize_dim1(w)
+        orc.mx_grouped_mm_fwd(dyq, dys, wtq, wts, None, 1)
+        dytq, dyts = orc.quantize_dim1(dy)
+        xtq, xts = orc.quantize_dim1(x)
+        orc.mx_grouped_mm_wgrad(dytq, dyts, xtq, xts, None, 1)
     dt = time.perf_counter() - t0
-    flops = 3 * 2 * rows * N * K
+    flops = experts * 3 * 2 * rows * N * K
     threads = max([i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()] or [1])
     return {"value": round(flops / dt / 1e12, 5), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "seconds": round(dt, 2),
-            "sample": f"expert-0 slice: {rows} token rows x W[{N},{K}]; oracle dim0+dim1 casts of X, W, dY and "
-                      "float64 fwd+dgrad+wgrad (numpy; casts single-threaded, BLAS matmul multi-threaded)"}
+            "sample": f"{experts} expert slices, each {rows} token rows x W[{N},{K}]; oracle dim0+dim1 casts of X, W, "
+                      "dY and float64 fwd+dgrad+wgrad (numpy; casts single-threaded, BLAS matmul multi-threaded)"}
 
 
 if __name__ == "__main__":

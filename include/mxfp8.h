@@ -24,13 +24,17 @@
  *
  * CONVENTIONS (every entry point)
  *   - Pointers are device pointers unless stated; the caller allocates and frees
- *     every buffer. The library allocates no device memory and keeps no state
- *     beyond a per-device architecture check.
+ *     every buffer. The library keeps no state beyond a per-device architecture
+ *     check and one exception: mx_grouped_mm_wgrad with few output tiles uses a
+ *     per-device fp32 workspace for split contractions (see there), which the
+ *     library allocates on first need and grows after synchronising the device.
  *   - bf16 data is passed as uint16_t bit patterns; E4M3 codes and E8M0 scales
  *     as uint8_t; `stream` is a hipStream_t (NULL = the default stream).
- *   - Work is enqueued asynchronously on `stream`. No call synchronises the host,
- *     copies device memory to the host or reads `offs` on the host, so sequences
- *     of calls can be captured into a HIP graph.
+ *   - Work is enqueued asynchronously on `stream`. No call copies device memory
+ *     to the host or reads `offs` on the host, and apart from the workspace
+ *     growth above no call synchronises the host, so sequences of calls can be
+ *     captured into a HIP graph once the largest split-contraction wgrad of the
+ *     sequence has run once before the capture (the workspace then exists).
  *   - Arguments are validated on the host before anything is launched. On any
  *     error nothing is launched, a negative status is returned and
  *     mx_last_error() describes the problem (thread-local string).
@@ -170,7 +174,13 @@ mx_status mx_grouped_mm_dgrad(const uint8_t* dy, const uint8_t* dy_s, const uint
  *   offs, groups  group g contracts over rows [offs[g-1], offs[g]) of m; NULL =
  *                 one group over all m. Same caller preconditions as fwd.
  *   dw            [groups x n x k] (written, every element)
- * m % 32 == 0 (the contraction), n >= 1, k >= 1. */
+ * m % 32 == 0 (the contraction), n >= 1, k >= 1.
+ * When the output has fewer 256 x 256 tiles than the device has compute units
+ * (narrow layers), each group's contraction is split at 256-token window
+ * boundaries into S parts (enough to fill the device once, at most 16); fp32
+ * partials go to a per-device workspace of S * groups * n * k * 4 bytes (rounded
+ * up to 16), allocated by the library on first need, and a second kernel sums
+ * them in split order, so results are deterministic. */
 mx_status mx_grouped_mm_wgrad(const uint8_t* dy_t, const uint8_t* dy_t_s, const uint8_t* x_t, const uint8_t* x_t_s,
                               const int32_t* offs, int32_t groups, int64_t m, int64_t n, int64_t k, void* dw,
                               int out_dtype, void* stream);
