@@ -36,6 +36,7 @@ PEAK_FP8_TFLOPS = 5000.0  # MI355X dense fp8 / MXFP8 MFMA
 PEAK_HBM_GBPS = 8000.0
 CAST_BYTES_PER_ELEM = 2 + 1 + 1 / 32  # read bf16, write e4m3 + one scale byte per 32
 W32_BYTES_PER_ELEM = 2 + 1 + 1 + 2 / 32  # both orientations, row and column scales
+BOTH_BYTES_PER_ELEM = 2 + 1 + 1 + 2 / 32  # one-pass dim0 + dim1: read once, both codes and scales
 M, K, N, G, NARROW = 16384, 4096, 4096, 8, 576
 
 
@@ -45,6 +46,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--separate-casts", action="store_true",
+                    help="cast each tensor with separate dim0 and dim1 kernels instead of the one-pass cast")
     ap.add_argument("--only", default=None,
                     help="run only the ops of the step whose name contains this text (for counter runs)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -126,41 +129,64 @@ def main():
 
     # (name, kind, work units, fn) ; kind "gemm": units = flops, "cast": units = bytes
     cast0 = lambda n_elem: n_elem * CAST_BYTES_PER_ELEM  # noqa: E731
-    ops = [
-        ("cast_dim0 X", "cast", cast0(M * K), lambda: mx.mx_quantize_dim0(X, buf["xq"], buf["xs"])),
-        ("cast_dim0 W", "cast", cast0(G * N * K), lambda: mx.mx_quantize_dim0(Wflat, buf["wq"], buf["ws"])),
-        ("gemm_fwd grouped", "gemm", 2 * M * N * K,
-         lambda: mx.mx_grouped_mm_fwd(buf["xq"], buf["xs"], buf["wq"], buf["ws"], offs, M, N, K, out=buf["y"])),
-        ("cast_dim0 dY", "cast", cast0(M * N), lambda: mx.mx_quantize_dim0(dY, buf["dyq"], buf["dys"])),
-        ("cast_dim1 W", "cast", cast0(G * N * K), lambda: mx.mx_quantize_dim1(W, buf["wtq"], buf["wts"])),
-        ("gemm_dgrad grouped", "gemm", 2 * M * N * K,
-         lambda: mx.mx_grouped_mm_dgrad(buf["dyq"], buf["dys"], buf["wtq"], buf["wts"], offs, M, N, K, out=buf["dx"])),
-        ("cast_dim1 dY", "cast", cast0(M * N), lambda: mx.mx_quantize_dim1(dY, buf["dytq"], buf["dyts"])),
-        ("cast_dim1 X", "cast", cast0(M * K), lambda: mx.mx_quantize_dim1(X, buf["xtq"], buf["xts"])),
-        ("gemm_wgrad grouped", "gemm", 2 * M * N * K,
-         lambda: mx.mx_grouped_mm_wgrad(buf["dytq"], buf["dyts"], buf["xtq"], buf["xts"], offs, M, N, K,
-                                        out=buf["dw"], out_dtype=mx.MX_OUT_BF16)),
-        ("cast_w32 W'", "cast", NARROW * K * W32_BYTES_PER_ELEM, None),  # set below (returns buffers)
-        ("gemm_fwd dense576", "gemm", 2 * M * NARROW * K, None),
-        ("cast_dim0 dY'", "cast", cast0(M * NARROW), lambda: mx.mx_quantize_dim0(dYn, buf["dynq"], buf["dyns"])),
-        ("gemm_dgrad dense576", "gemm", 2 * M * NARROW * K, None),
-        ("cast_dim1 dY'", "cast", cast0(M * NARROW), lambda: mx.mx_quantize_dim1(dYn, buf["dyntq"], buf["dynts"])),
-        ("gemm_wgrad dense576", "gemm", 2 * M * NARROW * K,
-         lambda: mx.mx_grouped_mm_wgrad(buf["dyntq"], buf["dynts"], buf["xtq"], buf["xts"], None, M, NARROW, K,
-                                        out=buf["dwn"], out_dtype=mx.MX_OUT_BF16)),
-    ]
+    both = lambda n_elem: n_elem * BOTH_BYTES_PER_ELEM  # noqa: E731
     w32 = {}
 
     def cast_w32():
         w32["q"], w32["qt"], w32["sr"], w32["sc"] = mx.mx_quantize_weight_32x32(Wn)
 
-    ops[9] = (ops[9][0], ops[9][1], ops[9][2], cast_w32)
-    ops[10] = (ops[10][0], ops[10][1], ops[10][2],
-               lambda: mx.mx_grouped_mm_fwd(buf["xq"], buf["xs"], w32["q"], w32["sr"], None, M, NARROW, K,
-                                            out=buf["yn"]))
-    ops[12] = (ops[12][0], ops[12][1], ops[12][2],
+    g_fwd = ("gemm_fwd grouped", "gemm", 2 * M * N * K,
+             lambda: mx.mx_grouped_mm_fwd(buf["xq"], buf["xs"], buf["wq"], buf["ws"], offs, M, N, K, out=buf["y"]))
+    g_dgrad = ("gemm_dgrad grouped", "gemm", 2 * M * N * K,
+               lambda: mx.mx_grouped_mm_dgrad(buf["dyq"], buf["dys"], buf["wtq"], buf["wts"], offs, M, N, K,
+                                              out=buf["dx"]))
+    g_wgrad = ("gemm_wgrad grouped", "gemm", 2 * M * N * K,
+               lambda: mx.mx_grouped_mm_wgrad(buf["dytq"], buf["dyts"], buf["xtq"], buf["xts"], offs, M, N, K,
+                                              out=buf["dw"], out_dtype=mx.MX_OUT_BF16))
+    n_w32 = ("cast_w32 W'", "cast", NARROW * K * W32_BYTES_PER_ELEM, cast_w32)
+    n_fwd = ("gemm_fwd dense576", "gemm", 2 * M * NARROW * K,
+             lambda: mx.mx_grouped_mm_fwd(buf["xq"], buf["xs"], w32["q"], w32["sr"], None, M, NARROW, K,
+                                          out=buf["yn"]))
+    n_dgrad = ("gemm_dgrad dense576", "gemm", 2 * M * NARROW * K,
                lambda: mx.mx_grouped_mm_dgrad(buf["dynq"], buf["dyns"], w32["qt"], w32["sc"], None, M, NARROW, K,
                                               out=buf["dxn"]))
+    n_wgrad = ("gemm_wgrad dense576", "gemm", 2 * M * NARROW * K,
+               lambda: mx.mx_grouped_mm_wgrad(buf["dyntq"], buf["dynts"], buf["xtq"], buf["xts"], None, M, NARROW,
+                                              K, out=buf["dwn"], out_dtype=mx.MX_OUT_BF16))
+    if args.separate_casts:
+        ops = [
+            ("cast_dim0 X", "cast", cast0(M * K), lambda: mx.mx_quantize_dim0(X, buf["xq"], buf["xs"])),
+            ("cast_dim0 W", "cast", cast0(G * N * K), lambda: mx.mx_quantize_dim0(Wflat, buf["wq"], buf["ws"])),
+            g_fwd,
+            ("cast_dim0 dY", "cast", cast0(M * N), lambda: mx.mx_quantize_dim0(dY, buf["dyq"], buf["dys"])),
+            ("cast_dim1 W", "cast", cast0(G * N * K), lambda: mx.mx_quantize_dim1(W, buf["wtq"], buf["wts"])),
+            g_dgrad,
+            ("cast_dim1 dY", "cast", cast0(M * N), lambda: mx.mx_quantize_dim1(dY, buf["dytq"], buf["dyts"])),
+            ("cast_dim1 X", "cast", cast0(M * K), lambda: mx.mx_quantize_dim1(X, buf["xtq"], buf["xts"])),
+            g_wgrad,
+            n_w32, n_fwd,
+            ("cast_dim0 dY'", "cast", cast0(M * NARROW), lambda: mx.mx_quantize_dim0(dYn, buf["dynq"], buf["dyns"])),
+            n_dgrad,
+            ("cast_dim1 dY'", "cast", cast0(M * NARROW),
+             lambda: mx.mx_quantize_dim1(dYn, buf["dyntq"], buf["dynts"])),
+            n_wgrad,
+        ]
+    else:
+        # every tensor here is needed in both orientations: one-pass casts
+        ops = [
+            ("cast_dim0+dim1 X", "cast", both(M * K),
+             lambda: mx.mx_quantize_dim0_dim1(X, buf["xq"], buf["xs"], buf["xtq"], buf["xts"])),
+            ("cast_dim0+dim1 W", "cast", both(G * N * K),
+             lambda: mx.mx_quantize_dim0_dim1(W, buf["wq"], buf["ws"], buf["wtq"], buf["wts"])),
+            g_fwd,
+            ("cast_dim0+dim1 dY", "cast", both(M * N),
+             lambda: mx.mx_quantize_dim0_dim1(dY, buf["dyq"], buf["dys"], buf["dytq"], buf["dyts"])),
+            g_dgrad, g_wgrad,
+            n_w32, n_fwd,
+            ("cast_dim0+dim1 dY'", "cast", both(M * NARROW),
+             lambda: mx.mx_quantize_dim0_dim1(dYn, buf["dynq"], buf["dyns"], buf["dyntq"], buf["dynts"])),
+            n_dgrad, n_wgrad,
+        ]
 
     if args.only:
         # the casts an op depends on still run once, untimed, so its inputs exist

@@ -115,6 +115,20 @@ mx_status mx_quantize_dim0(const uint16_t* x, int64_t rows, int64_t cols, int64_
 mx_status mx_quantize_dim1(const uint16_t* x, int64_t batch, int64_t rows, int64_t cols, int64_t ld_x,
                            uint8_t* q_t, uint8_t* scale_t, void* stream);
 
+/* dim0 and dim1 in one pass: reads x once and writes both casts, exactly as
+ * mx_quantize_dim0 on the stacked [batch*rows x cols] matrix plus mx_quantize_dim1
+ * would [torchtitan PR 5334, body: the fused dense rowwise/columnwise cast].
+ * 4.0625 bytes of HBM traffic per element instead of 2 x 3.03125.
+ *   x        batch x [rows x cols] bf16; batch b starts at x + b*rows*ld_x; row
+ *            pitch ld_x (ld_x >= cols, ld_x % 8 == 0)
+ *   q        [batch*rows x cols] codes, row pitch cols (written)
+ *   scale    mx_scale_bytes(batch*rows, cols) bytes (written)
+ *   q_t      batch x [cols x rows] codes, transposed (written)
+ *   scale_t  mx_scale_bytes(batch*cols, rows) bytes (written)
+ * rows % 32 == 0, cols % 32 == 0, batch >= 1. */
+mx_status mx_quantize_dim0_dim1(const uint16_t* x, int64_t batch, int64_t rows, int64_t cols, int64_t ld_x,
+                                uint8_t* q, uint8_t* scale, uint8_t* q_t, uint8_t* scale_t, void* stream);
+
 /* 32x32 weight cast: one scale per 32x32 tile [torchtitan PR 5334, body
  * ("32x32 RCEIL weight-scale policy") and review (the square weight kernel is
  * RCEIL-only)]. One set of codes, quantized with the tile scale, is written

@@ -19,6 +19,7 @@ __all__ = [
     "mx_scale_bytes",
     "mx_quantize_dim0",
     "mx_quantize_dim1",
+    "mx_quantize_dim0_dim1",
     "mx_quantize_weight_32x32",
     "mx_grouped_mm_fwd",
     "mx_grouped_mm_dgrad",
@@ -98,6 +99,35 @@ def mx_quantize_dim1(x, q_t=None, scale_t=None):
         scale_t = _u8(mx_scale_bytes(batch * cols, rows), x.device)
     _lib.call("mx_quantize_dim1", _ptr(x), batch, rows, cols, x.stride(-2), _ptr(q_t), _ptr(scale_t), _stream(x))
     return q_t, scale_t
+
+
+def mx_quantize_dim0_dim1(x, q=None, scale=None, q_t=None, scale_t=None):
+    """Both casts in one pass: x [rows, cols] or [batch, rows, cols] (batches contiguous)
+    -> (q [batch*rows, cols], scale, q_t [.., cols, rows], scale_t), the same as
+    mx_quantize_dim0 of the stacked rows plus mx_quantize_dim1."""
+    x = _bf16_bits(x)
+    if x.dim() == 2:
+        batch, (rows, cols) = 1, x.shape
+    elif x.dim() == 3:
+        batch, rows, cols = x.shape
+        if x.stride(0) != rows * x.stride(1):
+            raise ValueError("batches of x must be contiguous with the row pitch")
+    else:
+        raise ValueError("x must be 2D or 3D")
+    if x.stride(-1) != 1:
+        raise ValueError("x must have unit inner stride")
+    if q is None:
+        q = torch.empty((batch * rows, cols), dtype=torch.uint8, device=x.device)
+    if scale is None:
+        scale = _u8(mx_scale_bytes(batch * rows, cols), x.device)
+    if q_t is None:
+        shape = (cols, rows) if x.dim() == 2 else (batch, cols, rows)
+        q_t = torch.empty(shape, dtype=torch.uint8, device=x.device)
+    if scale_t is None:
+        scale_t = _u8(mx_scale_bytes(batch * cols, rows), x.device)
+    _lib.call("mx_quantize_dim0_dim1", _ptr(x), batch, rows, cols, x.stride(-2), _ptr(q), _ptr(scale), _ptr(q_t),
+              _ptr(scale_t), _stream(x))
+    return q, scale, q_t, scale_t
 
 
 def mx_quantize_weight_32x32(w, transposed=True):

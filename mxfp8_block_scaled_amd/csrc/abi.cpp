@@ -14,6 +14,8 @@
 
 hipError_t mx_launch_dim0(const uint16_t*, int64_t, int64_t, int64_t, uint8_t*, uint8_t*, hipStream_t);
 hipError_t mx_launch_dim1(const uint16_t*, int64_t, int64_t, int64_t, int64_t, uint8_t*, uint8_t*, hipStream_t);
+hipError_t mx_launch_both(const uint16_t*, int64_t, int64_t, int64_t, int64_t, uint8_t*, uint8_t*, uint8_t*, uint8_t*,
+                          hipStream_t);
 hipError_t mx_launch_w32(const uint16_t*, int64_t, int64_t, int64_t, int64_t, uint8_t*, uint8_t*, uint8_t*, uint8_t*,
                          hipStream_t);
 hipError_t mx_launch_gemm_mgroup(const uint8_t*, const uint8_t*, const uint8_t*, const uint8_t*, const int32_t*, int,
@@ -161,6 +163,25 @@ mx_status mx_quantize_dim1(const uint16_t* x, int64_t batch, int64_t rows, int64
   TRY(check_ptr("scale_t", scale_t));
   TRY(check_device());
   return launched(mx_launch_dim1(x, batch, rows, cols, ld_x, q_t, scale_t, (hipStream_t)stream), "mx_quantize_dim1");
+}
+
+mx_status mx_quantize_dim0_dim1(const uint16_t* x, int64_t batch, int64_t rows, int64_t cols, int64_t ld_x,
+                                uint8_t* q, uint8_t* scale, uint8_t* q_t, uint8_t* scale_t, void* stream) {
+  TRY(check_dim("batch", batch, 1));
+  TRY(check_dim("rows", rows, 32));
+  TRY(check_dim("cols", cols, 32));
+  TRY(check_mul32("rows", rows));
+  TRY(check_mul32("cols", cols));
+  TRY(check_pitch("ld_x", ld_x, cols));
+  if (batch * rows > kMaxDim || batch * cols > kMaxDim) return fail(MX_E_SHAPE, "batch * rows or batch * cols exceeds 2^31");
+  TRY(check_ptr("x", x));
+  TRY(check_ptr("q", q));
+  TRY(check_ptr("scale", scale));
+  TRY(check_ptr("q_t", q_t));
+  TRY(check_ptr("scale_t", scale_t));
+  TRY(check_device());
+  return launched(mx_launch_both(x, batch, rows, cols, ld_x, q, scale, q_t, scale_t, (hipStream_t)stream),
+                  "mx_quantize_dim0_dim1");
 }
 
 mx_status mx_quantize_weight_32x32(const uint16_t* w, int64_t batch, int64_t n, int64_t k, int64_t ld_w, uint8_t* q,

@@ -192,6 +192,124 @@ __global__ __launch_bounds__(256) void k_quant_dim1(const uint16_t* __restrict__
 }
 
 // ---------------------------------------------------------------------------------
+// dim0 + dim1 in one pass: a workgroup reads a 256-row x 256-column tile of one batch
+// once and writes both casts (4.0625 B per element instead of 2 x 3.03125).
+//   Wave w takes rows 64w..64w+63 as two 32-row sub-tiles; in a sub-tile lane l
+//   reads 16-byte chunk (l % 32) of rows 16(l/32) + i, i = 0..15 (two rows x 512
+//   bytes per load instruction).
+//   dim0: as k_quant_dim0 (quad amax per row block, codes to q, the sub-tile's
+//   256-byte scale tile assembled in the wave's LDS slice).
+//   dim1: per column, amax over the lane's 16 rows then with lane l ^ 32; adjacent
+//   rows of one column form each converter pair, so a column's 16 codes are 16
+//   contiguous bytes of its q_t row; they go to a 256 x 256-byte LDS tile (row =
+//   column of the tile, 16-byte chunk k at k ^ ((row / 8) % 16): conflict-free), read
+//   back as whole 256-byte q_t rows. The eight dim1 scale tiles (256 columns x 8
+//   blocks) are assembled in LDS and written whole.
+// ---------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_quant_both(const uint16_t* __restrict__ x, int64_t batch, int64_t rows,
+                                                    int64_t cols, int64_t ld, uint8_t* __restrict__ q,
+                                                    uint8_t* __restrict__ scale, uint8_t* __restrict__ q_t,
+                                                    uint8_t* __restrict__ scale_t, int64_t rtiles, int64_t ctiles) {
+  __shared__ __attribute__((aligned(16))) uint8_t s_t[256 * 256];  // transposed codes
+  __shared__ unsigned s_s1[8][64];                                 // dim1 scale tiles
+  __shared__ unsigned s_s0[4][64];                                 // dim0 scale tile per wave
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, h = l >> 5, c = l & 31;
+  const int64_t kt0 = scale_tiles_k(cols / 32), kt1 = scale_tiles_k(rows / 32);
+  const int64_t tiles = batch * rtiles * ctiles;
+  uint8_t* st0 = (uint8_t*)s_s0[w];
+  uint8_t* ss1 = (uint8_t*)s_s1;
+  for (int64_t t = blockIdx.x; t < tiles; t += gridDim.x) {
+    const int64_t b = t / (rtiles * ctiles), rem = t % (rtiles * ctiles);
+    const int64_t ct = rem / rtiles, rt = rem % rtiles;
+    const int64_t r0 = rt * 256, c0 = ct * 256;
+    const int64_t col = c0 + 8 * c;
+    const bool col_ok = col < cols;  // cols % 32 == 0: a quad's 32 columns are all in or all out
+    const uint16_t* xb = x + b * rows * ld;
+    const int64_t qrow0 = b * rows;  // dim0 rows of this batch in the stacked [batch*rows x cols]
+    s_s1[tid >> 5][tid & 31] = 0x7f7f7f7fu;  // pad blocks past the last row
+    s_s1[(tid >> 5)][32 + (tid & 31)] = 0x7f7f7f7fu;
+    __syncthreads();
+#pragma unroll 1
+    for (int sub = 0; sub < 2; ++sub) {
+      const int kb = 2 * w + sub;               // dim1 block (32 rows) within the tile
+      const int64_t base = r0 + 32 * kb;        // first row of the sub-tile
+      const bool rows_ok = base < rows;         // rows % 32 == 0: the sub-tile is all in or all out
+      u32x4 v[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        v[i] = (u32x4){0, 0, 0, 0};
+        if (col_ok && rows_ok) v[i] = *(const u32x4*)(xb + (base + 16 * h + i) * ld + col);
+      }
+      // ---- dim0 ----
+      s_s0[w][l] = 0x7f7f7f7fu;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        unsigned a = amax8(v[i]);
+        a = umax(a, dpp_xor1(a));
+        a = umax(a, dpp_xor2(a));
+        const int byte = rceil_byte(a);
+        const u32x2 codes = encode8(v[i], byte, a);
+        if (col_ok && rows_ok) {
+          *(u32x2*)(q + (qrow0 + base + 16 * h + i) * cols + col) = codes;
+          if ((c & 3) == 0) st0[scale_in_tile(16 * h + i, c >> 2)] = (uint8_t)byte;
+        }
+      }
+      if (rows_ok && c0 < cols)
+        ((unsigned*)(scale + scale_tile_base((qrow0 + base) / 32, ct, kt0)))[l] = s_s0[w][l];
+      // ---- dim1 ----
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {  // column pair (2p, 2p+1) of the lane's eight
+        unsigned am = 0;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) am = amax_pair(am, v[i][p]);
+        am = amax_pair(am, (unsigned)__shfl_xor((int)am, 32));
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const unsigned amax = e ? (am >> 16) : (am & 0xffff);
+          const int byte = rceil_byte(amax);
+          const bool tiny = byte == 0 && amax != 0;
+          const float sc = scale_operand(byte == 0 ? 1 : byte);
+          const unsigned sel = e ? 0x07060302u : 0x05040100u;
+          unsigned d[4];
+#pragma unroll
+          for (int m = 0; m < 4; ++m) {
+            unsigned p01 = __builtin_amdgcn_perm(v[4 * m + 1][p], v[4 * m][p], sel);  // rows 4m, 4m+1
+            unsigned p23 = __builtin_amdgcn_perm(v[4 * m + 3][p], v[4 * m + 2][p], sel);
+            if (tiny) {
+              p01 = double_bf16x2(p01);
+              p23 = double_bf16x2(p23);
+            }
+            d[m] = cvt2(p01, sc) | (cvt2(p23, sc) << 16);
+          }
+          const int cc = 8 * c + 2 * p + e;      // column within the tile = row of s_t
+          const int k = (64 * w + 32 * sub + 16 * h) >> 4;  // 16-byte chunk: the lane's 16 rows
+          *(u32x4*)(s_t + cc * 256 + ((k ^ ((cc >> 3) & 15)) << 4)) = (u32x4){d[0], d[1], d[2], d[3]};
+          if (h == 0 && rows_ok) ss1[(cc >> 5) * 256 + scale_in_tile(cc & 31, kb)] = (uint8_t)byte;
+        }
+      }
+    }
+    __syncthreads();
+    // q_t rows c0 + 64w .. +63 (columns of the tile), four per instruction, 256 bytes each
+    uint8_t* qtb = q_t + b * cols * rows;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const int orow = 64 * w + 4 * k + (l >> 4), ch = l & 15;
+      const int64_t cidx = c0 + orow, rr = r0 + 16 * ch;
+      const u32x4 d = *(const u32x4*)(s_t + orow * 256 + ((ch ^ ((orow >> 3) & 15)) << 4));
+      if (cidx < cols && rr < rows) *(u32x4*)(qtb + cidx * rows + rr) = d;
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int tile = 4 * j + w;  // dim1 scale tile (32 q_t rows) of this thread's dword
+      const int64_t out_row0 = c0 + 32 * tile;
+      if (out_row0 < cols)
+        ((unsigned*)(scale_t + scale_tile_base((b * cols + out_row0) / 32, rt, kt1)))[l] = s_s1[tile][l];
+    }
+    __syncthreads();  // s_t and s_s1 are reused by the next tile
+  }
+}
+
+// ---------------------------------------------------------------------------------
 // 32x32 weight cast: one wave per 32-row x 256-column strip (eight 32x32 tiles).
 // The tile amax reduces over the lane's 16 rows, the quad (32 columns) and the two
 // wave halves. Codes go out rowwise directly and, through LDS, transposed.
@@ -329,6 +447,19 @@ hipError_t mx_launch_dim1(const uint16_t* x, int64_t batch, int64_t rows, int64_
   if (blocks == 0) return hipSuccess;
   hipLaunchKernelGGL(mx::k_quant_dim1, dim3((unsigned)blocks), dim3(256), 0, stream, x, rows, cols, ld, q_t,
                      scale_t, rtiles, ctiles);
+  return hipGetLastError();
+}
+
+hipError_t mx_launch_both(const uint16_t* x, int64_t batch, int64_t rows, int64_t cols, int64_t ld, uint8_t* q,
+                          uint8_t* scale, uint8_t* q_t, uint8_t* scale_t, hipStream_t stream) {
+  const int64_t rtiles = (rows + 255) / 256, ctiles = (cols + 255) / 256;
+  const int64_t tiles = batch * rtiles * ctiles;
+  if (tiles == 0) return hipSuccess;
+  static int64_t fill = 0;
+  if (fill == 0) fill = resident_blocks((const void*)mx::k_quant_both, 256);
+  const int64_t blocks = std::min<int64_t>(tiles, fill);
+  hipLaunchKernelGGL(mx::k_quant_both, dim3((unsigned)blocks), dim3(256), 0, stream, x, batch, rows, cols, ld, q,
+                     scale, q_t, scale_t, rtiles, ctiles);
   return hipGetLastError();
 }
 

@@ -72,6 +72,17 @@ def test_dim0_validation(lib, args, status):
     assert len(lib.mx_last_error()) > 0
 
 
+def test_dim0_dim1_validation(lib):
+    f = lib.mx_quantize_dim0_dim1
+    assert f(P, 1, 48, 64, 64, P2, P2, P2, P2, None) == MX_E_SHAPE  # rows % 32
+    assert f(P, 1, 64, 48, 64, P2, P2, P2, P2, None) == MX_E_SHAPE  # cols % 32
+    assert f(P, 0, 64, 64, 64, P2, P2, P2, P2, None) == MX_E_SHAPE  # batch
+    assert f(P, 1, 64, 64, 32, P2, P2, P2, P2, None) == MX_E_LAYOUT  # pitch < cols
+    assert f(P, 1, 64, 64, 64, P2, P2, None, P2, None) == MX_E_NULL  # q_t
+    assert f(P, 1, 64, 64, 64, P2, P2, P2, None, None) == MX_E_NULL  # scale_t
+    assert f(P, 1, 64, 64, 64, P2 + 4, P2, P2, P2, None) == MX_E_ALIGN
+
+
 def test_dim1_and_w32_validation(lib):
     assert lib.mx_quantize_dim1(P, 1, 48, 64, 64, P2, P2, None) == MX_E_SHAPE  # rows % 32
     assert lib.mx_quantize_dim1(P, 0, 64, 64, 64, P2, P2, None) == MX_E_SHAPE  # batch

@@ -54,6 +54,26 @@ def check_w32(oracle, bits, name):
     assert np.array_equal(host(s_col), oracle.scales_to_physical(osc)), name
 
 
+def check_both(oracle, bits, name):
+    """The one-pass cast must equal dim0 of the stacked rows and dim1, bit for bit."""
+    say(f"[cast dim0+dim1] {name} shape={bits.shape}")
+    q, s, q_t, s_t = mx.mx_quantize_dim0_dim1(dev_bf16(bits))
+    stacked = bits.reshape(-1, bits.shape[-1])
+    oq, osl = oracle.quantize_dim0(stacked)
+    gq = host(q)
+    assert np.array_equal(gq, oq), f"{name}: {np.sum(gq != oq)} dim0 code mismatches"
+    assert np.array_equal(host(s), oracle.scales_to_physical(osl)), name
+    if bits.ndim == 2:
+        oqt, ost = oracle.quantize_dim1(bits)
+    else:
+        parts = [oracle.quantize_dim1(b) for b in bits]
+        oqt = np.stack([p[0] for p in parts])
+        ost = np.concatenate([p[1] for p in parts])
+    gqt = host(q_t)
+    assert np.array_equal(gqt, oqt), f"{name}: {np.sum(gqt != oqt)} dim1 code mismatches"
+    assert np.array_equal(host(s_t), oracle.scales_to_physical(ost)), name
+
+
 @pytest.fixture(scope="module", autouse=True)
 def gpu():
     require_gpu()
@@ -130,6 +150,43 @@ def test_dim1_full_size_sampled_columns(oracle):
     oq, osl = oracle.quantize_dim0(np.ascontiguousarray(x[:, cols].T))
     assert np.array_equal(gq[cols], oq)
     assert np.array_equal(oracle.scales_from_physical(gs, x.shape[1], x.shape[0] // 32)[cols], osl)
+
+
+@pytest.mark.parametrize("shape", [(32, 32), (64, 96), (96, 160), (288, 64), (256, 576), (544, 1056), (512, 768)])
+def test_dim0_dim1_shapes(oracle, shape):
+    rng = np.random.default_rng(shape[0] * 5 + shape[1])
+    check_both(oracle, synth.normal_bf16(rng, shape, 1.0), f"normal{shape}")
+
+
+def test_dim0_dim1_stress_every_amax(oracle):
+    """Every bf16 amax as a row block and, from transposed panels, as a column block."""
+    blocks = stress_blocks(2)
+    n_row = blocks.shape[0] // 256 * 256  # 8 blocks per 256-column row, rows a multiple of 32
+    check_both(oracle, np.ascontiguousarray(blocks[:n_row].reshape(-1, 256)), "row blocks")
+    n_col = blocks.shape[0] // 64 * 64
+    panels = blocks[:n_col].reshape(-1, 64, 32).transpose(0, 2, 1).reshape(-1, 64)  # column c of a panel = block c
+    check_both(oracle, np.ascontiguousarray(panels), "column blocks")
+
+
+def test_dim0_dim1_batched(oracle):
+    rng = np.random.default_rng(6)
+    check_both(oracle, synth.normal_bf16(rng, (3, 96, 320), 0.02), "batch3")
+
+
+def test_dim0_dim1_full_size_sampled(oracle):
+    d = synth.moe_g8(0, with_backward=False)
+    x = d["x"]
+    say("[cast dim0+dim1] 16384x4096 sampled")
+    q, s, q_t, s_t = mx.mx_quantize_dim0_dim1(dev_bf16(x))
+    rng = np.random.default_rng(3)
+    rows = np.sort(rng.choice(x.shape[0], 128, replace=False))
+    cols = np.sort(rng.choice(x.shape[1], 128, replace=False))
+    oq, osl = oracle.quantize_dim0(x[rows])
+    assert np.array_equal(host(q)[rows], oq)
+    assert np.array_equal(oracle.scales_from_physical(host(s), x.shape[0], x.shape[1] // 32)[rows], osl)
+    oqt, ost = oracle.quantize_dim0(np.ascontiguousarray(x[:, cols].T))
+    assert np.array_equal(host(q_t)[cols], oqt)
+    assert np.array_equal(oracle.scales_from_physical(host(s_t), x.shape[1], x.shape[0] // 32)[cols], ost)
 
 
 @pytest.mark.parametrize("shape", [(32, 32), (64, 96), (96, 288), (576, 512)])
