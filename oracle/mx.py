@@ -16,6 +16,10 @@ What is computed (sources):
     evidence") -- but print no formula. The formula is the OCP Microscaling (MX)
     definition: the scale exponent is ceil(log2(amax / 448)), 448 being the largest
     E4M3 value, and elements are encoded round-to-nearest-even with saturation.
+    The OCP default scale rule, FLOOR, is kept beside it (ao fork PR 10, "Known
+    follow-ups": FLOOR is reachable but untested there): the exponent is
+    floor(log2(amax)) - 8, 8 being the exponent of E4M3's largest power of two,
+    so the block maximum can land in [256, 512) and saturate to 448.
   * The GEMM: a grouped matmul over per-group row offsets `offs` (ao fork PR 10
     "Summary"; pytorch/ao PR 4705 body), with offs=None meaning one dense group
     (torchtitan PR 5334 body), in forward, dgrad and wgrad form.
@@ -107,6 +111,33 @@ def rceil_exponent(amax):
     return np.clip(s, SCALE_MIN_EXP, SCALE_MAX_EXP)
 
 
+def floor_exponent(amax):
+    """floor(log2(amax)) - 8, clamped to [-127, 127] (the OCP MX FLOOR scale rule).
+
+    floor(log2(a)) is read off the binary exponent: a = f * 2^e with f in [0.5, 1)
+    gives floor(log2(a)) = e - 1 exactly. amax = 0 gives the clamp of -inf, i.e.
+    -127; +Inf clamps to 127. Accepts a scalar or an array of non-negative float64
+    values; returns int64.
+    """
+    amax = np.asarray(amax, dtype=np.float64)
+    finite_pos = np.isfinite(amax) & (amax > 0)
+    a = np.where(finite_pos, amax, 1.0)
+    _, e = np.frexp(a)
+    s = e.astype(np.int64) - 1 - 8
+    s = np.where(amax == 0, SCALE_MIN_EXP, s)
+    s = np.where(np.isinf(amax), SCALE_MAX_EXP, s)
+    return np.clip(s, SCALE_MIN_EXP, SCALE_MAX_EXP)
+
+
+def scale_exponent(amax, scale_mode):
+    """The block scale exponent under `scale_mode` ("rceil" or "floor")."""
+    if scale_mode == "rceil":
+        return rceil_exponent(amax)
+    if scale_mode == "floor":
+        return floor_exponent(amax)
+    raise ValueError(f"unknown scale mode {scale_mode!r}")
+
+
 def e4m3_encode(v, negative):
     """Round-to-nearest-even, saturating E4M3 encode of float64 values `v`.
 
@@ -126,9 +157,10 @@ def e4m3_encode(v, negative):
     return code.astype(np.uint8)
 
 
-def quantize_blocks(bits):
+def quantize_blocks(bits, scale_mode="rceil"):
     """Quantize a [nblocks, blocksize] array of bf16 patterns, one scale per row.
 
+    scale_mode: "rceil" (the pages' rule) or "floor" (the OCP default).
     Returns (codes uint8 [nblocks, blocksize], scale bytes uint8 [nblocks]).
     """
     bits = np.asarray(bits, dtype=np.uint16)
@@ -139,7 +171,7 @@ def quantize_blocks(bits):
     scales = np.empty(nb, dtype=np.uint8)
     has_nan = np.isnan(x).any(axis=1)
     amax = np.where(np.isnan(x), 0.0, np.abs(x)).max(axis=1) if x.shape[1] else np.zeros(nb)
-    exps = rceil_exponent(amax)
+    exps = scale_exponent(amax, scale_mode)
     scales[:] = (exps + SCALE_BIAS).astype(np.uint8)
     v = np.ldexp(x, -exps[:, None])  # exact: a power-of-two scale
     codes[:] = e4m3_encode(v, neg)
@@ -153,7 +185,7 @@ def quantize_blocks(bits):
 # --------------------------------------------------------------------------------------
 
 
-def quantize_dim0(bits):
+def quantize_dim0(bits, scale_mode="rceil"):
     """1x32 rowwise cast of a [R, C] bf16 matrix (C % 32 == 0): blocks run along C.
 
     Returns q uint8 [R, C] and logical scales uint8 [R, C/32].
@@ -161,18 +193,18 @@ def quantize_dim0(bits):
     bits = np.asarray(bits, dtype=np.uint16)
     R, C = bits.shape
     assert C % BLOCK == 0
-    codes, scales = quantize_blocks(bits.reshape(R * C // BLOCK, BLOCK))
+    codes, scales = quantize_blocks(bits.reshape(R * C // BLOCK, BLOCK), scale_mode)
     return codes.reshape(R, C), scales.reshape(R, C // BLOCK)
 
 
-def quantize_dim1(bits):
+def quantize_dim1(bits, scale_mode="rceil"):
     """32x1 columnwise cast of a [R, C] bf16 matrix (R % 32 == 0): blocks run along R.
 
     The output is transposed so that the blocked axis is contiguous: q_t [C, R] and
     logical scales [C, R/32]. By definition this is dim0 of the transpose.
     """
     bits = np.asarray(bits, dtype=np.uint16)
-    return quantize_dim0(np.ascontiguousarray(bits.T))
+    return quantize_dim0(np.ascontiguousarray(bits.T), scale_mode)
 
 
 def quantize_weight_32x32(bits):

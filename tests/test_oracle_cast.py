@@ -135,6 +135,60 @@ def test_rceil_vs_floor(oracle):
     floor_s = np.floor(np.log2(amax)).astype(np.int64) - 8
     sig = amax / np.ldexp(1.0, np.floor(np.log2(amax)).astype(np.int64))
     assert np.array_equal(s, floor_s + (sig > 1.75))
+    assert np.array_equal(oracle.floor_exponent(amax), floor_s)
+
+
+def test_floor_exhaustive_closed_form(oracle):
+    """FLOOR on every non-negative finite bf16 amax: from the bits, floor(log2 amax) is
+    E - 127 for exponent field E >= 1, so s = E - 135, clamped at -127 (E = 0: zero or
+    bf16-denormal amax, below 2^-126, clamps too); the block maximum over 2^s then
+    lies in [256, 512) wherever s is not clamped."""
+    bits = np.arange(0, 0x7F80, dtype=np.uint32)
+    amax = oracle.bf16_to_f64(bits.astype(np.uint16))
+    E = (bits >> 7).astype(np.int64)
+    want = np.where(E == 0, -127, np.maximum(E - 135, -127))
+    s = oracle.floor_exponent(amax)
+    assert np.array_equal(s, want)
+    pos = amax > 0
+    assert np.array_equal(s[pos], np.clip(np.floor(np.log2(amax[pos])).astype(np.int64) - 8, -127, 127))
+    free = s > -127
+    ratio = amax[free] / np.ldexp(1.0, s[free])
+    assert np.all((ratio >= 256) & (ratio < 512))
+    # whole blocks: the scale byte of a block is s + 127 of its amax
+    blk = np.zeros((bits.size, 32), np.uint16)
+    blk[:, 5] = bits
+    _, sb = oracle.quantize_blocks(blk, "floor")
+    assert np.array_equal(sb.astype(np.int64), want + 127)
+
+
+def test_floor_worked_values(oracle):
+    """Worked by hand from floor(log2 amax) - 8 and the E4M3 grid (OCP MX FLOOR rule).
+
+    amax 1.875 (bf16 0x3FF0): floor(log2) = 0, s = -8, byte 119; 1.875 * 2^8 = 480 > 448
+    saturates to 0x7E (RCEIL gives byte 120 and 0x77 for the same block).
+    amax 1.0: s = -8, byte 119, 1.0 -> 256 = 2^8 -> code 0x78.
+    [2.5, 1.0]: floor(log2 2.5) = 1, s = -7, byte 120; 2.5 -> 320 = 1.25 * 2^8 -> 0x7A;
+    1.0 -> 128 -> 0x70.
+    [-448.0] (0xC3E0): floor(log2 448) = 8, s = 0, byte 127, code 0x80 | 0x7E = 0xFE.
+    zero block: byte 0, codes 0 (the sign of zero kept).
+    bf16 0x0040 = (64/128) * 2^-126 = 2^-127, a bf16 denormal: s clamps to -127 (byte 0)
+    and the element encodes 2^-127 / 2^-127 = 1.0 -> 0x38.
+    """
+    def one(vals):
+        blk = np.zeros((1, 32), np.uint16)
+        blk[0, : len(vals)] = vals
+        c, sb = oracle.quantize_blocks(blk, "floor")
+        return [int(x) for x in c[0, : len(vals)]], int(sb[0])
+
+    assert one([0x3FF0]) == ([0x7E], 119)
+    assert one([0x3F80]) == ([0x78], 119)
+    assert one([0x4020, 0x3F80]) == ([0x7A, 0x70], 120)
+    assert one([0xC3E0]) == ([0xFE], 127)
+    assert one([0x0000, 0x8000]) == ([0x00, 0x80], 0)
+    assert one([0x0040]) == ([0x38], 0)
+    # the same blocks under RCEIL, for contrast: 1.875 -> byte 120 and 1.875 * 2^7 = 240 -> 0x77
+    c, sb = oracle.quantize_blocks(np.array([[0x3FF0] + [0] * 31], np.uint16), "rceil")
+    assert (int(c[0, 0]), int(sb[0])) == (0x77, 120)
 
 
 def parse_block(spec):

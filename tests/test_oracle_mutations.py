@@ -43,6 +43,17 @@ def rceil_floor(amax):
     return np.clip(np.where(amax == 0, -127, s), -127, 127)
 
 
+def floor_via_ceil(amax):
+    amax = np.asarray(amax, dtype=np.float64)
+    a = np.where(amax > 0, amax, 1.0)
+    s = np.ceil(np.log2(a)).astype(np.int64) - 8
+    return np.clip(np.where(amax == 0, -127, s), -127, 127)
+
+
+def floor_emax_7(amax):
+    return np.clip(mx.__dict__["_orig_floor"](amax) + 1, -127, 127)
+
+
 def rceil_off_by_one(amax):
     return np.clip(mx.__dict__["_orig_rceil"](amax) + 1, -127, 127)
 
@@ -91,6 +102,8 @@ MUTANTS = [
     ("rceil_exponent", rceil_floor, tc.test_rceil_exhaustive_closed_form, {}),
     ("rceil_exponent", rceil_floor, tc.test_worked_values, {}),
     ("rceil_exponent", rceil_off_by_one, tc.test_roundtrip_representable_blocks, {}),
+    ("floor_exponent", floor_via_ceil, tc.test_floor_exhaustive_closed_form, {}),
+    ("floor_exponent", floor_emax_7, tc.test_floor_worked_values, {}),
     ("scale_offset", offset_swapped, tl.test_layout_feeds_mfma_lanes, {}),
     ("group_bounds", group_bounds_shifted, tg.test_grouped_mm_matches_loops, {}),
     ("grouped_mm_wgrad", wgrad_misaligned_rows, tg.test_wgrad_matches_loops_and_empty_group_is_zero, {}),
@@ -103,6 +116,7 @@ MUTANTS = [
 def test_pin_catches_mutant(monkeypatch, name, mutant, pin, kwargs):
     monkeypatch.setitem(mx.__dict__, "_orig_encode", mx.e4m3_encode)
     monkeypatch.setitem(mx.__dict__, "_orig_rceil", mx.rceil_exponent)
+    monkeypatch.setitem(mx.__dict__, "_orig_floor", mx.floor_exponent)
     monkeypatch.setattr(mx, name, mutant)
     with pytest.raises(AssertionError):
         pin(mx, **kwargs)
