@@ -74,7 +74,7 @@ typedef int mx_status;
 #define MX_E_SHAPE (-2)   /* a size is negative, too large, or not a required multiple */
 #define MX_E_ALIGN (-3)   /* a pointer or row pitch breaks the 16-byte alignment rule */
 #define MX_E_LAYOUT (-4)  /* a row pitch is smaller than the row length */
-#define MX_E_DTYPE (-5)   /* unknown output dtype */
+#define MX_E_DTYPE (-5)   /* unknown output dtype, cast form or scale rule */
 #define MX_E_DEVICE (-6)  /* no HIP device, or the current device is not gfx950 */
 #define MX_E_LAUNCH (-7)  /* the kernel launch failed (see mx_last_error) */
 
@@ -128,6 +128,23 @@ mx_status mx_quantize_dim1(const uint16_t* x, int64_t batch, int64_t rows, int64
  * rows % 32 == 0, cols % 32 == 0, batch >= 1. */
 mx_status mx_quantize_dim0_dim1(const uint16_t* x, int64_t batch, int64_t rows, int64_t cols, int64_t ld_x,
                                 uint8_t* q, uint8_t* scale, uint8_t* q_t, uint8_t* scale_t, void* stream);
+
+/* Forms and scale rules of mx_quantize_ex. */
+#define MX_FORM_DIM0 1
+#define MX_FORM_DIM1 2
+#define MX_SCALE_RCEIL 0 /* ceil(log2(amax / 448)): the rule of the other casts */
+#define MX_SCALE_FLOOR 1 /* floor(log2(amax)) - 8 (the OCP default): the block maximum
+                            can exceed 448 after scaling and saturates to 448 */
+
+/* Casts with a choice of form and scale rule [ao fork PR 10, Known follow-ups:
+ * FLOOR is reachable next to RCEIL]. forms = MX_FORM_DIM0, MX_FORM_DIM1 or both
+ * (the one-pass cast); arguments as mx_quantize_dim0 (on the stacked
+ * [batch*rows x cols] matrix), mx_quantize_dim1 and mx_quantize_dim0_dim1. Outputs
+ * of a form not requested may be NULL. rows % 32 == 0 when MX_FORM_DIM1 is
+ * requested; cols % 32 == 0 always. With MX_SCALE_RCEIL the results equal those of
+ * the other entry points. An unknown forms or scale_mode value is MX_E_DTYPE. */
+mx_status mx_quantize_ex(const uint16_t* x, int64_t batch, int64_t rows, int64_t cols, int64_t ld_x, int forms,
+                         int scale_mode, uint8_t* q, uint8_t* scale, uint8_t* q_t, uint8_t* scale_t, void* stream);
 
 /* 32x32 weight cast: one scale per 32x32 tile [torchtitan PR 5334, body
  * ("32x32 RCEIL weight-scale policy") and review (the square weight kernel is

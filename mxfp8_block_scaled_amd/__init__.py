@@ -20,6 +20,11 @@ __all__ = [
     "mx_quantize_dim0",
     "mx_quantize_dim1",
     "mx_quantize_dim0_dim1",
+    "mx_quantize_ex",
+    "MX_FORM_DIM0",
+    "MX_FORM_DIM1",
+    "MX_SCALE_RCEIL",
+    "MX_SCALE_FLOOR",
     "mx_quantize_weight_32x32",
     "mx_grouped_mm_fwd",
     "mx_grouped_mm_dgrad",
@@ -127,6 +132,39 @@ def mx_quantize_dim0_dim1(x, q=None, scale=None, q_t=None, scale_t=None):
         scale_t = _u8(mx_scale_bytes(batch * cols, rows), x.device)
     _lib.call("mx_quantize_dim0_dim1", _ptr(x), batch, rows, cols, x.stride(-2), _ptr(q), _ptr(scale), _ptr(q_t),
               _ptr(scale_t), _stream(x))
+    return q, scale, q_t, scale_t
+
+
+MX_FORM_DIM0, MX_FORM_DIM1 = 1, 2
+MX_SCALE_RCEIL, MX_SCALE_FLOOR = 0, 1
+
+
+def mx_quantize_ex(x, forms=MX_FORM_DIM0 | MX_FORM_DIM1, scale_mode=MX_SCALE_RCEIL):
+    """Cast with a choice of forms (MX_FORM_DIM0, MX_FORM_DIM1 or both) and scale rule.
+
+    x [rows, cols] or [batch, rows, cols] (batches contiguous). Returns (q, scale,
+    q_t, scale_t), None for a form not requested; shapes as mx_quantize_dim0_dim1.
+    """
+    x = _bf16_bits(x)
+    if x.dim() == 2:
+        batch, (rows, cols) = 1, x.shape
+    elif x.dim() == 3:
+        batch, rows, cols = x.shape
+        if x.stride(0) != rows * x.stride(1):
+            raise ValueError("batches of x must be contiguous with the row pitch")
+    else:
+        raise ValueError("x must be 2D or 3D")
+    if x.stride(-1) != 1:
+        raise ValueError("x must have unit inner stride")
+    q = scale = q_t = scale_t = None
+    if forms & MX_FORM_DIM0:
+        q = torch.empty((batch * rows, cols), dtype=torch.uint8, device=x.device)
+        scale = _u8(mx_scale_bytes(batch * rows, cols), x.device)
+    if forms & MX_FORM_DIM1:
+        q_t = torch.empty((cols, rows) if x.dim() == 2 else (batch, cols, rows), dtype=torch.uint8, device=x.device)
+        scale_t = _u8(mx_scale_bytes(batch * cols, rows), x.device)
+    _lib.call("mx_quantize_ex", _ptr(x), batch, rows, cols, x.stride(-2), int(forms), int(scale_mode), _ptr(q),
+              _ptr(scale), _ptr(q_t), _ptr(scale_t), _stream(x))
     return q, scale, q_t, scale_t
 
 

@@ -18,6 +18,7 @@ SIGNATURES = {
     "mx_quantize_dim0": (_INT, [_P, _I64, _I64, _I64, _P, _P, _P]),
     "mx_quantize_dim1": (_INT, [_P, _I64, _I64, _I64, _I64, _P, _P, _P]),
     "mx_quantize_dim0_dim1": (_INT, [_P, _I64, _I64, _I64, _I64, _P, _P, _P, _P, _P]),
+    "mx_quantize_ex": (_INT, [_P, _I64, _I64, _I64, _I64, _INT, _INT, _P, _P, _P, _P, _P]),
     "mx_quantize_weight_32x32": (_INT, [_P, _I64, _I64, _I64, _I64, _P, _P, _P, _P, _P]),
     "mx_grouped_mm_fwd": (_INT, [_P, _P, _P, _P, _P, _I32, _I64, _I64, _I64, _P, _INT, _P]),
     "mx_grouped_mm_dgrad": (_INT, [_P, _P, _P, _P, _P, _I32, _I64, _I64, _I64, _P, _INT, _P]),

@@ -12,10 +12,10 @@
 
 #include "../../include/mxfp8.h"
 
-hipError_t mx_launch_dim0(const uint16_t*, int64_t, int64_t, int64_t, uint8_t*, uint8_t*, hipStream_t);
-hipError_t mx_launch_dim1(const uint16_t*, int64_t, int64_t, int64_t, int64_t, uint8_t*, uint8_t*, hipStream_t);
+hipError_t mx_launch_dim0(const uint16_t*, int64_t, int64_t, int64_t, uint8_t*, uint8_t*, int, hipStream_t);
+hipError_t mx_launch_dim1(const uint16_t*, int64_t, int64_t, int64_t, int64_t, uint8_t*, uint8_t*, int, hipStream_t);
 hipError_t mx_launch_both(const uint16_t*, int64_t, int64_t, int64_t, int64_t, uint8_t*, uint8_t*, uint8_t*, uint8_t*,
-                          hipStream_t);
+                          int, hipStream_t);
 hipError_t mx_launch_w32(const uint16_t*, int64_t, int64_t, int64_t, int64_t, uint8_t*, uint8_t*, uint8_t*, uint8_t*,
                          hipStream_t);
 hipError_t mx_launch_gemm_mgroup(const uint8_t*, const uint8_t*, const uint8_t*, const uint8_t*, const int32_t*, int,
@@ -146,7 +146,7 @@ mx_status mx_quantize_dim0(const uint16_t* x, int64_t rows, int64_t cols, int64_
   TRY(check_ptr("q", q));
   TRY(check_ptr("scale", scale));
   TRY(check_device());
-  return launched(mx_launch_dim0(x, rows, cols, ld_x, q, scale, (hipStream_t)stream), "mx_quantize_dim0");
+  return launched(mx_launch_dim0(x, rows, cols, ld_x, q, scale, 0, (hipStream_t)stream), "mx_quantize_dim0");
 }
 
 mx_status mx_quantize_dim1(const uint16_t* x, int64_t batch, int64_t rows, int64_t cols, int64_t ld_x, uint8_t* q_t,
@@ -162,7 +162,7 @@ mx_status mx_quantize_dim1(const uint16_t* x, int64_t batch, int64_t rows, int64
   TRY(check_ptr("q_t", q_t));
   TRY(check_ptr("scale_t", scale_t));
   TRY(check_device());
-  return launched(mx_launch_dim1(x, batch, rows, cols, ld_x, q_t, scale_t, (hipStream_t)stream), "mx_quantize_dim1");
+  return launched(mx_launch_dim1(x, batch, rows, cols, ld_x, q_t, scale_t, 0, (hipStream_t)stream), "mx_quantize_dim1");
 }
 
 mx_status mx_quantize_dim0_dim1(const uint16_t* x, int64_t batch, int64_t rows, int64_t cols, int64_t ld_x,
@@ -180,8 +180,43 @@ mx_status mx_quantize_dim0_dim1(const uint16_t* x, int64_t batch, int64_t rows, 
   TRY(check_ptr("q_t", q_t));
   TRY(check_ptr("scale_t", scale_t));
   TRY(check_device());
-  return launched(mx_launch_both(x, batch, rows, cols, ld_x, q, scale, q_t, scale_t, (hipStream_t)stream),
+  return launched(mx_launch_both(x, batch, rows, cols, ld_x, q, scale, q_t, scale_t, 0, (hipStream_t)stream),
                   "mx_quantize_dim0_dim1");
+}
+
+mx_status mx_quantize_ex(const uint16_t* x, int64_t batch, int64_t rows, int64_t cols, int64_t ld_x, int forms,
+                         int scale_mode, uint8_t* q, uint8_t* scale, uint8_t* q_t, uint8_t* scale_t, void* stream) {
+  if (forms != MX_FORM_DIM0 && forms != MX_FORM_DIM1 && forms != (MX_FORM_DIM0 | MX_FORM_DIM1))
+    return fail(MX_E_DTYPE, "forms = %d must be MX_FORM_DIM0, MX_FORM_DIM1 or both", forms);
+  if (scale_mode != MX_SCALE_RCEIL && scale_mode != MX_SCALE_FLOOR)
+    return fail(MX_E_DTYPE, "scale_mode = %d must be MX_SCALE_RCEIL or MX_SCALE_FLOOR", scale_mode);
+  const bool d0 = forms & MX_FORM_DIM0, d1 = forms & MX_FORM_DIM1;
+  TRY(check_dim("batch", batch, 1));
+  TRY(check_dim("rows", rows, d1 ? 32 : 0));
+  TRY(check_dim("cols", cols, 32));
+  if (d1) TRY(check_mul32("rows", rows));
+  TRY(check_mul32("cols", cols));
+  TRY(check_pitch("ld_x", ld_x, cols));
+  if (batch * rows > kMaxDim || batch * cols > kMaxDim) return fail(MX_E_SHAPE, "batch * rows or batch * cols exceeds 2^31");
+  TRY(check_ptr("x", x));
+  if (d0) {
+    TRY(check_ptr("q", q));
+    TRY(check_ptr("scale", scale));
+  }
+  if (d1) {
+    TRY(check_ptr("q_t", q_t));
+    TRY(check_ptr("scale_t", scale_t));
+  }
+  TRY(check_device());
+  const int fl = scale_mode == MX_SCALE_FLOOR;
+  hipError_t e;
+  if (d0 && d1)
+    e = mx_launch_both(x, batch, rows, cols, ld_x, q, scale, q_t, scale_t, fl, (hipStream_t)stream);
+  else if (d0)  // batches are contiguous with the row pitch: one stacked matrix
+    e = mx_launch_dim0(x, batch * rows, cols, ld_x, q, scale, fl, (hipStream_t)stream);
+  else
+    e = mx_launch_dim1(x, batch, rows, cols, ld_x, q_t, scale_t, fl, (hipStream_t)stream);
+  return launched(e, "mx_quantize_ex");
 }
 
 mx_status mx_quantize_weight_32x32(const uint16_t* w, int64_t batch, int64_t n, int64_t k, int64_t ld_w, uint8_t* q,

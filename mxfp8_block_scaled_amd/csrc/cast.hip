@@ -5,8 +5,10 @@
 // patterns with the sign cleared (monotone for finite values); RCEIL E8M0 byte from
 // the amax bits by an integer closed form (no division, no log, so no fp32
 // flush-to-zero hazard); elements encoded by the gfx950 scaled convert
-// (v_cvt_scalef32_pk_fp8_bf16), which computes the RNE, saturating E4M3 code of
-// x / 2^(byte-127) directly from bf16, two elements per instruction. Scales are
+// (v_cvt_scalef32_pk_fp8_bf16), which computes the RNE E4M3 code of x / 2^(byte-127)
+// directly from bf16, two elements per instruction. The convert does not saturate:
+// under RCEIL no quotient exceeds 448; under FLOOR the block maximum scales into
+// [256, 512) and codes that overflowed to NaN are clamped to +-448 afterwards. Scales are
 // written in the MFMA-blocked layout the grouped GEMM reads, so no rearrange pass
 // follows (torchtitan PR 5334, body: blocked E8M0 scales emitted directly).
 
@@ -17,7 +19,8 @@
 namespace mx {
 
 // Encode 8 bf16 values (one 16-byte chunk) with scale byte `byte` of a block whose
-// amax bits are `amax`: returns 8 codes in two dwords.
+// amax bits are `amax`: returns 8 codes in two dwords (saturated when SAT).
+template <bool SAT>
 __device__ inline u32x2 encode8(u32x4 v, int byte, unsigned amax) {
   bool tiny = (byte == 0) && (amax != 0);
   float sc = scale_operand(byte == 0 ? 1 : byte);
@@ -28,6 +31,10 @@ __device__ inline u32x2 encode8(u32x4 v, int byte, unsigned amax) {
   } else {
     out.x = cvt2(v.x, sc) | (cvt2(v.y, sc) << 16);
     out.y = cvt2(v.z, sc) | (cvt2(v.w, sc) << 16);
+  }
+  if (SAT) {
+    out.x = sat_e4m3x4(out.x);
+    out.y = sat_e4m3x4(out.y);
   }
   return out;
 }
@@ -49,6 +56,7 @@ __device__ inline unsigned amax8(u32x4 v) {
 // scale tile is assembled in the wave's own LDS slice (one wave's LDS accesses
 // execute in order, so no barrier is needed).
 // ---------------------------------------------------------------------------------
+template <bool FLOOR>
 __global__ __launch_bounds__(256) void k_quant_dim0(const uint16_t* __restrict__ x, int64_t rows, int64_t cols,
                                                     int64_t ld, uint8_t* __restrict__ q, uint8_t* __restrict__ scale,
                                                     int64_t row_bands, int64_t ktiles) {
@@ -74,8 +82,8 @@ __global__ __launch_bounds__(256) void k_quant_dim0(const uint16_t* __restrict__
       unsigned a = amax8(v[i]);
       a = umax(a, dpp_xor1(a));
       a = umax(a, dpp_xor2(a));
-      const int byte = rceil_byte(a);
-      const u32x2 codes = encode8(v[i], byte, a);
+      const int byte = scale_byte<FLOOR>(a);
+      const u32x2 codes = encode8<FLOOR>(v[i], byte, a);
       if (col_ok && r < rows) {
         *(u32x2*)(q + r * cols + col0) = codes;
         if ((c & 3) == 0) st[scale_in_tile(2 * i + h, c >> 2)] = (uint8_t)byte;
@@ -101,6 +109,7 @@ __global__ __launch_bounds__(256) void k_quant_dim0(const uint16_t* __restrict__
 //   by ((c / 8) % 8) * 32, so the dword writes (64 lanes, 64 banks) and the 16-byte
 //   row reads are both conflict-free; the stores then write 256-byte rows of q_t.
 // ---------------------------------------------------------------------------------
+template <bool FLOOR>
 __global__ __launch_bounds__(256) void k_quant_dim1(const uint16_t* __restrict__ x, int64_t rows, int64_t cols,
                                                     int64_t ld, uint8_t* __restrict__ q_t,
                                                     uint8_t* __restrict__ scale_t, int64_t rtiles, int64_t ctiles) {
@@ -152,7 +161,7 @@ __global__ __launch_bounds__(256) void k_quant_dim1(const uint16_t* __restrict__
 #pragma unroll
       for (int e = 0; e < 2; ++e) {  // column 2p + e of the lane's eight
         const unsigned amax = e ? (am[p] >> 16) : (am[p] & 0xffff);
-        const int byte = rceil_byte(amax);
+        const int byte = scale_byte<FLOOR>(amax);
         const bool tiny = byte == 0 && amax != 0;
         const float sc = scale_operand(byte == 0 ? 1 : byte);
         const unsigned sel = e ? 0x07060302u : 0x05040100u;
@@ -162,7 +171,8 @@ __global__ __launch_bounds__(256) void k_quant_dim1(const uint16_t* __restrict__
           p01 = double_bf16x2(p01);
           p23 = double_bf16x2(p23);
         }
-        const unsigned codes = cvt2(p01, sc) | (cvt2(p23, sc) << 16);
+        unsigned codes = cvt2(p01, sc) | (cvt2(p23, sc) << 16);
+        if (FLOOR) codes = sat_e4m3x4(codes);
         const int c = 8 * cg + 2 * p + e;  // column within the tile = row of the code tile
         *(unsigned*)(s_codes + c * 256 + (rloc ^ swz)) = codes;
         if (g == 0 && r0 + 32 * kb < rows) ssc[(c >> 5) * 256 + scale_in_tile(c & 31, kb)] = (uint8_t)byte;
@@ -206,6 +216,7 @@ __global__ __launch_bounds__(256) void k_quant_dim1(const uint16_t* __restrict__
 //   back as whole 256-byte q_t rows. The eight dim1 scale tiles (256 columns x 8
 //   blocks) are assembled in LDS and written whole.
 // ---------------------------------------------------------------------------------
+template <bool FLOOR>
 __global__ __launch_bounds__(256) void k_quant_both(const uint16_t* __restrict__ x, int64_t batch, int64_t rows,
                                                     int64_t cols, int64_t ld, uint8_t* __restrict__ q,
                                                     uint8_t* __restrict__ scale, uint8_t* __restrict__ q_t,
@@ -247,8 +258,8 @@ __global__ __launch_bounds__(256) void k_quant_both(const uint16_t* __restrict__
         unsigned a = amax8(v[i]);
         a = umax(a, dpp_xor1(a));
         a = umax(a, dpp_xor2(a));
-        const int byte = rceil_byte(a);
-        const u32x2 codes = encode8(v[i], byte, a);
+        const int byte = scale_byte<FLOOR>(a);
+        const u32x2 codes = encode8<FLOOR>(v[i], byte, a);
         if (col_ok && rows_ok) {
           *(u32x2*)(q + (qrow0 + base + 16 * h + i) * cols + col) = codes;
           if ((c & 3) == 0) st0[scale_in_tile(16 * h + i, c >> 2)] = (uint8_t)byte;
@@ -266,7 +277,7 @@ __global__ __launch_bounds__(256) void k_quant_both(const uint16_t* __restrict__
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
           const unsigned amax = e ? (am >> 16) : (am & 0xffff);
-          const int byte = rceil_byte(amax);
+          const int byte = scale_byte<FLOOR>(amax);
           const bool tiny = byte == 0 && amax != 0;
           const float sc = scale_operand(byte == 0 ? 1 : byte);
           const unsigned sel = e ? 0x07060302u : 0x05040100u;
@@ -280,6 +291,7 @@ __global__ __launch_bounds__(256) void k_quant_both(const uint16_t* __restrict__
               p23 = double_bf16x2(p23);
             }
             d[m] = cvt2(p01, sc) | (cvt2(p23, sc) << 16);
+            if (FLOOR) d[m] = sat_e4m3x4(d[m]);
           }
           const int cc = 8 * c + 2 * p + e;      // column within the tile = row of s_t
           const int k = (64 * w + 32 * sub + 16 * h) >> 4;  // 16-byte chunk: the lane's 16 rows
@@ -349,7 +361,7 @@ __global__ __launch_bounds__(256) void k_quant_w32(const uint16_t* __restrict__ 
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     int64_t r = rb * 32 + 2 * i + h;
-    u32x2 codes = encode8(v[i], byte, a);
+    u32x2 codes = encode8<false>(v[i], byte, a);
     if (col_ok) *(u32x2*)(q + r * k + col0) = codes;
     *(u32x2*)(lq + (2 * i + h) * 256 + c * 8) = codes;
   }
@@ -427,39 +439,51 @@ int64_t resident_blocks(const void* kernel, int threads) {
 }
 }  // namespace
 hipError_t mx_launch_dim0(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, uint8_t* q, uint8_t* scale,
-                          hipStream_t stream) {
+                          int floor_mode, hipStream_t stream) {
   const int64_t row_bands = (rows + 31) / 32, ktiles = mx::scale_tiles_k(cols / 32);
   const int64_t tiles = row_bands * ktiles;
   if (tiles == 0) return hipSuccess;
   // enough 4-wave blocks to fill the device once, each wave striding over the tiles
   static int64_t fill = 0;  // per process; every gfx950 part has the same shape
-  if (fill == 0) fill = resident_blocks((const void*)mx::k_quant_dim0, 256);
+  if (fill == 0) fill = resident_blocks((const void*)mx::k_quant_dim0<false>, 256);
   const int64_t blocks = std::min<int64_t>((tiles + 3) / 4, fill);
-  hipLaunchKernelGGL(mx::k_quant_dim0, dim3((unsigned)blocks), dim3(256), 0, stream, x, rows, cols, ld, q, scale,
-                     row_bands, ktiles);
+  if (floor_mode)
+    hipLaunchKernelGGL(mx::k_quant_dim0<true>, dim3((unsigned)blocks), dim3(256), 0, stream, x, rows, cols, ld, q,
+                       scale, row_bands, ktiles);
+  else
+    hipLaunchKernelGGL(mx::k_quant_dim0<false>, dim3((unsigned)blocks), dim3(256), 0, stream, x, rows, cols, ld, q,
+                       scale, row_bands, ktiles);
   return hipGetLastError();
 }
 
 hipError_t mx_launch_dim1(const uint16_t* x, int64_t batch, int64_t rows, int64_t cols, int64_t ld, uint8_t* q_t,
-                          uint8_t* scale_t, hipStream_t stream) {
+                          uint8_t* scale_t, int floor_mode, hipStream_t stream) {
   const int64_t rtiles = (rows + 255) / 256, ctiles = (cols + 63) / 64;
   const int64_t blocks = batch * rtiles * ctiles;
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL(mx::k_quant_dim1, dim3((unsigned)blocks), dim3(256), 0, stream, x, rows, cols, ld, q_t,
-                     scale_t, rtiles, ctiles);
+  if (floor_mode)
+    hipLaunchKernelGGL(mx::k_quant_dim1<true>, dim3((unsigned)blocks), dim3(256), 0, stream, x, rows, cols, ld, q_t,
+                       scale_t, rtiles, ctiles);
+  else
+    hipLaunchKernelGGL(mx::k_quant_dim1<false>, dim3((unsigned)blocks), dim3(256), 0, stream, x, rows, cols, ld, q_t,
+                       scale_t, rtiles, ctiles);
   return hipGetLastError();
 }
 
 hipError_t mx_launch_both(const uint16_t* x, int64_t batch, int64_t rows, int64_t cols, int64_t ld, uint8_t* q,
-                          uint8_t* scale, uint8_t* q_t, uint8_t* scale_t, hipStream_t stream) {
+                          uint8_t* scale, uint8_t* q_t, uint8_t* scale_t, int floor_mode, hipStream_t stream) {
   const int64_t rtiles = (rows + 255) / 256, ctiles = (cols + 255) / 256;
   const int64_t tiles = batch * rtiles * ctiles;
   if (tiles == 0) return hipSuccess;
   static int64_t fill = 0;
-  if (fill == 0) fill = resident_blocks((const void*)mx::k_quant_both, 256);
+  if (fill == 0) fill = resident_blocks((const void*)mx::k_quant_both<false>, 256);
   const int64_t blocks = std::min<int64_t>(tiles, fill);
-  hipLaunchKernelGGL(mx::k_quant_both, dim3((unsigned)blocks), dim3(256), 0, stream, x, batch, rows, cols, ld, q,
-                     scale, q_t, scale_t, rtiles, ctiles);
+  if (floor_mode)
+    hipLaunchKernelGGL(mx::k_quant_both<true>, dim3((unsigned)blocks), dim3(256), 0, stream, x, batch, rows, cols, ld,
+                       q, scale, q_t, scale_t, rtiles, ctiles);
+  else
+    hipLaunchKernelGGL(mx::k_quant_both<false>, dim3((unsigned)blocks), dim3(256), 0, stream, x, batch, rows, cols,
+                       ld, q, scale, q_t, scale_t, rtiles, ctiles);
   return hipGetLastError();
 }
 

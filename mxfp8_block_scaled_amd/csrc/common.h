@@ -37,18 +37,41 @@ __device__ inline int rceil_byte(unsigned amax_bits) {
   return b < 0 ? 0 : b;
 }
 
+// FLOOR E8M0 byte (the OCP MX default): floor(log2(amax)) - 8 = E - 135 for bf16
+// exponent field E >= 1, so the byte is E - 8, clamped at 0 (zero and bf16-denormal
+// amax included).
+__device__ inline int floor_byte(unsigned amax_bits) {
+  int b = (int)(amax_bits >> 7) - 8;
+  return b < 0 ? 0 : b;
+}
+
+template <bool FLOOR>
+__device__ inline int scale_byte(unsigned amax_bits) {
+  return FLOOR ? floor_byte(amax_bits) : rceil_byte(amax_bits);
+}
+
 // E8M0 byte as the float operand of the scaled converts: only the exponent
 // field is used, so the bits are just byte << 23.
 __device__ inline float scale_operand(int byte) { return __builtin_bit_cast(float, (unsigned)byte << 23); }
 
 // Encode two bf16 values (packed in one dword) as two E4M3 codes (low 16 bits of
-// the result) = RNE-saturating E4M3 of x / 2^(byte - 127). `byte` must be >= 1
+// the result) = RNE E4M3 of x / 2^(byte - 127). A quotient that rounds above 448
+// comes out as NaN (S.1111.111), not saturated: the RCEIL rule never produces one,
+// the FLOOR rule does and fixes the codes with sat_e4m3x4. `byte` must be >= 1
 // here; blocks whose scale byte is 0 are handled by the callers by doubling the
 // input and using byte 1 (exact: x / 2^-127 == 2x / 2^-126).
 __device__ inline unsigned cvt2(unsigned two_bf16, float scale) {
   bf16x2 v = __builtin_bit_cast(bf16x2, two_bf16);
   s16x2 r = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16((s16x2){0, 0}, v, scale, false);
   return (unsigned)(unsigned short)r[0];
+}
+
+// Saturates four packed E4M3 codes: a NaN byte (S.1111.111), which from finite
+// input only the convert's overflow produces, becomes +-448 (S.1111.110). The low
+// seven bits of a byte plus one carry into its bit 7 exactly when they are all ones,
+// and never into the next byte.
+__device__ inline unsigned sat_e4m3x4(unsigned d) {
+  return d ^ ((((d & 0x7f7f7f7fu) + 0x01010101u) & 0x80808080u) >> 7);
 }
 
 // Doubles two packed bf16 values exactly, for |x| tiny (both inputs well below

@@ -83,6 +83,17 @@ def test_dim0_dim1_validation(lib):
     assert f(P, 1, 64, 64, 64, P2 + 4, P2, P2, P2, None) == MX_E_ALIGN
 
 
+def test_quantize_ex_validation(lib):
+    f = lib.mx_quantize_ex
+    assert f(P, 1, 64, 64, 64, 0, 0, P2, P2, P2, P2, None) == MX_E_DTYPE  # no form
+    assert f(P, 1, 64, 64, 64, 4, 0, P2, P2, P2, P2, None) == MX_E_DTYPE  # unknown form
+    assert f(P, 1, 64, 64, 64, 3, 2, P2, P2, P2, P2, None) == MX_E_DTYPE  # unknown scale rule
+    assert f(P, 1, 48, 64, 64, 2, 1, None, None, P2, P2, None) == MX_E_SHAPE  # dim1 needs rows % 32
+    assert f(P, 1, 48, 64, 64, 1, 1, P2, P2, None, None, None) in (MX_E_DEVICE, 0)  # dim0 alone: any rows
+    assert f(P, 1, 64, 64, 64, 1, 1, None, P2, None, None, None) == MX_E_NULL  # dim0 output missing
+    assert f(P, 1, 64, 64, 64, 3, 1, P2, P2, None, P2, None) == MX_E_NULL  # dim1 output missing
+
+
 def test_dim1_and_w32_validation(lib):
     assert lib.mx_quantize_dim1(P, 1, 48, 64, 64, P2, P2, None) == MX_E_SHAPE  # rows % 32
     assert lib.mx_quantize_dim1(P, 0, 64, 64, 64, P2, P2, None) == MX_E_SHAPE  # batch

@@ -219,3 +219,61 @@ def test_casts_deterministic():
     a = [host(t) for t in mx.mx_quantize_dim1(x)]
     b = [host(t) for t in mx.mx_quantize_dim1(x)]
     assert all(np.array_equal(u, v) for u, v in zip(a, b))
+
+
+def oracle_forms(oracle, bits, mode):
+    stacked = bits.reshape(-1, bits.shape[-1])
+    oq, osl = oracle.quantize_dim0(stacked, mode)
+    if bits.ndim == 2:
+        oqt, ost = oracle.quantize_dim1(bits, mode)
+    else:
+        parts = [oracle.quantize_dim1(b, mode) for b in bits]
+        oqt = np.stack([p[0] for p in parts])
+        ost = np.concatenate([p[1] for p in parts])
+    return oq, oracle.scales_to_physical(osl), oqt, oracle.scales_to_physical(ost)
+
+
+def check_ex(oracle, bits, forms, mode, name):
+    say(f"[cast ex] {name} forms={forms} mode={mode} shape={bits.shape}")
+    q, s, q_t, s_t = mx.mx_quantize_ex(dev_bf16(bits), forms, mode)
+    oq, os_, oqt, ost = oracle_forms(oracle, bits, "floor" if mode == mx.MX_SCALE_FLOOR else "rceil")
+    if forms & mx.MX_FORM_DIM0:
+        gq = host(q)
+        assert np.array_equal(gq, oq), f"{name}: {np.sum(gq != oq)} dim0 code mismatches"
+        assert np.array_equal(host(s), os_), name
+    else:
+        assert q is None and s is None
+    if forms & mx.MX_FORM_DIM1:
+        gqt = host(q_t)
+        assert np.array_equal(gqt, oqt), f"{name}: {np.sum(gqt != oqt)} dim1 code mismatches"
+        assert np.array_equal(host(s_t), ost), name
+    else:
+        assert q_t is None and s_t is None
+
+
+@pytest.mark.parametrize("forms", [1, 2, 3])
+@pytest.mark.parametrize("shape", [(64, 96), (288, 576), (3, 96, 320)])
+def test_floor_forms(oracle, forms, shape):
+    rng = np.random.default_rng(sum(shape) + forms)
+    check_ex(oracle, synth.normal_bf16(rng, shape, 1.0), forms, mx.MX_SCALE_FLOOR, f"normal{shape}")
+
+
+def test_floor_stress_every_amax(oracle):
+    blocks = stress_blocks(3)
+    n_row = blocks.shape[0] // 256 * 256
+    check_ex(oracle, np.ascontiguousarray(blocks[:n_row].reshape(-1, 256)), 3, mx.MX_SCALE_FLOOR, "row blocks")
+    n_col = blocks.shape[0] // 64 * 64
+    panels = blocks[:n_col].reshape(-1, 64, 32).transpose(0, 2, 1).reshape(-1, 64)
+    check_ex(oracle, np.ascontiguousarray(panels), 3, mx.MX_SCALE_FLOOR, "column blocks")
+    check_ex(oracle, np.ascontiguousarray(panels), 2, mx.MX_SCALE_FLOOR, "column blocks, dim1 kernel")
+    check_ex(oracle, np.ascontiguousarray(blocks[:n_row].reshape(-1, 256)), 1, mx.MX_SCALE_FLOOR, "rows, dim0 kernel")
+
+
+def test_ex_rceil_matches_plain_entry_points():
+    rng = np.random.default_rng(9)
+    x = dev_bf16(synth.normal_bf16(rng, (2, 160, 288), 1.0))
+    q, s, q_t, s_t = mx.mx_quantize_ex(x, 3, mx.MX_SCALE_RCEIL)
+    q0, s0 = mx.mx_quantize_dim0(x.view(-1, 288))
+    q1, s1 = mx.mx_quantize_dim1(x)
+    for a, b in ((q, q0), (s, s0), (q_t, q1), (s_t, s1)):
+        assert torch.equal(a, b)
