@@ -23,6 +23,9 @@ What is computed (sources):
   * The GEMM: a grouped matmul over per-group row offsets `offs` (ao fork PR 10
     "Summary"; pytorch/ao PR 4705 body), with offs=None meaning one dense group
     (torchtitan PR 5334 body), in forward, dgrad and wgrad form.
+  * Token-group padding: each group's token rows moved to a run that starts at a
+    multiple of 32, the rest zero, and the inverse gather (pytorch/ao PR 4705,
+    ghstack list: pad/unpad kernels; ao fork PR 10, "Known follow-ups").
 
 Readings where the pages are silent (each also listed in the design notes):
   * a zero block gets scale byte 0 (the clamp of -inf to the E8M0 floor -127);
@@ -339,6 +342,70 @@ def mx_grouped_mm_fwd(a_q, a_s, b_q, b_s, offs, groups):
 
 def mx_grouped_mm_wgrad(a_tq, a_ts, b_tq, b_ts, offs, groups):
     return grouped_mm_wgrad(dequantize(a_tq, a_ts), dequantize(b_tq, b_ts), offs, groups)
+
+
+# --------------------------------------------------------------------------------------
+# Token-group padding (group sizes that are not multiples of 32)
+# --------------------------------------------------------------------------------------
+#
+# The MoE stack pads each expert's token group to a multiple of the 32-row block
+# before the grouped GEMM and unpads the outputs afterwards (pytorch/ao PR 4705,
+# ghstack list: pad/unpad kernels; ao fork PR 10, "Known follow-ups": padded token
+# groups for the grouped mm feed padded offsets to the GEMM). The pages print no
+# layout. Reading taken here: group g's rows keep their order and move to a run
+# that starts at the padded offset of g, the padded offsets being the running sum
+# of the group sizes rounded up to 32; every other row of the padded buffer is
+# zero. The buffer has a size fixed by (rows, groups) alone, so that no device
+# value decides an allocation; rows after the last padded offset belong to no group.
+
+
+def padded_rows(rows, groups):
+    """Rows of the padded buffer for any `groups` sizes summing to at most `rows`.
+
+    A group grows by at most 31 rows and the padded total is a multiple of 32, so
+    the largest multiple of 32 not above rows + 31 * groups always suffices (and is
+    at least rows rounded up to 32 when groups >= 1).
+    """
+    return ((rows + 31 * groups) // 32) * 32
+
+
+def padded_offsets(offs):
+    """offs_pad[g] = sum over j <= g of (size of group j rounded up to 32)."""
+    out = []
+    total = 0
+    for start, end in group_bounds(offs, None):
+        size = end - start
+        total += ((size + 31) // 32) * 32
+        out.append(total)
+    return out
+
+
+def pad_token_groups(x, offs, rows_pad):
+    """x_pad [rows_pad, C]: row offs_pad[g-1] + i = row offs[g-1] + i of x for
+    i < size of group g; all other rows zero. Returns (x_pad, offs_pad)."""
+    x = np.asarray(x)
+    pad_ends = padded_offsets(offs)
+    out = np.zeros((rows_pad,) + x.shape[1:], dtype=x.dtype)
+    pad_start = 0
+    for (start, end), pad_end in zip(group_bounds(offs, None), pad_ends):
+        for i in range(end - start):
+            out[pad_start + i] = x[start + i]
+        pad_start = pad_end
+    return out, pad_ends
+
+
+def unpad_token_groups(y_pad, offs, rows):
+    """Inverse gather: row offs[g-1] + i of the result = row offs_pad[g-1] + i of
+    y_pad. Rows past offs[G-1] belong to no group and stay zero."""
+    y_pad = np.asarray(y_pad)
+    pad_ends = padded_offsets(offs)
+    out = np.zeros((rows,) + y_pad.shape[1:], dtype=y_pad.dtype)
+    pad_start = 0
+    for (start, end), pad_end in zip(group_bounds(offs, None), pad_ends):
+        for i in range(end - start):
+            out[start + i] = y_pad[pad_start + i]
+        pad_start = pad_end
+    return out
 
 
 # --------------------------------------------------------------------------------------

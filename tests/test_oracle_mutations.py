@@ -13,6 +13,7 @@ from oracle import mx
 import test_oracle_cast as tc
 import test_oracle_gemm as tg
 import test_oracle_layout as tl
+import test_oracle_pad as tp
 
 
 def enc_ties_away(v, negative):
@@ -94,6 +95,38 @@ def bf16_round_via_f32(x):
     return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
 
 
+def padded_offsets_round_down(offs):
+    out, total = [], 0
+    for start, end in mx.group_bounds(offs, None):
+        total += ((end - start) // 32) * 32
+        out.append(total)
+    return out
+
+
+def padded_rows_no_growth(rows, groups):
+    return ((rows + 31) // 32) * 32
+
+
+def pad_at_unpadded_start(x, offs, rows_pad):
+    """Moves each group to its unpadded start instead of its padded one."""
+    x = np.asarray(x)
+    out = np.zeros((rows_pad,) + x.shape[1:], dtype=x.dtype)
+    for start, end in mx.group_bounds(offs, None):
+        out[start:end] = x[start:end]
+    return out, mx.padded_offsets(offs)
+
+
+def unpad_from_previous_group(y_pad, offs, rows):
+    """Reads group g from the padded run of group g - 1's end (an off-by-one group)."""
+    y_pad = np.asarray(y_pad)
+    ends = mx.padded_offsets(offs)
+    out = np.zeros((rows,) + y_pad.shape[1:], dtype=y_pad.dtype)
+    for g, (start, end) in enumerate(mx.group_bounds(offs, None)):
+        base = ends[g - 2] if g >= 2 else 0
+        out[start:end] = y_pad[base:base + end - start]
+    return out
+
+
 MUTANTS = [
     ("e4m3_encode", enc_ties_away, tc.test_encoder_matches_brute_force_all_bf16, {"s": 0}),
     ("e4m3_encode", enc_ties_away, tc.test_worked_values, {}),
@@ -109,6 +142,10 @@ MUTANTS = [
     ("grouped_mm_wgrad", wgrad_misaligned_rows, tg.test_wgrad_matches_loops_and_empty_group_is_zero, {}),
     ("dequantize", dequant_bias128, tg.test_exact_integer_case_matches_rationals, {}),
     ("round_to_bf16_bits", bf16_round_via_f32, tg.test_bf16_rounding, {}),
+    ("padded_offsets", padded_offsets_round_down, tp.test_golden_cases, {}),
+    ("padded_rows", padded_rows_no_growth, tp.test_size_bound_exhaustive, {}),
+    ("pad_token_groups", pad_at_unpadded_start, tp.test_padded_wgrad_equals_per_group_brute_force, {}),
+    ("unpad_token_groups", unpad_from_previous_group, tp.test_pad_properties, {"seed": 1}),
 ]
 
 
