@@ -171,8 +171,9 @@ mx_status mx_quantize_weight_32x32(const uint16_t* w, int64_t batch, int64_t n, 
  *   offs      device int32[groups]: inclusive cumulative group ends; group g is
  *             rows [offs[g-1], offs[g]) with offs[-1] = 0. NULL = one dense group
  *             (groups must be 1). Caller precondition (not checked, offs stays on
- *             the device): non-decreasing, every entry % 32 == 0, offs[G-1] == m.
- *             Rows past offs[G-1] are left unwritten.
+ *             the device): non-decreasing, every entry % 32 == 0, offs[G-1] <= m.
+ *             Rows past offs[G-1] belong to no group and are left unwritten (the
+ *             buffers of mx_pad_token_groups end with such rows).
  *   out       [m x n], float32 or bf16 per out_dtype, row pitch n (written)
  * k % 32 == 0 (k need not be a multiple of 128: the tail is zero-padded inside
  * the kernel); m >= 0; n >= 1; if groups > 1, n % 32 == 0. fp32 accumulation.
@@ -203,7 +204,8 @@ mx_status mx_grouped_mm_dgrad(const uint8_t* dy, const uint8_t* dy_s, const uint
  *   dy_t, dy_t_s  [n x m] codes (dim1 of grad_out) + mx_scale_bytes(n, m)
  *   x_t, x_t_s    [k x m] codes (dim1 of the input) + mx_scale_bytes(k, m)
  *   offs, groups  group g contracts over rows [offs[g-1], offs[g]) of m; NULL =
- *                 one group over all m. Same caller preconditions as fwd.
+ *                 one group over all m. Same caller preconditions as fwd; rows
+ *                 past offs[G-1] are not read.
  *   dw            [groups x n x k] (written, every element)
  * m % 32 == 0 (the contraction), n >= 1, k >= 1.
  * When the output has fewer 256 x 256 tiles than the device has compute units
@@ -215,6 +217,53 @@ mx_status mx_grouped_mm_dgrad(const uint8_t* dy, const uint8_t* dy_s, const uint
 mx_status mx_grouped_mm_wgrad(const uint8_t* dy_t, const uint8_t* dy_t_s, const uint8_t* x_t, const uint8_t* x_t_s,
                               const int32_t* offs, int32_t groups, int64_t m, int64_t n, int64_t k, void* dw,
                               int out_dtype, void* stream);
+
+/* ---- Token-group padding (group sizes that are not multiples of 32) ----
+ * The grouped GEMM needs every group to start on a 32-row boundary (its scales
+ * and its wgrad blocks run in 32-row units). Padding moves each token group to
+ * such a boundary before the casts and unpadding gathers the GEMM outputs back
+ * [pytorch/ao PR 4705, ghstack list: pad/unpad kernels; ao fork PR 10, Known
+ * follow-ups: padded token groups feed padded offsets to the grouped GEMM].
+ * Group g's rows [offs[g-1], offs[g]) move, in order, to the run starting at
+ * offs_pad[g-1], offs_pad[g] = sum over j <= g of (size_j rounded up to 32);
+ * every other row of the padded buffer is zero. The padded buffer's size depends
+ * only on (rows, groups), so nothing is read back to the host.
+ *
+ * offs here may hold any non-decreasing ends with offs[G-1] <= rows (no 32-row
+ * alignment needed). The kernels clamp each end into [0, rows] and make the
+ * sequence non-decreasing while reading it, so an out-of-contract offs moves the
+ * wrong rows but never addresses memory outside the buffers. groups <= 1024.
+ * A row buffer with zero rows may be NULL. */
+
+/* Rows of the padded buffer for any split of `rows` rows into `groups` groups:
+ * 32 * floor((rows + 31 * groups) / 32). -1 if rows < 0, rows > 2^31 or
+ * groups < 1. */
+int64_t mx_padded_rows(int64_t rows, int32_t groups);
+
+/* Pads bf16 token rows.
+ *   x         [rows x cols] bf16, row pitch ld_x (ld_x % 8 == 0), cols % 8 == 0
+ *   offs      device int32[groups], unpadded group ends (see above)
+ *   x_pad     [rows_pad x cols] bf16, row pitch cols (written, every row)
+ *   rows_pad  >= mx_padded_rows(rows, groups), < 2^31
+ *   offs_pad  device int32[groups] (written): padded group ends, each % 32 == 0,
+ *             offs_pad[G-1] <= rows_pad; pass it as `offs` to the casts' users
+ *             (the grouped GEMM calls) with m = rows_pad.
+ * rows + 31 * groups < 2^31. */
+mx_status mx_pad_token_groups(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, const int32_t* offs,
+                              int32_t groups, uint16_t* x_pad, int64_t rows_pad, int32_t* offs_pad, void* stream);
+
+/* Unpads rows (the inverse gather): y[offs[g-1] + i] = y_pad[offs_pad[g-1] + i]
+ * for every row of group g, offs_pad being recomputed from offs as above.
+ *   y_pad     [rows_pad x cols], row pitch ld_pad, element type `dtype`
+ *             (MX_OUT_F32 or MX_OUT_BF16): e.g. a grouped GEMM output
+ *   offs      the same unpadded group ends given to mx_pad_token_groups
+ *   y         [rows x cols], row pitch ld_y (rows of the groups written; rows
+ *             past offs[G-1] untouched)
+ * cols * element size and both pitches * element size multiples of 16 bytes;
+ * rows_pad >= mx_padded_rows(rows, groups). */
+mx_status mx_unpad_token_groups(const void* y_pad, int64_t rows_pad, int64_t cols, int64_t ld_pad,
+                                const int32_t* offs, int32_t groups, void* y, int64_t rows, int64_t ld_y, int dtype,
+                                void* stream);
 
 #ifdef __cplusplus
 }

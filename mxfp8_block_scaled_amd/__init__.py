@@ -29,6 +29,9 @@ __all__ = [
     "mx_grouped_mm_fwd",
     "mx_grouped_mm_dgrad",
     "mx_grouped_mm_wgrad",
+    "mx_padded_rows",
+    "mx_pad_token_groups",
+    "mx_unpad_token_groups",
     "MXError",
     "library_path",
 ]
@@ -236,3 +239,54 @@ def mx_grouped_mm_wgrad(dy_t, dy_t_s, x_t, x_t_s, offs, m, n, k, groups=None, ou
     _lib.call("mx_grouped_mm_wgrad", _ptr(dy_t), _ptr(dy_t_s), _ptr(x_t), _ptr(x_t_s), _ptr(offs), G, m, n, k,
               _ptr(out), out_dtype, _stream(dy_t))
     return out
+
+
+def mx_padded_rows(rows, groups):
+    """Rows of the padded buffer for `rows` token rows in `groups` groups."""
+    n = _lib.load().mx_padded_rows(int(rows), int(groups))
+    if n < 0:
+        raise ValueError(f"mx_padded_rows({rows}, {groups}): need rows in [0, 2^31] and groups >= 1")
+    return n
+
+
+def mx_pad_token_groups(x, offs, rows_pad=None, x_pad=None, offs_pad=None):
+    """Pads each token group of x [rows, cols] to a multiple of 32 rows.
+
+    Returns (x_pad [rows_pad, cols], offs_pad int32[G]); offs_pad is written on
+    the device and is what the grouped GEMM calls take, with m = rows_pad.
+    """
+    x = _bf16_bits(x)
+    if x.dim() != 2 or (x.numel() and x.stride(1) != 1):
+        raise ValueError("x must be a 2D tensor with unit inner stride")
+    G = _groups(offs, None)
+    rows, cols = x.shape
+    ld = x.stride(0) if x.numel() else cols  # an empty tensor's strides are arbitrary
+    if rows_pad is None:
+        rows_pad = mx_padded_rows(rows, G)
+    if x_pad is None:
+        x_pad = torch.empty((rows_pad, cols), dtype=x.dtype, device=x.device)
+    if offs_pad is None:
+        offs_pad = torch.empty(G, dtype=torch.int32, device=x.device)
+    _lib.call("mx_pad_token_groups", _ptr(x), rows, cols, ld, _ptr(offs), G, _ptr(x_pad), rows_pad,
+              _ptr(offs_pad), _stream(x))
+    return x_pad, offs_pad
+
+
+def mx_unpad_token_groups(y_pad, offs, rows, y=None):
+    """Gathers the rows of every group of y_pad [rows_pad, cols] (float32 or bf16)
+    back to their unpadded positions in y [rows, cols]."""
+    if y_pad.dim() != 2 or y_pad.stride(1) != 1:
+        raise ValueError("y_pad must be a 2D tensor with unit inner stride")
+    if y_pad.dtype == torch.float32:
+        dt = MX_OUT_F32
+    elif y_pad.dtype in (torch.bfloat16, torch.int16, torch.uint16):
+        dt = MX_OUT_BF16
+    else:
+        raise TypeError(f"y_pad must be float32 or bf16, got {y_pad.dtype}")
+    G = _groups(offs, None)
+    rows_pad, cols = y_pad.shape
+    if y is None:
+        y = torch.empty((rows, cols), dtype=y_pad.dtype, device=y_pad.device)
+    _lib.call("mx_unpad_token_groups", _ptr(y_pad), rows_pad, cols, y_pad.stride(0), _ptr(offs), G, _ptr(y), rows,
+              y.stride(0), dt, _stream(y_pad))
+    return y

@@ -18,6 +18,10 @@ hipError_t mx_launch_both(const uint16_t*, int64_t, int64_t, int64_t, int64_t, u
                           int, hipStream_t);
 hipError_t mx_launch_w32(const uint16_t*, int64_t, int64_t, int64_t, int64_t, uint8_t*, uint8_t*, uint8_t*, uint8_t*,
                          hipStream_t);
+hipError_t mx_launch_pad(const uint16_t*, int64_t, int64_t, int64_t, const int32_t*, int, uint16_t*, int64_t, int32_t*,
+                         hipStream_t);
+hipError_t mx_launch_unpad(const void*, int64_t, int64_t, int64_t, const int32_t*, int, void*, int64_t, int64_t,
+                           hipStream_t);
 hipError_t mx_launch_gemm_mgroup(const uint8_t*, const uint8_t*, const uint8_t*, const uint8_t*, const int32_t*, int,
                                  int64_t, int64_t, int64_t, void*, int, hipStream_t);
 hipError_t mx_launch_gemm_kgroup(const uint8_t*, const uint8_t*, const uint8_t*, const uint8_t*, const int32_t*, int,
@@ -300,6 +304,79 @@ mx_status mx_grouped_mm_wgrad(const uint8_t* dy_t, const uint8_t* dy_t_s, const 
   // dW_g[n x k] = dY^T[n x m] . (X^T[k x m])^T over group g's range of m
   return launched(mx_launch_gemm_kgroup(dy_t, dy_t_s, x_t, x_t_s, offs, groups, n, k, m, dw, out_dtype, (hipStream_t)stream),
                   "mx_grouped_mm_wgrad");
+}
+
+// ---- token-group padding ----
+
+namespace {
+
+constexpr int32_t kPadMaxGroups = 1024;
+constexpr int64_t kInt32Max = 2147483647;
+
+mx_status check_pad_common(int64_t rows, int32_t groups, int64_t rows_pad, const int32_t* offs) {
+  if (groups < 1 || groups > kPadMaxGroups)
+    return fail(MX_E_SHAPE, "groups = %d is outside [1, %d]", groups, kPadMaxGroups);
+  if (rows < 0 || rows + 31 * (int64_t)groups > kInt32Max)
+    return fail(MX_E_SHAPE, "rows = %lld: rows + 31 * groups must stay below 2^31 (int32 offsets)", (long long)rows);
+  const int64_t need = mx_padded_rows(rows, groups);
+  if (rows_pad < need || rows_pad > kInt32Max)
+    return fail(MX_E_SHAPE, "rows_pad = %lld: the padded buffer needs mx_padded_rows(%lld, %d) = %lld rows (and < 2^31)",
+                (long long)rows_pad, (long long)rows, groups, (long long)need);
+  if (!offs) return fail(MX_E_NULL, "offs is NULL");
+  if ((uintptr_t)offs & 3) return fail(MX_E_ALIGN, "offs is not 4-byte aligned");
+  return MX_OK;
+}
+
+// A buffer of zero rows may be NULL (nothing is read or written there).
+mx_status check_rows_ptr(const char* name, const void* p, int64_t rows) {
+  if (!p && rows == 0) return MX_OK;
+  return check_ptr(name, p);
+}
+
+}  // namespace
+
+int64_t mx_padded_rows(int64_t rows, int32_t groups) {
+  if (rows < 0 || groups < 1 || rows > kMaxDim) return -1;
+  return ((rows + 31 * (int64_t)groups) / 32) * 32;
+}
+
+mx_status mx_pad_token_groups(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, const int32_t* offs,
+                              int32_t groups, uint16_t* x_pad, int64_t rows_pad, int32_t* offs_pad, void* stream) {
+  TRY(check_pad_common(rows, groups, rows_pad, offs));
+  TRY(check_dim("cols", cols, 8));
+  if (cols % 8 != 0) return fail(MX_E_SHAPE, "cols = %lld must be a multiple of 8 (16-byte bf16 rows)", (long long)cols);
+  TRY(check_pitch("ld_x", ld_x, cols));
+  TRY(check_rows_ptr("x", x, rows));
+  TRY(check_rows_ptr("x_pad", x_pad, rows_pad));
+  if (!offs_pad) return fail(MX_E_NULL, "offs_pad is NULL");
+  if ((uintptr_t)offs_pad & 3) return fail(MX_E_ALIGN, "offs_pad is not 4-byte aligned");
+  TRY(check_device());
+  return launched(mx_launch_pad(x, rows, cols, ld_x, offs, groups, x_pad, rows_pad, offs_pad, (hipStream_t)stream),
+                  "mx_pad_token_groups");
+}
+
+mx_status mx_unpad_token_groups(const void* y_pad, int64_t rows_pad, int64_t cols, int64_t ld_pad,
+                                const int32_t* offs, int32_t groups, void* y, int64_t rows, int64_t ld_y, int dtype,
+                                void* stream) {
+  if (dtype != MX_OUT_F32 && dtype != MX_OUT_BF16)
+    return fail(MX_E_DTYPE, "dtype = %d is neither MX_OUT_F32 (0) nor MX_OUT_BF16 (1)", dtype);
+  TRY(check_pad_common(rows, groups, rows_pad, offs));
+  const int64_t es = dtype == MX_OUT_F32 ? 4 : 2;
+  TRY(check_dim("cols", cols, 1));
+  if ((cols * es) % 16 != 0)
+    return fail(MX_E_SHAPE, "cols = %lld: rows must be a whole number of 16-byte chunks", (long long)cols);
+  if (ld_pad < cols || ld_y < cols)
+    return fail(MX_E_LAYOUT, "ld_pad = %lld / ld_y = %lld is smaller than cols = %lld", (long long)ld_pad,
+                (long long)ld_y, (long long)cols);
+  if ((ld_pad * es) % 16 != 0 || (ld_y * es) % 16 != 0)
+    return fail(MX_E_ALIGN, "row pitches must be multiples of 16 bytes");
+  if (ld_pad > kMaxDim || ld_y > kMaxDim) return fail(MX_E_SHAPE, "row pitch too large");
+  TRY(check_rows_ptr("y_pad", y_pad, rows_pad));
+  TRY(check_rows_ptr("y", y, rows));
+  TRY(check_device());
+  return launched(mx_launch_unpad(y_pad, rows_pad, cols * es, ld_pad * es, offs, groups, y, rows, ld_y * es,
+                                  (hipStream_t)stream),
+                  "mx_unpad_token_groups");
 }
 
 }  // extern "C"
