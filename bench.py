@@ -17,6 +17,11 @@ One step runs, in order:
   dim0 dY', dense dgrad over the 576-wide contraction -> dX' [16384, 4096] bf16
   dim1 dY', dense wgrad (reuses dim1 X)               -> dW' [576, 4096] bf16
 `value` = all GEMM flops of the step / step time (casts included).
+
+--unaligned-groups: the same tokens with per-row (not 32-aligned) group sizes;
+the step pads X and dY to 32-row group boundaries (ao fork PR 10, "Known
+follow-ups": padded token groups), runs the casts and the grouped passes on the
+padded rows and offsets, and unpads Y and dX; flops still count real rows only.
 """
 
 import argparse
@@ -50,6 +55,9 @@ def parse():
                     help="cast each tensor with separate dim0 and dim1 kernels instead of the one-pass cast")
     ap.add_argument("--only", default=None,
                     help="run only the ops of the step whose name contains this text (for counter runs)")
+    ap.add_argument("--unaligned-groups", action="store_true",
+                    help="group sizes drawn per row (not multiples of 32): the step pads X and dY to 32-row "
+                         "group boundaries, runs the grouped passes on the padded offsets and unpads Y and dX")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a 1 GiB device-to-device copy instead (reference for HBM byte counters)")
     return ap.parse_args()
@@ -107,20 +115,27 @@ def main():
     offs_np = d["offs"]
     X, W, dY = to_dev(d["x"]), to_dev(d["w"]), to_dev(d["dy"])
     Wn, dYn = to_dev(d["w_narrow"]), to_dev(d["dy_narrow"])
-    offs = torch.from_numpy(offs_np).to(dev)
     del d
+    unaligned = args.unaligned_groups
+    if unaligned:
+        # per-row multinomial group sizes; the grouped passes see the padded rows
+        offs_np = np.cumsum(np.random.default_rng(1).multinomial(M, np.full(G, 1.0 / G))).astype(np.int32)
+    offs = torch.from_numpy(offs_np).to(dev)
+    Mg = mx.mx_padded_rows(M, G) if unaligned else M
+    offs_pad = torch.empty(G, dtype=torch.int32, device=dev)
+    goffs = offs_pad if unaligned else offs
 
     u8 = lambda *s: torch.empty(s, dtype=torch.uint8, device=dev)  # noqa: E731
     sb = mx.mx_scale_bytes
     bf = lambda *s: torch.empty(s, dtype=torch.bfloat16, device=dev)  # noqa: E731
     buf = {
-        "xq": u8(M, K), "xs": u8(sb(M, K)),
+        "xq": u8(Mg, K), "xs": u8(sb(Mg, K)),
         "wq": u8(G * N, K), "ws": u8(sb(G * N, K)),
-        "dyq": u8(M, N), "dys": u8(sb(M, N)),
+        "dyq": u8(Mg, N), "dys": u8(sb(Mg, N)),
         "wtq": u8(G, K, N), "wts": u8(sb(G * K, N)),
-        "dytq": u8(N, M), "dyts": u8(sb(N, M)),
-        "xtq": u8(K, M), "xts": u8(sb(K, M)),
-        "y": bf(M, N), "dx": bf(M, K), "dw": bf(G, N, K),
+        "dytq": u8(N, Mg), "dyts": u8(sb(N, Mg)),
+        "xtq": u8(K, Mg), "xts": u8(sb(K, Mg)),
+        "y": bf(Mg, N), "dx": bf(Mg, K), "dw": bf(G, N, K),
         "dynq": u8(M, NARROW), "dyns": u8(sb(M, NARROW)),
         "dyntq": u8(NARROW, M), "dynts": u8(sb(NARROW, M)),
         "yn": bf(M, NARROW), "dxn": bf(M, K), "dwn": bf(1, NARROW, K),
@@ -135,13 +150,15 @@ def main():
     def cast_w32():
         w32["q"], w32["qt"], w32["sr"], w32["sc"] = mx.mx_quantize_weight_32x32(Wn)
 
+    # flops count the real token rows (padding rows are overhead, not work)
     g_fwd = ("gemm_fwd grouped", "gemm", 2 * M * N * K,
-             lambda: mx.mx_grouped_mm_fwd(buf["xq"], buf["xs"], buf["wq"], buf["ws"], offs, M, N, K, out=buf["y"]))
+             lambda: mx.mx_grouped_mm_fwd(buf["xq"], buf["xs"], buf["wq"], buf["ws"], goffs, Mg, N, K,
+                                          out=buf["y"]))
     g_dgrad = ("gemm_dgrad grouped", "gemm", 2 * M * N * K,
-               lambda: mx.mx_grouped_mm_dgrad(buf["dyq"], buf["dys"], buf["wtq"], buf["wts"], offs, M, N, K,
+               lambda: mx.mx_grouped_mm_dgrad(buf["dyq"], buf["dys"], buf["wtq"], buf["wts"], goffs, Mg, N, K,
                                               out=buf["dx"]))
     g_wgrad = ("gemm_wgrad grouped", "gemm", 2 * M * N * K,
-               lambda: mx.mx_grouped_mm_wgrad(buf["dytq"], buf["dyts"], buf["xtq"], buf["xts"], offs, M, N, K,
+               lambda: mx.mx_grouped_mm_wgrad(buf["dytq"], buf["dyts"], buf["xtq"], buf["xts"], goffs, Mg, N, K,
                                               out=buf["dw"], out_dtype=mx.MX_OUT_BF16))
     n_w32 = ("cast_w32 W'", "cast", NARROW * K * W32_BYTES_PER_ELEM, cast_w32)
     n_fwd = ("gemm_fwd dense576", "gemm", 2 * M * NARROW * K,
@@ -153,7 +170,26 @@ def main():
     n_wgrad = ("gemm_wgrad dense576", "gemm", 2 * M * NARROW * K,
                lambda: mx.mx_grouped_mm_wgrad(buf["dyntq"], buf["dynts"], buf["xtq"], buf["xts"], None, M, NARROW,
                                               K, out=buf["dwn"], out_dtype=mx.MX_OUT_BF16))
-    if args.separate_casts:
+    if unaligned:
+        # the MoE grouped part only (the dense layer has no groups); pad bytes: read the
+        # real rows, write every padded row; unpad: read and write the real rows (bf16)
+        Xp, dYp, y_u, dx_u = bf(Mg, K), bf(Mg, N), bf(M, N), bf(M, K)
+        ops = [
+            ("pad X", "pad", 2 * M * K + 2 * Mg * K, lambda: mx.mx_pad_token_groups(X, offs, Mg, Xp, offs_pad)),
+            ("cast_dim0+dim1 X", "cast", both(Mg * K),
+             lambda: mx.mx_quantize_dim0_dim1(Xp, buf["xq"], buf["xs"], buf["xtq"], buf["xts"])),
+            ("cast_dim0+dim1 W", "cast", both(G * N * K),
+             lambda: mx.mx_quantize_dim0_dim1(W, buf["wq"], buf["ws"], buf["wtq"], buf["wts"])),
+            g_fwd,
+            ("unpad Y", "pad", 4 * M * N, lambda: mx.mx_unpad_token_groups(buf["y"], offs, M, y_u)),
+            ("pad dY", "pad", 2 * M * N + 2 * Mg * N, lambda: mx.mx_pad_token_groups(dY, offs, Mg, dYp, offs_pad)),
+            ("cast_dim0+dim1 dY", "cast", both(Mg * N),
+             lambda: mx.mx_quantize_dim0_dim1(dYp, buf["dyq"], buf["dys"], buf["dytq"], buf["dyts"])),
+            g_dgrad,
+            ("unpad dX", "pad", 4 * M * K, lambda: mx.mx_unpad_token_groups(buf["dx"], offs, M, dx_u)),
+            g_wgrad,
+        ]
+    elif args.separate_casts:
         ops = [
             ("cast_dim0 X", "cast", cast0(M * K), lambda: mx.mx_quantize_dim0(X, buf["xq"], buf["xs"])),
             ("cast_dim0 W", "cast", cast0(G * N * K), lambda: mx.mx_quantize_dim0(Wflat, buf["wq"], buf["ws"])),
@@ -266,22 +302,28 @@ def main():
     dom_name, dom_kind, dom_units, _ = ops[dom_i]
     dom = per_op[dom_name]
     achieved = dom_units / (dom["us"] * 1e-6) / 1e12
-    traffic = load_traffic(dom_name, dom_units)
+    traffic = None if unaligned else load_traffic(dom_name, dom_units)
     roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_FP8_TFLOPS, 4), "traffic": traffic, "kernel": dom_name,
                 "flops_per_launch": dom_units, "avg_launch_us": dom["us"]}
 
-    cpu = None if args.no_cpu_baseline else cpu_baseline()
+    cpu = None if (args.no_cpu_baseline or unaligned) else cpu_baseline()
+    workload = ("moe_g8 fwd+dgrad+wgrad: G=8 experts, M=16384 tokens, K=N=4096, "
+                "grad_out 16384x4096, plus dense 576x4096 layer (32x32 weight scales, "
+                "576-wide contraction in dgrad)")
+    if unaligned:
+        workload = (f"moe_g8 unaligned groups: G=8 experts, M=16384 tokens (per-row group sizes), K=N=4096; "
+                    f"pad X and dY to {Mg} rows, one-pass casts, grouped fwd/dgrad/wgrad on padded offsets, "
+                    f"unpad Y and dX (no dense layer)")
 
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "mxfp8 (e4m3 x e4m3, e8m0 block scales, fp32 accumulate)",
         "data": "synthetic (seeded N(0,sigma) bf16, multinomial group sizes)",
-        "config": {"workload": "moe_g8 fwd+dgrad+wgrad: G=8 experts, M=16384 tokens, K=N=4096, "
-                               "grad_out 16384x4096, plus dense 576x4096 layer (32x32 weight scales, "
-                               "576-wide contraction in dgrad)",
-                   "M": M, "K": K, "N": N, "G": G, "narrow": NARROW, "offs": offs_np.tolist(),
+        "config": {"workload": workload,
+                   "M": M, "K": K, "N": N, "G": G, "narrow": None if unaligned else NARROW,
+                   "offs": offs_np.tolist(), "rows_padded": Mg if unaligned else None,
                    "parallelism": "none (1 GPU)"},
         "gemm_tflops": round(gemm_flops / (gemm_us * 1e-6) / 1e12, 1),
         "gemm_frac_of_peak": round(gemm_flops / (gemm_us * 1e-6) / 1e12 / PEAK_FP8_TFLOPS, 4),

@@ -236,8 +236,10 @@ mx_status mx_grouped_mm_wgrad(const uint8_t* dy_t, const uint8_t* dy_t_s, const 
  * A row buffer with zero rows may be NULL. */
 
 /* Rows of the padded buffer for any split of `rows` rows into `groups` groups:
- * 32 * floor((rows + 31 * groups) / 32). -1 if rows < 0, rows > 2^31 or
- * groups < 1. */
+ * rows + 31 * groups rounded up to a multiple of 256 (a group grows by at most 31
+ * rows; the rounding keeps the token axis, which is the row pitch of the dim1
+ * codes fed to wgrad, a whole number of 256-byte windows, so no GEMM load
+ * straddles cache lines). -1 if rows < 0, rows > 2^31 or groups < 1. */
 int64_t mx_padded_rows(int64_t rows, int32_t groups);
 
 /* Pads bf16 token rows.

@@ -337,7 +337,7 @@ mx_status check_rows_ptr(const char* name, const void* p, int64_t rows) {
 
 int64_t mx_padded_rows(int64_t rows, int32_t groups) {
   if (rows < 0 || groups < 1 || rows > kMaxDim) return -1;
-  return ((rows + 31 * (int64_t)groups) / 32) * 32;
+  return ((rows + 31 * (int64_t)groups + 255) / 256) * 256;
 }
 
 mx_status mx_pad_token_groups(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, const int32_t* offs,

@@ -356,17 +356,18 @@ def mx_grouped_mm_wgrad(a_tq, a_ts, b_tq, b_ts, offs, groups):
 # that starts at the padded offset of g, the padded offsets being the running sum
 # of the group sizes rounded up to 32; every other row of the padded buffer is
 # zero. The buffer has a size fixed by (rows, groups) alone, so that no device
-# value decides an allocation; rows after the last padded offset belong to no group.
+# value decides an allocation (rows + 31 * groups rounded up to 256); rows after
+# the last padded offset belong to no group.
 
 
 def padded_rows(rows, groups):
     """Rows of the padded buffer for any `groups` sizes summing to at most `rows`.
 
-    A group grows by at most 31 rows and the padded total is a multiple of 32, so
-    the largest multiple of 32 not above rows + 31 * groups always suffices (and is
-    at least rows rounded up to 32 when groups >= 1).
+    A group grows by at most 31 rows, so rows + 31 * groups always suffices; the
+    count is rounded up to a multiple of 256 so that the token axis, which becomes
+    the row pitch of the transposed (dim1) codes, keeps whole 256-byte rows.
     """
-    return ((rows + 31 * groups) // 32) * 32
+    return -(-(rows + 31 * groups) // 256) * 256
 
 
 def padded_offsets(offs):

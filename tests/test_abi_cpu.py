@@ -150,28 +150,28 @@ def test_padded_rows(lib, oracle):
 
 def test_pad_validation(lib):
     f = lib.mx_pad_token_groups
-    assert f(P, 40, 64, 64, P2, 3, P2, 128, P2, None) in (MX_E_DEVICE, 0)  # valid (no GPU here)
+    assert f(P, 40, 64, 64, P2, 3, P2, 256, P2, None) in (MX_E_DEVICE, 0)  # valid (no GPU here)
     assert f(P, 40, 64, 64, P2, 0, P2, 128, P2, None) == MX_E_SHAPE  # groups
     assert f(P, 40, 64, 64, P2, 1025, P2, 1 << 16, P2, None) == MX_E_SHAPE  # more than 1024 groups
-    assert f(P, 40, 64, 64, P2, 3, P2, 96, P2, None) == MX_E_SHAPE  # rows_pad below the bound (128)
+    assert f(P, 40, 64, 64, P2, 3, P2, 224, P2, None) == MX_E_SHAPE  # rows_pad below the bound (256)
     assert b"mx_padded_rows" in lib.mx_last_error()
-    assert f(P, 40, 60, 64, P2, 3, P2, 128, P2, None) == MX_E_SHAPE  # cols % 8
-    assert f(P, 40, 64, 32, P2, 3, P2, 128, P2, None) == MX_E_LAYOUT  # pitch < cols
-    assert f(P, 40, 64, 64, None, 3, P2, 128, P2, None) == MX_E_NULL  # offs
-    assert f(P, 40, 64, 64, P2 + 2, 3, P2, 128, P2, None) == MX_E_ALIGN  # offs alignment
-    assert f(None, 40, 64, 64, P2, 3, P2, 128, P2, None) == MX_E_NULL  # x
-    assert f(P, 40, 64, 64, P2, 3, P2, 128, None, None) == MX_E_NULL  # offs_pad
+    assert f(P, 40, 60, 64, P2, 3, P2, 256, P2, None) == MX_E_SHAPE  # cols % 8
+    assert f(P, 40, 64, 32, P2, 3, P2, 256, P2, None) == MX_E_LAYOUT  # pitch < cols
+    assert f(P, 40, 64, 64, None, 3, P2, 256, P2, None) == MX_E_NULL  # offs
+    assert f(P, 40, 64, 64, P2 + 2, 3, P2, 256, P2, None) == MX_E_ALIGN  # offs alignment
+    assert f(None, 40, 64, 64, P2, 3, P2, 256, P2, None) == MX_E_NULL  # x
+    assert f(P, 40, 64, 64, P2, 3, P2, 256, None, None) == MX_E_NULL  # offs_pad
     assert f(P, (1 << 31) - 16, 64, 64, P2, 3, P2, 1 << 31, P2, None) == MX_E_SHAPE  # int32 offsets overflow
-    assert f(None, 0, 64, 64, P2, 2, P2, 32, P2, None) in (MX_E_DEVICE, 0)  # no rows: x may be NULL
+    assert f(None, 0, 64, 64, P2, 2, P2, 256, P2, None) in (MX_E_DEVICE, 0)  # no rows: x may be NULL
 
 
 def test_unpad_validation(lib):
     f = lib.mx_unpad_token_groups
-    assert f(P, 128, 64, 64, P2, 3, P2, 40, 64, 0, None) in (MX_E_DEVICE, 0)
-    assert f(P, 128, 64, 64, P2, 3, P2, 40, 64, 2, None) == MX_E_DTYPE
-    assert f(P, 128, 6, 6, P2, 3, P2, 40, 6, 0, None) == MX_E_SHAPE  # 24-byte f32 rows
-    assert f(P, 128, 4, 4, P2, 3, P2, 40, 4, 1, None) == MX_E_SHAPE  # 8-byte bf16 rows
-    assert f(P, 128, 64, 68, P2, 3, P2, 40, 64, 1, None) == MX_E_ALIGN  # bf16 pitch 136 bytes
-    assert f(P, 128, 64, 32, P2, 3, P2, 40, 64, 0, None) == MX_E_LAYOUT
-    assert f(P, 96, 64, 64, P2, 3, P2, 40, 64, 0, None) == MX_E_SHAPE  # rows_pad too small
-    assert f(P, 128, 64, 64, P2, 3, None, 40, 64, 0, None) == MX_E_NULL  # y
+    assert f(P, 256, 64, 64, P2, 3, P2, 40, 64, 0, None) in (MX_E_DEVICE, 0)
+    assert f(P, 256, 64, 64, P2, 3, P2, 40, 64, 2, None) == MX_E_DTYPE
+    assert f(P, 256, 6, 6, P2, 3, P2, 40, 6, 0, None) == MX_E_SHAPE  # 24-byte f32 rows
+    assert f(P, 256, 4, 4, P2, 3, P2, 40, 4, 1, None) == MX_E_SHAPE  # 8-byte bf16 rows
+    assert f(P, 256, 64, 68, P2, 3, P2, 40, 64, 1, None) == MX_E_ALIGN  # bf16 pitch 136 bytes
+    assert f(P, 256, 64, 32, P2, 3, P2, 40, 64, 0, None) == MX_E_LAYOUT
+    assert f(P, 224, 64, 64, P2, 3, P2, 40, 64, 0, None) == MX_E_SHAPE  # rows_pad too small
+    assert f(P, 256, 64, 64, P2, 3, None, 40, 64, 0, None) == MX_E_NULL  # y

@@ -51,8 +51,8 @@ def test_golden_cases(oracle):
 
 def test_size_bound_exhaustive(oracle):
     """padded_rows(rows, G) covers every way to split at most `rows` rows into G
-    groups, and is reached whenever rows >= G (sizes 1, ..., 1, rows - G + 1 with
-    each small group growing by 31)."""
+    groups; the worst split, for rows >= G, is sizes 1, ..., 1, rows - G + 1 (each
+    small group growing by 31), and the bound is rows + 31 G rounded up to 256."""
     mx = oracle
     for G, max_rows in ((1, 100), (2, 100), (3, 70), (4, 40)):
         for rows in range(0, max_rows):
@@ -61,14 +61,13 @@ def test_size_bound_exhaustive(oracle):
                 worst = max(worst, mx.padded_offsets(list(cuts))[-1])
             bound = mx.padded_rows(rows, G)
             assert worst <= bound, (rows, G)
-            assert bound % 32 == 0
+            assert bound % 256 == 0 and rows + 31 * G <= bound < rows + 31 * G + 256
             if rows >= G:
                 # the closed form of the worst case
                 sizes = [1] * (G - 1) + [rows - G + 1]
                 worst_closed = 32 * (G - 1) + 32 * ((rows - G + 1 + 31) // 32)
                 assert mx.padded_offsets(list(np.cumsum(sizes)))[-1] == worst_closed
                 assert worst == worst_closed
-                assert bound - worst < 32 * G, (rows, G)
 
 
 def random_offs(rng, rows, G, empty=0):
