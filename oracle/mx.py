@@ -23,6 +23,9 @@ What is computed (sources):
   * The GEMM: a grouped matmul over per-group row offsets `offs` (ao fork PR 10
     "Summary"; pytorch/ao PR 4705 body), with offs=None meaning one dense group
     (torchtitan PR 5334 body), in forward, dgrad and wgrad form.
+  * The backward override arms: gradients from the saved bf16 operands, or from
+    the dequantized forward operands, through bf16 grouped GEMMs (ao fork PR 10,
+    "Design notes" and review pass).
   * Token-group padding: each group's token rows moved to a run that starts at a
     multiple of 32, the rest zero, and the inverse gather (pytorch/ao PR 4705,
     ghstack list: pad/unpad kernels; ao fork PR 10, "Known follow-ups").
@@ -345,6 +348,53 @@ def mx_grouped_mm_wgrad(a_tq, a_ts, b_tq, b_ts, offs, groups):
 
 
 # --------------------------------------------------------------------------------------
+# Backward override arms (bf16 grouped GEMMs)
+# --------------------------------------------------------------------------------------
+#
+# ao fork PR 10 ("Design notes") lets the backward of the MXFP8 grouped GEMM come
+# from elsewhere while the quantized forward stays as it is: "high_precision" takes
+# both gradients from the saved bf16 operands with plain bf16 grouped GEMMs;
+# "dequantized" dequantizes the saved quantized forward operands (the dim0 codes and
+# their logical scales) and runs the same two GEMMs, so the gradients belong to the
+# function the quantized forward computes; the review pass of that page also names a
+# wgrad-only high-precision switch. A bf16 grouped GEMM multiplies bf16 operands and
+# accumulates in fp32; its exact value is the float64 product below.
+
+
+def dequantize_to_bf16_bits(q, scales):
+    """value(code) * 2^(byte - 127) rounded to bf16 (round-to-nearest-even)."""
+    return round_to_bf16_bits(dequantize(q, scales))
+
+
+def _per_group_transpose(w, groups):
+    """[G * N, K] -> [G * K, N]: each group's matrix transposed in place."""
+    w = np.asarray(w, dtype=np.float64)
+    N = w.shape[0] // groups
+    return np.concatenate([w[g * N:(g + 1) * N].T for g in range(groups)])
+
+
+def backward_bf16(x, w, dy, offs, groups):
+    """Both gradients of Y = X W_g^T from float64 operands (bf16 values):
+    dX = dY W_g per row group, dW_g = dY_g^T X_g. w is [G * N, K]."""
+    dx = grouped_mm(dy, _per_group_transpose(w, groups), offs, groups)
+    dw = grouped_mm_wgrad(np.asarray(dy, dtype=np.float64).T, np.asarray(x, dtype=np.float64).T, offs, groups)
+    return dx, dw
+
+
+def backward_high_precision(x_bits, w_bits, dy_bits, offs, groups):
+    """The high-precision arm: the saved bf16 input and weight, unquantized."""
+    return backward_bf16(bf16_to_f64(x_bits), bf16_to_f64(w_bits), bf16_to_f64(dy_bits), offs, groups)
+
+
+def backward_dequantized(x_q, x_s, w_q, w_s, dy_bits, offs, groups):
+    """The dequantized arm: the forward's dim0 codes of X [M, K] and W [G * N, K]
+    (logical scales) dequantized to bf16; grad_out stays bf16."""
+    xd = bf16_to_f64(dequantize_to_bf16_bits(x_q, x_s))
+    wd = bf16_to_f64(dequantize_to_bf16_bits(w_q, w_s))
+    return backward_bf16(xd, wd, bf16_to_f64(dy_bits), offs, groups)
+
+
+# --------------------------------------------------------------------------------------
 # Token-group padding (group sizes that are not multiples of 32)
 # --------------------------------------------------------------------------------------
 #
@@ -433,7 +483,8 @@ def round_to_bf16_bits(x):
     out = np.ldexp(np.rint(np.ldexp(a, -q_exp)), q_exp)  # rint is round-half-even
     out = np.where(a == 0, 0.0, out)
     out = np.copysign(out, x)
-    f32 = out.astype(np.float32)  # exact: out has <= 8 significant bits
+    with np.errstate(over="ignore"):  # values at or above 2^128 become inf just below
+        f32 = out.astype(np.float32)  # exact: out has <= 8 significant bits
     bits = (f32.view(np.uint32) >> 16).astype(np.uint16)
     bits = np.where(np.abs(out) >= 2.0**128, (bits & 0x8000) | 0x7F80, bits)
     return bits.astype(np.uint16)

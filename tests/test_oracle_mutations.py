@@ -14,6 +14,7 @@ import test_oracle_cast as tc
 import test_oracle_gemm as tg
 import test_oracle_layout as tl
 import test_oracle_pad as tp
+import test_oracle_backward as tb
 
 
 def enc_ties_away(v, negative):
@@ -127,6 +128,20 @@ def unpad_from_previous_group(y_pad, offs, rows):
     return out
 
 
+def transpose_whole_stack(w, groups):
+    """Transposes the stacked [G * N, K] weight as one matrix and cuts it into
+    groups along the wrong axis."""
+    w = np.asarray(w, dtype=np.float64)
+    N = w.shape[0] // groups
+    t = w.T  # [K, G * N]
+    return np.concatenate([t[:, g * N:(g + 1) * N].T.reshape(-1, N)[: t.shape[0]] for g in range(groups)])
+
+
+def dequant_bf16_truncating(q, scales):
+    f = mx.dequantize(q, scales).astype(np.float32)
+    return (f.view(np.uint32) >> 16).astype(np.uint16)
+
+
 MUTANTS = [
     ("e4m3_encode", enc_ties_away, tc.test_encoder_matches_brute_force_all_bf16, {"s": 0}),
     ("e4m3_encode", enc_ties_away, tc.test_worked_values, {}),
@@ -146,6 +161,8 @@ MUTANTS = [
     ("padded_rows", padded_rows_no_growth, tp.test_size_bound_exhaustive, {}),
     ("pad_token_groups", pad_at_unpadded_start, tp.test_padded_wgrad_equals_per_group_brute_force, {}),
     ("unpad_token_groups", unpad_from_previous_group, tp.test_pad_properties, {"seed": 1}),
+    ("_per_group_transpose", transpose_whole_stack, tb.test_backward_matches_loops, {}),
+    ("dequantize_to_bf16_bits", dequant_bf16_truncating, tb.test_dequantize_to_bf16_every_code_and_scale, {}),
 ]
 
 
