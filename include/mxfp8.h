@@ -218,6 +218,57 @@ mx_status mx_grouped_mm_wgrad(const uint8_t* dy_t, const uint8_t* dy_t_s, const 
                               const int32_t* offs, int32_t groups, int64_t m, int64_t n, int64_t k, void* dw,
                               int out_dtype, void* stream);
 
+/* ---- Backward override arms ----
+ * The backward of the MXFP8 grouped GEMM may take its gradients from elsewhere
+ * while the quantized forward is kept [ao fork PR 10, Design notes]: the
+ * high-precision arm from the saved bf16 input and weight, the dequantized arm
+ * from the forward's quantized operands dequantized to bf16 (with their logical,
+ * pre-blocking scales), both through bf16 grouped GEMMs (fp32 accumulation):
+ *   dX = dY . W_g per row group          -> mx_grouped_mm_bf16_dgrad(dy, W_g^T)
+ *   dW_g = dY_g^T . X_g per group        -> mx_grouped_mm_bf16_wgrad(dy^T, X^T)
+ * Every GEMM operand is contraction-contiguous; the transposed operands come from
+ * mx_transpose_bf16 (saved bf16 tensors) or mx_dequantize(transpose = 1) (codes). */
+
+/* Dequantizes codes to bf16: out = value(code) * 2^(byte - 127) rounded to
+ * nearest even in bf16 (exact unless below 2^-126 or at 2^128 and above, which
+ * gives infinity; NaN codes give a bf16 NaN).
+ *   q, scale  [batch*rows x cols] codes (row pitch cols) and their
+ *             mx_scale_bytes(batch*rows, cols) MFMA-blocked scales (a dim0 cast)
+ *   transpose 0: out [batch*rows x cols]; 1: out [batch][cols][rows] (each
+ *             batch's matrix transposed; rows % 8 == 0)
+ *   out       bf16 bit patterns (written)
+ * cols % 32 == 0. */
+mx_status mx_dequantize(const uint8_t* q, const uint8_t* scale, int64_t batch, int64_t rows, int64_t cols,
+                        int transpose, uint16_t* out, void* stream);
+
+/* Logical view of MFMA-blocked scales: logical[r * (cols/32) + kb] = the byte
+ * of row r, block kb (the dequantized arm needs pre-blocking scales [ao fork
+ * PR 10, Design notes]). cols % 32 == 0. */
+mx_status mx_scales_to_logical(const uint8_t* scale, int64_t rows, int64_t cols, uint8_t* logical, void* stream);
+
+/* bf16 transpose: x [batch][rows][cols] (row pitch ld_x, batches contiguous at
+ * rows * ld_x) -> out [batch][cols][rows]. rows % 8 == 0, cols % 8 == 0. */
+mx_status mx_transpose_bf16(const uint16_t* x, int64_t batch, int64_t rows, int64_t cols, int64_t ld_x, uint16_t* out,
+                            void* stream);
+
+/* bf16 grouped GEMMs: the same three calls as the MXFP8 ones with bf16 operands
+ * (bit patterns, no scales) and fp32 accumulation; out_dtype as there.
+ *   fwd:   out [m x n] = a [m x k] . b_g [n x k]^T for the rows of group g
+ *   dgrad: dx [m x k] = dy [m x n] . (w_t_g [k x n])^T, w_t = [groups*k x n]
+ *   wgrad: dw [groups x n x k], dw[g] = dy_t[:, rows_g] . x_t[:, rows_g]^T,
+ *          dy_t [n x m], x_t [k x m]; an empty group gives zeros
+ * offs as for the MXFP8 calls but with no alignment: any non-decreasing ends with
+ * offs[G-1] <= m (group edges inside a 16-byte chunk of the contraction are
+ * masked element by element). The contraction (k, n, m respectively) is a
+ * multiple of 8 and at most 2^21. The wgrad workspace rule of
+ * mx_grouped_mm_wgrad applies here too. */
+mx_status mx_grouped_mm_bf16_fwd(const uint16_t* a, const uint16_t* b, const int32_t* offs, int32_t groups, int64_t m,
+                                 int64_t n, int64_t k, void* out, int out_dtype, void* stream);
+mx_status mx_grouped_mm_bf16_dgrad(const uint16_t* dy, const uint16_t* w_t, const int32_t* offs, int32_t groups,
+                                   int64_t m, int64_t n, int64_t k, void* dx, int out_dtype, void* stream);
+mx_status mx_grouped_mm_bf16_wgrad(const uint16_t* dy_t, const uint16_t* x_t, const int32_t* offs, int32_t groups,
+                                   int64_t m, int64_t n, int64_t k, void* dw, int out_dtype, void* stream);
+
 /* ---- Token-group padding (group sizes that are not multiples of 32) ----
  * The grouped GEMM needs every group to start on a 32-row boundary (its scales
  * and its wgrad blocks run in 32-row units). Padding moves each token group to

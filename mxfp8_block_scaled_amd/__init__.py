@@ -29,6 +29,12 @@ __all__ = [
     "mx_grouped_mm_fwd",
     "mx_grouped_mm_dgrad",
     "mx_grouped_mm_wgrad",
+    "mx_dequantize",
+    "mx_scales_to_logical",
+    "mx_transpose_bf16",
+    "mx_grouped_mm_bf16_fwd",
+    "mx_grouped_mm_bf16_dgrad",
+    "mx_grouped_mm_bf16_wgrad",
     "mx_padded_rows",
     "mx_pad_token_groups",
     "mx_unpad_token_groups",
@@ -290,3 +296,75 @@ def mx_unpad_token_groups(y_pad, offs, rows, y=None):
     _lib.call("mx_unpad_token_groups", _ptr(y_pad), rows_pad, cols, y_pad.stride(0), _ptr(offs), G, _ptr(y), rows,
               y.stride(0), dt, _stream(y_pad))
     return y
+
+
+def mx_dequantize(q, scale, transpose=False, out=None):
+    """Codes q [rows, cols] or [batch, rows, cols] (a dim0 cast's output, scales in
+    the blocked layout) -> bf16 [rows, cols], or per batch [cols, rows] when
+    `transpose`."""
+    if q.dim() == 2:
+        batch, (rows, cols) = 1, q.shape
+    elif q.dim() == 3:
+        batch, rows, cols = q.shape
+    else:
+        raise ValueError("q must be 2D or 3D")
+    if out is None:
+        shape = (cols, rows) if transpose else (rows, cols)
+        out = torch.empty((batch,) + shape if q.dim() == 3 else shape, dtype=torch.bfloat16, device=q.device)
+    _lib.call("mx_dequantize", _ptr(q), _ptr(scale), batch, rows, cols, int(bool(transpose)), _ptr(out), _stream(q))
+    return out
+
+
+def mx_scales_to_logical(scale, rows, cols, out=None):
+    """Blocked scale bytes -> logical uint8 [rows, cols / 32]."""
+    if out is None:
+        out = torch.empty((rows, cols // 32), dtype=torch.uint8, device=scale.device)
+    _lib.call("mx_scales_to_logical", _ptr(scale), rows, cols, _ptr(out), _stream(scale))
+    return out
+
+
+def mx_transpose_bf16(x, out=None):
+    """bf16 [rows, cols] -> [cols, rows]; [batch, rows, cols] -> [batch, cols, rows]."""
+    x = _bf16_bits(x)
+    if x.dim() == 2:
+        batch, (rows, cols) = 1, x.shape
+    elif x.dim() == 3:
+        batch, rows, cols = x.shape
+        if x.stride(0) != rows * x.stride(1):
+            raise ValueError("batches of x must be contiguous with the row pitch")
+    else:
+        raise ValueError("x must be 2D or 3D")
+    if x.numel() and x.stride(-1) != 1:
+        raise ValueError("x must have unit inner stride")
+    if out is None:
+        shape = (cols, rows) if x.dim() == 2 else (batch, cols, rows)
+        out = torch.empty(shape, dtype=x.dtype, device=x.device)
+    ld = x.stride(-2) if x.numel() else cols
+    _lib.call("mx_transpose_bf16", _ptr(x), batch, rows, cols, ld, _ptr(out), _stream(x))
+    return out
+
+
+def mx_grouped_mm_bf16_fwd(a, b, offs, m, n, k, groups=None, out_dtype=MX_OUT_BF16, out=None):
+    """out [m, n] = a [m, k] . b_g [n, k]^T per row group, bf16 operands."""
+    G = _groups(offs, groups)
+    out = _out((m, n), out_dtype, a.device, out)
+    _lib.call("mx_grouped_mm_bf16_fwd", _ptr(a), _ptr(b), _ptr(offs), G, m, n, k, _ptr(out), out_dtype, _stream(a))
+    return out
+
+
+def mx_grouped_mm_bf16_dgrad(dy, w_t, offs, m, n, k, groups=None, out_dtype=MX_OUT_BF16, out=None):
+    """dx [m, k] = dy [m, n] . W_g [n, k] per row group, with W_g^T given as w_t [G*k, n]."""
+    G = _groups(offs, groups)
+    out = _out((m, k), out_dtype, dy.device, out)
+    _lib.call("mx_grouped_mm_bf16_dgrad", _ptr(dy), _ptr(w_t), _ptr(offs), G, m, n, k, _ptr(out), out_dtype,
+              _stream(dy))
+    return out
+
+
+def mx_grouped_mm_bf16_wgrad(dy_t, x_t, offs, m, n, k, groups=None, out_dtype=MX_OUT_F32, out=None):
+    """dw [G, n, k]: dw[g] = dy_t[:, rows_g] . x_t[:, rows_g]^T, bf16 operands."""
+    G = _groups(offs, groups)
+    out = _out((G, n, k), out_dtype, dy_t.device, out)
+    _lib.call("mx_grouped_mm_bf16_wgrad", _ptr(dy_t), _ptr(x_t), _ptr(offs), G, m, n, k, _ptr(out), out_dtype,
+              _stream(dy_t))
+    return out

@@ -22,6 +22,13 @@ hipError_t mx_launch_pad(const uint16_t*, int64_t, int64_t, int64_t, const int32
                          hipStream_t);
 hipError_t mx_launch_unpad(const void*, int64_t, int64_t, int64_t, const int32_t*, int, void*, int64_t, int64_t,
                            hipStream_t);
+hipError_t mx_launch_dequant(const uint8_t*, const uint8_t*, int64_t, int64_t, int64_t, int, uint16_t*, hipStream_t);
+hipError_t mx_launch_transpose_bf16(const uint16_t*, int64_t, int64_t, int64_t, int64_t, uint16_t*, hipStream_t);
+hipError_t mx_launch_scales_logical(const uint8_t*, int64_t, int64_t, uint8_t*, hipStream_t);
+hipError_t mx_launch_gemm_bf16_mgroup(const uint16_t*, const uint16_t*, const int32_t*, int, int64_t, int64_t, int64_t,
+                                      void*, int, hipStream_t);
+hipError_t mx_launch_gemm_bf16_kgroup(const uint16_t*, const uint16_t*, const int32_t*, int, int64_t, int64_t, int64_t,
+                                      void*, int, hipStream_t);
 hipError_t mx_launch_gemm_mgroup(const uint8_t*, const uint8_t*, const uint8_t*, const uint8_t*, const int32_t*, int,
                                  int64_t, int64_t, int64_t, void*, int, hipStream_t);
 hipError_t mx_launch_gemm_kgroup(const uint8_t*, const uint8_t*, const uint8_t*, const uint8_t*, const int32_t*, int,
@@ -85,6 +92,12 @@ mx_status check_ptr(const char* name, const void* p) {
   if (!p) return fail(MX_E_NULL, "%s is NULL", name);
   if (!aligned16(p)) return fail(MX_E_ALIGN, "%s is not 16-byte aligned", name);
   return MX_OK;
+}
+
+// A buffer of zero rows may be NULL (nothing is read or written there).
+mx_status check_rows_ptr(const char* name, const void* p, int64_t rows) {
+  if (!p && rows == 0) return MX_OK;
+  return check_ptr(name, p);
 }
 
 mx_status check_pitch(const char* name, int64_t ld, int64_t cols) {
@@ -306,6 +319,109 @@ mx_status mx_grouped_mm_wgrad(const uint8_t* dy_t, const uint8_t* dy_t_s, const 
                   "mx_grouped_mm_wgrad");
 }
 
+// ---- backward override arms: conversions and bf16 grouped GEMMs ----
+
+mx_status mx_dequantize(const uint8_t* q, const uint8_t* scale, int64_t batch, int64_t rows, int64_t cols,
+                        int transpose, uint16_t* out, void* stream) {
+  if (transpose != 0 && transpose != 1) return fail(MX_E_DTYPE, "transpose = %d must be 0 or 1", transpose);
+  TRY(check_dim("batch", batch, 1));
+  TRY(check_dim("rows", rows, 0));
+  TRY(check_dim("cols", cols, 32));
+  TRY(check_mul32("cols", cols));
+  if (batch * rows > kMaxDim) return fail(MX_E_SHAPE, "batch * rows exceeds 2^31");
+  if (transpose && rows % 8 != 0)
+    return fail(MX_E_SHAPE, "rows = %lld: a transposed output needs rows %% 8 == 0 (16-byte rows)", (long long)rows);
+  TRY(check_rows_ptr("q", q, batch * rows));
+  TRY(check_rows_ptr("out", out, batch * rows));
+  if (!scale && batch * rows) return fail(MX_E_NULL, "scale is NULL");
+  TRY(check_device());
+  return launched(mx_launch_dequant(q, scale, batch, rows, cols, transpose, out, (hipStream_t)stream), "mx_dequantize");
+}
+
+mx_status mx_scales_to_logical(const uint8_t* scale, int64_t rows, int64_t cols, uint8_t* logical, void* stream) {
+  TRY(check_dim("rows", rows, 0));
+  TRY(check_dim("cols", cols, 32));
+  TRY(check_mul32("cols", cols));
+  if (rows && (!scale || !logical)) return fail(MX_E_NULL, "scale or logical is NULL");
+  TRY(check_device());
+  return launched(mx_launch_scales_logical(scale, rows, cols, logical, (hipStream_t)stream), "mx_scales_to_logical");
+}
+
+mx_status mx_transpose_bf16(const uint16_t* x, int64_t batch, int64_t rows, int64_t cols, int64_t ld_x, uint16_t* out,
+                            void* stream) {
+  TRY(check_dim("batch", batch, 1));
+  TRY(check_dim("rows", rows, 0));
+  TRY(check_dim("cols", cols, 8));
+  if (rows % 8 != 0 || cols % 8 != 0)
+    return fail(MX_E_SHAPE, "rows = %lld, cols = %lld: both must be multiples of 8 (16-byte rows in and out)",
+                (long long)rows, (long long)cols);
+  TRY(check_pitch("ld_x", ld_x, cols));
+  if (batch * rows > kMaxDim || batch * cols > kMaxDim) return fail(MX_E_SHAPE, "batch * rows or batch * cols exceeds 2^31");
+  TRY(check_rows_ptr("x", x, batch * rows));
+  TRY(check_rows_ptr("out", out, batch * rows));
+  TRY(check_device());
+  return launched(mx_launch_transpose_bf16(x, batch, rows, cols, ld_x, out, (hipStream_t)stream), "mx_transpose_bf16");
+}
+
+namespace {
+
+// bf16 operands: 16-byte rows along the contraction, which is at most 2^21
+// elements (2^22 bytes, the byte limit of the MXFP8 GEMM).
+mx_status check_bf16_gemm(const void* a, const void* b, const void* out, int out_dtype, int32_t groups,
+                          const int32_t* offs, const char* cname, int64_t contraction, int64_t a_rows,
+                          int64_t b_rows) {
+  TRY(check_ptr("a", a));
+  TRY(check_ptr("b", b));
+  TRY(check_ptr("out", out));
+  if (out_dtype != MX_OUT_F32 && out_dtype != MX_OUT_BF16)
+    return fail(MX_E_DTYPE, "out_dtype = %d is neither MX_OUT_F32 (0) nor MX_OUT_BF16 (1)", out_dtype);
+  if (groups < 1 || groups > 65536) return fail(MX_E_SHAPE, "groups = %d is outside [1, 65536]", groups);
+  if (!offs && groups != 1) return fail(MX_E_SHAPE, "offs is NULL (dense) but groups = %d", groups);
+  if (offs && ((uintptr_t)offs & 3)) return fail(MX_E_ALIGN, "offs is not 4-byte aligned");
+  if (contraction % 8 != 0)
+    return fail(MX_E_SHAPE, "%s = %lld must be a multiple of 8 (16-byte bf16 rows)", cname, (long long)contraction);
+  if (contraction > ((int64_t)1 << 21))
+    return fail(MX_E_SHAPE, "%s = %lld exceeds the bf16 contraction limit 2^21", cname, (long long)contraction);
+  if (a_rows > kMaxDim || b_rows > kMaxDim) return fail(MX_E_SHAPE, "operand rows exceed 2^31");
+  return MX_OK;
+}
+
+}  // namespace
+
+mx_status mx_grouped_mm_bf16_fwd(const uint16_t* a, const uint16_t* b, const int32_t* offs, int32_t groups, int64_t m,
+                                 int64_t n, int64_t k, void* out, int out_dtype, void* stream) {
+  TRY(check_dim("m", m, 0));
+  TRY(check_dim("n", n, 1));
+  TRY(check_dim("k", k, 8));
+  TRY(check_bf16_gemm(a, b, out, out_dtype, groups, offs, "k", k, m, (int64_t)groups * n));
+  TRY(check_device());
+  return launched(mx_launch_gemm_bf16_mgroup(a, b, offs, groups, m, n, k, out, out_dtype, (hipStream_t)stream),
+                  "mx_grouped_mm_bf16_fwd");
+}
+
+mx_status mx_grouped_mm_bf16_dgrad(const uint16_t* dy, const uint16_t* w_t, const int32_t* offs, int32_t groups,
+                                   int64_t m, int64_t n, int64_t k, void* dx, int out_dtype, void* stream) {
+  TRY(check_dim("m", m, 0));
+  TRY(check_dim("n", n, 8));
+  TRY(check_dim("k", k, 1));
+  TRY(check_bf16_gemm(dy, w_t, dx, out_dtype, groups, offs, "n", n, m, (int64_t)groups * k));
+  TRY(check_device());
+  return launched(mx_launch_gemm_bf16_mgroup(dy, w_t, offs, groups, m, k, n, dx, out_dtype, (hipStream_t)stream),
+                  "mx_grouped_mm_bf16_dgrad");
+}
+
+mx_status mx_grouped_mm_bf16_wgrad(const uint16_t* dy_t, const uint16_t* x_t, const int32_t* offs, int32_t groups,
+                                   int64_t m, int64_t n, int64_t k, void* dw, int out_dtype, void* stream) {
+  TRY(check_dim("m", m, 8));
+  TRY(check_dim("n", n, 1));
+  TRY(check_dim("k", k, 1));
+  TRY(check_bf16_gemm(dy_t, x_t, dw, out_dtype, groups, offs, "m", m, n, k));
+  if ((int64_t)groups * n > kMaxDim) return fail(MX_E_SHAPE, "groups * n exceeds 2^31");
+  TRY(check_device());
+  return launched(mx_launch_gemm_bf16_kgroup(dy_t, x_t, offs, groups, n, k, m, dw, out_dtype, (hipStream_t)stream),
+                  "mx_grouped_mm_bf16_wgrad");
+}
+
 // ---- token-group padding ----
 
 namespace {
@@ -325,12 +441,6 @@ mx_status check_pad_common(int64_t rows, int32_t groups, int64_t rows_pad, const
   if (!offs) return fail(MX_E_NULL, "offs is NULL");
   if ((uintptr_t)offs & 3) return fail(MX_E_ALIGN, "offs is not 4-byte aligned");
   return MX_OK;
-}
-
-// A buffer of zero rows may be NULL (nothing is read or written there).
-mx_status check_rows_ptr(const char* name, const void* p, int64_t rows) {
-  if (!p && rows == 0) return MX_OK;
-  return check_ptr(name, p);
 }
 
 }  // namespace

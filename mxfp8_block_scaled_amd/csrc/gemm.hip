@@ -29,6 +29,11 @@
 namespace mx {
 
 enum { MODE_MGROUP = 0, MODE_KGROUP = 1 };
+// Operand element kind: E4M3 codes with E8M0 block scales (the block-scaled MFMA),
+// or plain bf16 (two bf16 MFMAs per 64-byte k-step, no scales).
+enum { EL_MXFP8 = 0, EL_BF16 = 1 };
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 struct GemmArgs {
   const uint8_t* a;    // [a_rows x lda] codes
@@ -37,11 +42,12 @@ struct GemmArgs {
   const uint8_t* b_s;
   const int32_t* offs;  // device, may be null (one group)
   void* out;
-  int64_t lda, ldb;          // row pitch in bytes (= contraction length)
+  int64_t lda, ldb;          // row pitch in bytes (= contraction length x element size)
   int64_t a_rows, b_rows;    // rows of the whole operand buffers
   int64_t a_ktiles, b_ktiles;  // scale tiles along the contraction
   int64_t M, N, K;  // M-grouped: M = token rows, N = per-group output columns, K = contraction
                     // K-grouped: M = rows of A, N = rows of B, K = contraction (tokens)
+                    // (K and offs in elements; the kernel works in bytes of the contraction)
   int64_t ldo;      // output row pitch (elements)
   int64_t mt_total, nt;  // tile grid: m-tiles (upper bound for M-grouped), n-tiles
   int64_t tiles;         // logical tiles (some M-grouped ones may be empty)
@@ -75,10 +81,7 @@ struct Cfg {
   static constexpr int A_LOADS = A_ROWS_W / 16, B_LOADS = B_ROWS_W / 16;
   static constexpr int AB_LOADS = A_LOADS + B_LOADS;
   static constexpr int SC_WAVES = BANDS / 4;
-  // LDS reads per k-step (two 16-byte fragment halves and one scale dword per tile)
-  // spread over the second half's MFMAs
   static constexpr int HALF_MFMAS = TM / 2 * TN;
-  static constexpr int DS_PER_MFMA = (3 * (TM + TN) + HALF_MFMAS - 1) / HALF_MFMAS;
   static_assert(BM == BN && BANDS % 8 == 0 && SC_WAVES <= WAVES && A_ROWS_W % 16 == 0, "tile shape");
   static_assert(TM % 2 == 0 && 2 * AB_LOADS + 2 < 64, "");
 };
@@ -107,9 +110,10 @@ struct Tile {
 // [x * per_xcd, (x+1) * per_xcd) and its blocks advance through it together; with
 // a raster of GM m-tiles by all n-tiles, the ~32 tiles in flight on one XCD share
 // their A and B slices in its L2.
-template <int BM, int BN, int MODE, int OUT_BF16>
+template <int BM, int BN, int MODE, int OUT_BF16, int EL>
 __device__ inline Tile tile_at(const GemmArgs& p, int64_t t) {
   constexpr int64_t GM = 4;
+  constexpr int64_t EB = EL == EL_BF16 ? 2 : 1;  // bytes per contraction element
   constexpr int out_es = OUT_BF16 ? 2 : 4;
   Tile T{};
   T.out_base = (uint8_t*)p.out;
@@ -163,15 +167,15 @@ __device__ inline Tile tile_at(const GemmArgs& p, int64_t t) {
     T.b_row0 = (int64_t)g * p.N + n_tile * BN;
     T.b_row_end = (int64_t)g * p.N + p.N;
     T.k_beg = 0;
-    T.k_end = p.K;
+    T.k_end = p.K * EB;
   } else {
     T.valid = true;
     T.a_row0 = mt * BM;
     T.a_row_end = p.M;
     T.b_row0 = n_tile * BN;
     T.b_row_end = p.N;
-    T.k_beg = p.offs ? group_start(p.offs, g) : 0;
-    T.k_end = p.offs ? p.offs[g] : p.K;
+    T.k_beg = EB * (p.offs ? group_start(p.offs, g) : 0);
+    T.k_end = EB * (p.offs ? p.offs[g] : p.K);
     if (p.splits > 1) {
       // split sp of `splits` takes a run of whole 256-wide windows (counted from the
       // 256-aligned start of the group's range), so no split adds masked steps; it
@@ -207,16 +211,21 @@ __device__ inline int64_t xcd_remap(int64_t bid, int64_t nblk) {
   return bid < per_xcd * 8 ? (bid % 8) * per_xcd + bid / 8 : bid;
 }
 
-template <int BM, int BN, int WGM, int WGN, int MODE, int OUT_BF16>
+template <int BM, int BN, int WGM, int WGN, int MODE, int OUT_BF16, int EL>
 __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm(GemmArgs p) {
   using C = Cfg<BM, BN, WGM, WGN>;
   constexpr int NST = C::NST, BK = C::BK;
+  constexpr bool SCALED = EL == EL_MXFP8;
+  constexpr int MPK = SCALED ? 1 : 2;  // MFMAs per 32x32 tile and 64-byte k-step
+  // LDS reads per k-step (two 16-byte fragment halves per tile, plus one scale dword
+  // per tile when scaled) spread over the second half's MFMAs
+  constexpr int DS_PER_MFMA = ((SCALED ? 3 : 2) * (C::TM + C::TN) + C::HALF_MFMAS - 1) / C::HALF_MFMAS;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
 
   const int tid = threadIdx.x, l = tid & 63, h = l >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int wm = wave / WGN, wn = wave % WGN;
-  Tile T = tile_at<BM, BN, MODE, OUT_BF16>(p, xcd_remap(blockIdx.x, gridDim.x));
+  Tile T = tile_at<BM, BN, MODE, OUT_BF16, EL>(p, xcd_remap(blockIdx.x, gridDim.x));
   if (!__builtin_amdgcn_readfirstlane((int)T.valid)) return;
   T.a_row0 = uniform(T.a_row0); T.a_row_end = uniform(T.a_row_end);
   T.b_row0 = uniform(T.b_row0); T.b_row_end = uniform(T.b_row_end);
@@ -271,7 +280,10 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm(GemmArgs p) {
     const int64_t k0 = k_first + s_idx * BK;
     uint8_t* st = lds + (int)(s_idx % NST) * C::STAGE_BYTES;
     const int kk = (int)k0 + kc_l * 16;
-    const bool drop = !live || kk < kb32 || kk >= ke32;  // this lane's chunk is masked
+    // this lane's chunk is masked; in bf16 a group edge may fall inside a 16-byte
+    // chunk (8 tokens): such chunks are loaded and their outside elements zeroed in
+    // the fragment registers (read_frags)
+    const bool drop = !live || (SCALED ? kk < kb32 : kk + 16 <= kb32) || kk >= ke32;
     const int soff = live ? (int)k0 : 0;
 #pragma unroll
     for (int q = 0; q < C::A_LOADS; ++q)
@@ -281,7 +293,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm(GemmArgs p) {
     for (int q = 0; q < C::B_LOADS; ++q)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(b_rsrc, (lds_ptr_t)(st + C::A_BYTES + wave * C::B_ROWS_W * 64 + q * 1024),
                                                16, drop ? 0x80000000u : b_off0 + q * b_offq, soff, 0, 0);
-    if (s_mod4 == 0) {
+    if (SCALED && s_mod4 == 0) {
       const int64_t kwin = k0 / 256;
       uint8_t* dst = lds + NST * C::STAGE_BYTES + (int)(kwin & 1) * C::SC_BYTES + wave * 1024;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(sc_is_a ? as_rsrc : bs_rsrc, (lds_ptr_t)dst, 16,
@@ -291,7 +303,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm(GemmArgs p) {
   // loads this wave issues for the `count` stages following a stage with s % 4 == s_mod4
   auto loads_after = [&](int s_mod4, int count) -> int {
     int n = 0;
-    for (int q = 1; q <= count; ++q) n += C::AB_LOADS + (((s_mod4 + q) & 3) == 0 ? 1 : 0);
+    for (int q = 1; q <= count; ++q) n += C::AB_LOADS + ((SCALED && ((s_mod4 + q) & 3) == 0) ? 1 : 0);
     return n;
   };
   auto wait_n = [&](int n) {  // s_waitcnt needs an immediate; n takes one of a few values
@@ -321,14 +333,31 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm(GemmArgs p) {
       u32x4 lo = *(const u32x4*)(lb + j * 2048 + off_lo);
       u32x4 hi = *(const u32x4*)(lb + j * 2048 + off_hi);
       f.b[j] = (v8i){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-      f.sb[j] = *(const unsigned*)(sc + (BM / 32 + wn * C::TN + j) * 256 + 4 * l) >> sh;
+      if (SCALED) f.sb[j] = *(const unsigned*)(sc + (BM / 32 + wn * C::TN + j) * 256 + 4 * l) >> sh;
     }
 #pragma unroll
     for (int i = 0; i < C::TM; ++i) {
       u32x4 lo = *(const u32x4*)(la + i * 2048 + off_lo);
       u32x4 hi = *(const u32x4*)(la + i * 2048 + off_hi);
       f.a[i] = (v8i){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-      f.sa[i] = *(const unsigned*)(sc + (wm * C::TM + i) * 256 + 4 * l) >> sh;
+      if (SCALED) f.sa[i] = *(const unsigned*)(sc + (wm * C::TM + i) * 256 + 4 * l) >> sh;
+    }
+    if (!SCALED && MODE == MODE_KGROUP) {
+      // a k-step that a group edge cuts: zero A's elements outside [k_beg, k_end)
+      // (A alone suffices: the products with them vanish)
+      const int kb = (int)k0;
+      if (kb < kb32 || kb + BK > ke32) {
+        int mk[8];
+#pragma unroll
+        for (int d = 0; d < 8; ++d) {
+          const int byte = kb + (d < 4 ? 16 * h + 4 * d : 32 + 16 * h + 4 * (d - 4));
+          mk[d] = (byte >= kb32 && byte < ke32 ? 0xFFFF : 0) | (byte + 2 >= kb32 && byte + 2 < ke32 ? (int)0xFFFF0000 : 0);
+        }
+#pragma unroll
+        for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+          for (int d = 0; d < 8; ++d) f.a[i][d] &= mk[d];
+      }
     }
   };
 
@@ -338,8 +367,19 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm(GemmArgs p) {
     for (int i = i0; i < i1; ++i)
 #pragma unroll
       for (int j = 0; j < C::TN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.b[j], f.a[i], acc[i][j], 0, 0, 0, (int)f.sb[j],
-                                                                    0, (int)f.sa[i]);
+        if (SCALED) {
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.b[j], f.a[i], acc[i][j], 0, 0, 0,
+                                                                      (int)f.sb[j], 0, (int)f.sa[i]);
+        } else {
+          // the lane's two 16-byte halves are the two 16-element k-slices of the step
+          const v8i bj = f.b[j], ai = f.a[i];
+          const bf16x8 b_lo = __builtin_bit_cast(bf16x8, (u32x4){(unsigned)bj[0], (unsigned)bj[1], (unsigned)bj[2], (unsigned)bj[3]});
+          const bf16x8 b_hi = __builtin_bit_cast(bf16x8, (u32x4){(unsigned)bj[4], (unsigned)bj[5], (unsigned)bj[6], (unsigned)bj[7]});
+          const bf16x8 a_lo = __builtin_bit_cast(bf16x8, (u32x4){(unsigned)ai[0], (unsigned)ai[1], (unsigned)ai[2], (unsigned)ai[3]});
+          const bf16x8 a_hi = __builtin_bit_cast(bf16x8, (u32x4){(unsigned)ai[4], (unsigned)ai[5], (unsigned)ai[6], (unsigned)ai[7]});
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b_lo, a_lo, acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b_hi, a_hi, acc[i][j], 0, 0, 0);
+        }
   };
 
   // One pipeline step over an NST-deep LDS ring. Step `it` issues stage it+NST-1,
@@ -354,7 +394,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm(GemmArgs p) {
     // spread the loads over the MFMAs so no load waits in front of an idle matrix core
 #pragma unroll
     for (int q = 0; q < C::TM / 2 * C::TN; ++q) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x008, MPK, 0);  // MFMA
       __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // VALU (load offsets)
       __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read
     }
@@ -367,8 +407,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm(GemmArgs p) {
     // interleave: one MFMA, then a share of the LDS reads
 #pragma unroll
     for (int q = 0; q < C::HALF_MFMAS; ++q) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, C::DS_PER_MFMA, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, MPK, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, DS_PER_MFMA, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
   };
@@ -486,7 +526,7 @@ constexpr int64_t kComputeUnits = 256;
 
 // Tile configurations: 256x256 for large problems; 128x128 where 256x256 tiles
 // would leave most compute units idle.
-template <int BM, int BN, int WGM, int WGN, int MODE>
+template <int BM, int BN, int WGM, int WGN, int MODE, int EL>
 hipError_t launch_cfg(mx::GemmArgs p, int out_bf16, hipStream_t stream) {
   using C = mx::Cfg<BM, BN, WGM, WGN>;
   const int64_t mt_extra = (MODE == mx::MODE_MGROUP && p.offs) ? p.groups : 0;
@@ -500,18 +540,18 @@ hipError_t launch_cfg(mx::GemmArgs p, int out_bf16, hipStream_t stream) {
   hipError_t e = hipSuccess;
   if (out_bf16) {
     if (!attr_set[1])
-      e = hipFuncSetAttribute((const void*)mx::k_gemm<BM, BN, WGM, WGN, MODE, 1>,
+      e = hipFuncSetAttribute((const void*)mx::k_gemm<BM, BN, WGM, WGN, MODE, 1, EL>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     attr_set[1] = true;
-    hipLaunchKernelGGL((mx::k_gemm<BM, BN, WGM, WGN, MODE, 1>), dim3((unsigned)blocks), dim3(C::THREADS), lds, stream, p);
+    hipLaunchKernelGGL((mx::k_gemm<BM, BN, WGM, WGN, MODE, 1, EL>), dim3((unsigned)blocks), dim3(C::THREADS), lds, stream, p);
   } else {
     if (!attr_set[0])
-      e = hipFuncSetAttribute((const void*)mx::k_gemm<BM, BN, WGM, WGN, MODE, 0>,
+      e = hipFuncSetAttribute((const void*)mx::k_gemm<BM, BN, WGM, WGN, MODE, 0, EL>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     attr_set[0] = true;
-    hipLaunchKernelGGL((mx::k_gemm<BM, BN, WGM, WGN, MODE, 0>), dim3((unsigned)blocks), dim3(C::THREADS), lds, stream, p);
+    hipLaunchKernelGGL((mx::k_gemm<BM, BN, WGM, WGN, MODE, 0, EL>), dim3((unsigned)blocks), dim3(C::THREADS), lds, stream, p);
   }
   return hipGetLastError();
 }
@@ -570,21 +610,21 @@ hipError_t split_workspace(size_t bytes, float** ptr) {
 // K-grouped outputs with fewer 256x256 tiles than compute units, over a long
 // contraction (weight gradients of narrow layers): split each group's contraction
 // so the splits fill about one round of the chip. Returns 1 for no split.
-int choose_splits(const mx::GemmArgs& p) {
+int choose_splits(const mx::GemmArgs& p, int64_t elem_bytes) {
   const int64_t tiles = (int64_t)p.groups * ((p.M + 255) / 256) * ((p.N + 255) / 256);
   if (tiles >= kComputeUnits || tiles == 0) return 1;
-  const int64_t wins_per_group = (p.K + 255) / 256 / p.groups;  // 256-wide windows per group, on average
+  const int64_t wins_per_group = (p.K * elem_bytes + 255) / 256 / p.groups;  // 256-byte windows per group, on average
   int64_t s = kComputeUnits / tiles;
   s = std::min<int64_t>(s, wins_per_group / 2);  // at least two windows (8 k-steps) per split
   s = std::min<int64_t>(s, 16);
   return s >= 2 ? (int)s : 1;
 }
 
-template <int MODE>
+template <int MODE, int EL>
 hipError_t launch(mx::GemmArgs& p, int out_bf16, hipStream_t stream) {
   p.splits = 1;
   if (MODE == mx::MODE_KGROUP) {
-    const int splits = choose_splits(p);
+    const int splits = choose_splits(p, EL == mx::EL_BF16 ? 2 : 1);
     if (splits > 1) {
       const int64_t n_out = (int64_t)p.groups * p.M * p.N;
       const int64_t stride = (n_out + 3) / 4 * 4;  // keeps every partial 16-byte aligned
@@ -595,7 +635,7 @@ hipError_t launch(mx::GemmArgs& p, int out_bf16, hipStream_t stream) {
       q.splits = splits;
       q.split_stride = stride;
       q.out = ws;
-      e = launch_cfg<256, 256, 2, 2, MODE>(q, 0, stream);
+      e = launch_cfg<256, 256, 2, 2, MODE, EL>(q, 0, stream);
       if (e != hipSuccess) return e;
       const int64_t blocks = std::min<int64_t>((n_out + 1023) / 1024, 4096);
       hipLaunchKernelGGL(k_split_reduce, dim3((unsigned)std::max<int64_t>(blocks, 1)), dim3(256), 0, stream, ws,
@@ -607,8 +647,8 @@ hipError_t launch(mx::GemmArgs& p, int out_bf16, hipStream_t stream) {
   const int64_t big_tiles = groups_tiles * ((p.M + 255) / 256) * ((p.N + 255) / 256);
   // 2 x 2 waves of 128 x 128 (256 accumulators each, one wave per SIMD); 8-wave
   // grids of 128 x 64 per wave (two per SIMD) measured the same on the MoE shapes
-  if (big_tiles >= 512) return launch_cfg<256, 256, 2, 2, MODE>(p, out_bf16, stream);
-  return launch_cfg<128, 128, 2, 2, MODE>(p, out_bf16, stream);
+  if (big_tiles >= 512) return launch_cfg<256, 256, 2, 2, MODE, EL>(p, out_bf16, stream);
+  return launch_cfg<128, 128, 2, 2, MODE, EL>(p, out_bf16, stream);
 }
 }  // namespace
 
@@ -623,7 +663,7 @@ hipError_t mx_launch_gemm_mgroup(const uint8_t* a, const uint8_t* a_s, const uin
   p.a_ktiles = p.b_ktiles = mx::scale_tiles_k(k / 32);
   p.M = m; p.N = n; p.K = k; p.ldo = n;
   p.groups = groups;
-  return launch<mx::MODE_MGROUP>(p, out_bf16, stream);
+  return launch<mx::MODE_MGROUP, mx::EL_MXFP8>(p, out_bf16, stream);
 }
 
 // K-grouped: C_g[m x n] = A[m x K_g] . B[n x K_g]^T over each group's contraction range (wgrad).
@@ -637,5 +677,28 @@ hipError_t mx_launch_gemm_kgroup(const uint8_t* a, const uint8_t* a_s, const uin
   p.a_ktiles = p.b_ktiles = mx::scale_tiles_k(k / 32);
   p.M = m; p.N = n; p.K = k; p.ldo = n;
   p.groups = groups;
-  return launch<mx::MODE_KGROUP>(p, out_bf16, stream);
+  return launch<mx::MODE_KGROUP, mx::EL_MXFP8>(p, out_bf16, stream);
+}
+
+// bf16 operands, no scales: the same two cores with pitches of 2 bytes per element.
+hipError_t mx_launch_gemm_bf16_mgroup(const uint16_t* a, const uint16_t* b, const int32_t* offs, int groups,
+                                      int64_t m, int64_t n, int64_t k, void* out, int out_bf16, hipStream_t stream) {
+  mx::GemmArgs p{};
+  p.a = (const uint8_t*)a; p.b = (const uint8_t*)b; p.offs = offs; p.out = out;
+  p.lda = 2 * k; p.ldb = 2 * k;
+  p.a_rows = m; p.b_rows = (int64_t)groups * n;
+  p.M = m; p.N = n; p.K = k; p.ldo = n;
+  p.groups = groups;
+  return launch<mx::MODE_MGROUP, mx::EL_BF16>(p, out_bf16, stream);
+}
+
+hipError_t mx_launch_gemm_bf16_kgroup(const uint16_t* a, const uint16_t* b, const int32_t* offs, int groups,
+                                      int64_t m, int64_t n, int64_t k, void* out, int out_bf16, hipStream_t stream) {
+  mx::GemmArgs p{};
+  p.a = (const uint8_t*)a; p.b = (const uint8_t*)b; p.offs = offs; p.out = out;
+  p.lda = 2 * k; p.ldb = 2 * k;
+  p.a_rows = m; p.b_rows = n;
+  p.M = m; p.N = n; p.K = k; p.ldo = n;
+  p.groups = groups;
+  return launch<mx::MODE_KGROUP, mx::EL_BF16>(p, out_bf16, stream);
 }

@@ -175,3 +175,26 @@ def test_unpad_validation(lib):
     assert f(P, 256, 64, 32, P2, 3, P2, 40, 64, 0, None) == MX_E_LAYOUT
     assert f(P, 224, 64, 64, P2, 3, P2, 40, 64, 0, None) == MX_E_SHAPE  # rows_pad too small
     assert f(P, 256, 64, 64, P2, 3, None, 40, 64, 0, None) == MX_E_NULL  # y
+
+
+def test_backward_arm_calls_validation(lib):
+    dq = lib.mx_dequantize
+    assert dq(P, P2, 1, 64, 64, 0, P2, None) in (MX_E_DEVICE, 0)
+    assert dq(P, P2, 1, 64, 48, 0, P2, None) == MX_E_SHAPE  # cols % 32
+    assert dq(P, P2, 1, 36, 64, 1, P2, None) == MX_E_SHAPE  # transposed rows % 8
+    assert dq(P, P2, 1, 64, 64, 2, P2, None) == MX_E_DTYPE
+    assert dq(P, None, 1, 64, 64, 0, P2, None) == MX_E_NULL
+    assert lib.mx_scales_to_logical(P, 64, 40, P2, None) == MX_E_SHAPE
+    tr = lib.mx_transpose_bf16
+    assert tr(P, 1, 64, 64, 64, P2, None) in (MX_E_DEVICE, 0)
+    assert tr(P, 1, 60, 64, 64, P2, None) == MX_E_SHAPE  # rows % 8
+    assert tr(P, 1, 64, 64, 32, P2, None) == MX_E_LAYOUT
+    f = lib.mx_grouped_mm_bf16_fwd
+    assert f(P, P, P2, 3, 100, 40, 64, P2, 0, None) in (MX_E_DEVICE, 0)  # any group rows, n not % 32
+    assert f(P, P, P2, 3, 100, 40, 60, P2, 0, None) == MX_E_SHAPE  # k % 8
+    assert f(P, P, None, 3, 100, 40, 64, P2, 0, None) == MX_E_SHAPE  # dense with groups
+    assert f(P, P, None, 1, 100, 40, (1 << 21) + 8, P2, 0, None) == MX_E_SHAPE  # contraction limit
+    assert f(P, P, P2, 1, 100, 40, 64, P2, 5, None) == MX_E_DTYPE
+    assert lib.mx_grouped_mm_bf16_dgrad(P, P, P2, 3, 100, 36, 64, P2, 0, None) == MX_E_SHAPE  # n % 8
+    assert lib.mx_grouped_mm_bf16_wgrad(P, P, P2, 3, 100, 36, 64, P2, 0, None) == MX_E_SHAPE  # m % 8
+    assert lib.mx_grouped_mm_bf16_wgrad(P, P, P2, 3, 104, 36, 64, P2, 0, None) in (MX_E_DEVICE, 0)
