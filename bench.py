@@ -22,6 +22,12 @@ One step runs, in order:
 the step pads X and dY to 32-row group boundaries (ao fork PR 10, "Known
 follow-ups": padded token groups), runs the casts and the grouped passes on the
 padded rows and offsets, and unpads Y and dX; flops still count real rows only.
+
+--backward ARM: the MoE grouped step (no dense layer) with the backward override
+arm ARM (ao fork PR 10, "Design notes"): "quantized" (the MXFP8 backward),
+"high_precision" (transposes of the saved bf16 W, X, dY and bf16 grouped GEMMs) or
+"dequantized" (the forward's codes of W and X dequantized transposed, dY
+transposed, bf16 grouped GEMMs); bf16 GEMMs are priced against the bf16 peak.
 """
 
 import argparse
@@ -38,6 +44,8 @@ sys.path.insert(0, ROOT)
 
 METRIC = "MXFP8 grouped GEMM TFLOP/s (fwd+bwd) and cast GB/s vs roofline, 1 GPU"
 PEAK_FP8_TFLOPS = 5000.0  # MI355X dense fp8 / MXFP8 MFMA
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAKS = {"gemm": PEAK_FP8_TFLOPS, "gemm16": PEAK_BF16_TFLOPS}
 PEAK_HBM_GBPS = 8000.0
 CAST_BYTES_PER_ELEM = 2 + 1 + 1 / 32  # read bf16, write e4m3 + one scale byte per 32
 W32_BYTES_PER_ELEM = 2 + 1 + 1 + 2 / 32  # both orientations, row and column scales
@@ -58,6 +66,8 @@ def parse():
     ap.add_argument("--unaligned-groups", action="store_true",
                     help="group sizes drawn per row (not multiples of 32): the step pads X and dY to 32-row "
                          "group boundaries, runs the grouped passes on the padded offsets and unpads Y and dX")
+    ap.add_argument("--backward", default=None, choices=["quantized", "high_precision", "dequantized"],
+                    help="time the MoE grouped step (forward + the named backward override arm) instead")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a 1 GiB device-to-device copy instead (reference for HBM byte counters)")
     return ap.parse_args()
@@ -142,7 +152,8 @@ def main():
     }
     Wflat = W.view(G * N, K)
 
-    # (name, kind, work units, fn) ; kind "gemm": units = flops, "cast": units = bytes
+    # (name, kind, work units, fn) ; kind "gemm" (MXFP8) / "gemm16" (bf16): units = flops,
+    # "cast" / "pad": units = bytes
     cast0 = lambda n_elem: n_elem * CAST_BYTES_PER_ELEM  # noqa: E731
     both = lambda n_elem: n_elem * BOTH_BYTES_PER_ELEM  # noqa: E731
     w32 = {}
@@ -170,7 +181,47 @@ def main():
     n_wgrad = ("gemm_wgrad dense576", "gemm", 2 * M * NARROW * K,
                lambda: mx.mx_grouped_mm_wgrad(buf["dyntq"], buf["dynts"], buf["xtq"], buf["xts"], None, M, NARROW,
                                               K, out=buf["dwn"], out_dtype=mx.MX_OUT_BF16))
-    if unaligned:
+    if args.backward in ("high_precision", "dequantized"):
+        # forward as MXFP8 (dim0 casts), backward from bf16 operands: transposes or
+        # transposed dequantization (2 B written per element; 2 B read for bf16, 1 + 1/32
+        # for codes) and bf16 grouped GEMMs
+        from mxfp8_block_scaled_amd import backward as bwd  # noqa: F401
+        wt16, xt16, dyt16 = bf(G, K, N), bf(K, M), bf(N, M)
+        tb = lambda n_elem: 4 * n_elem  # noqa: E731
+        db = lambda n_elem: n_elem * (2 + 1 + 1 / 32)  # noqa: E731
+        if args.backward == "high_precision":
+            w_src = ("transpose W", "cast", tb(G * N * K), lambda: mx.mx_transpose_bf16(W, wt16))
+            x_src = ("transpose X", "cast", tb(M * K), lambda: mx.mx_transpose_bf16(X, xt16))
+        else:
+            w_src = ("dequant^T W", "cast", db(G * N * K),
+                     lambda: mx.mx_dequantize(buf["wq"].view(G, N, K), buf["ws"], transpose=True, out=wt16))
+            x_src = ("dequant^T X", "cast", db(M * K),
+                     lambda: mx.mx_dequantize(buf["xq"], buf["xs"], transpose=True, out=xt16))
+        ops = [
+            ("cast_dim0 X", "cast", cast0(M * K), lambda: mx.mx_quantize_dim0(X, buf["xq"], buf["xs"])),
+            ("cast_dim0 W", "cast", cast0(G * N * K), lambda: mx.mx_quantize_dim0(Wflat, buf["wq"], buf["ws"])),
+            g_fwd,
+            w_src,
+            ("bf16 dgrad grouped", "gemm16", 2 * M * N * K,
+             lambda: mx.mx_grouped_mm_bf16_dgrad(dY, wt16, offs, M, N, K, out=buf["dx"])),
+            ("transpose dY", "cast", tb(M * N), lambda: mx.mx_transpose_bf16(dY, dyt16)),
+            x_src,
+            ("bf16 wgrad grouped", "gemm16", 2 * M * N * K,
+             lambda: mx.mx_grouped_mm_bf16_wgrad(dyt16, xt16, offs, M, N, K, out=buf["dw"],
+                                                 out_dtype=mx.MX_OUT_BF16)),
+        ]
+    elif args.backward == "quantized":
+        ops = [
+            ("cast_dim0+dim1 X", "cast", both(M * K),
+             lambda: mx.mx_quantize_dim0_dim1(X, buf["xq"], buf["xs"], buf["xtq"], buf["xts"])),
+            ("cast_dim0+dim1 W", "cast", both(G * N * K),
+             lambda: mx.mx_quantize_dim0_dim1(W, buf["wq"], buf["ws"], buf["wtq"], buf["wts"])),
+            g_fwd,
+            ("cast_dim0+dim1 dY", "cast", both(M * N),
+             lambda: mx.mx_quantize_dim0_dim1(dY, buf["dyq"], buf["dys"], buf["dytq"], buf["dyts"])),
+            g_dgrad, g_wgrad,
+        ]
+    elif unaligned:
         # the MoE grouped part only (the dense layer has no groups); pad bytes: read the
         # real rows, write every padded row; unpad: read and write the real rows (bf16)
         Xp, dYp, y_u, dx_u = bf(Mg, K), bf(Mg, N), bf(M, N), bf(M, K)
@@ -263,7 +314,7 @@ def main():
     if args.warmup:
         dom_i = max(range(len(ops)), key=lambda i: mean_ms(wev[1:] or wev, i))
     else:
-        dom_i = max(range(len(ops)), key=lambda i: ops[i][2] if ops[i][1] == "gemm" else 0)
+        dom_i = max(range(len(ops)), key=lambda i: ops[i][2] if ops[i][1] in PEAKS else 0)
 
     # timed region: exactly `steps` steps; events only around the dominant kernel's
     # launches (on the current stream, where every op runs), for its launch duration
@@ -287,14 +338,15 @@ def main():
     per_op = {}
     for i, (name, kind, units, _) in enumerate(ops):
         ms = dom_ms if i == dom_i else mean_ms(bev, i)
-        rate = units / (ms * 1e-3) / (1e12 if kind == "gemm" else 1e9)
-        peak = PEAK_FP8_TFLOPS if kind == "gemm" else PEAK_HBM_GBPS
-        per_op[name] = {"us": round(ms * 1e3, 2), ("tflops" if kind == "gemm" else "gbps"): round(rate, 1),
+        mm = kind in PEAKS
+        rate = units / (ms * 1e-3) / (1e12 if mm else 1e9)
+        peak = PEAKS[kind] if mm else PEAK_HBM_GBPS
+        per_op[name] = {"us": round(ms * 1e3, 2), ("tflops" if mm else "gbps"): round(rate, 1),
                         "frac": round(rate / peak, 4)}
 
-    gemm_flops = sum(u for _, k, u, _ in ops if k == "gemm")
+    gemm_flops = sum(u for _, k, u, _ in ops if k in PEAKS)
     cast_bytes = sum(u for _, k, u, _ in ops if k == "cast")
-    gemm_us = sum(per_op[n]["us"] for n, k, _, _ in ops if k == "gemm")
+    gemm_us = sum(per_op[n]["us"] for n, k, _, _ in ops if k in PEAKS)
     cast_us = sum(per_op[n]["us"] for n, k, _, _ in ops if k == "cast")
     value = gemm_flops / (ms_per_step * 1e-3) / 1e12
 
@@ -302,15 +354,24 @@ def main():
     dom_name, dom_kind, dom_units, _ = ops[dom_i]
     dom = per_op[dom_name]
     achieved = dom_units / (dom["us"] * 1e-6) / 1e12
-    traffic = None if unaligned else load_traffic(dom_name, dom_units)
-    roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / PEAK_FP8_TFLOPS, 4), "traffic": traffic, "kernel": dom_name,
+    traffic = None if (unaligned or args.backward) else load_traffic(dom_name, dom_units)
+    dom_peak = PEAKS[dom_kind]
+    roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": dom_peak, "unit": "TFLOP/s",
+                "frac": round(achieved / dom_peak, 4), "traffic": traffic, "kernel": dom_name,
                 "flops_per_launch": dom_units, "avg_launch_us": dom["us"]}
+    # the GEMMs' time at their own peaks over their measured time
+    gemm_ideal_us = sum(u / (PEAKS[k] * 1e12) * 1e6 for _, k, u, _ in ops if k in PEAKS)
 
-    cpu = None if (args.no_cpu_baseline or unaligned) else cpu_baseline()
+    cpu = None if (args.no_cpu_baseline or unaligned or args.backward) else cpu_baseline()
     workload = ("moe_g8 fwd+dgrad+wgrad: G=8 experts, M=16384 tokens, K=N=4096, "
                 "grad_out 16384x4096, plus dense 576x4096 layer (32x32 weight scales, "
                 "576-wide contraction in dgrad)")
+    if args.backward:
+        workload = (f"moe_g8 grouped step with the {args.backward} backward: G=8 experts, M=16384 tokens, "
+                    f"K=N=4096; MXFP8 forward" + ("" if args.backward == "quantized" else
+                                                  ", bf16 grouped dgrad and wgrad from "
+                                                  + ("the saved bf16 operands" if args.backward == "high_precision"
+                                                     else "the dequantized forward codes")) + " (no dense layer)")
     if unaligned:
         workload = (f"moe_g8 unaligned groups: G=8 experts, M=16384 tokens (per-row group sizes), K=N=4096; "
                     f"pad X and dY to {Mg} rows, one-pass casts, grouped fwd/dgrad/wgrad on padded offsets, "
@@ -319,14 +380,16 @@ def main():
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "mxfp8 (e4m3 x e4m3, e8m0 block scales, fp32 accumulate)",
+        "vs_baseline": None,
+        "dtype": "mxfp8 (e4m3 x e4m3, e8m0 block scales, fp32 accumulate)" + (
+            "; bf16 backward GEMMs" if args.backward in ("high_precision", "dequantized") else ""),
         "data": "synthetic (seeded N(0,sigma) bf16, multinomial group sizes)",
         "config": {"workload": workload,
-                   "M": M, "K": K, "N": N, "G": G, "narrow": None if unaligned else NARROW,
+                   "M": M, "K": K, "N": N, "G": G, "narrow": None if (unaligned or args.backward) else NARROW,
                    "offs": offs_np.tolist(), "rows_padded": Mg if unaligned else None,
                    "parallelism": "none (1 GPU)"},
         "gemm_tflops": round(gemm_flops / (gemm_us * 1e-6) / 1e12, 1),
-        "gemm_frac_of_peak": round(gemm_flops / (gemm_us * 1e-6) / 1e12 / PEAK_FP8_TFLOPS, 4),
+        "gemm_frac_of_peak": round(gemm_ideal_us / gemm_us, 4),
         "cast_gbps": round(cast_bytes / (cast_us * 1e-6) / 1e9, 1),
         "cast_frac_of_hbm": round(cast_bytes / (cast_us * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4),
         "step_gemm_gflop": round(gemm_flops / 1e9, 2), "step_cast_gb": round(cast_bytes / 1e9, 4),

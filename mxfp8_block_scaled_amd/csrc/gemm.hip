@@ -23,6 +23,7 @@
 
 #include <algorithm>
 #include <mutex>
+#include <type_traits>
 
 #include "common.h"
 
@@ -322,7 +323,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm(GemmArgs p) {
     v8i a[C::TM], b[C::TN];
     unsigned sa[C::TM], sb[C::TN];
   };
-  auto read_frags = [&](Frag& f, int buf, int64_t k0) {
+  // `masked` (a compile-time flag): the tile's contraction range cuts a 16-byte chunk
+  auto read_frags = [&](Frag& f, int buf, int64_t k0, auto masked) {
     const uint8_t* st = lds + buf * C::STAGE_BYTES;
     const uint8_t* sc = lds + NST * C::STAGE_BYTES + (int)((k0 >> 8) & 1) * C::SC_BYTES;
     const uint8_t* la = st + wm * C::WM * 64;
@@ -342,7 +344,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm(GemmArgs p) {
       f.a[i] = (v8i){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
       if (SCALED) f.sa[i] = *(const unsigned*)(sc + (wm * C::TM + i) * 256 + 4 * l) >> sh;
     }
-    if (!SCALED && MODE == MODE_KGROUP) {
+    if constexpr (decltype(masked)::value) {
       // a k-step that a group edge cuts: zero A's elements outside [k_beg, k_end)
       // (A alone suffices: the products with them vanish)
       const int kb = (int)k0;
@@ -388,7 +390,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm(GemmArgs p) {
   // (so stage it+1 is complete in LDS and every wave is past stage it-1, whose slot
   // the next issue overwrites), then reads stage it+1's fragments interleaved with
   // the second half of stage it's MFMAs.
-  auto step = [&](int64_t it, int slot, const Frag& cur, Frag& nxt) {
+  auto step = [&](int64_t it, int slot, const Frag& cur, Frag& nxt, auto masked) {
     issue_stage(it + NST - 1, (slot + NST - 1) & 3, it + NST - 1 < n_iter);
     mfma_rows(cur, 0, C::TM / 2);
     // spread the loads over the MFMAs so no load waits in front of an idle matrix core
@@ -402,7 +404,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm(GemmArgs p) {
     wait_n(loads_after((slot + 1) & 3, NST - 2));
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    read_frags(nxt, (slot + 1) % NST, k_first + (it + 1) * BK);
+    read_frags(nxt, (slot + 1) % NST, k_first + (it + 1) * BK, masked);
     mfma_rows(cur, C::TM / 2, C::TM);
     // interleave: one MFMA, then a share of the LDS reads
 #pragma unroll
@@ -455,7 +457,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm(GemmArgs p) {
                 *(v4f*)dst = (v4f){c[4 * q], c[4 * q + 1], c[4 * q + 2], c[4 * q + 3]};
             }
         }
-#pragma unroll
+#pragma unroll 4  // fully unrolled, the read-back keeps too many loads in flight beside the live accumulators
         for (int k = 0; k < RP / RPI; ++k) {
           const int r = k * RPI + l / CPR;
           const u32x4 d = *(const u32x4*)(stg + r * ROW_BYTES + (((ch ^ r) & (CPR - 1)) << 4));
@@ -493,27 +495,37 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm(GemmArgs p) {
   for (int i = 0; i < C::TM; ++i)
 #pragma unroll
     for (int j = 0; j < C::TN; ++j) acc[i][j] = (v16f){};
-  if (n_iter > 0) {
+  auto main_loop = [&](auto masked) {
+    if (n_iter <= 0) return;
     for (int s = 0; s < NST - 1; ++s) issue_stage(s, s & 3, s < n_iter);
     wait_n(loads_after(0, NST - 2));
     __builtin_amdgcn_s_barrier();
     // The main loop is unrolled by the ring depth, so ring slots are compile-time
     // constants, and alternates two register sets, so no fragment is ever copied.
     Frag f0, f1;
-    read_frags(f0, 0, k_first);
+    read_frags(f0, 0, k_first, masked);
     int64_t it = 0;
     for (; it + NST <= n_iter; it += NST) {
-      step(it, 0, f0, f1);
-      step(it + 1, 1, f1, f0);
-      step(it + 2, 2, f0, f1);
-      step(it + 3, 3, f1, f0);
+      step(it, 0, f0, f1, masked);
+      step(it + 1, 1, f1, f0, masked);
+      step(it + 2, 2, f0, f1, masked);
+      step(it + 3, 3, f1, f0, masked);
     }
     for (; it < n_iter; ++it) {  // 0 to 3 remaining steps
-      step(it, (int)(it % NST), f0, f1);
+      step(it, (int)(it % NST), f0, f1, masked);
       f0 = f1;
     }
     MX_WAIT_VMCNT(0);  // every load has landed
     __builtin_amdgcn_s_barrier();  // every wave is done with the ring
+  };
+  // bf16 K-grouped tiles whose range cuts a 16-byte chunk take the masked copy of
+  // the loop; every other tile runs the loop without the per-step edge test (a
+  // branch inside the step would split the MFMA / LDS-read interleaving)
+  if constexpr (!SCALED && MODE == MODE_KGROUP) {
+    if ((kb32 | ke32) & 15) main_loop(std::true_type{});
+    else main_loop(std::false_type{});
+  } else {
+    main_loop(std::false_type{});
   }
   epilogue();
 }
