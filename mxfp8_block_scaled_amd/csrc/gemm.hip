@@ -457,7 +457,11 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm(GemmArgs p) {
                 *(v4f*)dst = (v4f){c[4 * q], c[4 * q + 1], c[4 * q + 2], c[4 * q + 3]};
             }
         }
-#pragma unroll 4  // fully unrolled, the read-back keeps too many loads in flight beside the live accumulators
+// bf16 rows: fully unrolled; fp32 (two staging passes): by 4, as the full
+        // unroll keeps too many read-back loads in flight beside the accumulators
+        // still live for the second pass and spills
+        constexpr int EPI_UNROLL = OUT_BF16 ? RP / RPI : 4;
+#pragma unroll EPI_UNROLL
         for (int k = 0; k < RP / RPI; ++k) {
           const int r = k * RPI + l / CPR;
           const u32x4 d = *(const u32x4*)(stg + r * ROW_BYTES + (((ch ^ r) & (CPR - 1)) << 4));
