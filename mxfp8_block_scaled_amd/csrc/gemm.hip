@@ -466,7 +466,12 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm(GemmArgs p) {
           const int r = k * RPI + l / CPR;
           const u32x4 d = *(const u32x4*)(stg + r * ROW_BYTES + (((ch ^ r) & (CPR - 1)) << 4));
           const int64_t row = wrow0 + pass * RP + r;
-          if (row < row_limit) *(u32x4*)(T.out_base + (row * p.ldo + wcol0) * ES + ch * 16) = d;
+          // Non-temporal: the output bypasses the caches, so a tile's stores drain
+          // faster and no dirty lines are left for the kernels that follow to write
+          // back. Split partials too: re-read once by the reduction, they cost that
+          // reduction a little but left dirty they slowed the casts that follow more
+          // (MoE step 1.42-1.45 -> 1.36-1.38 ms, against plain stores on one box).
+          if (row < row_limit) __builtin_nontemporal_store(d, (u32x4*)(T.out_base + (row * p.ldo + wcol0) * ES + ch * 16));
         }
       }
     } else {
