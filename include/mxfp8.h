@@ -177,6 +177,9 @@ mx_status mx_quantize_weight_32x32(const uint16_t* w, int64_t batch, int64_t n, 
  *   out       [m x n], float32 or bf16 per out_dtype, row pitch n (written)
  * k % 32 == 0 (k need not be a multiple of 128: the tail is zero-padded inside
  * the kernel); m >= 0; n >= 1; if groups > 1, n % 32 == 0. fp32 accumulation.
+ * A buffer that holds no element (a, a_s, out when m == 0; for wgrad the two
+ * operands when the contraction m == 0, whose dw is then all zeros) may be NULL;
+ * the same holds for every other call's empty buffers.
  * Extent limits (all three GEMM calls, MX_E_SHAPE otherwise): the contraction
  * length (k here, n for dgrad, m for wgrad) is at most 2^22, and each operand's
  * scale buffer (mx_scale_bytes of its rows and the contraction) is below 2^31

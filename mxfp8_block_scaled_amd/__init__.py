@@ -75,17 +75,28 @@ def _u8(n, device):
     return torch.empty(int(n), dtype=torch.uint8, device=device)
 
 
+def _pitch(x):
+    """Row pitch of x (elements); an empty tensor's strides are arbitrary, so its
+    rows are taken as packed."""
+    if x.numel() == 0:
+        return x.shape[-1]
+    if x.stride(-1) != 1:
+        raise ValueError("x must have unit inner stride")
+    return x.stride(-2)
+
+
 def mx_quantize_dim0(x, q=None, scale=None):
     """1x32 rowwise cast of x [rows, cols] (row pitch x.stride(0)) -> (q [rows, cols], scale)."""
     x = _bf16_bits(x)
-    if x.dim() != 2 or x.stride(1) != 1:
-        raise ValueError("x must be a 2D tensor with unit inner stride")
+    if x.dim() != 2:
+        raise ValueError("x must be a 2D tensor")
     rows, cols = x.shape
+    ld = _pitch(x)
     if q is None:
         q = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
     if scale is None:
         scale = _u8(mx_scale_bytes(rows, cols), x.device)
-    _lib.call("mx_quantize_dim0", _ptr(x), rows, cols, x.stride(0), _ptr(q), _ptr(scale), _stream(x))
+    _lib.call("mx_quantize_dim0", _ptr(x), rows, cols, ld, _ptr(q), _ptr(scale), _stream(x))
     return q, scale
 
 
@@ -163,8 +174,7 @@ def mx_quantize_ex(x, forms=MX_FORM_DIM0 | MX_FORM_DIM1, scale_mode=MX_SCALE_RCE
             raise ValueError("batches of x must be contiguous with the row pitch")
     else:
         raise ValueError("x must be 2D or 3D")
-    if x.stride(-1) != 1:
-        raise ValueError("x must have unit inner stride")
+    ld = _pitch(x)
     q = scale = q_t = scale_t = None
     if forms & MX_FORM_DIM0:
         q = torch.empty((batch * rows, cols), dtype=torch.uint8, device=x.device)
@@ -172,7 +182,7 @@ def mx_quantize_ex(x, forms=MX_FORM_DIM0 | MX_FORM_DIM1, scale_mode=MX_SCALE_RCE
     if forms & MX_FORM_DIM1:
         q_t = torch.empty((cols, rows) if x.dim() == 2 else (batch, cols, rows), dtype=torch.uint8, device=x.device)
         scale_t = _u8(mx_scale_bytes(batch * cols, rows), x.device)
-    _lib.call("mx_quantize_ex", _ptr(x), batch, rows, cols, x.stride(-2), int(forms), int(scale_mode), _ptr(q),
+    _lib.call("mx_quantize_ex", _ptr(x), batch, rows, cols, ld, int(forms), int(scale_mode), _ptr(q),
               _ptr(scale), _ptr(q_t), _ptr(scale_t), _stream(x))
     return q, scale, q_t, scale_t
 

@@ -112,13 +112,15 @@ mx_status check_mul32(const char* name, int64_t v) {
   return MX_OK;
 }
 
+// a_rows / b_rows / out_rows: 0 when that buffer holds no element (it may be NULL)
 mx_status check_gemm_common(const void* a, const void* a_s, const void* b, const void* b_s, const void* out,
-                            int out_dtype, int32_t groups, const int32_t* offs) {
-  TRY(check_ptr("a", a));
-  TRY(check_ptr("a_scale", a_s));
-  TRY(check_ptr("b", b));
-  TRY(check_ptr("b_scale", b_s));
-  TRY(check_ptr("out", out));
+                            int out_dtype, int32_t groups, const int32_t* offs, int64_t a_elems, int64_t b_elems,
+                            int64_t out_elems) {
+  TRY(check_rows_ptr("a", a, a_elems));
+  TRY(check_rows_ptr("a_scale", a_s, a_elems));
+  TRY(check_rows_ptr("b", b, b_elems));
+  TRY(check_rows_ptr("b_scale", b_s, b_elems));
+  TRY(check_rows_ptr("out", out, out_elems));
   if (out_dtype != MX_OUT_F32 && out_dtype != MX_OUT_BF16)
     return fail(MX_E_DTYPE, "out_dtype = %d is neither MX_OUT_F32 (0) nor MX_OUT_BF16 (1)", out_dtype);
   if (groups < 1 || groups > 65536) return fail(MX_E_SHAPE, "groups = %d is outside [1, 65536]", groups);
@@ -159,9 +161,9 @@ mx_status mx_quantize_dim0(const uint16_t* x, int64_t rows, int64_t cols, int64_
   TRY(check_dim("cols", cols, 32));
   TRY(check_mul32("cols", cols));
   TRY(check_pitch("ld_x", ld_x, cols));
-  TRY(check_ptr("x", x));
-  TRY(check_ptr("q", q));
-  TRY(check_ptr("scale", scale));
+  TRY(check_rows_ptr("x", x, rows));
+  TRY(check_rows_ptr("q", q, rows));
+  TRY(check_rows_ptr("scale", scale, rows));
   TRY(check_device());
   return launched(mx_launch_dim0(x, rows, cols, ld_x, q, scale, 0, (hipStream_t)stream), "mx_quantize_dim0");
 }
@@ -215,10 +217,10 @@ mx_status mx_quantize_ex(const uint16_t* x, int64_t batch, int64_t rows, int64_t
   TRY(check_mul32("cols", cols));
   TRY(check_pitch("ld_x", ld_x, cols));
   if (batch * rows > kMaxDim || batch * cols > kMaxDim) return fail(MX_E_SHAPE, "batch * rows or batch * cols exceeds 2^31");
-  TRY(check_ptr("x", x));
+  TRY(check_rows_ptr("x", x, batch * rows));
   if (d0) {
-    TRY(check_ptr("q", q));
-    TRY(check_ptr("scale", scale));
+    TRY(check_rows_ptr("q", q, batch * rows));
+    TRY(check_rows_ptr("scale", scale, batch * rows));
   }
   if (d1) {
     TRY(check_ptr("q_t", q_t));
@@ -273,7 +275,7 @@ mx_status check_gemm_extent(const char* name, int64_t contraction, int64_t a_row
 mx_status mx_grouped_mm_fwd(const uint8_t* a, const uint8_t* a_s, const uint8_t* b, const uint8_t* b_s,
                             const int32_t* offs, int32_t groups, int64_t m, int64_t n, int64_t k, void* out,
                             int out_dtype, void* stream) {
-  TRY(check_gemm_common(a, a_s, b, b_s, out, out_dtype, groups, offs));
+  TRY(check_gemm_common(a, a_s, b, b_s, out, out_dtype, groups, offs, m * k, n * k, m * n));
   TRY(check_dim("m", m, 0));
   TRY(check_dim("n", n, 1));
   TRY(check_dim("k", k, 32));
@@ -289,7 +291,7 @@ mx_status mx_grouped_mm_fwd(const uint8_t* a, const uint8_t* a_s, const uint8_t*
 mx_status mx_grouped_mm_dgrad(const uint8_t* dy, const uint8_t* dy_s, const uint8_t* w_t, const uint8_t* w_t_s,
                               const int32_t* offs, int32_t groups, int64_t m, int64_t n, int64_t k, void* dx,
                               int out_dtype, void* stream) {
-  TRY(check_gemm_common(dy, dy_s, w_t, w_t_s, dx, out_dtype, groups, offs));
+  TRY(check_gemm_common(dy, dy_s, w_t, w_t_s, dx, out_dtype, groups, offs, m * n, k * n, m * k));
   TRY(check_dim("m", m, 0));
   TRY(check_dim("n", n, 32));
   TRY(check_dim("k", k, 1));
@@ -306,7 +308,7 @@ mx_status mx_grouped_mm_dgrad(const uint8_t* dy, const uint8_t* dy_s, const uint
 mx_status mx_grouped_mm_wgrad(const uint8_t* dy_t, const uint8_t* dy_t_s, const uint8_t* x_t, const uint8_t* x_t_s,
                               const int32_t* offs, int32_t groups, int64_t m, int64_t n, int64_t k, void* dw,
                               int out_dtype, void* stream) {
-  TRY(check_gemm_common(dy_t, dy_t_s, x_t, x_t_s, dw, out_dtype, groups, offs));
+  TRY(check_gemm_common(dy_t, dy_t_s, x_t, x_t_s, dw, out_dtype, groups, offs, n * m, k * m, n * k));
   TRY(check_dim("m", m, 0));
   TRY(check_dim("n", n, 1));
   TRY(check_dim("k", k, 1));
@@ -369,10 +371,10 @@ namespace {
 // elements (2^22 bytes, the byte limit of the MXFP8 GEMM).
 mx_status check_bf16_gemm(const void* a, const void* b, const void* out, int out_dtype, int32_t groups,
                           const int32_t* offs, const char* cname, int64_t contraction, int64_t a_rows,
-                          int64_t b_rows) {
-  TRY(check_ptr("a", a));
-  TRY(check_ptr("b", b));
-  TRY(check_ptr("out", out));
+                          int64_t b_rows, int64_t out_elems) {
+  TRY(check_rows_ptr("a", a, a_rows * contraction));
+  TRY(check_rows_ptr("b", b, b_rows * contraction));
+  TRY(check_rows_ptr("out", out, out_elems));
   if (out_dtype != MX_OUT_F32 && out_dtype != MX_OUT_BF16)
     return fail(MX_E_DTYPE, "out_dtype = %d is neither MX_OUT_F32 (0) nor MX_OUT_BF16 (1)", out_dtype);
   if (groups < 1 || groups > 65536) return fail(MX_E_SHAPE, "groups = %d is outside [1, 65536]", groups);
@@ -393,7 +395,7 @@ mx_status mx_grouped_mm_bf16_fwd(const uint16_t* a, const uint16_t* b, const int
   TRY(check_dim("m", m, 0));
   TRY(check_dim("n", n, 1));
   TRY(check_dim("k", k, 8));
-  TRY(check_bf16_gemm(a, b, out, out_dtype, groups, offs, "k", k, m, (int64_t)groups * n));
+  TRY(check_bf16_gemm(a, b, out, out_dtype, groups, offs, "k", k, m, (int64_t)groups * n, m * n));
   TRY(check_device());
   return launched(mx_launch_gemm_bf16_mgroup(a, b, offs, groups, m, n, k, out, out_dtype, (hipStream_t)stream),
                   "mx_grouped_mm_bf16_fwd");
@@ -404,7 +406,7 @@ mx_status mx_grouped_mm_bf16_dgrad(const uint16_t* dy, const uint16_t* w_t, cons
   TRY(check_dim("m", m, 0));
   TRY(check_dim("n", n, 8));
   TRY(check_dim("k", k, 1));
-  TRY(check_bf16_gemm(dy, w_t, dx, out_dtype, groups, offs, "n", n, m, (int64_t)groups * k));
+  TRY(check_bf16_gemm(dy, w_t, dx, out_dtype, groups, offs, "n", n, m, (int64_t)groups * k, m * k));
   TRY(check_device());
   return launched(mx_launch_gemm_bf16_mgroup(dy, w_t, offs, groups, m, k, n, dx, out_dtype, (hipStream_t)stream),
                   "mx_grouped_mm_bf16_dgrad");
@@ -412,10 +414,10 @@ mx_status mx_grouped_mm_bf16_dgrad(const uint16_t* dy, const uint16_t* w_t, cons
 
 mx_status mx_grouped_mm_bf16_wgrad(const uint16_t* dy_t, const uint16_t* x_t, const int32_t* offs, int32_t groups,
                                    int64_t m, int64_t n, int64_t k, void* dw, int out_dtype, void* stream) {
-  TRY(check_dim("m", m, 8));
+  TRY(check_dim("m", m, 0));
   TRY(check_dim("n", n, 1));
   TRY(check_dim("k", k, 1));
-  TRY(check_bf16_gemm(dy_t, x_t, dw, out_dtype, groups, offs, "m", m, n, k));
+  TRY(check_bf16_gemm(dy_t, x_t, dw, out_dtype, groups, offs, "m", m, n, k, (int64_t)groups * n * k));
   if ((int64_t)groups * n > kMaxDim) return fail(MX_E_SHAPE, "groups * n exceeds 2^31");
   TRY(check_device());
   return launched(mx_launch_gemm_bf16_kgroup(dy_t, x_t, offs, groups, n, k, m, dw, out_dtype, (hipStream_t)stream),

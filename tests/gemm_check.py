@@ -5,7 +5,8 @@ same dequantized operands (shared by the small and the full-size tests):
     inside one 64-element dot product it drops product bits below about 2^-14 of
     the largest product (measured on adversarial random codes: worst error
     3.2e-4 = 2^-11.6 of sum |a b| per instruction). HW_REL = 2^-11 covers that;
-  * relative Frobenius error reported for every case and held to REL_FRO_HW;
+  * relative Frobenius error reported for every case and held to REL_FRO_HW plus
+    the growth of fp32 accumulation rounding with the contraction (rel_fro_gate);
   * bf16 output within 1 bf16 ulp of the correctly rounded value, or inside the
     per-element bound above plus half a bf16 ulp.
 """
@@ -19,10 +20,23 @@ REL_FRO_HW = 5e-5  # gate: measured 1.5e-5 on N(0,1) x N(0,0.02) data, K = 512
 HW_REL = 2.0**-11
 
 
+def rel_fro_gate(K):
+    """The Frobenius gate for a contraction of length K: REL_FRO_HW (measured at
+    K = 512) plus the growth of the accumulator's own rounding, one fp32 rounding
+    per 64-element MFMA k-step; n such roundings walk randomly to about sqrt(n) u,
+    and 8 u per sqrt(step) leaves room for the instruction's internal truncation.
+    At K = 4096 the gate is 5.4e-5, at K = 2^22 1.7e-4."""
+    if not K:
+        return REL_FRO_HW
+    return REL_FRO_HW + (K / 64) ** 0.5 * 2.0**-21
+
+
 def check_f32(oracle, got, ref, name, absprod=None, K=None):
     err = oracle.rel_frobenius(got, ref)
-    say(f"    {name}: rel frobenius {err:.3e} (IEEE-fp32 bar {REL_FRO:g}: {'met' if err <= REL_FRO else 'not met'})")
-    assert err <= REL_FRO_HW, f"{name}: relative Frobenius error {err:.3e} > {REL_FRO_HW}"
+    gate = rel_fro_gate(K)
+    say(f"    {name}: rel frobenius {err:.3e} (gate {gate:.2e}; IEEE-fp32 bar {REL_FRO:g}: "
+        f"{'met' if err <= REL_FRO else 'not met'})")
+    assert err <= gate, f"{name}: relative Frobenius error {err:.3e} > {gate:.2e}"
     if absprod is not None:
         u = 2.0**-24
         bound = (HW_REL + K * u / (1 - K * u)) * absprod + 1e-30
