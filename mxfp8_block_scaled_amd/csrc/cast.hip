@@ -325,19 +325,23 @@ __global__ __launch_bounds__(256) void k_quant_both(const uint16_t* __restrict__
 }
 
 // ---------------------------------------------------------------------------------
-// 32x32 weight cast: one wave per 32-row x 256-column strip (eight 32x32 tiles).
-// The tile amax reduces over the lane's 16 rows, the quad (32 columns) and the two
-// wave halves. Codes go out rowwise directly and, through LDS, transposed.
+// 32x32 weight cast: one wave per 32-row x 256-column strip (eight 32x32 tiles),
+// one wave per workgroup so that the few strips of a narrow weight spread over all
+// compute units. The tile amax reduces over the lane's 16 rows, the quad (32
+// columns) and the two wave halves. Codes go out rowwise directly and, through
+// LDS, transposed.
 // ---------------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_quant_w32(const uint16_t* __restrict__ w, int64_t batch, int64_t n,
+constexpr int kW32Waves = 1;  // waves per workgroup
+
+__global__ __launch_bounds__(64 * kW32Waves) void k_quant_w32(const uint16_t* __restrict__ w, int64_t batch, int64_t n,
                                                    int64_t k, int64_t ld, uint8_t* __restrict__ q,
                                                    uint8_t* __restrict__ q_t, uint8_t* __restrict__ s_row,
                                                    uint8_t* __restrict__ s_col, int64_t ktiles) {
-  __shared__ unsigned lds_q[4][32 * 64];  // per wave: 32 rows x 256 bytes
-  __shared__ uint8_t lds_tb[4][8];
+  __shared__ unsigned lds_q[kW32Waves][32 * 64];  // per wave: 32 rows x 256 bytes
+  __shared__ uint8_t lds_tb[kW32Waves][8];
   const int wv = threadIdx.x >> 6, l = threadIdx.x & 63, h = l >> 5, c = l & 31;
   const int64_t row_bands = batch * n / 32;
-  const int64_t t = (int64_t)blockIdx.x * 4 + wv;
+  const int64_t t = (int64_t)blockIdx.x * kW32Waves + wv;
   const bool active = t < row_bands * ktiles;
   const int64_t rb = active ? t / ktiles : 0, kt = active ? t % ktiles : 0;
   const int64_t col0 = kt * 256 + c * 8;
@@ -495,8 +499,9 @@ hipError_t mx_launch_w32(const uint16_t* w, int64_t batch, int64_t n, int64_t k,
   const int64_t ktiles = mx::scale_tiles_k(k / 32);
   const int64_t tiles = batch * n / 32 * ktiles;
   if (tiles == 0) return hipSuccess;
-  const int64_t blocks = (tiles + 3) / 4;
-  hipLaunchKernelGGL(mx::k_quant_w32, dim3((unsigned)blocks), dim3(256), 0, stream, w, batch, n, k, ld, q, q_t,
+  const int64_t blocks = (tiles + mx::kW32Waves - 1) / mx::kW32Waves;
+  hipLaunchKernelGGL(mx::k_quant_w32, dim3((unsigned)blocks), dim3(64 * mx::kW32Waves), 0, stream, w, batch, n, k, ld,
+                     q, q_t,
                      s_row, s_col, ktiles);
   return hipGetLastError();
 }
