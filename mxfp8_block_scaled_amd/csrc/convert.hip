@@ -57,13 +57,36 @@ __device__ inline int scale_at(const uint8_t* scale, int64_t row, int64_t kb, in
   return scale[scale_tile_base(row / 32, kb / 8, kt) + scale_in_tile((int)(row & 31), (int)(kb & 7))];
 }
 
+// deq_bf16 for scale bytes 10..246, where every non-zero code lands in bf16's normal
+// range (the smallest, 2^-9, has exponent field byte - 9 >= 1; the largest, 448, has
+// byte + 8 <= 254): the fields are placed directly, with selects instead of branches.
+__device__ inline unsigned deq_bf16_normal(unsigned code, int byte) {
+  const unsigned sign = (code & 0x80) << 8;
+  const unsigned e = (code >> 3) & 15, m = code & 7;
+  const unsigned lz = m >= 4 ? 1 : (m >= 2 ? 2 : 3);  // E4M3 subnormal m 2^-9 = (m << lz) 2^(-9-lz)
+  const unsigned normal = ((e + (unsigned)byte - 7) << 7) | (m << 4);
+  const unsigned subnormal = (((unsigned)byte - 6 - lz) << 7) | (((m << lz) - 8) << 4);
+  unsigned bits = e ? normal : subnormal;
+  bits = (code & 0x7f) == 0 ? 0u : bits;
+  bits = (code & 0x7f) == 0x7f ? 0x7FC0u : bits;
+  return sign | bits;
+}
+
 // 16 codes (one half-block) -> 16 bf16 in eight dwords
 __device__ inline void deq16(u32x4 c, int byte, unsigned out[8]) {
   const unsigned w[4] = {c.x, c.y, c.z, c.w};
+  if (byte >= 10 && byte <= 246) {
 #pragma unroll
-  for (int d = 0; d < 4; ++d) {
-    out[2 * d] = deq_bf16(w[d] & 0xff, byte) | (deq_bf16((w[d] >> 8) & 0xff, byte) << 16);
-    out[2 * d + 1] = deq_bf16((w[d] >> 16) & 0xff, byte) | (deq_bf16(w[d] >> 24, byte) << 16);
+    for (int d = 0; d < 4; ++d) {
+      out[2 * d] = deq_bf16_normal(w[d] & 0xff, byte) | (deq_bf16_normal((w[d] >> 8) & 0xff, byte) << 16);
+      out[2 * d + 1] = deq_bf16_normal((w[d] >> 16) & 0xff, byte) | (deq_bf16_normal(w[d] >> 24, byte) << 16);
+    }
+  } else {
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      out[2 * d] = deq_bf16(w[d] & 0xff, byte) | (deq_bf16((w[d] >> 8) & 0xff, byte) << 16);
+      out[2 * d + 1] = deq_bf16((w[d] >> 16) & 0xff, byte) | (deq_bf16(w[d] >> 24, byte) << 16);
+    }
   }
 }
 
@@ -83,11 +106,14 @@ __global__ __launch_bounds__(256) void k_dequant(const uint8_t* __restrict__ q, 
 }
 
 enum { IN_BF16 = 0, IN_MXFP8 = 1 };
-constexpr int kT = 64;          // tile edge (elements)
-constexpr int kTP = kT + 2;     // LDS row pitch in bf16: 132 bytes, 33 banks
+constexpr int kT = 64;  // tile rows (elements)
+// tile columns: 64 for bf16 input; 128 for codes, so that each thread moves two 16-byte
+// chunks of codes (more bytes in flight per workgroup)
+template <int IN>
+constexpr int tile_cols() { return IN == IN_BF16 ? 64 : 128; }
 
-// One 64 x 64 tile per workgroup (256 threads): rows [r0, r0+64) x cols [c0, c0+64)
-// of batch b of `in` go to rows [c0, c0+64) x cols [r0, r0+64) of batch b of `out`.
+// One 64 x TC tile per workgroup (256 threads): rows [r0, r0+64) x cols [c0, c0+TC)
+// of batch b of `in` go to rows [c0, c0+TC) x cols [r0, r0+64) of batch b of `out`.
 // The input is read as whole 16-byte chunks, staged in LDS row by row (padded pitch),
 // and written as 16-byte chunks of the transposed rows. Ragged edges: rows and
 // columns past the matrix are skipped (cols % 8 == 0, rows % 8 == 0 for bf16 input;
@@ -96,11 +122,13 @@ template <int IN>
 __global__ __launch_bounds__(256) void k_tile_t(const void* __restrict__ in, const uint8_t* __restrict__ scale,
                                                 int64_t rows, int64_t cols, int64_t ld_in, int64_t tiles_r,
                                                 int64_t tiles_c, uint16_t* __restrict__ out) {
-  __shared__ uint16_t t[kT * kTP];
+  constexpr int TC = tile_cols<IN>();
+  constexpr int TP = TC + 2;  // LDS row pitch in bf16 (an odd number of 4-byte banks)
+  __shared__ uint16_t t[kT * TP];
   const int tid = threadIdx.x;
   const int64_t per_batch = tiles_r * tiles_c;
   const int64_t b = blockIdx.x / per_batch, rest = blockIdx.x - b * per_batch;
-  const int64_t r0 = (rest / tiles_c) * kT, c0 = (rest % tiles_c) * kT;
+  const int64_t r0 = (rest / tiles_c) * kT, c0 = (rest % tiles_c) * TC;
   if (IN == IN_BF16) {
     const uint16_t* x = (const uint16_t*)in + b * rows * ld_in;
 #pragma unroll
@@ -108,32 +136,44 @@ __global__ __launch_bounds__(256) void k_tile_t(const void* __restrict__ in, con
       const int id = tid + 256 * k, r = id >> 3, ch = id & 7;
       u32x4 v = (u32x4){0, 0, 0, 0};
       if (r0 + r < rows && c0 + 8 * ch < cols) v = __builtin_nontemporal_load((const u32x4*)(x + (r0 + r) * ld_in + c0 + 8 * ch));
-      unsigned* dst = (unsigned*)(t + r * kTP + 8 * ch);
+      unsigned* dst = (unsigned*)(t + r * TP + 8 * ch);
       dst[0] = v.x; dst[1] = v.y; dst[2] = v.z; dst[3] = v.w;
     }
   } else {
     const uint8_t* qb = (const uint8_t*)in + b * rows * ld_in;
     const int64_t kt = scale_tiles_k(cols / 32);
-    const int r = tid >> 2, ch = tid & 3;  // 64 rows x 4 chunks of 16 codes
-    unsigned o[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    if (r0 + r < rows && c0 + 16 * ch < cols) {
-      const u32x4 codes = __builtin_nontemporal_load((const u32x4*)(qb + (r0 + r) * ld_in + c0 + 16 * ch));
-      deq16(codes, scale_at(scale, b * rows + r0 + r, (c0 + 16 * ch) / 32, kt), o);
-    }
-    unsigned* dst = (unsigned*)(t + r * kTP + 16 * ch);
+    u32x4 codes[2];
+    int byte[2];
 #pragma unroll
-    for (int d = 0; d < 8; ++d) dst[d] = o[d];
+    for (int k = 0; k < 2; ++k) {  // 64 rows x 8 chunks of 16 codes: loads first, then the math
+      const int id = tid + 256 * k, r = id >> 3, ch = id & 7;
+      codes[k] = (u32x4){0, 0, 0, 0};
+      byte[k] = 127;
+      if (r0 + r < rows && c0 + 16 * ch < cols) {
+        codes[k] = __builtin_nontemporal_load((const u32x4*)(qb + (r0 + r) * ld_in + c0 + 16 * ch));
+        byte[k] = scale_at(scale, b * rows + r0 + r, (c0 + 16 * ch) / 32, kt);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int id = tid + 256 * k, r = id >> 3, ch = id & 7;
+      unsigned o[8];
+      deq16(codes[k], byte[k], o);
+      unsigned* dst = (unsigned*)(t + r * TP + 16 * ch);
+#pragma unroll
+      for (int d = 0; d < 8; ++d) dst[d] = o[d];
+    }
   }
   __syncthreads();
   uint16_t* ob = out + b * cols * rows;
 #pragma unroll
-  for (int k = 0; k < 2; ++k) {  // 64 output rows (input columns) x 8 chunks of 8 input rows
+  for (int k = 0; k < TC / 32; ++k) {  // TC output rows (input columns) x 8 chunks of 8 input rows
     const int id = tid + 256 * k, c = id >> 3, rc = id & 7;
     if (c0 + c >= cols || r0 + 8 * rc >= rows) continue;
     unsigned w[4];
 #pragma unroll
     for (int d = 0; d < 4; ++d)
-      w[d] = (unsigned)t[(8 * rc + 2 * d) * kTP + c] | ((unsigned)t[(8 * rc + 2 * d + 1) * kTP + c] << 16);
+      w[d] = (unsigned)t[(8 * rc + 2 * d) * TP + c] | ((unsigned)t[(8 * rc + 2 * d + 1) * TP + c] << 16);
     *(u32x4*)(ob + (c0 + c) * rows + r0 + 8 * rc) = (u32x4){w[0], w[1], w[2], w[3]};
   }
 }
@@ -162,7 +202,8 @@ hipError_t mx_launch_dequant(const uint8_t* q, const uint8_t* scale, int64_t bat
     hipLaunchKernelGGL(mx::k_dequant, dim3(mx::grid_for(batch * rows * cols / 16)), dim3(256), 0, stream, q, scale,
                        batch * rows, cols, out);
   } else {
-    const int64_t tr = (rows + mx::kT - 1) / mx::kT, tc = (cols + mx::kT - 1) / mx::kT;
+    constexpr int TC = mx::tile_cols<mx::IN_MXFP8>();
+    const int64_t tr = (rows + mx::kT - 1) / mx::kT, tc = (cols + TC - 1) / TC;
     hipLaunchKernelGGL(mx::k_tile_t<mx::IN_MXFP8>, dim3((unsigned)(batch * tr * tc)), dim3(256), 0, stream,
                        (const void*)q, scale, rows, cols, cols, tr, tc, out);
   }
@@ -172,7 +213,8 @@ hipError_t mx_launch_dequant(const uint8_t* q, const uint8_t* scale, int64_t bat
 hipError_t mx_launch_transpose_bf16(const uint16_t* x, int64_t batch, int64_t rows, int64_t cols, int64_t ld,
                                     uint16_t* out, hipStream_t stream) {
   if (batch * rows == 0) return hipSuccess;
-  const int64_t tr = (rows + mx::kT - 1) / mx::kT, tc = (cols + mx::kT - 1) / mx::kT;
+  constexpr int TC = mx::tile_cols<mx::IN_BF16>();
+  const int64_t tr = (rows + mx::kT - 1) / mx::kT, tc = (cols + TC - 1) / TC;
   hipLaunchKernelGGL(mx::k_tile_t<mx::IN_BF16>, dim3((unsigned)(batch * tr * tc)), dim3(256), 0, stream,
                      (const void*)x, (const uint8_t*)nullptr, rows, cols, ld, tr, tc, out);
   return hipGetLastError();
