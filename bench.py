@@ -19,9 +19,10 @@ One step runs, in order:
 `value` = all GEMM flops of the step / step time (casts included).
 
 --unaligned-groups: the same tokens with per-row (not 32-aligned) group sizes;
-the step pads X and dY to 32-row group boundaries (ao fork PR 10, "Known
-follow-ups": padded token groups), runs the casts and the grouped passes on the
-padded rows and offsets, and unpads Y and dX; flops still count real rows only.
+the step pads X and dY to 32-row group boundaries inside the casts (ao fork PR 10,
+"Known follow-ups": padded token groups), runs the grouped passes on the padded
+rows and offsets, fwd and dgrad writing Y and dX unpadded; flops count real rows
+only.
 
 --backward ARM: the MoE grouped step (no dense layer) with the backward override
 arm ARM (ao fork PR 10, "Design notes"): "quantized" (the MXFP8 backward),
@@ -222,22 +223,27 @@ def main():
             g_dgrad, g_wgrad,
         ]
     elif unaligned:
-        # the MoE grouped part only (the dense layer has no groups); pad bytes: read the
-        # real rows, write every padded row; unpad: read and write the real rows (bf16)
-        Xp, dYp, y_u, dx_u = bf(Mg, K), bf(Mg, N), bf(M, N), bf(M, K)
+        # the MoE grouped part only (the dense layer has no groups). The padding is fused:
+        # the casts read the real rows once and write the codes of every padded row
+        # (bytes: 2 per real element read, 2 + 2/32 per padded element written); fwd and
+        # dgrad write their outputs unpadded; wgrad contracts over the padded rows.
+        padded_both = lambda n_real, n_pad: 2 * n_real + n_pad * (2 + 2 / 32)  # noqa: E731
+        y_u, dx_u = bf(M, N), bf(M, K)
         ops = [
-            ("pad X", "pad", 2 * M * K + 2 * Mg * K, lambda: mx.mx_pad_token_groups(X, offs, Mg, Xp, offs_pad)),
-            ("cast_dim0+dim1 X", "cast", both(Mg * K),
-             lambda: mx.mx_quantize_dim0_dim1(Xp, buf["xq"], buf["xs"], buf["xtq"], buf["xts"])),
+            ("cast_dim0+dim1 X (padded)", "cast", padded_both(M * K, Mg * K),
+             lambda: mx.mx_pad_quantize_dim0_dim1(X, offs, Mg, buf["xq"], buf["xs"], buf["xtq"], buf["xts"],
+                                                  offs_pad)),
             ("cast_dim0+dim1 W", "cast", both(G * N * K),
              lambda: mx.mx_quantize_dim0_dim1(W, buf["wq"], buf["ws"], buf["wtq"], buf["wts"])),
-            g_fwd,
-            ("unpad Y", "pad", 4 * M * N, lambda: mx.mx_unpad_token_groups(buf["y"], offs, M, y_u)),
-            ("pad dY", "pad", 2 * M * N + 2 * Mg * N, lambda: mx.mx_pad_token_groups(dY, offs, Mg, dYp, offs_pad)),
-            ("cast_dim0+dim1 dY", "cast", both(Mg * N),
-             lambda: mx.mx_quantize_dim0_dim1(dYp, buf["dyq"], buf["dys"], buf["dytq"], buf["dyts"])),
-            g_dgrad,
-            ("unpad dX", "pad", 4 * M * K, lambda: mx.mx_unpad_token_groups(buf["dx"], offs, M, dx_u)),
+            ("gemm_fwd grouped", "gemm", 2 * M * N * K,
+             lambda: mx.mx_grouped_mm_fwd_padded(buf["xq"], buf["xs"], buf["wq"], buf["ws"], offs_pad, offs, Mg, M,
+                                                 N, K, out=y_u)),
+            ("cast_dim0+dim1 dY (padded)", "cast", padded_both(M * N, Mg * N),
+             lambda: mx.mx_pad_quantize_dim0_dim1(dY, offs, Mg, buf["dyq"], buf["dys"], buf["dytq"], buf["dyts"],
+                                                  offs_pad)),
+            ("gemm_dgrad grouped", "gemm", 2 * M * N * K,
+             lambda: mx.mx_grouped_mm_dgrad_padded(buf["dyq"], buf["dys"], buf["wtq"], buf["wts"], offs_pad, offs,
+                                                   Mg, M, N, K, out=dx_u)),
             g_wgrad,
         ]
     elif args.separate_casts:
@@ -374,8 +380,8 @@ def main():
                                                      else "the dequantized forward codes")) + " (no dense layer)")
     if unaligned:
         workload = (f"moe_g8 unaligned groups: G=8 experts, M=16384 tokens (per-row group sizes), K=N=4096; "
-                    f"pad X and dY to {Mg} rows, one-pass casts, grouped fwd/dgrad/wgrad on padded offsets, "
-                    f"unpad Y and dX (no dense layer)")
+                    f"casts of X and dY padded to {Mg} rows in one pass, grouped fwd/dgrad/wgrad on padded "
+                    f"offsets, Y and dX written unpadded (no dense layer)")
 
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,

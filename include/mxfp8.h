@@ -321,6 +321,36 @@ mx_status mx_unpad_token_groups(const void* y_pad, int64_t rows_pad, int64_t col
                                 const int32_t* offs, int32_t groups, void* y, int64_t rows, int64_t ld_y, int dtype,
                                 void* stream);
 
+/* The padding fused into the casts and the GEMM outputs: no padded bf16 copy of the
+ * tokens or grad_out is written, and the forward / dgrad outputs come out unpadded.
+ *
+ * One-pass dim0 + dim1 cast of the padded rows: the codes and scales are those of
+ * mx_quantize_dim0_dim1 applied to the output of mx_pad_token_groups(x, offs), and
+ * offs_pad is written as there.
+ *   x         [rows x cols] bf16 (pitch ld_x), offs the unpadded group ends
+ *   q, scale  [rows_pad x cols] + mx_scale_bytes(rows_pad, cols) (written)
+ *   q_t, scale_t  [cols x rows_pad] + mx_scale_bytes(cols, rows_pad) (written)
+ * rows_pad >= mx_padded_rows(rows, groups), a multiple of 32; cols % 32 == 0. */
+mx_status mx_pad_quantize_dim0_dim1(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
+                                    const int32_t* offs, int32_t groups, int64_t rows_pad, uint8_t* q,
+                                    uint8_t* scale, uint8_t* q_t, uint8_t* scale_t, int32_t* offs_pad,
+                                    void* stream);
+
+/* Forward / dgrad on padded token rows with unpadded outputs: the result equals
+ * mx_unpad_token_groups of mx_grouped_mm_fwd(..., offs_pad, m = m_pad, ...) (resp.
+ * dgrad): row offs_pad[g-1] + i of group g is written to row offs[g-1] + i of out
+ * [m x n] (dx [m x k]) for i < offs[g] - offs[g-1]; no other row is written.
+ *   offs_pad  padded group ends (from mx_pad_quantize_dim0_dim1 or
+ *             mx_pad_token_groups); offs the unpadded ends; m <= m_pad
+ * Other arguments and conditions as for mx_grouped_mm_fwd / mx_grouped_mm_dgrad
+ * with m = m_pad for the operands. */
+mx_status mx_grouped_mm_fwd_padded(const uint8_t* a, const uint8_t* a_s, const uint8_t* b, const uint8_t* b_s,
+                                   const int32_t* offs_pad, const int32_t* offs, int32_t groups, int64_t m_pad,
+                                   int64_t m, int64_t n, int64_t k, void* out, int out_dtype, void* stream);
+mx_status mx_grouped_mm_dgrad_padded(const uint8_t* dy, const uint8_t* dy_s, const uint8_t* w_t, const uint8_t* w_t_s,
+                                     const int32_t* offs_pad, const int32_t* offs, int32_t groups, int64_t m_pad,
+                                     int64_t m, int64_t n, int64_t k, void* dx, int out_dtype, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

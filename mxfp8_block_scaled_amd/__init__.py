@@ -37,6 +37,9 @@ __all__ = [
     "mx_grouped_mm_bf16_wgrad",
     "mx_padded_rows",
     "mx_pad_token_groups",
+    "mx_pad_quantize_dim0_dim1",
+    "mx_grouped_mm_fwd_padded",
+    "mx_grouped_mm_dgrad_padded",
     "mx_unpad_token_groups",
     "MXError",
     "library_path",
@@ -377,4 +380,51 @@ def mx_grouped_mm_bf16_wgrad(dy_t, x_t, offs, m, n, k, groups=None, out_dtype=MX
     out = _out((G, n, k), out_dtype, dy_t.device, out)
     _lib.call("mx_grouped_mm_bf16_wgrad", _ptr(dy_t), _ptr(x_t), _ptr(offs), G, m, n, k, _ptr(out), out_dtype,
               _stream(dy_t))
+    return out
+
+
+def mx_pad_quantize_dim0_dim1(x, offs, rows_pad=None, q=None, scale=None, q_t=None, scale_t=None, offs_pad=None):
+    """Token-group padding fused into the one-pass cast: the casts of
+    mx_pad_token_groups(x, offs) without writing the padded bf16 rows.
+    Returns (q, scale, q_t, scale_t, offs_pad)."""
+    x = _bf16_bits(x)
+    if x.dim() != 2:
+        raise ValueError("x must be a 2D tensor")
+    G = _groups(offs, None)
+    rows, cols = x.shape
+    ld = _pitch(x)
+    if rows_pad is None:
+        rows_pad = mx_padded_rows(rows, G)
+    dev = x.device
+    if q is None:
+        q = torch.empty((rows_pad, cols), dtype=torch.uint8, device=dev)
+    if scale is None:
+        scale = _u8(mx_scale_bytes(rows_pad, cols), dev)
+    if q_t is None:
+        q_t = torch.empty((cols, rows_pad), dtype=torch.uint8, device=dev)
+    if scale_t is None:
+        scale_t = _u8(mx_scale_bytes(cols, rows_pad), dev)
+    if offs_pad is None:
+        offs_pad = torch.empty(G, dtype=torch.int32, device=dev)
+    _lib.call("mx_pad_quantize_dim0_dim1", _ptr(x), rows, cols, ld, _ptr(offs), G, rows_pad, _ptr(q), _ptr(scale),
+              _ptr(q_t), _ptr(scale_t), _ptr(offs_pad), _stream(x))
+    return q, scale, q_t, scale_t, offs_pad
+
+
+def mx_grouped_mm_fwd_padded(a, a_s, b, b_s, offs_pad, offs, m_pad, m, n, k, out_dtype=MX_OUT_BF16, out=None):
+    """Forward on padded token rows, output unpadded: out [m, n]."""
+    G = _groups(offs, None)
+    out = _out((m, n), out_dtype, a.device, out)
+    _lib.call("mx_grouped_mm_fwd_padded", _ptr(a), _ptr(a_s), _ptr(b), _ptr(b_s), _ptr(offs_pad), _ptr(offs), G,
+              m_pad, m, n, k, _ptr(out), out_dtype, _stream(a))
+    return out
+
+
+def mx_grouped_mm_dgrad_padded(dy, dy_s, w_t, w_t_s, offs_pad, offs, m_pad, m, n, k, out_dtype=MX_OUT_BF16,
+                               out=None):
+    """dgrad on padded token rows, output unpadded: dx [m, k]."""
+    G = _groups(offs, None)
+    out = _out((m, k), out_dtype, dy.device, out)
+    _lib.call("mx_grouped_mm_dgrad_padded", _ptr(dy), _ptr(dy_s), _ptr(w_t), _ptr(w_t_s), _ptr(offs_pad), _ptr(offs),
+              G, m_pad, m, n, k, _ptr(out), out_dtype, _stream(dy))
     return out

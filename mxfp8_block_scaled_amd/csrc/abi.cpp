@@ -29,8 +29,10 @@ hipError_t mx_launch_gemm_bf16_mgroup(const uint16_t*, const uint16_t*, const in
                                       void*, int, hipStream_t);
 hipError_t mx_launch_gemm_bf16_kgroup(const uint16_t*, const uint16_t*, const int32_t*, int, int64_t, int64_t, int64_t,
                                       void*, int, hipStream_t);
-hipError_t mx_launch_gemm_mgroup(const uint8_t*, const uint8_t*, const uint8_t*, const uint8_t*, const int32_t*, int,
-                                 int64_t, int64_t, int64_t, void*, int, hipStream_t);
+hipError_t mx_launch_gemm_mgroup(const uint8_t*, const uint8_t*, const uint8_t*, const uint8_t*, const int32_t*,
+                                 const int32_t*, int, int64_t, int64_t, int64_t, void*, int, hipStream_t);
+hipError_t mx_launch_pad_both(const uint16_t*, int64_t, int64_t, int64_t, const int32_t*, int, int64_t, uint8_t*,
+                              uint8_t*, uint8_t*, uint8_t*, int32_t*, hipStream_t);
 hipError_t mx_launch_gemm_kgroup(const uint8_t*, const uint8_t*, const uint8_t*, const uint8_t*, const int32_t*, int,
                                  int64_t, int64_t, int64_t, void*, int, hipStream_t);
 
@@ -284,7 +286,8 @@ mx_status mx_grouped_mm_fwd(const uint8_t* a, const uint8_t* a_s, const uint8_t*
   if ((int64_t)groups * n > kMaxDim) return fail(MX_E_SHAPE, "groups * n exceeds 2^31");
   TRY(check_gemm_extent("k", k, m, (int64_t)groups * n));
   TRY(check_device());
-  return launched(mx_launch_gemm_mgroup(a, a_s, b, b_s, offs, groups, m, n, k, out, out_dtype, (hipStream_t)stream),
+  return launched(mx_launch_gemm_mgroup(a, a_s, b, b_s, offs, nullptr, groups, m, n, k, out, out_dtype,
+                                        (hipStream_t)stream),
                   "mx_grouped_mm_fwd");
 }
 
@@ -301,7 +304,8 @@ mx_status mx_grouped_mm_dgrad(const uint8_t* dy, const uint8_t* dy_s, const uint
   TRY(check_gemm_extent("n", n, m, (int64_t)groups * k));
   TRY(check_device());
   // dX[m x k] = dY[m x n] . (W_g^T [k x n])^T : the M-grouped core with contraction n
-  return launched(mx_launch_gemm_mgroup(dy, dy_s, w_t, w_t_s, offs, groups, m, k, n, dx, out_dtype, (hipStream_t)stream),
+  return launched(mx_launch_gemm_mgroup(dy, dy_s, w_t, w_t_s, offs, nullptr, groups, m, k, n, dx, out_dtype,
+                                        (hipStream_t)stream),
                   "mx_grouped_mm_dgrad");
 }
 
@@ -489,6 +493,79 @@ mx_status mx_unpad_token_groups(const void* y_pad, int64_t rows_pad, int64_t col
   return launched(mx_launch_unpad(y_pad, rows_pad, cols * es, ld_pad * es, offs, groups, y, rows, ld_y * es,
                                   (hipStream_t)stream),
                   "mx_unpad_token_groups");
+}
+
+// ---- token-group padding fused into the cast and the GEMM outputs ----
+
+mx_status mx_pad_quantize_dim0_dim1(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
+                                    const int32_t* offs, int32_t groups, int64_t rows_pad, uint8_t* q,
+                                    uint8_t* scale, uint8_t* q_t, uint8_t* scale_t, int32_t* offs_pad,
+                                    void* stream) {
+  TRY(check_pad_common(rows, groups, rows_pad, offs));
+  if (rows_pad % 32 != 0) return fail(MX_E_SHAPE, "rows_pad = %lld must be a multiple of 32", (long long)rows_pad);
+  TRY(check_dim("cols", cols, 32));
+  TRY(check_mul32("cols", cols));
+  TRY(check_pitch("ld_x", ld_x, cols));
+  if (rows_pad * cols > ((int64_t)1 << 40)) return fail(MX_E_SHAPE, "rows_pad * cols is too large");
+  TRY(check_rows_ptr("x", x, rows));
+  TRY(check_ptr("q", q));
+  TRY(check_ptr("scale", scale));
+  TRY(check_ptr("q_t", q_t));
+  TRY(check_ptr("scale_t", scale_t));
+  if (!offs_pad) return fail(MX_E_NULL, "offs_pad is NULL");
+  if ((uintptr_t)offs_pad & 3) return fail(MX_E_ALIGN, "offs_pad is not 4-byte aligned");
+  TRY(check_device());
+  return launched(mx_launch_pad_both(x, rows, cols, ld_x, offs, groups, rows_pad, q, scale, q_t, scale_t, offs_pad,
+                                     (hipStream_t)stream),
+                  "mx_pad_quantize_dim0_dim1");
+}
+
+namespace {
+
+mx_status check_padded_gemm(const int32_t* offs_pad, const int32_t* offs, int32_t groups, int64_t m_pad, int64_t m) {
+  if (!offs_pad || !offs) return fail(MX_E_NULL, "offs_pad and offs must both be given");
+  if (((uintptr_t)offs_pad & 3) || ((uintptr_t)offs & 3)) return fail(MX_E_ALIGN, "offs arrays must be 4-byte aligned");
+  if (groups < 1 || groups > 65536) return fail(MX_E_SHAPE, "groups = %d is outside [1, 65536]", groups);
+  TRY(check_dim("m", m, 0));
+  TRY(check_dim("m_pad", m_pad, 0));
+  if (m > m_pad) return fail(MX_E_SHAPE, "m = %lld exceeds m_pad = %lld", (long long)m, (long long)m_pad);
+  return MX_OK;
+}
+
+}  // namespace
+
+mx_status mx_grouped_mm_fwd_padded(const uint8_t* a, const uint8_t* a_s, const uint8_t* b, const uint8_t* b_s,
+                                   const int32_t* offs_pad, const int32_t* offs, int32_t groups, int64_t m_pad,
+                                   int64_t m, int64_t n, int64_t k, void* out, int out_dtype, void* stream) {
+  TRY(check_padded_gemm(offs_pad, offs, groups, m_pad, m));
+  TRY(check_gemm_common(a, a_s, b, b_s, out, out_dtype, groups, offs_pad, m_pad * k, n * k, m * n));
+  TRY(check_dim("n", n, 1));
+  TRY(check_dim("k", k, 32));
+  TRY(check_mul32("k", k));
+  if (groups > 1 && n % 32 != 0) return fail(MX_E_SHAPE, "n = %lld must be a multiple of 32 when groups > 1", (long long)n);
+  if ((int64_t)groups * n > kMaxDim) return fail(MX_E_SHAPE, "groups * n exceeds 2^31");
+  TRY(check_gemm_extent("k", k, m_pad, (int64_t)groups * n));
+  TRY(check_device());
+  return launched(mx_launch_gemm_mgroup(a, a_s, b, b_s, offs_pad, offs, groups, m_pad, n, k, out, out_dtype,
+                                        (hipStream_t)stream),
+                  "mx_grouped_mm_fwd_padded");
+}
+
+mx_status mx_grouped_mm_dgrad_padded(const uint8_t* dy, const uint8_t* dy_s, const uint8_t* w_t, const uint8_t* w_t_s,
+                                     const int32_t* offs_pad, const int32_t* offs, int32_t groups, int64_t m_pad,
+                                     int64_t m, int64_t n, int64_t k, void* dx, int out_dtype, void* stream) {
+  TRY(check_padded_gemm(offs_pad, offs, groups, m_pad, m));
+  TRY(check_gemm_common(dy, dy_s, w_t, w_t_s, dx, out_dtype, groups, offs_pad, m_pad * n, k * n, m * k));
+  TRY(check_dim("n", n, 32));
+  TRY(check_dim("k", k, 1));
+  TRY(check_mul32("n", n));
+  if (groups > 1 && k % 32 != 0) return fail(MX_E_SHAPE, "k = %lld must be a multiple of 32 when groups > 1", (long long)k);
+  if ((int64_t)groups * k > kMaxDim) return fail(MX_E_SHAPE, "groups * k exceeds 2^31");
+  TRY(check_gemm_extent("n", n, m_pad, (int64_t)groups * k));
+  TRY(check_device());
+  return launched(mx_launch_gemm_mgroup(dy, dy_s, w_t, w_t_s, offs_pad, offs, groups, m_pad, k, n, dx, out_dtype,
+                                        (hipStream_t)stream),
+                  "mx_grouped_mm_dgrad_padded");
 }
 
 }  // extern "C"

@@ -16,8 +16,9 @@
 // codes are stored normally: the GEMMs read them next.
 
 #include <algorithm>
+#include <type_traits>
 
-#include "common.h"
+#include "group_table.h"
 
 namespace mx {
 
@@ -218,16 +219,33 @@ __global__ __launch_bounds__(256) void k_quant_dim1(const uint16_t* __restrict__
 //   column of the tile, 16-byte chunk k at k ^ ((row / 8) % 16): conflict-free), read
 //   back as whole 256-byte q_t rows. The eight dim1 scale tiles (256 columns x 8
 //   blocks) are assembled in LDS and written whole.
+// GATHER (token-group padding fused in, one 2D input): `rows` counts the padded rows;
+// padded row p holds row padded_source(p) of x, or zeros (ao fork PR 10, "Known
+// follow-ups": padded token groups), so the padded bf16 copy is never written.
 // ---------------------------------------------------------------------------------
-template <bool FLOOR>
+struct RowGather {
+  const int32_t* offs;  // unpadded group ends (device)
+  int groups;
+  int32_t src_rows;     // rows of x
+  int32_t* offs_pad;    // padded group ends (written by workgroup 0)
+};
+
+template <bool FLOOR, bool GATHER>
 __global__ __launch_bounds__(256) void k_quant_both(const uint16_t* __restrict__ x, int64_t batch, int64_t rows,
                                                     int64_t cols, int64_t ld, uint8_t* __restrict__ q,
                                                     uint8_t* __restrict__ scale, uint8_t* __restrict__ q_t,
-                                                    uint8_t* __restrict__ scale_t, int64_t rtiles, int64_t ctiles) {
+                                                    uint8_t* __restrict__ scale_t, int64_t rtiles, int64_t ctiles,
+                                                    RowGather gth) {
   __shared__ __attribute__((aligned(16))) uint8_t s_t[256 * 256];  // transposed codes
   __shared__ unsigned s_s1[8][64];                                 // dim1 scale tiles
   __shared__ unsigned s_s0[4][64];                                 // dim0 scale tile per wave
+  __shared__ std::conditional_t<GATHER, GroupTable, char> s_grp;  // the group table (gather only)
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, h = l >> 5, c = l & 31;
+  if constexpr (GATHER) {
+    build_table(s_grp, gth.offs, gth.groups, gth.src_rows);
+    if (blockIdx.x == 0)
+      for (int g = tid; g < gth.groups; g += 256) gth.offs_pad[g] = s_grp.pad_end[g];
+  }
   const int64_t kt0 = scale_tiles_k(cols / 32), kt1 = scale_tiles_k(rows / 32);
   const int64_t tiles = batch * rtiles * ctiles;
   uint8_t* st0 = (uint8_t*)s_s0[w];
@@ -249,10 +267,31 @@ __global__ __launch_bounds__(256) void k_quant_both(const uint16_t* __restrict__
       const int64_t base = r0 + 32 * kb;        // first row of the sub-tile
       const bool rows_ok = base < rows;         // rows % 32 == 0: the sub-tile is all in or all out
       u32x4 v[16];
+      if constexpr (GATHER) {
+        // The lane's 16 consecutive padded rows: find the first row's group, then step
+        // through group edges. (All 32 rows of a sub-tile share one padded group, whose
+        // edges are multiples of 32, but a single lookup per sub-tile with the sources
+        // as plain adds measured 102 against 85 us on the MoE tokens, same box.)
+        const GroupTable& gt = s_grp;
+        const int64_t p0 = base + 16 * h;
+        int g = upper_index(gt.pad_end, gth.groups, p0);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        v[i] = (u32x4){0, 0, 0, 0};
-        if (col_ok && rows_ok) v[i] = __builtin_nontemporal_load((const u32x4*)(xb + (base + 16 * h + i) * ld + col));
+        for (int i = 0; i < 16; ++i) {
+          while (g < gth.groups && p0 + i >= gt.pad_end[g]) ++g;
+          int64_t src = -1;
+          if (g < gth.groups) {
+            const int64_t start = g ? gt.end[g - 1] : 0, off = p0 + i - (g ? gt.pad_end[g - 1] : 0);
+            if (off < gt.end[g] - start) src = start + off;
+          }
+          v[i] = (u32x4){0, 0, 0, 0};
+          if (col_ok && rows_ok && src >= 0) v[i] = __builtin_nontemporal_load((const u32x4*)(x + src * ld + col));
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          v[i] = (u32x4){0, 0, 0, 0};
+          if (col_ok && rows_ok) v[i] = __builtin_nontemporal_load((const u32x4*)(xb + (base + 16 * h + i) * ld + col));
+        }
       }
       // ---- dim0 ----
       s_s0[w][l] = 0x7f7f7f7fu;
@@ -483,14 +522,31 @@ hipError_t mx_launch_both(const uint16_t* x, int64_t batch, int64_t rows, int64_
   const int64_t tiles = batch * rtiles * ctiles;
   if (tiles == 0) return hipSuccess;
   static int64_t fill = 0;
-  if (fill == 0) fill = resident_blocks((const void*)mx::k_quant_both<false>, 256);
+  if (fill == 0) fill = resident_blocks((const void*)mx::k_quant_both<false, false>, 256);
   const int64_t blocks = std::min<int64_t>(tiles, fill);
+  const mx::RowGather none{nullptr, 0, 0, nullptr};
   if (floor_mode)
-    hipLaunchKernelGGL(mx::k_quant_both<true>, dim3((unsigned)blocks), dim3(256), 0, stream, x, batch, rows, cols, ld,
-                       q, scale, q_t, scale_t, rtiles, ctiles);
+    hipLaunchKernelGGL((mx::k_quant_both<true, false>), dim3((unsigned)blocks), dim3(256), 0, stream, x, batch, rows,
+                       cols, ld, q, scale, q_t, scale_t, rtiles, ctiles, none);
   else
-    hipLaunchKernelGGL(mx::k_quant_both<false>, dim3((unsigned)blocks), dim3(256), 0, stream, x, batch, rows, cols,
-                       ld, q, scale, q_t, scale_t, rtiles, ctiles);
+    hipLaunchKernelGGL((mx::k_quant_both<false, false>), dim3((unsigned)blocks), dim3(256), 0, stream, x, batch, rows,
+                       cols, ld, q, scale, q_t, scale_t, rtiles, ctiles, none);
+  return hipGetLastError();
+}
+
+// Padded one-pass cast: x [rows x cols] with unpadded group ends offs -> codes of the
+// [rows_pad x cols] padded rows (both forms), offs_pad written.
+hipError_t mx_launch_pad_both(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, const int32_t* offs,
+                              int groups, int64_t rows_pad, uint8_t* q, uint8_t* scale, uint8_t* q_t,
+                              uint8_t* scale_t, int32_t* offs_pad, hipStream_t stream) {
+  const int64_t rtiles = (rows_pad + 255) / 256, ctiles = (cols + 255) / 256;
+  const int64_t tiles = rtiles * ctiles;
+  static int64_t fill = 0;
+  if (fill == 0) fill = resident_blocks((const void*)mx::k_quant_both<false, true>, 256);
+  const int64_t blocks = std::max<int64_t>(1, std::min<int64_t>(tiles, fill));  // one workgroup writes offs_pad
+  const mx::RowGather gth{offs, groups, (int32_t)rows, offs_pad};
+  hipLaunchKernelGGL((mx::k_quant_both<false, true>), dim3((unsigned)blocks), dim3(256), 0, stream, x, (int64_t)1,
+                     rows_pad, cols, ld, q, scale, q_t, scale_t, rtiles, ctiles, gth);
   return hipGetLastError();
 }
 

@@ -42,6 +42,10 @@ struct GemmArgs {
   const uint8_t* b;
   const uint8_t* b_s;
   const int32_t* offs;  // device, may be null (one group)
+  // M-grouped only, may be null: the groups' unpadded row ends when A's rows are the
+  // token-group padded ones; the output is then written unpadded (row r of group g
+  // at r - offs[g-1] + offs_out[g-1]) and the padding rows are not written
+  const int32_t* offs_out;
   void* out;
   int64_t lda, ldb;          // row pitch in bytes (= contraction length x element size)
   int64_t a_rows, b_rows;    // rows of the whole operand buffers
@@ -102,6 +106,7 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 // One output tile: where it sits and what it contracts over.
 struct Tile {
   int64_t a_row0, a_row_end, b_row0, b_row_end, k_beg, k_end, col0;
+  int64_t out_limit, out_shift;  // M-grouped: output rows [a_row0, out_limit) go to row + out_shift
   uint8_t* out_base;
   bool valid;
 };
@@ -159,6 +164,13 @@ __device__ inline Tile tile_at(const GemmArgs& p, int64_t t) {
         found = gg;
         T.a_row0 = s + (mt - cum) * BM;
         T.a_row_end = e;
+        T.out_limit = e;
+        if (p.offs_out) {
+          const int64_t so = group_start(p.offs_out, gg), eo = p.offs_out[gg];
+          const int64_t real_end = s + (eo > so ? eo - so : 0);  // the group's real rows, padded coordinates
+          T.out_shift = so - s;
+          T.out_limit = real_end < e ? real_end : e;
+        }
         break;
       }
       cum += tiles;
@@ -232,6 +244,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm(GemmArgs p) {
   T.b_row0 = uniform(T.b_row0); T.b_row_end = uniform(T.b_row_end);
   T.k_beg = uniform(T.k_beg); T.k_end = uniform(T.k_end); T.col0 = uniform(T.col0);
   T.out_base = (uint8_t*)uniform((int64_t)T.out_base);
+  T.out_limit = uniform(T.out_limit); T.out_shift = uniform(T.out_shift);
 
   const int64_t a_bands = (p.a_rows + 31) / 32, b_bands = (p.b_rows + 31) / 32;
   const __amdgpu_buffer_rsrc_t as_rsrc = __builtin_amdgcn_make_buffer_rsrc(
@@ -424,7 +437,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm(GemmArgs p) {
   // banks. It then writes whole row segments (WN * ES bytes) with 16-byte stores.
   // Otherwise (the ragged right edge) lanes store elements with a bounds check.
   auto epilogue = [&]() {
-    const int64_t row_limit = MODE == MODE_MGROUP ? T.a_row_end : p.M;
+    const int64_t row_limit = MODE == MODE_MGROUP ? T.out_limit : p.M;
+    const int64_t row_shift = MODE == MODE_MGROUP ? T.out_shift : 0;
     constexpr int ES = OUT_BF16 ? 2 : 4;
     constexpr int ROW_BYTES = C::WN * ES;
     constexpr int CPR = ROW_BYTES / 16;                      // 16-byte chunks per row
@@ -471,7 +485,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm(GemmArgs p) {
           // back. Split partials too: re-read once by the reduction, they cost that
           // reduction a little but left dirty they slowed the casts that follow more
           // (MoE step 1.42-1.45 -> 1.36-1.38 ms, against plain stores on one box).
-          if (row < row_limit) __builtin_nontemporal_store(d, (u32x4*)(T.out_base + (row * p.ldo + wcol0) * ES + ch * 16));
+          if (row < row_limit)
+            __builtin_nontemporal_store(d, (u32x4*)(T.out_base + ((row + row_shift) * p.ldo + wcol0) * ES + ch * 16));
         }
       }
     } else {
@@ -479,7 +494,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm(GemmArgs p) {
       for (int i = 0; i < C::TM; ++i) {
         const int64_t row = wrow0 + 32 * i + (l & 31);
         if (row >= row_limit) continue;
-        uint8_t* dst_row = T.out_base + (row * p.ldo + wcol0 + 4 * h) * ES;
+        uint8_t* dst_row = T.out_base + ((row + row_shift) * p.ldo + wcol0 + 4 * h) * ES;
         const int cols_left = (int)(p.N - wcol0 - 4 * h);  // valid columns from this lane's first
 #pragma unroll
         for (int j = 0; j < C::TN; ++j)
@@ -675,10 +690,10 @@ hipError_t launch(mx::GemmArgs& p, int out_bf16, hipStream_t stream) {
 
 // M-grouped: C[m x n] = A[m x k] . B_g[n x k]^T per row group (forward and dgrad).
 hipError_t mx_launch_gemm_mgroup(const uint8_t* a, const uint8_t* a_s, const uint8_t* b, const uint8_t* b_s,
-                                 const int32_t* offs, int groups, int64_t m, int64_t n, int64_t k, void* out,
-                                 int out_bf16, hipStream_t stream) {
+                                 const int32_t* offs, const int32_t* offs_out, int groups, int64_t m, int64_t n,
+                                 int64_t k, void* out, int out_bf16, hipStream_t stream) {
   mx::GemmArgs p{};
-  p.a = a; p.a_s = a_s; p.b = b; p.b_s = b_s; p.offs = offs; p.out = out;
+  p.a = a; p.a_s = a_s; p.b = b; p.b_s = b_s; p.offs = offs; p.offs_out = offs_out; p.out = out;
   p.lda = k; p.ldb = k;
   p.a_rows = m; p.b_rows = (int64_t)groups * n;
   p.a_ktiles = p.b_ktiles = mx::scale_tiles_k(k / 32);
@@ -703,7 +718,8 @@ hipError_t mx_launch_gemm_kgroup(const uint8_t* a, const uint8_t* a_s, const uin
 
 // bf16 operands, no scales: the same two cores with pitches of 2 bytes per element.
 hipError_t mx_launch_gemm_bf16_mgroup(const uint16_t* a, const uint16_t* b, const int32_t* offs, int groups,
-                                      int64_t m, int64_t n, int64_t k, void* out, int out_bf16, hipStream_t stream) {
+                                      int64_t m, int64_t n, int64_t k, void* out, int out_bf16,
+                                      hipStream_t stream) {
   mx::GemmArgs p{};
   p.a = (const uint8_t*)a; p.b = (const uint8_t*)b; p.offs = offs; p.out = out;
   p.lda = 2 * k; p.ldb = 2 * k;

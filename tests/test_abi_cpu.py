@@ -198,3 +198,21 @@ def test_backward_arm_calls_validation(lib):
     assert lib.mx_grouped_mm_bf16_dgrad(P, P, P2, 3, 100, 36, 64, P2, 0, None) == MX_E_SHAPE  # n % 8
     assert lib.mx_grouped_mm_bf16_wgrad(P, P, P2, 3, 100, 36, 64, P2, 0, None) == MX_E_SHAPE  # m % 8
     assert lib.mx_grouped_mm_bf16_wgrad(P, P, P2, 3, 104, 36, 64, P2, 0, None) in (MX_E_DEVICE, 0)
+
+
+def test_fused_padding_calls_validation(lib):
+    f = lib.mx_pad_quantize_dim0_dim1
+    assert f(P, 40, 64, 64, P2, 3, 256, P2, P2, P2, P2, P2, None) in (MX_E_DEVICE, 0)
+    assert f(P, 40, 48, 64, P2, 3, 256, P2, P2, P2, P2, P2, None) == MX_E_SHAPE  # cols % 32
+    assert f(P, 40, 64, 64, P2, 3, 224, P2, P2, P2, P2, P2, None) == MX_E_SHAPE  # rows_pad below the bound
+    assert f(P, 40, 64, 64, P2, 3, 256, P2, P2, None, P2, P2, None) == MX_E_NULL  # q_t
+    assert f(P, 40, 64, 64, P2, 3, 256, P2, P2, P2, P2, None, None) == MX_E_NULL  # offs_pad
+    g = lib.mx_grouped_mm_fwd_padded
+    assert g(P, P, P, P, P2, P2, 3, 256, 40, 64, 64, P2, 0, None) in (MX_E_DEVICE, 0)
+    assert g(P, P, P, P, None, P2, 3, 256, 40, 64, 64, P2, 0, None) == MX_E_NULL  # offs_pad
+    assert g(P, P, P, P, P2, None, 3, 256, 40, 64, 64, P2, 0, None) == MX_E_NULL  # offs
+    assert g(P, P, P, P, P2, P2, 3, 256, 300, 64, 64, P2, 0, None) == MX_E_SHAPE  # m > m_pad
+    assert g(P, P, P, P, P2, P2, 3, 256, 40, 40, 64, P2, 0, None) == MX_E_SHAPE  # grouped n % 32
+    d = lib.mx_grouped_mm_dgrad_padded
+    assert d(P, P, P, P, P2, P2, 3, 256, 40, 64, 64, P2, 0, None) in (MX_E_DEVICE, 0)
+    assert d(P, P, P, P, P2, P2, 3, 256, 40, 48, 64, P2, 0, None) == MX_E_SHAPE  # contraction n % 32

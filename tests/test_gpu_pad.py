@@ -204,3 +204,76 @@ def test_gemm_rows_past_last_group(oracle):
                                 dev_u8(oracle.scales_to_physical(x_ts)), dev_i32(offs), m, n, k, groups=G,
                                 out_dtype=mx.MX_OUT_F32)
     assert np.array_equal(host(dw), oracle.mx_grouped_mm_wgrad(dy_t, dy_ts, x_t, x_ts, offs, G).astype(np.float32))
+
+
+FUSED_CASES = [
+    (600, 256, 256, [100, 0, 37, 200, 263]),
+    (70, 288, 320, [33, 32]),  # rows past the last group; pitch wider than the row
+    (0, 64, 64, [0, 0]),
+    (1000, 96, 96, random_sizes(np.random.default_rng(6), 1000, 6, 1).tolist()),
+    (3000, 128, 128, _many_groups()),
+]
+
+
+@pytest.mark.parametrize("rows,cols,ld,sizes", FUSED_CASES, ids=[f"r{c[0]}c{c[1]}g{len(c[3])}" for c in FUSED_CASES])
+def test_pad_quantize_matches_oracle(oracle, rows, cols, ld, sizes):
+    """The padded one-pass cast equals the oracle's padding followed by its casts:
+    codes, physical scale bytes (pads included) and padded offsets, bit for bit."""
+    rng = np.random.default_rng(rows + cols + 11)
+    offs = offs_of(sizes)
+    G = len(sizes)
+    x_full = synth.normal_bf16(rng, (rows, ld), 1.0) if rows else np.zeros((0, ld), np.uint16)
+    x = x_full[:, :cols]
+    rows_pad = mx.mx_padded_rows(rows, G)
+    say(f"[pad+cast] rows={rows} cols={cols} G={G} rows_pad={rows_pad}")
+    q, s, qt, st, offs_pad = mx.mx_pad_quantize_dim0_dim1(dev_bf16(x_full)[:, :cols], dev_i32(offs))
+    x_pad, ref_offs = oracle.pad_token_groups(x, offs.tolist(), rows_pad)
+    assert host(offs_pad).tolist() == ref_offs
+    oq, os_ = oracle.quantize_dim0(x_pad)
+    oqt, ost = oracle.quantize_dim1(x_pad)
+    assert np.array_equal(host(q), oq)
+    assert np.array_equal(host(qt), oqt)
+    assert np.array_equal(host(s), oracle.scales_to_physical(os_))
+    assert np.array_equal(host(st), oracle.scales_to_physical(ost))
+
+
+@pytest.mark.parametrize("M,N,K,sizes", [
+    (600, 192, 256, [100, 0, 37, 200, 263]),
+    (1000, 128, 576, random_sizes(np.random.default_rng(3), 1000, 6, 1).tolist()),
+    (700, 96, 128, [64, 0, 600]),  # 36 rows past the last group stay untouched
+])
+def test_padded_gemm_outputs(oracle, M, N, K, sizes):
+    """fwd / dgrad on padded rows writing unpadded outputs equal the unpadded
+    oracle results; rows past the last group are not written."""
+    rng = np.random.default_rng(M + K + 5)
+    G = len(sizes)
+    offs = offs_of(sizes)
+    x = synth.normal_bf16(rng, (M, K), 1.0)
+    w = synth.normal_bf16(rng, (G, N, K), 0.02)
+    dy = synth.normal_bf16(rng, (M, N), 1e-2)
+    rows_pad = mx.mx_padded_rows(M, G)
+    say(f"[padded gemm] M={M} N={N} K={K} sizes={sizes}")
+    doffs = dev_i32(offs)
+    xq, xs, _, _, offs_pad = mx.mx_pad_quantize_dim0_dim1(dev_bf16(x), doffs)
+    dyq, dys, _, _, _ = mx.mx_pad_quantize_dim0_dim1(dev_bf16(dy), doffs)
+    wq, ws = mx.mx_quantize_dim0(dev_bf16(w.reshape(G * N, K)))
+    wtq, wts = mx.mx_quantize_dim1(dev_bf16(w))
+    y = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda:0")
+    dx = torch.full((M, K), float("nan"), dtype=torch.float32, device="cuda:0")
+    mx.mx_grouped_mm_fwd_padded(xq, xs, wq, ws, offs_pad, doffs, rows_pad, M, N, K, out_dtype=mx.MX_OUT_F32, out=y)
+    mx.mx_grouped_mm_dgrad_padded(dyq, dys, wtq, wts, offs_pad, doffs, rows_pad, M, N, K, out_dtype=mx.MX_OUT_F32,
+                                  out=dx)
+    grouped = int(offs[-1])
+    oxq, oxs = oracle.quantize_dim0(x)
+    owq, ows = oracle.quantize_dim0(w.reshape(G * N, K))
+    ref_y = oracle.mx_grouped_mm_fwd(oxq, oxs, owq, ows, offs, G)
+    abs_y = oracle.grouped_mm(np.abs(oracle.dequantize(oxq, oxs)), np.abs(oracle.dequantize(owq, ows)), offs, G)
+    gy, gdx = host(y), host(dx)
+    check_f32(oracle, gy[:grouped], ref_y[:grouped], "fwd padded->unpadded", abs_y[:grouped], K)
+    odyq, odys = oracle.quantize_dim0(dy)
+    parts = [oracle.quantize_dim1(w[g]) for g in range(G)]
+    owt, owts = np.concatenate([p[0] for p in parts]), np.concatenate([p[1] for p in parts])
+    ref_dx = oracle.mx_grouped_mm_fwd(odyq, odys, owt, owts, offs, G)
+    abs_dx = oracle.grouped_mm(np.abs(oracle.dequantize(odyq, odys)), np.abs(oracle.dequantize(owt, owts)), offs, G)
+    check_f32(oracle, gdx[:grouped], ref_dx[:grouped], "dgrad padded->unpadded", abs_dx[:grouped], N)
+    assert np.all(np.isnan(gy[grouped:])) and np.all(np.isnan(gdx[grouped:]))
