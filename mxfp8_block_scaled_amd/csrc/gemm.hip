@@ -63,20 +63,23 @@ struct GemmArgs {
 
 // Block tile BM x BN over a WGM x WGN grid of waves, each wave (BM/WGM) x (BN/WGN)
 // in 32x32 MFMA tiles; the contraction advances 64 elements (one MFMA k-step) per
-// pipeline stage.
-template <int BM, int BN, int WGM, int WGN>
+// pipeline stage, over a ring of NST stages in LDS.
+template <int BM, int BN, int WGM, int WGN, int NST_>
 struct Cfg {
   static constexpr int WAVES = WGM * WGN;
   static constexpr int THREADS = 64 * WAVES;
   static constexpr int BK = 64;
-  static constexpr int NST = 4;  // LDS ring depth: stages in flight
+  static constexpr int NST = NST_;  // LDS ring depth: NST - 1 stages are loaded ahead
   static constexpr int WM = BM / WGM, WN = BN / WGN;
   static constexpr int TM = WM / 32, TN = WN / 32;
   static constexpr int A_BYTES = BM * BK, B_BYTES = BN * BK;
   static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
-  // scale tiles of one 256-wide window: A bands then B bands, 256 B each; two
-  // windows are resident (the one in use and the next)
-  static constexpr int BANDS = (BM + BN) / 32;
+  // scale tiles of one 256-wide window: A's bands, then B's, 256 B each, each side
+  // in a whole number of 1 KB slots (four bands; a slot past the side's last band
+  // holds scales of rows outside the tile, never read); two windows are resident
+  // (the one in use and the next)
+  static constexpr int A_SLOTS = (BM / 32 + 3) / 4 * 4, B_SLOTS = (BN / 32 + 3) / 4 * 4;
+  static constexpr int BANDS = A_SLOTS + B_SLOTS;
   static constexpr int SC_BYTES = WAVES * 1024;  // 1 KB per wave; waves past BANDS/4 fill theirs with zeros
   static constexpr int LDS_BYTES = NST * STAGE_BYTES + 2 * SC_BYTES;
   // per wave and stage: its share of A and B rows in 1 KB loads (16 rows x 64 B);
@@ -87,13 +90,21 @@ struct Cfg {
   static constexpr int AB_LOADS = A_LOADS + B_LOADS;
   static constexpr int SC_WAVES = BANDS / 4;
   static constexpr int HALF_MFMAS = TM / 2 * TN;
-  static_assert(BM == BN && BANDS % 8 == 0 && SC_WAVES <= WAVES && A_ROWS_W % 16 == 0, "tile shape");
-  static_assert(TM % 2 == 0 && 2 * AB_LOADS + 2 < 64, "");
+  static_assert(SC_WAVES <= WAVES && A_ROWS_W % 16 == 0 && B_ROWS_W % 16 == 0, "tile shape");
+  static_assert(TM % 2 == 0 && 2 * AB_LOADS + 2 < 64 && NST >= 2 && NST <= 4, "");
 };
 
 // LDS holds each 64-byte row (four 16-byte chunks of one k-step) with chunk c of
 // row r at slot c ^ ((r >> 2) & 3): sixteen consecutive rows reading the same chunk
 // then hit sixteen different 16-byte bank groups.
+
+// Rows per epilogue staging pass: the largest multiple of 32 that divides the wave's
+// rows `wm` and fits `cap` rows of staging.
+constexpr int epi_rows(int wm, int cap) {
+  int r = wm;
+  while (r > 32 && (r > cap || wm % r != 0)) r -= 32;
+  return r;
+}
 
 __device__ inline int32_t group_start(const int32_t* offs, int g) { return g == 0 ? 0 : offs[g - 1]; }
 
@@ -224,9 +235,11 @@ __device__ inline int64_t xcd_remap(int64_t bid, int64_t nblk) {
   return bid < per_xcd * 8 ? (bid % 8) * per_xcd + bid / 8 : bid;
 }
 
-template <int BM, int BN, int WGM, int WGN, int MODE, int OUT_BF16, int EL>
-__global__ __launch_bounds__(64 * WGM * WGN) void k_gemm(GemmArgs p) {
-  using C = Cfg<BM, BN, WGM, WGN>;
+// WPE: waves per SIMD the register allocation must allow (2 where two blocks
+// share a compute unit).
+template <int BM, int BN, int WGM, int WGN, int NST_, int WPE, int MODE, int OUT_BF16, int EL>
+__global__ __launch_bounds__(64 * WGM * WGN) __attribute__((amdgpu_waves_per_eu(WPE))) void k_gemm(GemmArgs p) {
+  using C = Cfg<BM, BN, WGM, WGN, NST_>;
   constexpr int NST = C::NST, BK = C::BK;
   constexpr bool SCALED = EL == EL_MXFP8;
   constexpr int MPK = SCALED ? 1 : 2;  // MFMAs per 32x32 tile and 64-byte k-step
@@ -259,7 +272,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm(GemmArgs p) {
   const unsigned a_off0 = (unsigned)(a_row_l * p.lda + kc_l * 16), a_offq = (unsigned)(16 * p.lda);
   const unsigned b_off0 = (unsigned)(b_row_l * p.ldb + kc_l * 16), b_offq = (unsigned)(16 * p.ldb);
   const int sc_band = wave * 4 + (l >> 4);  // index in the A-then-B band list
-  const bool sc_is_a = wave < C::SC_WAVES / 2;  // square tiles: the first half of the list is A's
+  const bool sc_is_a = wave < C::A_SLOTS / 4;  // A's slots come first, whole waves each
 
   // contraction steps of BK from the 256-aligned position at or below k_beg (a scale
   // window boundary: every fourth stage opens a window; stages before k_beg are
@@ -277,7 +290,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm(GemmArgs p) {
       (void*)(p.a + T.a_row0 * p.lda), (short)0, (int)(a_valid * p.lda), 0x00020000);
   const __amdgpu_buffer_rsrc_t b_rsrc = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(p.b + T.b_row0 * p.ldb), (short)0, (int)(b_valid * p.ldb), 0x00020000);
-  const int64_t sc_row_band = sc_is_a ? T.a_row0 / 32 + sc_band : T.b_row0 / 32 + (sc_band - BM / 32);
+  const int64_t sc_row_band = sc_is_a ? T.a_row0 / 32 + sc_band : T.b_row0 / 32 + (sc_band - C::A_SLOTS);
   const int64_t sc_ktiles = sc_is_a ? p.a_ktiles : p.b_ktiles;
   const unsigned sc_off = wave < C::SC_WAVES && sc_row_band < (sc_is_a ? a_bands : b_bands)
                               ? (unsigned)(sc_row_band * sc_ktiles * 256 + (l & 15) * 16)
@@ -292,7 +305,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm(GemmArgs p) {
   // pass s % 4 as a compile-time constant where they can (the unrolled steps)
   auto issue_stage = [&](int64_t s_idx, int s_mod4, bool live) {
     const int64_t k0 = k_first + s_idx * BK;
-    uint8_t* st = lds + (int)(s_idx % NST) * C::STAGE_BYTES;
+    uint8_t* st = lds + ((int)s_idx % NST) * C::STAGE_BYTES;
     const int kk = (int)k0 + kc_l * 16;
     // this lane's chunk is masked; in bf16 a group edge may fall inside a 16-byte
     // chunk (8 tokens): such chunks are loaded and their outside elements zeroed in
@@ -348,7 +361,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm(GemmArgs p) {
       u32x4 lo = *(const u32x4*)(lb + j * 2048 + off_lo);
       u32x4 hi = *(const u32x4*)(lb + j * 2048 + off_hi);
       f.b[j] = (v8i){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-      if (SCALED) f.sb[j] = *(const unsigned*)(sc + (BM / 32 + wn * C::TN + j) * 256 + 4 * l) >> sh;
+      if (SCALED) f.sb[j] = *(const unsigned*)(sc + (C::A_SLOTS + wn * C::TN + j) * 256 + 4 * l) >> sh;
     }
 #pragma unroll
     for (int i = 0; i < C::TM; ++i) {
@@ -402,8 +415,10 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm(GemmArgs p) {
   // (at most NST-2 later stages stay in flight), meets the other waves at a barrier
   // (so stage it+1 is complete in LDS and every wave is past stage it-1, whose slot
   // the next issue overwrites), then reads stage it+1's fragments interleaved with
-  // the second half of stage it's MFMAs.
-  auto step = [&](int64_t it, int slot, const Frag& cur, Frag& nxt, auto masked) {
+  // the second half of stage it's MFMAs. `s4` is it % 4 (a constant in the unrolled
+  // loop): it places the scale windows, and the ring slots for NST 2 and 4.
+  auto step = [&](int64_t it, int s4, const Frag& cur, Frag& nxt, auto masked) {
+    const int slot = s4;
     issue_stage(it + NST - 1, (slot + NST - 1) & 3, it + NST - 1 < n_iter);
     mfma_rows(cur, 0, C::TM / 2);
     // spread the loads over the MFMAs so no load waits in front of an idle matrix core
@@ -417,7 +432,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm(GemmArgs p) {
     wait_n(loads_after((slot + 1) & 3, NST - 2));
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    read_frags(nxt, (slot + 1) % NST, k_first + (it + 1) * BK, masked);
+    read_frags(nxt, NST == 3 ? (int)(it + 1) % 3 : (slot + 1) % NST, k_first + (it + 1) * BK, masked);
     mfma_rows(cur, C::TM / 2, C::TM);
     // interleave: one MFMA, then a share of the LDS reads
 #pragma unroll
@@ -443,9 +458,10 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm(GemmArgs p) {
     constexpr int ROW_BYTES = C::WN * ES;
     constexpr int CPR = ROW_BYTES / 16;                      // 16-byte chunks per row
     constexpr int EPI_BYTES = NST * C::STAGE_BYTES / C::WAVES;  // staging bytes per wave
-    constexpr int RP = EPI_BYTES / ROW_BYTES < C::WM ? EPI_BYTES / ROW_BYTES : C::WM;  // rows per pass
+    constexpr int RP = epi_rows(C::WM, EPI_BYTES / ROW_BYTES);  // rows per pass
     constexpr int RPI = 64 / CPR;                            // rows per 16-byte read / store
-    static_assert(RP % 32 == 0 && RP % RPI == 0 && C::WM % RP == 0, "epilogue staging shape");
+    static_assert((CPR & (CPR - 1)) == 0 && CPR <= 64, "rows of whole power-of-two 16-byte chunks");
+    static_assert(RP * ROW_BYTES <= EPI_BYTES && RP % RPI == 0 && C::WM % RP == 0, "epilogue staging shape");
     const int64_t wrow0 = T.a_row0 + wm * C::WM;
     const int64_t wcol0 = T.col0 + wn * C::WN;
     if (((p.ldo * ES) & 15) == 0 && wcol0 + C::WN <= p.N) {
@@ -524,19 +540,20 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm(GemmArgs p) {
     for (int s = 0; s < NST - 1; ++s) issue_stage(s, s & 3, s < n_iter);
     wait_n(loads_after(0, NST - 2));
     __builtin_amdgcn_s_barrier();
-    // The main loop is unrolled by the ring depth, so ring slots are compile-time
+    // The main loop is unrolled by four (one 256-wide scale window), so window
+    // boundaries, and the ring slots of a 2- or 4-deep ring, are compile-time
     // constants, and alternates two register sets, so no fragment is ever copied.
     Frag f0, f1;
     read_frags(f0, 0, k_first, masked);
     int64_t it = 0;
-    for (; it + NST <= n_iter; it += NST) {
+    for (; it + 4 <= n_iter; it += 4) {
       step(it, 0, f0, f1, masked);
       step(it + 1, 1, f1, f0, masked);
       step(it + 2, 2, f0, f1, masked);
       step(it + 3, 3, f1, f0, masked);
     }
     for (; it < n_iter; ++it) {  // 0 to 3 remaining steps
-      step(it, (int)(it % NST), f0, f1, masked);
+      step(it, (int)(it & 3), f0, f1, masked);
       f0 = f1;
     }
     MX_WAIT_VMCNT(0);  // every load has landed
@@ -560,11 +577,10 @@ namespace {
 
 constexpr int64_t kComputeUnits = 256;
 
-// Tile configurations: 256x256 for large problems; 128x128 where 256x256 tiles
-// would leave most compute units idle.
-template <int BM, int BN, int WGM, int WGN, int MODE, int EL>
+// Launches one tile configuration over the whole problem (p.splits already set).
+template <int BM, int BN, int WGM, int WGN, int NST, int WPE, int MODE, int EL>
 hipError_t launch_cfg(mx::GemmArgs p, int out_bf16, hipStream_t stream) {
-  using C = mx::Cfg<BM, BN, WGM, WGN>;
+  using C = mx::Cfg<BM, BN, WGM, WGN, NST>;
   const int64_t mt_extra = (MODE == mx::MODE_MGROUP && p.offs) ? p.groups : 0;
   p.mt_total = (p.M + BM - 1) / BM + mt_extra;
   p.nt = (p.N + BN - 1) / BN;
@@ -573,22 +589,19 @@ hipError_t launch_cfg(mx::GemmArgs p, int out_bf16, hipStream_t stream) {
   const int64_t blocks = p.tiles;
   const size_t lds = (size_t)C::LDS_BYTES;
   static bool attr_set[2] = {false, false};
-  hipError_t e = hipSuccess;
-  if (out_bf16) {
-    if (!attr_set[1])
-      e = hipFuncSetAttribute((const void*)mx::k_gemm<BM, BN, WGM, WGN, MODE, 1, EL>,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  const void* fn = out_bf16 ? (const void*)mx::k_gemm<BM, BN, WGM, WGN, NST, WPE, MODE, 1, EL>
+                            : (const void*)mx::k_gemm<BM, BN, WGM, WGN, NST, WPE, MODE, 0, EL>;
+  if (!attr_set[out_bf16 ? 1 : 0]) {
+    const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    attr_set[1] = true;
-    hipLaunchKernelGGL((mx::k_gemm<BM, BN, WGM, WGN, MODE, 1, EL>), dim3((unsigned)blocks), dim3(C::THREADS), lds, stream, p);
-  } else {
-    if (!attr_set[0])
-      e = hipFuncSetAttribute((const void*)mx::k_gemm<BM, BN, WGM, WGN, MODE, 0, EL>,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    attr_set[0] = true;
-    hipLaunchKernelGGL((mx::k_gemm<BM, BN, WGM, WGN, MODE, 0, EL>), dim3((unsigned)blocks), dim3(C::THREADS), lds, stream, p);
+    attr_set[out_bf16 ? 1 : 0] = true;
   }
+  if (out_bf16)
+    hipLaunchKernelGGL((mx::k_gemm<BM, BN, WGM, WGN, NST, WPE, MODE, 1, EL>), dim3((unsigned)blocks),
+                       dim3(C::THREADS), lds, stream, p);
+  else
+    hipLaunchKernelGGL((mx::k_gemm<BM, BN, WGM, WGN, NST, WPE, MODE, 0, EL>), dim3((unsigned)blocks),
+                       dim3(C::THREADS), lds, stream, p);
   return hipGetLastError();
 }
 
@@ -656,6 +669,52 @@ int choose_splits(const mx::GemmArgs& p, int64_t elem_bytes) {
   return s >= 2 ? (int)s : 1;
 }
 
+// Tile configurations (block tile, wave grid, ring depth, blocks per compute unit):
+enum Tiling {
+  TILE_256 = 0,      // 256x256, 2x2 waves of 128x128, 4-deep ring, 136 KB LDS: one block per CU
+  TILE_128 = 1,      // 128x128, 2x2 waves of 64x64, 4-deep ring, 68 KB: two blocks per CU
+  TILE_128x256 = 2,  // 128x256, 2x2 waves of 64x128, 3-deep ring, 80 KB: two blocks per CU
+  TILE_192x256 = 3,  // 192x256, 1x4 waves of 192x64, 4-deep ring, 120 KB: one block per CU
+  TILE_256_8W = 4,   // 256x256, 2x4 waves of 128x64, 4-deep ring, 144 KB: one block, two waves per SIMD
+};
+
+template <int MODE, int EL>
+hipError_t launch_tiling(int tiling, const mx::GemmArgs& p, int out_bf16, hipStream_t stream) {
+  switch (tiling) {
+    case TILE_128: return launch_cfg<128, 128, 2, 2, 4, 2, MODE, EL>(p, out_bf16, stream);
+    case TILE_128x256: return launch_cfg<128, 256, 2, 2, 3, 2, MODE, EL>(p, out_bf16, stream);
+    case TILE_192x256: return launch_cfg<192, 256, 1, 4, 4, 1, MODE, EL>(p, out_bf16, stream);
+    case TILE_256_8W: return launch_cfg<256, 256, 2, 4, 4, 2, MODE, EL>(p, out_bf16, stream);
+    default: return launch_cfg<256, 256, 2, 2, 4, 1, MODE, EL>(p, out_bf16, stream);
+  }
+}
+
+// The tiling for a problem (p.splits set). Measured on the MoE training step's
+// GEMMs (G=8, M=16384, K=N=4096, and a dense 576-wide layer); every tiling gives
+// bit-identical results, since each output element sums its k-steps in the same
+// order.
+template <int MODE>
+int choose_tiling(const mx::GemmArgs& p) {
+  const int64_t groups_tiles = MODE == mx::MODE_KGROUP ? (int64_t)p.groups * p.splits : 1;
+  const int64_t big_tiles = groups_tiles * ((p.M + 255) / 256) * ((p.N + 255) / 256);
+  // few output tiles: quarter-size tiles spread the work over more compute units
+  if (big_tiles < 128) return TILE_128;
+  // a short contraction (a few k-steps per tile): the output stores dominate, and two
+  // blocks per compute unit overlap one block's stores with the other's loop
+  // (16384x4096 output over K=576: 51 us against 62 us for 256x256 tiles)
+  if (MODE == mx::MODE_MGROUP && p.K <= 1024) return TILE_128x256;
+  // K-grouped output rows that 192-row tiles cover with less padding than 256-row
+  // ones (576 rows: 53 us against 59 us)
+  if (MODE == mx::MODE_KGROUP && (p.M + 191) / 192 * 192 < (p.M + 255) / 256 * 256) return TILE_192x256;
+  // M-grouped with many tiles (the grouped forward and dgrad): one wave per SIMD
+  // (inside the training step 278-294 us against 295-304 us with two)
+  if (MODE == mx::MODE_MGROUP && big_tiles >= 512) return TILE_256;
+  // otherwise two waves per SIMD hide each tile's prologue and epilogue better: the
+  // grouped wgrad (MXFP8 306-308 us against 308-317 us; bf16 531 us against 620 us)
+  // and the 576-wide forward's single round of tiles (57 us against 63-67 us)
+  return TILE_256_8W;
+}
+
 template <int MODE, int EL>
 hipError_t launch(mx::GemmArgs& p, int out_bf16, hipStream_t stream) {
   p.splits = 1;
@@ -671,7 +730,7 @@ hipError_t launch(mx::GemmArgs& p, int out_bf16, hipStream_t stream) {
       q.splits = splits;
       q.split_stride = stride;
       q.out = ws;
-      e = launch_cfg<256, 256, 2, 2, MODE, EL>(q, 0, stream);
+      e = launch_tiling<MODE, EL>(choose_tiling<MODE>(q), q, 0, stream);
       if (e != hipSuccess) return e;
       const int64_t blocks = std::min<int64_t>((n_out + 1023) / 1024, 4096);
       hipLaunchKernelGGL(k_split_reduce, dim3((unsigned)std::max<int64_t>(blocks, 1)), dim3(256), 0, stream, ws,
@@ -679,12 +738,7 @@ hipError_t launch(mx::GemmArgs& p, int out_bf16, hipStream_t stream) {
       return hipGetLastError();
     }
   }
-  const int64_t groups_tiles = MODE == mx::MODE_KGROUP ? p.groups : 1;
-  const int64_t big_tiles = groups_tiles * ((p.M + 255) / 256) * ((p.N + 255) / 256);
-  // 2 x 2 waves of 128 x 128 (256 accumulators each, one wave per SIMD); 8-wave
-  // grids of 128 x 64 per wave (two per SIMD) measured the same on the MoE shapes
-  if (big_tiles >= 512) return launch_cfg<256, 256, 2, 2, MODE, EL>(p, out_bf16, stream);
-  return launch_cfg<128, 128, 2, 2, MODE, EL>(p, out_bf16, stream);
+  return launch_tiling<MODE, EL>(choose_tiling<MODE>(p), p, out_bf16, stream);
 }
 }  // namespace
 

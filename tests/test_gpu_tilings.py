@@ -1,0 +1,153 @@
+"""GPU parity of every GEMM tile configuration, full outputs against the oracle.
+
+The library picks a tiling from the problem's shape; each case here is shaped to
+select one of them, with groups that end inside tiles (MXFP8 groups on 32-row
+boundaries, as the calls require; bf16 groups anywhere), one group empty, and
+partial tiles on both output edges:
+  * 256x256 with eight waves (two per SIMD): K-grouped with >= 128 tiles of 256x256,
+    and M-grouped with 128..511 such tiles over a contraction above 1024;
+  * 128x256 over a three-deep ring, two blocks per compute unit: M-grouped with a
+    contraction of at most 1024 and >= 128 tiles;
+  * 192x256: K-grouped outputs whose rows 192-row tiles cover with less padding
+    than 256-row ones, without and with split contractions.
+The 128x128 and four-wave 256x256 tilings are covered by the small-shape and
+full-size tests.
+"""
+
+import numpy as np
+import pytest
+
+import mxfp8_block_scaled_amd as mx
+from mxfp8_block_scaled_amd import synth
+
+from gemm_check import check_bf16, check_f32
+from gpu_util import dev_bf16, dev_i32, host, require_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    require_gpu()
+
+
+def fwd_case(oracle, m, n, k, sizes, seed, name):
+    """M-grouped forward, fp32 and bf16 outputs, against the oracle's product of the
+    oracle's own casts (the casts are bit-exact, tested elsewhere)."""
+    rng = np.random.default_rng(seed)
+    G = len(sizes)
+    offs = synth.offs_from_sizes(np.array(sizes))
+    x = synth.normal_bf16(rng, (m, k), 1.0)
+    w = synth.normal_bf16(rng, (G * n, k), 0.02)
+    say(f"[tiling {name}] fwd m={m} n={n} k={k} offs={offs.tolist()}")
+    xq, xs = mx.mx_quantize_dim0(dev_bf16(x))
+    wq, ws = mx.mx_quantize_dim0(dev_bf16(w))
+    doffs = dev_i32(offs)
+    got = host(mx.mx_grouped_mm_fwd(xq, xs, wq, ws, doffs, m, n, k, out_dtype=mx.MX_OUT_F32))
+    got16 = host(mx.mx_grouped_mm_fwd(xq, xs, wq, ws, doffs, m, n, k, out_dtype=mx.MX_OUT_BF16))
+    oxq, oxs = oracle.quantize_dim0(x)
+    owq, ows = oracle.quantize_dim0(w)
+    da, db = oracle.dequantize(oxq, oxs), oracle.dequantize(owq, ows)
+    ref = oracle.grouped_mm(da, db, offs, G)
+    absp = oracle.grouped_mm(np.abs(da), np.abs(db), offs, G)
+    check_f32(oracle, got, ref, f"{name} fwd f32", absp, k)
+    check_bf16(oracle, got16, ref, absp, k, f"{name} fwd bf16")
+    return offs, rng
+
+
+def wgrad_case(oracle, n, k, m, sizes, seed, name):
+    """K-grouped wgrad (dw[g] = dy_t[:, rows_g] . x_t[:, rows_g]^T), fp32 and bf16."""
+    rng = np.random.default_rng(seed)
+    G = len(sizes)
+    offs = synth.offs_from_sizes(np.array(sizes))
+    dy = synth.normal_bf16(rng, (m, n), 1e-2)
+    x = synth.normal_bf16(rng, (m, k), 1.0)
+    say(f"[tiling {name}] wgrad n={n} k={k} m={m} offs={offs.tolist()}")
+    dytq, dyts = mx.mx_quantize_dim1(dev_bf16(dy))
+    xtq, xts = mx.mx_quantize_dim1(dev_bf16(x))
+    doffs = dev_i32(offs)
+    got = host(mx.mx_grouped_mm_wgrad(dytq, dyts, xtq, xts, doffs, m, n, k, out_dtype=mx.MX_OUT_F32))
+    got16 = host(mx.mx_grouped_mm_wgrad(dytq, dyts, xtq, xts, doffs, m, n, k, out_dtype=mx.MX_OUT_BF16))
+    odyt, odyts = oracle.quantize_dim1(dy)
+    oxt, oxts = oracle.quantize_dim1(x)
+    da, db = oracle.dequantize(odyt, odyts), oracle.dequantize(oxt, oxts)
+    ref = oracle.grouped_mm_wgrad(da, db, offs, G)
+    absw = oracle.grouped_mm_wgrad(np.abs(da), np.abs(db), offs, G)
+    kmax = int(np.max(sizes))
+    check_f32(oracle, got, ref, f"{name} wgrad f32", absw, kmax)
+    check_bf16(oracle, got16, ref, absw, kmax, f"{name} wgrad bf16")
+    for g in np.flatnonzero(np.array(sizes) == 0):
+        assert not got[g].any() and not got16[g].any(), f"empty group {g} must give zeros"
+
+
+def test_mgroup_eight_waves(oracle):
+    """16 x 8 = 128 tiles of 256x256 over K = 1280: the eight-wave tiling."""
+    fwd_case(oracle, 4000, 2016, 1280, [992, 0, 1504, 1504], 61, "8-wave")
+
+
+def test_mgroup_short_contraction(oracle):
+    """K = 576 with 128 tiles: 128x256 tiles, two blocks per compute unit; grouped and
+    dense, and the dgrad form (contraction over the 576 output columns of the forward)."""
+    fwd_case(oracle, 4000, 2016, 576, [992, 0, 1504, 1504], 62, "128x256 grouped")
+    fwd_case(oracle, 4000, 2016, 576, [4000], 63, "128x256 dense")
+    rng = np.random.default_rng(64)
+    m, n, k, sizes = 4000, 576, 2016, [1504, 992, 0, 1504]
+    G = len(sizes)
+    offs = synth.offs_from_sizes(np.array(sizes))
+    dy = synth.normal_bf16(rng, (m, n), 1e-2)
+    w_t = synth.normal_bf16(rng, (G * k, n), 0.02)
+    say(f"[tiling 128x256] dgrad m={m} n={n} k={k} offs={offs.tolist()}")
+    dyq, dys = mx.mx_quantize_dim0(dev_bf16(dy))
+    wtq, wts = mx.mx_quantize_dim0(dev_bf16(w_t))
+    got = host(mx.mx_grouped_mm_dgrad(dyq, dys, wtq, wts, dev_i32(offs), m, n, k, out_dtype=mx.MX_OUT_F32))
+    da = oracle.dequantize(*oracle.quantize_dim0(dy))
+    db = oracle.dequantize(*oracle.quantize_dim0(w_t))
+    ref = oracle.grouped_mm(da, db, offs, G)
+    check_f32(oracle, got, ref, "128x256 dgrad f32", oracle.grouped_mm(np.abs(da), np.abs(db), offs, G), n)
+
+
+def test_kgroup_eight_waves(oracle):
+    """992 x 1056 outputs per group, 8 groups (one empty): 4 x 5 x 8 = 160 tiles."""
+    wgrad_case(oracle, 992, 1056, 4096, [640, 512, 0, 736, 480, 576, 608, 544], 65, "8-wave")
+
+
+def test_kgroup_192_row_tiles(oracle):
+    """352-row outputs (two 192-row tiles, the second partial) x 2016 columns, 8 groups."""
+    wgrad_case(oracle, 352, 2016, 4096, [480, 0, 640, 512, 736, 544, 608, 576], 66, "192x256")
+
+
+def test_kgroup_192_row_tiles_split(oracle):
+    """576 x 1024 outputs over 16384 tokens in one group: 12 output tiles, so the
+    contraction is split 16 ways (192x256 tiles, fp32 partials summed in order)."""
+    wgrad_case(oracle, 576, 1024, 16384, [16384], 67, "192x256 split")
+
+
+@pytest.mark.parametrize("sizes", [[1001, 0, 1999, 1096], [4095, 0, 0, 1]])
+def test_bf16_tilings(oracle, sizes):
+    """bf16 operands through the eight-wave (forward K=1280; wgrad, 128 tiles so its
+    contraction splits two ways) and 128x256 (forward K=576) tilings; token groups end
+    off 8-element boundaries, so the wgrad masks group edges inside 16-byte chunks."""
+    rng = np.random.default_rng(sum(sizes))
+    G = len(sizes)
+    m = int(sum(sizes))
+    offs = synth.offs_from_sizes(np.array(sizes))
+    doffs = dev_i32(offs)
+    for n, k, name in ((2016, 1280, "8-wave"), (2016, 576, "128x256")):
+        a = synth.normal_bf16(rng, (m, k), 1.0)
+        b = synth.normal_bf16(rng, (G * n, k), 0.02)
+        say(f"[tiling bf16 {name}] fwd m={m} n={n} k={k} offs={offs.tolist()}")
+        got = host(mx.mx_grouped_mm_bf16_fwd(dev_bf16(a), dev_bf16(b), doffs, m, n, k, out_dtype=mx.MX_OUT_F32))
+        fa, fb = oracle.bf16_to_f64(a), oracle.bf16_to_f64(b)
+        check_f32(oracle, got, oracle.grouped_mm(fa, fb, offs, G), f"bf16 {name} fwd f32",
+                  oracle.grouped_mm(np.abs(fa), np.abs(fb), offs, G), k)
+    n, k = 1000, 2000
+    dy = synth.normal_bf16(rng, (m, n), 1e-2)
+    x = synth.normal_bf16(rng, (m, k), 1.0)
+    say(f"[tiling bf16 8-wave] wgrad n={n} k={k} m={m}")
+    dw = host(mx.mx_grouped_mm_bf16_wgrad(dev_bf16(np.ascontiguousarray(dy.T)), dev_bf16(np.ascontiguousarray(x.T)),
+                                          doffs, m, n, k, out_dtype=mx.MX_OUT_F32))
+    fdy, fx = oracle.bf16_to_f64(dy), oracle.bf16_to_f64(x)
+    check_f32(oracle, dw, oracle.grouped_mm_wgrad(fdy.T, fx.T, offs, G), "bf16 8-wave wgrad f32",
+              oracle.grouped_mm_wgrad(np.abs(fdy).T, np.abs(fx).T, offs, G), int(max(sizes)))
+    for g in np.flatnonzero(np.array(sizes) == 0):
+        assert not dw[g].any()
