@@ -208,7 +208,8 @@ __global__ __launch_bounds__(256) void k_quant_dim1(const uint16_t* __restrict__
 // ---------------------------------------------------------------------------------
 // dim0 + dim1 in one pass: a workgroup reads a 256-row x 256-column tile of one batch
 // once and writes both casts (4.0625 B per element instead of 2 x 3.03125).
-//   Wave w takes rows 64w..64w+63 as two 32-row sub-tiles; in a sub-tile lane l
+//   With four waves, wave w takes rows 64w..64w+63 as two 32-row sub-tiles in turn;
+//   with eight, wave w takes rows 32w..32w+31. In a sub-tile lane l
 //   reads 16-byte chunk (l % 32) of rows 16(l/32) + i, i = 0..15 (two rows x 512
 //   bytes per load instruction).
 //   dim0: as k_quant_dim0 (quad amax per row block, codes to q, the sub-tile's
@@ -230,21 +231,22 @@ struct RowGather {
   int32_t* offs_pad;    // padded group ends (written by workgroup 0)
 };
 
-template <bool FLOOR, bool GATHER>
-__global__ __launch_bounds__(256) void k_quant_both(const uint16_t* __restrict__ x, int64_t batch, int64_t rows,
+template <bool FLOOR, bool GATHER, int WV>
+__global__ __launch_bounds__(64 * WV) void k_quant_both(const uint16_t* __restrict__ x, int64_t batch, int64_t rows,
                                                     int64_t cols, int64_t ld, uint8_t* __restrict__ q,
                                                     uint8_t* __restrict__ scale, uint8_t* __restrict__ q_t,
                                                     uint8_t* __restrict__ scale_t, int64_t rtiles, int64_t ctiles,
                                                     RowGather gth) {
   __shared__ __attribute__((aligned(16))) uint8_t s_t[256 * 256];  // transposed codes
   __shared__ unsigned s_s1[8][64];                                 // dim1 scale tiles
-  __shared__ unsigned s_s0[4][64];                                 // dim0 scale tile per wave
+  __shared__ unsigned s_s0[WV][64];                                // dim0 scale tile per wave
+  constexpr int SUBS = 8 / WV;  // 32-row sub-tiles per wave, one after the other
   __shared__ std::conditional_t<GATHER, GroupTable, char> s_grp;  // the group table (gather only)
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, h = l >> 5, c = l & 31;
   if constexpr (GATHER) {
     build_table(s_grp, gth.offs, gth.groups, gth.src_rows);
     if (blockIdx.x == 0)
-      for (int g = tid; g < gth.groups; g += 256) gth.offs_pad[g] = s_grp.pad_end[g];
+      for (int g = tid; g < gth.groups; g += 64 * WV) gth.offs_pad[g] = s_grp.pad_end[g];
   }
   const int64_t kt0 = scale_tiles_k(cols / 32), kt1 = scale_tiles_k(rows / 32);
   const int64_t tiles = batch * rtiles * ctiles;
@@ -258,12 +260,11 @@ __global__ __launch_bounds__(256) void k_quant_both(const uint16_t* __restrict__
     const bool col_ok = col < cols;  // cols % 32 == 0: a quad's 32 columns are all in or all out
     const uint16_t* xb = x + b * rows * ld;
     const int64_t qrow0 = b * rows;  // dim0 rows of this batch in the stacked [batch*rows x cols]
-    s_s1[tid >> 5][tid & 31] = 0x7f7f7f7fu;  // pad blocks past the last row
-    s_s1[(tid >> 5)][32 + (tid & 31)] = 0x7f7f7f7fu;
+    for (int i = tid; i < 8 * 64; i += 64 * WV) s_s1[i >> 6][i & 63] = 0x7f7f7f7fu;  // pad blocks past the last row
     __syncthreads();
 #pragma unroll 1
-    for (int sub = 0; sub < 2; ++sub) {
-      const int kb = 2 * w + sub;               // dim1 block (32 rows) within the tile
+    for (int sub = 0; sub < SUBS; ++sub) {
+      const int kb = SUBS * w + sub;            // dim1 block (32 rows) within the tile
       const int64_t base = r0 + 32 * kb;        // first row of the sub-tile
       const bool rows_ok = base < rows;         // rows % 32 == 0: the sub-tile is all in or all out
       u32x4 v[16];
@@ -336,25 +337,25 @@ __global__ __launch_bounds__(256) void k_quant_both(const uint16_t* __restrict__
             if (FLOOR) d[m] = sat_e4m3x4(d[m]);
           }
           const int cc = 8 * c + 2 * p + e;      // column within the tile = row of s_t
-          const int k = (64 * w + 32 * sub + 16 * h) >> 4;  // 16-byte chunk: the lane's 16 rows
+          const int k = 2 * kb + h;  // 16-byte chunk: the lane's 16 rows
           *(u32x4*)(s_t + cc * 256 + ((k ^ ((cc >> 3) & 15)) << 4)) = (u32x4){d[0], d[1], d[2], d[3]};
           if (h == 0 && rows_ok) ss1[(cc >> 5) * 256 + scale_in_tile(cc & 31, kb)] = (uint8_t)byte;
         }
       }
     }
     __syncthreads();
-    // q_t rows c0 + 64w .. +63 (columns of the tile), four per instruction, 256 bytes each
+    // q_t rows c0 + (256/WV)w .. (columns of the tile), four per instruction, 256 bytes each
     uint8_t* qtb = q_t + b * cols * rows;
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      const int orow = 64 * w + 4 * k + (l >> 4), ch = l & 15;
+    for (int k = 0; k < 64 / WV; ++k) {
+      const int orow = 256 / WV * w + 4 * k + (l >> 4), ch = l & 15;
       const int64_t cidx = c0 + orow, rr = r0 + 16 * ch;
       const u32x4 d = *(const u32x4*)(s_t + orow * 256 + ((ch ^ ((orow >> 3) & 15)) << 4));
       if (cidx < cols && rr < rows) *(u32x4*)(qtb + cidx * rows + rr) = d;
     }
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int tile = 4 * j + w;  // dim1 scale tile (32 q_t rows) of this thread's dword
+    for (int j = 0; j < 8 / WV; ++j) {
+      const int tile = WV * j + w;  // dim1 scale tile (32 q_t rows) of this thread's dword
       const int64_t out_row0 = c0 + 32 * tile;
       if (out_row0 < cols)
         ((unsigned*)(scale_t + scale_tile_base((b * cols + out_row0) / 32, rt, kt1)))[l] = s_s1[tile][l];
@@ -516,38 +517,63 @@ hipError_t mx_launch_dim1(const uint16_t* x, int64_t batch, int64_t rows, int64_
   return hipGetLastError();
 }
 
+namespace {
+// One launch of the one-pass cast with WV waves per workgroup: at most one
+// workgroup per resident slot, each walking tiles.
+template <bool FLOOR, bool GATHER, int WV>
+hipError_t launch_both_wv(const uint16_t* x, int64_t batch, int64_t rows, int64_t cols, int64_t ld, uint8_t* q,
+                          uint8_t* scale, uint8_t* q_t, uint8_t* scale_t, int64_t rtiles, int64_t ctiles,
+                          mx::RowGather gth, hipStream_t stream) {
+  static int64_t fill = 0;
+  if (fill == 0) fill = resident_blocks((const void*)mx::k_quant_both<FLOOR, GATHER, WV>, 64 * WV);
+  const int64_t blocks = std::max<int64_t>(1, std::min<int64_t>(batch * rtiles * ctiles, fill));
+  hipLaunchKernelGGL((mx::k_quant_both<FLOOR, GATHER, WV>), dim3((unsigned)blocks), dim3(64 * WV), 0, stream, x,
+                     batch, rows, cols, ld, q, scale, q_t, scale_t, rtiles, ctiles, gth);
+  return hipGetLastError();
+}
+
+// Waves per workgroup of the one-pass cast for `tiles` 256x256 tiles. Four waves
+// (each two 32-row sub-tiles in turn), two workgroups per compute unit, whose
+// phases overlap; where there is at most one tile per compute unit, eight waves
+// (one sub-tile each) finish a tile sooner (16384 x 576 grad_out: 14 against 18 us;
+// 16384 x 4096: 70 against 58 us).
+int both_waves(int64_t tiles) {
+  static int cus = 0;
+  if (cus == 0) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+      cus = 256;
+  }
+  return tiles <= cus ? 8 : 4;
+}
+}  // namespace
+
 hipError_t mx_launch_both(const uint16_t* x, int64_t batch, int64_t rows, int64_t cols, int64_t ld, uint8_t* q,
                           uint8_t* scale, uint8_t* q_t, uint8_t* scale_t, int floor_mode, hipStream_t stream) {
   const int64_t rtiles = (rows + 255) / 256, ctiles = (cols + 255) / 256;
   const int64_t tiles = batch * rtiles * ctiles;
   if (tiles == 0) return hipSuccess;
-  static int64_t fill = 0;
-  if (fill == 0) fill = resident_blocks((const void*)mx::k_quant_both<false, false>, 256);
-  const int64_t blocks = std::min<int64_t>(tiles, fill);
   const mx::RowGather none{nullptr, 0, 0, nullptr};
+  const bool eight = both_waves(tiles) == 8;
   if (floor_mode)
-    hipLaunchKernelGGL((mx::k_quant_both<true, false>), dim3((unsigned)blocks), dim3(256), 0, stream, x, batch, rows,
-                       cols, ld, q, scale, q_t, scale_t, rtiles, ctiles, none);
-  else
-    hipLaunchKernelGGL((mx::k_quant_both<false, false>), dim3((unsigned)blocks), dim3(256), 0, stream, x, batch, rows,
-                       cols, ld, q, scale, q_t, scale_t, rtiles, ctiles, none);
-  return hipGetLastError();
+    return eight ? launch_both_wv<true, false, 8>(x, batch, rows, cols, ld, q, scale, q_t, scale_t, rtiles, ctiles, none, stream)
+                 : launch_both_wv<true, false, 4>(x, batch, rows, cols, ld, q, scale, q_t, scale_t, rtiles, ctiles, none, stream);
+  return eight ? launch_both_wv<false, false, 8>(x, batch, rows, cols, ld, q, scale, q_t, scale_t, rtiles, ctiles, none, stream)
+               : launch_both_wv<false, false, 4>(x, batch, rows, cols, ld, q, scale, q_t, scale_t, rtiles, ctiles, none, stream);
 }
 
 // Padded one-pass cast: x [rows x cols] with unpadded group ends offs -> codes of the
-// [rows_pad x cols] padded rows (both forms), offs_pad written.
+// [rows_pad x cols] padded rows (both forms), offs_pad written (one workgroup is
+// launched even for no tiles, to write offs_pad).
 hipError_t mx_launch_pad_both(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, const int32_t* offs,
                               int groups, int64_t rows_pad, uint8_t* q, uint8_t* scale, uint8_t* q_t,
                               uint8_t* scale_t, int32_t* offs_pad, hipStream_t stream) {
   const int64_t rtiles = (rows_pad + 255) / 256, ctiles = (cols + 255) / 256;
-  const int64_t tiles = rtiles * ctiles;
-  static int64_t fill = 0;
-  if (fill == 0) fill = resident_blocks((const void*)mx::k_quant_both<false, true>, 256);
-  const int64_t blocks = std::max<int64_t>(1, std::min<int64_t>(tiles, fill));  // one workgroup writes offs_pad
   const mx::RowGather gth{offs, groups, (int32_t)rows, offs_pad};
-  hipLaunchKernelGGL((mx::k_quant_both<false, true>), dim3((unsigned)blocks), dim3(256), 0, stream, x, (int64_t)1,
-                     rows_pad, cols, ld, q, scale, q_t, scale_t, rtiles, ctiles, gth);
-  return hipGetLastError();
+  if (both_waves(rtiles * ctiles) == 8)
+    return launch_both_wv<false, true, 8>(x, 1, rows_pad, cols, ld, q, scale, q_t, scale_t, rtiles, ctiles, gth, stream);
+  return launch_both_wv<false, true, 4>(x, 1, rows_pad, cols, ld, q, scale, q_t, scale_t, rtiles, ctiles, gth, stream);
 }
 
 hipError_t mx_launch_w32(const uint16_t* w, int64_t batch, int64_t n, int64_t k, int64_t ld, uint8_t* q,
