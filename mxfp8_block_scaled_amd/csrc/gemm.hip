@@ -690,10 +690,10 @@ hipError_t launch_tiling(int tiling, const mx::GemmArgs& p, int out_bf16, hipStr
 }
 
 // The tiling for a problem (p.splits set). Measured on the MoE training step's
-// GEMMs (G=8, M=16384, K=N=4096, and a dense 576-wide layer); every tiling gives
-// bit-identical results, since each output element sums its k-steps in the same
-// order.
-template <int MODE>
+// GEMMs (G=8, M=16384, K=N=4096, and a dense 576-wide layer), A/B inside the step on
+// one box; every tiling gives bit-identical results, since each output element sums
+// its k-steps in the same order.
+template <int MODE, int EL>
 int choose_tiling(const mx::GemmArgs& p) {
   const int64_t groups_tiles = MODE == mx::MODE_KGROUP ? (int64_t)p.groups * p.splits : 1;
   const int64_t big_tiles = groups_tiles * ((p.M + 255) / 256) * ((p.N + 255) / 256);
@@ -701,17 +701,19 @@ int choose_tiling(const mx::GemmArgs& p) {
   if (big_tiles < 128) return TILE_128;
   // a short contraction (a few k-steps per tile): the output stores dominate, and two
   // blocks per compute unit overlap one block's stores with the other's loop
-  // (16384x4096 output over K=576: 51 us against 62 us for 256x256 tiles)
+  // (16384x4096 output over K=576: 55 us against 69-75 us for 256x256 tiles)
   if (MODE == mx::MODE_MGROUP && p.K <= 1024) return TILE_128x256;
   // K-grouped output rows that 192-row tiles cover with less padding than 256-row
-  // ones (576 rows: 53 us against 59 us)
+  // ones (576 rows: 58-59 us against 68-72 us)
   if (MODE == mx::MODE_KGROUP && (p.M + 191) / 192 * 192 < (p.M + 255) / 256 * 256) return TILE_192x256;
-  // M-grouped with many tiles (the grouped forward and dgrad): one wave per SIMD
-  // (inside the training step 278-294 us against 295-304 us with two)
-  if (MODE == mx::MODE_MGROUP && big_tiles >= 512) return TILE_256;
-  // otherwise two waves per SIMD hide each tile's prologue and epilogue better: the
-  // grouped wgrad (MXFP8 306-308 us against 308-317 us; bf16 531 us against 620 us)
-  // and the 576-wide forward's single round of tiles (57 us against 63-67 us)
+  // many tiles: one wave per SIMD (grouped forward / dgrad 279-281 / 269-272 us
+  // against 287-288 / 277-278 with two; MXFP8 wgrad 296-298 against 301-304), except
+  // the bf16 K-grouped wgrad, where two waves per SIMD hide its masked, longer steps
+  // better (531-548 against 620-627 us)
+  if (big_tiles >= 512 && !(EL == mx::EL_BF16 && MODE == mx::MODE_KGROUP)) return TILE_256;
+  // otherwise (128-511 tiles: one round or two) two waves per SIMD hide each tile's
+  // prologue and epilogue better (the 576-wide forward's single round of 192 tiles:
+  // 53-54 us against 63-68 us)
   return TILE_256_8W;
 }
 
@@ -730,7 +732,7 @@ hipError_t launch(mx::GemmArgs& p, int out_bf16, hipStream_t stream) {
       q.splits = splits;
       q.split_stride = stride;
       q.out = ws;
-      e = launch_tiling<MODE, EL>(choose_tiling<MODE>(q), q, 0, stream);
+      e = launch_tiling<MODE, EL>(choose_tiling<MODE, EL>(q), q, 0, stream);
       if (e != hipSuccess) return e;
       const int64_t blocks = std::min<int64_t>((n_out + 1023) / 1024, 4096);
       hipLaunchKernelGGL(k_split_reduce, dim3((unsigned)std::max<int64_t>(blocks, 1)), dim3(256), 0, stream, ws,
@@ -738,7 +740,7 @@ hipError_t launch(mx::GemmArgs& p, int out_bf16, hipStream_t stream) {
       return hipGetLastError();
     }
   }
-  return launch_tiling<MODE, EL>(choose_tiling<MODE>(p), p, out_bf16, stream);
+  return launch_tiling<MODE, EL>(choose_tiling<MODE, EL>(p), p, out_bf16, stream);
 }
 }  // namespace
 

@@ -4,8 +4,8 @@ The library picks a tiling from the problem's shape; each case here is shaped to
 select one of them, with groups that end inside tiles (MXFP8 groups on 32-row
 boundaries, as the calls require; bf16 groups anywhere), one group empty, and
 partial tiles on both output edges:
-  * 256x256 with eight waves (two per SIMD): K-grouped with >= 128 tiles of 256x256,
-    and M-grouped with 128..511 such tiles over a contraction above 1024;
+  * 256x256 with eight waves (two per SIMD): 128..511 tiles of 256x256 (M-grouped
+    over a contraction above 1024, or K-grouped), and bf16 K-grouped with more;
   * 128x256 over a three-deep ring, two blocks per compute unit: M-grouped with a
     contraction of at most 1024 and >= 128 tiles;
   * 192x256: K-grouped outputs whose rows 192-row tiles cover with less padding
