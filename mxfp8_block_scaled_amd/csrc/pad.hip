@@ -56,14 +56,8 @@ __global__ __launch_bounds__(kPadThreads) void k_pad_rows(const uint16_t* __rest
   const int64_t waves = (int64_t)gridDim.x * (kPadThreads / 64);
   const int64_t chunks = cols / 8;
   for (int64_t p = (int64_t)blockIdx.x * (kPadThreads / 64) + (threadIdx.x >> 6); p < rows_pad; p += waves) {
-    const int g = upper_index(t.pad_end, groups, p);
-    const u32x4* src = nullptr;
-    if (g < groups) {
-      const int64_t start = g ? t.end[g - 1] : 0;
-      const int64_t i = p - (g ? t.pad_end[g - 1] : 0);
-      if (i < t.end[g] - start) src = (const u32x4*)(x + (start + i) * ld_x);
-    }
-    move_row(src, (u32x4*)(x_pad + p * cols), chunks, lane);
+    const int64_t s = padded_source(t, groups, p);
+    move_row(s >= 0 ? (const u32x4*)(x + s * ld_x) : nullptr, (u32x4*)(x_pad + p * cols), chunks, lane);
   }
 }
 
