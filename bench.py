@@ -57,7 +57,7 @@ M, K, N, G, NARROW = 16384, 4096, 4096, 8, 576
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=100)
     # 100 untimed steps (~0.13 s): after 5 the timed steps still ran ~7% slower (1.366-1.371 against
     # 1.274-1.283 ms, same box), the device still raising its clocks
     ap.add_argument("--warmup", type=int, default=100)
@@ -313,6 +313,9 @@ def main():
     def mean_ms(evs, i):
         return float(np.mean([e[i][0].elapsed_time(e[i][1]) for e in evs]))
 
+    def all_ms(evs, i):
+        return [e[i][0].elapsed_time(e[i][1]) for e in evs]
+
     # W warm-up steps, with events around every launch: they pick the dominant
     # (longest) kernel; without warm-up, the op with the most work is taken
     wev = new_events(args.warmup)
@@ -349,14 +352,32 @@ def main():
         mm = kind in PEAKS
         rate = units / (ms * 1e-3) / (1e12 if mm else 1e9)
         peak = PEAKS[kind] if mm else PEAK_HBM_GBPS
+        each = all_ms(ev if i == dom_i else bev, i)
         per_op[name] = {"us": round(ms * 1e3, 2), ("tflops" if mm else "gbps"): round(rate, 1),
-                        "frac": round(rate / peak, 4)}
+                        "frac": round(rate / peak, 4), "us_median": round(float(np.median(each)) * 1e3, 2),
+                        "us_min": round(float(np.min(each)) * 1e3, 2)}
 
     gemm_flops = sum(u for _, k, u, _ in ops if k in PEAKS)
     cast_bytes = sum(u for _, k, u, _ in ops if k == "cast")
     gemm_us = sum(per_op[n]["us"] for n, k, _, _ in ops if k in PEAKS)
     cast_us = sum(per_op[n]["us"] for n, k, _, _ in ops if k == "cast")
     value = gemm_flops / (ms_per_step * 1e-3) / 1e12
+
+    # practical HBM ceiling, measured after the timed region: a 1 GiB device-to-device
+    # copy (2 GiB moved per copy), best of five
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    cps = []
+    for _ in range(5):
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        c0.record()
+        dst.copy_(src)
+        c1.record()
+        torch.cuda.synchronize()
+        cps.append(c0.elapsed_time(c1))
+    copy_gbps = round(2 * (1 << 30) / (min(cps) * 1e-3) / 1e9, 1)
+    del src, dst
 
     # dominant kernel: the longest launch of the step (timed inside the timed region)
     dom_name, dom_kind, dom_units, _ = ops[dom_i]
@@ -400,6 +421,8 @@ def main():
         "gemm_frac_of_peak": round(gemm_ideal_us / gemm_us, 4),
         "cast_gbps": round(cast_bytes / (cast_us * 1e-6) / 1e9, 1),
         "cast_frac_of_hbm": round(cast_bytes / (cast_us * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4),
+        "hbm_copy_gbps": copy_gbps,
+        "cast_frac_of_copy": round(cast_bytes / (cast_us * 1e-6) / 1e9 / copy_gbps, 4),
         "step_gemm_gflop": round(gemm_flops / 1e9, 2), "step_cast_gb": round(cast_bytes / 1e9, 4),
         "roofline": roofline, "cpu_baseline": cpu, "kernels": per_op, "source_hash": src_hash(),
     }
