@@ -122,11 +122,11 @@ struct Tile {
   bool valid;
 };
 
-// Persistent blocks (one per compute unit) walk the logical tiles. Blocks are dealt
-// round-robin to the 8 XCDs, so XCD x takes the contiguous tile range
-// [x * per_xcd, (x+1) * per_xcd) and its blocks advance through it together; with
-// a raster of GM m-tiles by all n-tiles, the ~32 tiles in flight on one XCD share
-// their A and B slices in its L2.
+// Logical tile t -> its output tile and contraction range (one block per tile).
+// Blocks are dealt round-robin to the 8 XCDs and xcd_remap gives XCD x the
+// contiguous tile range [x * per_xcd, (x+1) * per_xcd), which its blocks take in
+// order; with a raster of GM m-tiles by all n-tiles, the ~32 tiles in flight on one
+// XCD share their A and B slices in its L2 (GM = 4 measured best among 1..16).
 template <int BM, int BN, int MODE, int OUT_BF16, int EL>
 __device__ inline Tile tile_at(const GemmArgs& p, int64_t t) {
   constexpr int64_t GM = 4;
@@ -445,9 +445,10 @@ __global__ __launch_bounds__(64 * WGM * WGN) __attribute__((amdgpu_waves_per_eu(
 
   // ---- epilogue ------------------------------------------------------------------
   // Each lane holds four consecutive columns of one row per v/4. In the common case
-  // (the wave's columns inside N, rows 16-byte aligned) each wave stages its whole
-  // WM x WN output, or half of it for fp32 at 256x256, in its quarter of the idle
-  // ring: 8- or 16-byte LDS writes, 16-byte chunks of a row XOR-swizzled by the row
+  // (the wave's columns inside N, rows 16-byte aligned) each wave stages its WM x WN
+  // output in its share of the idle ring, in passes of RP rows where the share holds
+  // fewer (fp32 at 256x256: two): 8- or 16-byte LDS writes, 16-byte chunks of a row
+  // XOR-swizzled by the row
   // so neither the writes (32 rows, one chunk) nor the reads (whole rows) collide in
   // banks. It then writes whole row segments (WN * ES bytes) with 16-byte stores.
   // Otherwise (the ragged right edge) lanes store elements with a bounds check.
