@@ -35,6 +35,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -77,10 +78,15 @@ def parse():
 
 
 def src_hash():
+    """Hash of the GEMM and cast kernel sources with comments and whitespace removed:
+    the counters in profiles/traffic.json hold while it matches."""
     h = hashlib.sha256()
-    for f in ("gemm.hip", "cast.hip", "common.h"):
-        with open(os.path.join(ROOT, "mxfp8_block_scaled_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+    for f in ("gemm.hip", "cast.hip", "common.h", "group_table.h"):
+        with open(os.path.join(ROOT, "mxfp8_block_scaled_amd", "csrc", f)) as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        h.update("".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 
