@@ -710,7 +710,7 @@ int choose_tiling(const mx::GemmArgs& p) {
   // many tiles: one wave per SIMD (grouped forward / dgrad 279-281 / 269-272 us
   // against 287-288 / 277-278 with two; MXFP8 wgrad 296-298 against 301-304), except
   // the bf16 K-grouped wgrad, where two waves per SIMD hide its masked, longer steps
-  // better (531-548 against 620-627 us)
+  // better (540 against 564 us)
   if (big_tiles >= 512 && !(EL == mx::EL_BF16 && MODE == mx::MODE_KGROUP)) return TILE_256;
   // otherwise (128-511 tiles: one round or two) two waves per SIMD hide each tile's
   // prologue and epilogue better (the 576-wide forward's single round of 192 tiles:
