@@ -704,9 +704,11 @@ int choose_tiling(const mx::GemmArgs& p) {
   // blocks per compute unit overlap one block's stores with the other's loop
   // (16384x4096 output over K=576: 55 us against 69-75 us for 256x256 tiles)
   if (MODE == mx::MODE_MGROUP && p.K <= 1024) return TILE_128x256;
-  // K-grouped output rows that 192-row tiles cover with less padding than 256-row
-  // ones (576 rows: 58-59 us against 68-72 us)
-  if (MODE == mx::MODE_KGROUP && (p.M + 191) / 192 * 192 < (p.M + 255) / 256 * 256) return TILE_192x256;
+  // K-grouped output rows that 192-row tiles cover with at least 1/8 less padding
+  // than 256-row ones (576 rows: 576 against 768, 58-59 us against 68-72 us); a
+  // smaller saving does not repay the lower operand reuse of 192-row tiles (4096 rows
+  // ran 294 us against 263 us as 256x256)
+  if (MODE == mx::MODE_KGROUP && (p.M + 191) / 192 * 192 * 8 <= (p.M + 255) / 256 * 256 * 7) return TILE_192x256;
   // many tiles: one wave per SIMD (grouped forward / dgrad 279-281 / 269-272 us
   // against 287-288 / 277-278 with two; MXFP8 wgrad 296-298 against 301-304), except
   // the bf16 K-grouped wgrad, where two waves per SIMD hide its masked, longer steps

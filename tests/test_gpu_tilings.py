@@ -8,8 +8,8 @@ partial tiles on both output edges:
     over a contraction above 1024, or K-grouped), and bf16 K-grouped with more;
   * 128x256 over a three-deep ring, two blocks per compute unit: M-grouped with a
     contraction of at most 1024 and >= 128 tiles;
-  * 192x256: K-grouped outputs whose rows 192-row tiles cover with less padding
-    than 256-row ones, without and with split contractions.
+  * 192x256: K-grouped outputs whose rows 192-row tiles cover with at least 1/8
+    less padding than 256-row ones, without and with split contractions.
 The 128x128 and four-wave 256x256 tilings are covered by the small-shape and
 full-size tests.
 """
@@ -21,7 +21,7 @@ import mxfp8_block_scaled_amd as mx
 from mxfp8_block_scaled_amd import synth
 
 from gemm_check import check_bf16, check_f32
-from gpu_util import dev_bf16, dev_i32, host, require_gpu, say
+from gpu_util import dev_bf16, dev_i32, dev_u8, host, require_gpu, say
 
 pytestmark = pytest.mark.gpu
 
@@ -151,3 +151,87 @@ def test_bf16_tilings(oracle, sizes):
               oracle.grouped_mm_wgrad(np.abs(fdy).T, np.abs(fx).T, offs, G), int(max(sizes)))
     for g in np.flatnonzero(np.array(sizes) == 0):
         assert not dw[g].any()
+
+
+# ---- bit-exact sweep -------------------------------------------------------------------
+# Codes in {0, +-0.5, +-1, +-2} with scales 2^-1..2^1: every product is a power of two in
+# [2^-4, 2^4] and every partial sum is exact in fp32, so each tiling must reproduce the
+# oracle bit for bit. Large cases compare a seeded sample of output rows.
+
+def exact_codes(rng, rows, k):
+    choices = np.array([0x00, 0x30, 0xB0, 0x38, 0xB8, 0x40, 0xC0], np.uint8)
+    return rng.choice(choices, size=(rows, k)), rng.integers(126, 129, size=(rows, k // 32)).astype(np.uint8)
+
+
+def phys(oracle, logical):
+    return dev_u8(oracle.scales_to_physical(logical))
+
+
+def random_sizes(rng, total, groups):
+    """Group sizes in 32-row units summing to `total`, one group forced empty."""
+    units = rng.multinomial(total // 32, np.full(groups, 1.0 / groups))
+    units[rng.integers(groups)] = 0
+    units[rng.integers(groups)] += total // 32 - units.sum()
+    return units * 32
+
+
+def sample_rows(rng, upto, count):
+    return np.sort(rng.choice(upto, size=min(count, upto), replace=False))
+
+
+@pytest.mark.parametrize("m,n,k,G,name", [
+    (3104, 2336, 1280, 3, "8-wave"),        # 13 x 10 = 130 tiles, K > 1024
+    (3104, 2336, 576, 3, "128x256"),        # K <= 1024
+    (8192, 4128, 1088, 4, "256x256"),       # 32 x 17 = 544 tiles
+    (1000, 800, 320, 3, "128x128"),         # 4 x 4 tiles
+])
+def test_exact_fwd_tilings(oracle, m, n, k, G, name):
+    rng = np.random.default_rng(m + n + k)
+    used = m - 96  # rows past the last group are not written
+    sizes = random_sizes(rng, used // 32 * 32, G)
+    offs = np.cumsum(sizes).astype(np.int32)
+    a, a_s = exact_codes(rng, m, k)
+    b, b_s = exact_codes(rng, G * n, k)
+    say(f"[exact {name}] fwd m={m} n={n} k={k} offs={offs.tolist()}")
+    got = host(mx.mx_grouped_mm_fwd(dev_u8(a), phys(oracle, a_s), dev_u8(b), phys(oracle, b_s), dev_i32(offs),
+                                    m, n, k, out_dtype=mx.MX_OUT_F32))
+    rows = sample_rows(rng, int(offs[-1]), 384)
+    sub_offs = np.searchsorted(rows, offs, side="left").astype(np.int32)  # group ends within the sample
+    ref = oracle.grouped_mm(oracle.dequantize(a[rows], a_s[rows]), oracle.dequantize(b, b_s), sub_offs, G)
+    assert np.array_equal(got[rows], ref.astype(np.float32)), f"{name}: fwd differs from the exact result"
+
+
+@pytest.mark.parametrize("n,k,m,G,name", [
+    (352, 2080, 4096, 8, "192x256"),        # 8 x 2 x 9 = 144 tiles, 352 rows in 192-row tiles
+    (1056, 1056, 4096, 8, "8-wave"),        # 8 x 5 x 5 = 200 tiles (1152 rows as 192s: too little saved)
+    (4128, 2080, 2048, 8, "256x256"),       # 8 x 17 x 9 = 1224 tiles
+    (576, 1056, 8192, 2, "192x256 split"),  # 2 x 3 x 5 = 30 tiles: contraction split 8 ways
+])
+def test_exact_wgrad_tilings(oracle, n, k, m, G, name):
+    rng = np.random.default_rng(n + k + m + G)
+    sizes = random_sizes(rng, m, G)
+    offs = np.cumsum(sizes).astype(np.int32)
+    a, a_s = exact_codes(rng, n, m)
+    b, b_s = exact_codes(rng, k, m)
+    say(f"[exact {name}] wgrad n={n} k={k} m={m} offs={offs.tolist()}")
+    got = host(mx.mx_grouped_mm_wgrad(dev_u8(a), phys(oracle, a_s), dev_u8(b), phys(oracle, b_s), dev_i32(offs),
+                                      m, n, k, out_dtype=mx.MX_OUT_F32))
+    rows = sample_rows(rng, n, 160)
+    ref = oracle.grouped_mm_wgrad(oracle.dequantize(a[rows], a_s[rows]), oracle.dequantize(b, b_s), offs, G)
+    assert np.array_equal(got[:, rows], ref.astype(np.float32)), f"{name}: wgrad differs from the exact result"
+    for g in np.flatnonzero(sizes == 0):
+        assert not got[g].any()
+
+
+def test_exact_dgrad_short_contraction(oracle):
+    """dgrad over a 576-wide contraction, 13 x 10 tiles: 128x256 tiles, two blocks per CU."""
+    rng = np.random.default_rng(81)
+    m, n, k, G = 3104, 576, 2336, 3
+    offs = np.cumsum(random_sizes(rng, m, G)).astype(np.int32)
+    dy, dy_s = exact_codes(rng, m, n)
+    w_t, w_t_s = exact_codes(rng, G * k, n)
+    say(f"[exact 128x256] dgrad m={m} n={n} k={k} offs={offs.tolist()}")
+    got = host(mx.mx_grouped_mm_dgrad(dev_u8(dy), phys(oracle, dy_s), dev_u8(w_t), phys(oracle, w_t_s),
+                                      dev_i32(offs), m, n, k, out_dtype=mx.MX_OUT_F32))
+    ref = oracle.mx_grouped_mm_fwd(dy, dy_s, w_t, w_t_s, offs, G)
+    assert np.array_equal(got, ref.astype(np.float32))
