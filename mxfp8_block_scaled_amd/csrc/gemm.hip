@@ -672,7 +672,7 @@ int choose_splits(const mx::GemmArgs& p, int64_t elem_bytes) {
 
 // Tile configurations (block tile, wave grid, ring depth, blocks per compute unit):
 enum Tiling {
-  TILE_256 = 0,      // 256x256, 2x2 waves of 128x128, 4-deep ring, 136 KB LDS: one block per CU
+  TILE_256 = 0,      // 256x256, 2x2 waves of 128x128, 4-deep ring, 136 KB LDS: one block per CU (bf16 out)
   TILE_128 = 1,      // 128x128, 2x2 waves of 64x64, 4-deep ring, 68 KB: two blocks per CU
   TILE_128x256 = 2,  // 128x256, 2x2 waves of 64x128, 3-deep ring, 80 KB: two blocks per CU
   TILE_192x256 = 3,  // 192x256, 1x4 waves of 192x64, 4-deep ring, 120 KB: one block per CU
@@ -695,7 +695,7 @@ hipError_t launch_tiling(int tiling, const mx::GemmArgs& p, int out_bf16, hipStr
 // one box; every tiling gives bit-identical results, since each output element sums
 // its k-steps in the same order.
 template <int MODE, int EL>
-int choose_tiling(const mx::GemmArgs& p) {
+int choose_tiling(const mx::GemmArgs& p, int out_bf16) {
   const int64_t groups_tiles = MODE == mx::MODE_KGROUP ? (int64_t)p.groups * p.splits : 1;
   const int64_t big_tiles = groups_tiles * ((p.M + 255) / 256) * ((p.N + 255) / 256);
   // few output tiles: quarter-size tiles spread the work over more compute units
@@ -709,11 +709,13 @@ int choose_tiling(const mx::GemmArgs& p) {
   // smaller saving does not repay the lower operand reuse of 192-row tiles (4096 rows
   // ran 294 us against 263 us as 256x256)
   if (MODE == mx::MODE_KGROUP && (p.M + 191) / 192 * 192 * 8 <= (p.M + 255) / 256 * 256 * 7) return TILE_192x256;
-  // many tiles: one wave per SIMD (grouped forward / dgrad 279-281 / 269-272 us
-  // against 287-288 / 277-278 with two; MXFP8 wgrad 296-298 against 301-304), except
-  // the bf16 K-grouped wgrad, where two waves per SIMD hide its masked, longer steps
-  // better (540 against 564 us)
-  if (big_tiles >= 512 && !(EL == mx::EL_BF16 && MODE == mx::MODE_KGROUP)) return TILE_256;
+  // many tiles, bf16 output: one wave per SIMD (grouped forward / dgrad 279-281 /
+  // 269-272 us against 287-288 / 277-278 with two; MXFP8 wgrad 296-298 against
+  // 301-304), except the bf16 K-grouped wgrad, where two waves per SIMD hide its
+  // masked, longer steps better (540 against 564 us). fp32 output keeps two waves per
+  // SIMD: 128 accumulators per wave leave room for the fp32 epilogue, which with 256
+  // spills (forward 286 against 287 us, wgrad 292 against 310 us)
+  if (big_tiles >= 512 && out_bf16 && !(EL == mx::EL_BF16 && MODE == mx::MODE_KGROUP)) return TILE_256;
   // otherwise (128-511 tiles: one round or two) two waves per SIMD hide each tile's
   // prologue and epilogue better (the 576-wide forward's single round of 192 tiles:
   // 53-54 us against 63-68 us)
@@ -735,7 +737,7 @@ hipError_t launch(mx::GemmArgs& p, int out_bf16, hipStream_t stream) {
       q.splits = splits;
       q.split_stride = stride;
       q.out = ws;
-      e = launch_tiling<MODE, EL>(choose_tiling<MODE, EL>(q), q, 0, stream);
+      e = launch_tiling<MODE, EL>(choose_tiling<MODE, EL>(q, 0), q, 0, stream);
       if (e != hipSuccess) return e;
       const int64_t blocks = std::min<int64_t>((n_out + 1023) / 1024, 4096);
       hipLaunchKernelGGL(k_split_reduce, dim3((unsigned)std::max<int64_t>(blocks, 1)), dim3(256), 0, stream, ws,
@@ -743,7 +745,7 @@ hipError_t launch(mx::GemmArgs& p, int out_bf16, hipStream_t stream) {
       return hipGetLastError();
     }
   }
-  return launch_tiling<MODE, EL>(choose_tiling<MODE, EL>(p), p, out_bf16, stream);
+  return launch_tiling<MODE, EL>(choose_tiling<MODE, EL>(p, out_bf16), p, out_bf16, stream);
 }
 }  // namespace
 

@@ -5,13 +5,14 @@ select one of them, with groups that end inside tiles (MXFP8 groups on 32-row
 boundaries, as the calls require; bf16 groups anywhere), one group empty, and
 partial tiles on both output edges:
   * 256x256 with eight waves (two per SIMD): 128..511 tiles of 256x256 (M-grouped
-    over a contraction above 1024, or K-grouped), and bf16 K-grouped with more;
+    over a contraction above 1024, or K-grouped), and with more tiles for fp32
+    outputs and the bf16 K-grouped wgrad;
   * 128x256 over a three-deep ring, two blocks per compute unit: M-grouped with a
     contraction of at most 1024 and >= 128 tiles;
   * 192x256: K-grouped outputs whose rows 192-row tiles cover with at least 1/8
     less padding than 256-row ones, without and with split contractions.
-The 128x128 and four-wave 256x256 tilings are covered by the small-shape and
-full-size tests.
+The bit-exact sweep below also reaches 128x128 and the four-wave 256x256 (bf16
+output, 512 or more tiles), which the small-shape and full-size tests cover too.
 """
 
 import numpy as np
@@ -156,7 +157,8 @@ def test_bf16_tilings(oracle, sizes):
 # ---- bit-exact sweep -------------------------------------------------------------------
 # Codes in {0, +-0.5, +-1, +-2} with scales 2^-1..2^1: every product is a power of two in
 # [2^-4, 2^4] and every partial sum is exact in fp32, so each tiling must reproduce the
-# oracle bit for bit. Large cases compare a seeded sample of output rows.
+# oracle bit for bit: fp32 outputs equal the exact sums, bf16 outputs their correctly
+# rounded value. Large cases compare a seeded sample of output rows.
 
 def exact_codes(rng, rows, k):
     choices = np.array([0x00, 0x30, 0xB0, 0x38, 0xB8, 0x40, 0xC0], np.uint8)
@@ -182,7 +184,7 @@ def sample_rows(rng, upto, count):
 @pytest.mark.parametrize("m,n,k,G,name", [
     (3104, 2336, 1280, 3, "8-wave"),        # 13 x 10 = 130 tiles, K > 1024
     (3104, 2336, 576, 3, "128x256"),        # K <= 1024
-    (8192, 4128, 1088, 4, "256x256"),       # 32 x 17 = 544 tiles
+    (8192, 4128, 1088, 4, "256x256"),       # 32 x 17 = 544 tiles (bf16 out; fp32: 8-wave)
     (1000, 800, 320, 3, "128x128"),         # 4 x 4 tiles
 ])
 def test_exact_fwd_tilings(oracle, m, n, k, G, name):
@@ -193,18 +195,20 @@ def test_exact_fwd_tilings(oracle, m, n, k, G, name):
     a, a_s = exact_codes(rng, m, k)
     b, b_s = exact_codes(rng, G * n, k)
     say(f"[exact {name}] fwd m={m} n={n} k={k} offs={offs.tolist()}")
-    got = host(mx.mx_grouped_mm_fwd(dev_u8(a), phys(oracle, a_s), dev_u8(b), phys(oracle, b_s), dev_i32(offs),
-                                    m, n, k, out_dtype=mx.MX_OUT_F32))
+    args = (dev_u8(a), phys(oracle, a_s), dev_u8(b), phys(oracle, b_s), dev_i32(offs), m, n, k)
+    got = host(mx.mx_grouped_mm_fwd(*args, out_dtype=mx.MX_OUT_F32))
+    got16 = host(mx.mx_grouped_mm_fwd(*args, out_dtype=mx.MX_OUT_BF16))
     rows = sample_rows(rng, int(offs[-1]), 384)
     sub_offs = np.searchsorted(rows, offs, side="left").astype(np.int32)  # group ends within the sample
     ref = oracle.grouped_mm(oracle.dequantize(a[rows], a_s[rows]), oracle.dequantize(b, b_s), sub_offs, G)
     assert np.array_equal(got[rows], ref.astype(np.float32)), f"{name}: fwd differs from the exact result"
+    assert np.array_equal(got16[rows], oracle.round_to_bf16_bits(ref)), f"{name}: bf16 fwd is not the rounded exact result"
 
 
 @pytest.mark.parametrize("n,k,m,G,name", [
     (352, 2080, 4096, 8, "192x256"),        # 8 x 2 x 9 = 144 tiles, 352 rows in 192-row tiles
     (1056, 1056, 4096, 8, "8-wave"),        # 8 x 5 x 5 = 200 tiles (1152 rows as 192s: too little saved)
-    (4128, 2080, 2048, 8, "256x256"),       # 8 x 17 x 9 = 1224 tiles
+    (4128, 2080, 2048, 8, "256x256"),       # 8 x 17 x 9 = 1224 tiles (bf16 out; fp32: 8-wave)
     (576, 1056, 8192, 2, "192x256 split"),  # 2 x 3 x 5 = 30 tiles: contraction split 8 ways
 ])
 def test_exact_wgrad_tilings(oracle, n, k, m, G, name):
@@ -214,13 +218,15 @@ def test_exact_wgrad_tilings(oracle, n, k, m, G, name):
     a, a_s = exact_codes(rng, n, m)
     b, b_s = exact_codes(rng, k, m)
     say(f"[exact {name}] wgrad n={n} k={k} m={m} offs={offs.tolist()}")
-    got = host(mx.mx_grouped_mm_wgrad(dev_u8(a), phys(oracle, a_s), dev_u8(b), phys(oracle, b_s), dev_i32(offs),
-                                      m, n, k, out_dtype=mx.MX_OUT_F32))
+    args = (dev_u8(a), phys(oracle, a_s), dev_u8(b), phys(oracle, b_s), dev_i32(offs), m, n, k)
+    got = host(mx.mx_grouped_mm_wgrad(*args, out_dtype=mx.MX_OUT_F32))
+    got16 = host(mx.mx_grouped_mm_wgrad(*args, out_dtype=mx.MX_OUT_BF16))
     rows = sample_rows(rng, n, 160)
     ref = oracle.grouped_mm_wgrad(oracle.dequantize(a[rows], a_s[rows]), oracle.dequantize(b, b_s), offs, G)
     assert np.array_equal(got[:, rows], ref.astype(np.float32)), f"{name}: wgrad differs from the exact result"
+    assert np.array_equal(got16[:, rows], oracle.round_to_bf16_bits(ref)), f"{name}: bf16 wgrad is not the rounded exact result"
     for g in np.flatnonzero(sizes == 0):
-        assert not got[g].any()
+        assert not got[g].any() and not got16[g].any()
 
 
 def test_exact_dgrad_short_contraction(oracle):
