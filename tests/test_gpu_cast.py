@@ -173,6 +173,15 @@ def test_dim0_dim1_batched(oracle):
     check_both(oracle, synth.normal_bf16(rng, (3, 96, 320), 0.02), "batch3")
 
 
+def test_dim0_dim1_four_wave_path(oracle):
+    """More tiles than compute units (17 x 17 tiles of 256 x 256, the last column tile
+    partial): the four-wave workgroups, which small shapes never reach; full outputs,
+    and batched: 5 x 5 x 13 tiles with a partial row tile per batch."""
+    rng = np.random.default_rng(7)
+    check_both(oracle, synth.normal_bf16(rng, (4352, 4160), 1.0), "2D 289 tiles")
+    check_both(oracle, synth.normal_bf16(rng, (5, 1056, 3328), 0.02), "batch5 325 tiles")
+
+
 def test_dim0_dim1_full_size_sampled(oracle):
     d = synth.moe_g8(0, with_backward=False)
     x = d["x"]
@@ -256,6 +265,12 @@ def check_ex(oracle, bits, forms, mode, name):
 def test_floor_forms(oracle, forms, shape):
     rng = np.random.default_rng(sum(shape) + forms)
     check_ex(oracle, synth.normal_bf16(rng, shape, 1.0), forms, mx.MX_SCALE_FLOOR, f"normal{shape}")
+
+
+def test_floor_four_wave_path(oracle):
+    """FLOOR through the four-wave one-pass workgroups (17 x 17 tiles)."""
+    rng = np.random.default_rng(8)
+    check_ex(oracle, synth.normal_bf16(rng, (4352, 4160), 1.0), 3, mx.MX_SCALE_FLOOR, "2D 289 tiles")
 
 
 def test_floor_stress_every_amax(oracle):
