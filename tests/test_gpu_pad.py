@@ -212,6 +212,8 @@ FUSED_CASES = [
     (0, 64, 64, [0, 0]),
     (1000, 96, 96, random_sizes(np.random.default_rng(6), 1000, 6, 1).tolist()),
     (3000, 128, 128, _many_groups()),
+    # more tiles than compute units (18 x 17): the four-wave workgroups of the bench's size
+    (4400, 4160, 4160, random_sizes(np.random.default_rng(9), 4300, 7, 1).tolist()),
 ]
 
 
