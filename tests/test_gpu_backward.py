@@ -118,6 +118,46 @@ def test_bf16_wgrad_exact(oracle, n, k, m, sizes):
     assert np.array_equal(got, ref.astype(np.float32))
 
 
+def test_bf16_large_tilings_exact(oracle):
+    """bf16 grouped GEMMs at sizes that pick the large tilings, on dyadic operands (exact
+    sums): M-grouped 32 x 17 tiles over K=1088 (bf16 out: 256x256 one wave per SIMD;
+    fp32 out: eight waves), M-grouped over a 576-wide contraction (128x256, two blocks
+    per CU), K-grouped 8 x 9 x 9 tiles (eight waves) with token edges inside 16-byte
+    chunks. Seeded samples of output rows; bf16 outputs are the rounded exact sums."""
+    rng = np.random.default_rng(91)
+
+    def rows_of(upto, count):
+        return np.sort(rng.choice(upto, size=count, replace=False))
+
+    for m, n, k, G in ((8192, 4128, 1088, 4), (3104, 2336, 576, 3)):
+        sizes = rng.multinomial(m - 37, np.full(G, 1.0 / G))
+        sizes[1] = 0
+        sizes[0] = m - 37 - sizes[1:].sum()
+        offs = np.cumsum(sizes).astype(np.int32)
+        a, b = dyadic(rng, (m, k)), dyadic(rng, (G * n, k))
+        say(f"[bf16 large exact] fwd m={m} n={n} k={k} offs={offs.tolist()}")
+        args = (dev_bf16(a), dev_bf16(b), dev_i32(offs), m, n, k)
+        got = host(mx.mx_grouped_mm_bf16_fwd(*args, out_dtype=mx.MX_OUT_F32))
+        got16 = host(mx.mx_grouped_mm_bf16_fwd(*args, out_dtype=mx.MX_OUT_BF16))
+        rows = rows_of(int(offs[-1]), 256)
+        sub = np.searchsorted(rows, offs, side="left").astype(np.int32)
+        ref = oracle.grouped_mm(oracle.bf16_to_f64(a[rows]), oracle.bf16_to_f64(b), sub, G)
+        assert np.array_equal(got[rows], ref.astype(np.float32))
+        assert np.array_equal(got16[rows], oracle.round_to_bf16_bits(ref))
+    n, k, m, G = 2080, 2080, 2048, 8
+    offs = np.array([216, 579, 579, 1100, 1501, 1671, 1861, 2048], np.int32)  # group 2 empty; most edges off 8
+    dy_t, x_t = dyadic(rng, (n, m)), dyadic(rng, (k, m))
+    say(f"[bf16 large exact] wgrad n={n} k={k} m={m} offs={offs.tolist()}")
+    args = (dev_bf16(dy_t), dev_bf16(x_t), dev_i32(offs), m, n, k)
+    got = host(mx.mx_grouped_mm_bf16_wgrad(*args, out_dtype=mx.MX_OUT_F32))
+    got16 = host(mx.mx_grouped_mm_bf16_wgrad(*args, out_dtype=mx.MX_OUT_BF16))
+    rows = rows_of(n, 128)
+    ref = oracle.grouped_mm_wgrad(oracle.bf16_to_f64(dy_t[rows]), oracle.bf16_to_f64(x_t), offs, G)
+    assert np.array_equal(got[:, rows], ref.astype(np.float32))
+    assert np.array_equal(got16[:, rows], oracle.round_to_bf16_bits(ref))
+    assert not got[2].any(), "the empty group's gradient must be zero"
+
+
 @pytest.mark.parametrize("m,n,k,G", [(1000, 256, 512, 4), (2048, 384, 1024, 8)])
 def test_bf16_gemm_random(oracle, m, n, k, G):
     rng = np.random.default_rng(m + G)
