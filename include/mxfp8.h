@@ -170,10 +170,16 @@ mx_status mx_quantize_weight_32x32(const uint16_t* w, int64_t batch, int64_t n, 
  *             mx_scale_bytes(groups*n, k) scales
  *   offs      device int32[groups]: inclusive cumulative group ends; group g is
  *             rows [offs[g-1], offs[g]) with offs[-1] = 0. NULL = one dense group
- *             (groups must be 1). Caller precondition (not checked, offs stays on
- *             the device): non-decreasing, every entry % 32 == 0, offs[G-1] <= m.
+ *             (groups must be 1). Caller precondition (not checked on the host, offs
+ *             stays on the device; mx_check_offs tests it on the device):
+ *             non-decreasing, every entry % 32 == 0, offs[G-1] <= m.
  *             Rows past offs[G-1] belong to no group and are left unwritten (the
- *             buffers of mx_pad_token_groups end with such rows).
+ *             buffers of mx_pad_token_groups end with such rows). The kernel reads
+ *             the ends as their running maximum clamped into [0, m], so an
+ *             out-of-contract offs gives unspecified output rows but no access
+ *             outside a, b, their scales and out (the same holds for dgrad, wgrad,
+ *             whose token ranges are clamped into [0, m], the padded calls and the
+ *             bf16 calls).
  *   out       [m x n], float32 or bf16 per out_dtype, row pitch n (written)
  * k % 32 == 0 (k need not be a multiple of 128: the tail is zero-padded inside
  * the kernel); m >= 0; n >= 1; if groups > 1, n % 32 == 0. fp32 accumulation.
@@ -288,6 +294,25 @@ mx_status mx_grouped_mm_bf16_wgrad(const uint16_t* dy_t, const uint16_t* x_t, co
  * sequence non-decreasing while reading it, so an out-of-contract offs moves the
  * wrong rows but never addresses memory outside the buffers. groups <= 1024.
  * A row buffer with zero rows may be NULL. */
+
+/* Device check of offs for the grouped calls (a debugging aid for callers whose
+ * offs come from elsewhere; the GEMMs themselves never read offs on the host).
+ *   offs      device int32[groups], groups >= 1
+ *   m         rows (M-grouped calls) or tokens (wgrad) the ends must stay within
+ *   multiple  required divisor of every end: 32 for the MXFP8 calls, 1 for the
+ *             bf16 calls and the padding calls
+ *   result    device int32[2] (written, asynchronously on `stream`): result[0] =
+ *             OR of MX_OFFS_DECREASING, MX_OFFS_NOT_MULTIPLE, MX_OFFS_OUT_OF_RANGE
+ *             over all groups (0 = offs meets the preconditions), result[1] = the
+ *             first group with a violation, or -1.
+ * A group's end is compared with the previous end (0 before group 0). Errors:
+ * MX_E_SHAPE (groups < 1, m outside [0, 2^31], multiple < 1), MX_E_NULL,
+ * MX_E_ALIGN (a pointer not 4-byte aligned). */
+#define MX_OFFS_DECREASING 1    /* an end below the previous one */
+#define MX_OFFS_NOT_MULTIPLE 2  /* an end that is not a multiple of `multiple` */
+#define MX_OFFS_OUT_OF_RANGE 4  /* an end below 0 or above m */
+mx_status mx_check_offs(const int32_t* offs, int32_t groups, int64_t m, int32_t multiple, int32_t* result,
+                        void* stream);
 
 /* Rows of the padded buffer for any split of `rows` rows into `groups` groups:
  * rows + 31 * groups rounded up to a multiple of 256 (a group grows by at most 31

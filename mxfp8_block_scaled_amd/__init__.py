@@ -260,6 +260,24 @@ def mx_grouped_mm_wgrad(dy_t, dy_t_s, x_t, x_t_s, offs, m, n, k, groups=None, ou
     return out
 
 
+MX_OFFS_DECREASING, MX_OFFS_NOT_MULTIPLE, MX_OFFS_OUT_OF_RANGE = 1, 2, 4
+
+
+def mx_check_offs(offs, m, multiple=32, result=None):
+    """Device check of offs (int32[G]) against the grouped calls' preconditions.
+
+    Returns `result`, a device int32[2] written on the current stream: result[0] = OR
+    of MX_OFFS_DECREASING / MX_OFFS_NOT_MULTIPLE / MX_OFFS_OUT_OF_RANGE over the
+    groups (0 = valid), result[1] = the first offending group or -1. `multiple` is 32
+    for the MXFP8 calls, 1 for the bf16 and padding calls."""
+    if offs.dtype != torch.int32 or offs.dim() != 1 or not offs.is_contiguous():
+        raise ValueError("offs must be a contiguous 1D int32 tensor")
+    if result is None:
+        result = torch.empty(2, dtype=torch.int32, device=offs.device)
+    _lib.call("mx_check_offs", _ptr(offs), offs.numel(), m, multiple, _ptr(result), _stream(offs))
+    return result
+
+
 def mx_padded_rows(rows, groups):
     """Rows of the padded buffer for `rows` token rows in `groups` groups."""
     n = _lib.load().mx_padded_rows(int(rows), int(groups))

@@ -30,7 +30,8 @@ hipError_t mx_launch_gemm_bf16_mgroup(const uint16_t*, const uint16_t*, const in
 hipError_t mx_launch_gemm_bf16_kgroup(const uint16_t*, const uint16_t*, const int32_t*, int, int64_t, int64_t, int64_t,
                                       void*, int, hipStream_t);
 hipError_t mx_launch_gemm_mgroup(const uint8_t*, const uint8_t*, const uint8_t*, const uint8_t*, const int32_t*,
-                                 const int32_t*, int, int64_t, int64_t, int64_t, void*, int, hipStream_t);
+                                 const int32_t*, int, int64_t, int64_t, int64_t, int64_t, void*, int, hipStream_t);
+hipError_t mx_launch_check_offs(const int32_t*, int, int64_t, int, int32_t*, hipStream_t);
 hipError_t mx_launch_pad_both(const uint16_t*, int64_t, int64_t, int64_t, const int32_t*, int, int64_t, uint8_t*,
                               uint8_t*, uint8_t*, uint8_t*, int32_t*, hipStream_t);
 hipError_t mx_launch_gemm_kgroup(const uint8_t*, const uint8_t*, const uint8_t*, const uint8_t*, const int32_t*, int,
@@ -286,7 +287,7 @@ mx_status mx_grouped_mm_fwd(const uint8_t* a, const uint8_t* a_s, const uint8_t*
   if ((int64_t)groups * n > kMaxDim) return fail(MX_E_SHAPE, "groups * n exceeds 2^31");
   TRY(check_gemm_extent("k", k, m, (int64_t)groups * n));
   TRY(check_device());
-  return launched(mx_launch_gemm_mgroup(a, a_s, b, b_s, offs, nullptr, groups, m, n, k, out, out_dtype,
+  return launched(mx_launch_gemm_mgroup(a, a_s, b, b_s, offs, nullptr, groups, m, m, n, k, out, out_dtype,
                                         (hipStream_t)stream),
                   "mx_grouped_mm_fwd");
 }
@@ -304,7 +305,7 @@ mx_status mx_grouped_mm_dgrad(const uint8_t* dy, const uint8_t* dy_s, const uint
   TRY(check_gemm_extent("n", n, m, (int64_t)groups * k));
   TRY(check_device());
   // dX[m x k] = dY[m x n] . (W_g^T [k x n])^T : the M-grouped core with contraction n
-  return launched(mx_launch_gemm_mgroup(dy, dy_s, w_t, w_t_s, offs, nullptr, groups, m, k, n, dx, out_dtype,
+  return launched(mx_launch_gemm_mgroup(dy, dy_s, w_t, w_t_s, offs, nullptr, groups, m, m, k, n, dx, out_dtype,
                                         (hipStream_t)stream),
                   "mx_grouped_mm_dgrad");
 }
@@ -456,6 +457,19 @@ int64_t mx_padded_rows(int64_t rows, int32_t groups) {
   return ((rows + 31 * (int64_t)groups + 255) / 256) * 256;
 }
 
+mx_status mx_check_offs(const int32_t* offs, int32_t groups, int64_t m, int32_t multiple, int32_t* result,
+                        void* stream) {
+  if (groups < 1) return fail(MX_E_SHAPE, "groups = %d must be >= 1", groups);
+  if (m < 0 || m > kMaxDim) return fail(MX_E_SHAPE, "m = %lld must be in [0, 2^31)", (long long)m);
+  if (multiple < 1) return fail(MX_E_SHAPE, "multiple = %d must be >= 1", multiple);
+  if (!offs) return fail(MX_E_NULL, "offs is NULL");
+  if ((uintptr_t)offs & 3) return fail(MX_E_ALIGN, "offs is not 4-byte aligned");
+  if (!result) return fail(MX_E_NULL, "result is NULL");
+  if ((uintptr_t)result & 3) return fail(MX_E_ALIGN, "result is not 4-byte aligned");
+  TRY(check_device());
+  return launched(mx_launch_check_offs(offs, groups, m, multiple, result, (hipStream_t)stream), "mx_check_offs");
+}
+
 mx_status mx_pad_token_groups(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, const int32_t* offs,
                               int32_t groups, uint16_t* x_pad, int64_t rows_pad, int32_t* offs_pad, void* stream) {
   TRY(check_pad_common(rows, groups, rows_pad, offs));
@@ -546,7 +560,7 @@ mx_status mx_grouped_mm_fwd_padded(const uint8_t* a, const uint8_t* a_s, const u
   if ((int64_t)groups * n > kMaxDim) return fail(MX_E_SHAPE, "groups * n exceeds 2^31");
   TRY(check_gemm_extent("k", k, m_pad, (int64_t)groups * n));
   TRY(check_device());
-  return launched(mx_launch_gemm_mgroup(a, a_s, b, b_s, offs_pad, offs, groups, m_pad, n, k, out, out_dtype,
+  return launched(mx_launch_gemm_mgroup(a, a_s, b, b_s, offs_pad, offs, groups, m_pad, m, n, k, out, out_dtype,
                                         (hipStream_t)stream),
                   "mx_grouped_mm_fwd_padded");
 }
@@ -563,7 +577,7 @@ mx_status mx_grouped_mm_dgrad_padded(const uint8_t* dy, const uint8_t* dy_s, con
   if ((int64_t)groups * k > kMaxDim) return fail(MX_E_SHAPE, "groups * k exceeds 2^31");
   TRY(check_gemm_extent("n", n, m_pad, (int64_t)groups * k));
   TRY(check_device());
-  return launched(mx_launch_gemm_mgroup(dy, dy_s, w_t, w_t_s, offs_pad, offs, groups, m_pad, k, n, dx, out_dtype,
+  return launched(mx_launch_gemm_mgroup(dy, dy_s, w_t, w_t_s, offs_pad, offs, groups, m_pad, m, k, n, dx, out_dtype,
                                         (hipStream_t)stream),
                   "mx_grouped_mm_dgrad_padded");
 }

@@ -47,6 +47,7 @@ struct GemmArgs {
   // at r - offs[g-1] + offs_out[g-1]) and the padding rows are not written
   const int32_t* offs_out;
   void* out;
+  int64_t out_rows;  // M-grouped: rows of the output (M, or the unpadded rows with offs_out)
   int64_t lda, ldb;          // row pitch in bytes (= contraction length x element size)
   int64_t a_rows, b_rows;    // rows of the whole operand buffers
   int64_t a_ktiles, b_ktiles;  // scale tiles along the contraction
@@ -163,13 +164,21 @@ __device__ inline Tile tile_at(const GemmArgs& p, int64_t t) {
   const int64_t n_tile = in_band / gm;
   T.col0 = n_tile * BN;
   if (MODE == MODE_MGROUP) {
-    // find the group owning m-tile `mt` of the concatenated per-group tile lists
-    int64_t cum = 0;
+    // find the group owning m-tile `mt` of the concatenated per-group tile lists. The
+    // group ends are read as the running maximum clamped into [0, M] (and the output
+    // ends into [0, out_rows]): identical for valid offs, and an out-of-contract offs
+    // gives wrong rows but no access outside the operand and output buffers.
+    int64_t cum = 0, s = 0, so = 0;
     int found = -1;
     const int G = p.offs ? p.groups : 1;
     for (int gg = 0; gg < G; ++gg) {
-      const int64_t s = p.offs ? group_start(p.offs, gg) : 0;
-      const int64_t e = p.offs ? p.offs[gg] : p.M;
+      int64_t e = p.offs ? p.offs[gg] : p.M;
+      e = e < s ? s : (e > p.M ? p.M : e);
+      int64_t eo = 0;
+      if (p.offs_out) {
+        eo = p.offs_out[gg];
+        eo = eo < so ? so : (eo > p.out_rows ? p.out_rows : eo);
+      }
       const int64_t tiles = (e - s + BM - 1) / BM;
       if (mt < cum + tiles) {
         found = gg;
@@ -177,14 +186,15 @@ __device__ inline Tile tile_at(const GemmArgs& p, int64_t t) {
         T.a_row_end = e;
         T.out_limit = e;
         if (p.offs_out) {
-          const int64_t so = group_start(p.offs_out, gg), eo = p.offs_out[gg];
-          const int64_t real_end = s + (eo > so ? eo - so : 0);  // the group's real rows, padded coordinates
+          const int64_t real_end = s + (eo - so);  // the group's real rows, padded coordinates
           T.out_shift = so - s;
           T.out_limit = real_end < e ? real_end : e;
         }
         break;
       }
       cum += tiles;
+      s = e;
+      so = eo;
     }
     T.valid = found >= 0;
     g = found < 0 ? 0 : found;
@@ -198,8 +208,13 @@ __device__ inline Tile tile_at(const GemmArgs& p, int64_t t) {
     T.a_row_end = p.M;
     T.b_row0 = n_tile * BN;
     T.b_row_end = p.N;
-    T.k_beg = EB * (p.offs ? group_start(p.offs, g) : 0);
-    T.k_end = EB * (p.offs ? p.offs[g] : p.K);
+    // the group's token range clamped into [0, K] (out-of-contract offs: wrong sums,
+    // no access outside the operands)
+    int64_t kb = p.offs ? group_start(p.offs, g) : 0, ke = p.offs ? p.offs[g] : p.K;
+    kb = kb < 0 ? 0 : (kb > p.K ? p.K : kb);
+    ke = ke < kb ? kb : (ke > p.K ? p.K : ke);
+    T.k_beg = EB * kb;
+    T.k_end = EB * ke;
     if (p.splits > 1) {
       // split sp of `splits` takes a run of whole 256-wide windows (counted from the
       // 256-aligned start of the group's range), so no split adds masked steps; it
@@ -751,14 +766,15 @@ hipError_t launch(mx::GemmArgs& p, int out_bf16, hipStream_t stream) {
 
 // M-grouped: C[m x n] = A[m x k] . B_g[n x k]^T per row group (forward and dgrad).
 hipError_t mx_launch_gemm_mgroup(const uint8_t* a, const uint8_t* a_s, const uint8_t* b, const uint8_t* b_s,
-                                 const int32_t* offs, const int32_t* offs_out, int groups, int64_t m, int64_t n,
-                                 int64_t k, void* out, int out_bf16, hipStream_t stream) {
+                                 const int32_t* offs, const int32_t* offs_out, int groups, int64_t m, int64_t out_rows,
+                                 int64_t n, int64_t k, void* out, int out_bf16, hipStream_t stream) {
   mx::GemmArgs p{};
   p.a = a; p.a_s = a_s; p.b = b; p.b_s = b_s; p.offs = offs; p.offs_out = offs_out; p.out = out;
   p.lda = k; p.ldb = k;
   p.a_rows = m; p.b_rows = (int64_t)groups * n;
   p.a_ktiles = p.b_ktiles = mx::scale_tiles_k(k / 32);
   p.M = m; p.N = n; p.K = k; p.ldo = n;
+  p.out_rows = offs_out ? out_rows : m;
   p.groups = groups;
   return launch<mx::MODE_MGROUP, mx::EL_MXFP8>(p, out_bf16, stream);
 }
@@ -786,6 +802,7 @@ hipError_t mx_launch_gemm_bf16_mgroup(const uint16_t* a, const uint16_t* b, cons
   p.lda = 2 * k; p.ldb = 2 * k;
   p.a_rows = m; p.b_rows = (int64_t)groups * n;
   p.M = m; p.N = n; p.K = k; p.ldo = n;
+  p.out_rows = m;
   p.groups = groups;
   return launch<mx::MODE_MGROUP, mx::EL_BF16>(p, out_bf16, stream);
 }

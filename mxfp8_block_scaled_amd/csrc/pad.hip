@@ -81,6 +81,39 @@ __global__ __launch_bounds__(kPadThreads) void k_unpad_rows(const uint8_t* __res
   }
 }
 
+// Checks offs against the grouped calls' preconditions. One workgroup: each thread
+// tests its groups' ends against the previous end, the required multiple and
+// [0, m]; the violation bits and the first offending group are reduced in LDS and
+// written by thread 0 (no global atomics, nothing read back on the host).
+__global__ __launch_bounds__(kPadThreads) void k_check_offs(const int32_t* __restrict__ offs, int groups, int64_t m,
+                                                            int multiple, int32_t* __restrict__ result) {
+  __shared__ int s_bits, s_first;
+  if (threadIdx.x == 0) {
+    s_bits = 0;
+    s_first = 0x7FFFFFFF;
+  }
+  __syncthreads();
+  int bits = 0, first = 0x7FFFFFFF;
+  for (int g = threadIdx.x; g < groups; g += kPadThreads) {
+    const int64_t e = offs[g], prev = g ? offs[g - 1] : 0;
+    int b = 0;
+    if (e < prev) b |= 1;                // decreasing
+    if (e % multiple != 0) b |= 2;       // not a multiple
+    if (e < 0 || e > m) b |= 4;          // outside [0, m]
+    if (b) {
+      bits |= b;
+      first = g < first ? g : first;
+    }
+  }
+  atomicOr(&s_bits, bits);
+  atomicMin(&s_first, first);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    result[0] = s_bits;
+    result[1] = s_first == 0x7FFFFFFF ? -1 : s_first;
+  }
+}
+
 // Workgroups: enough waves for every row, at most 8 workgroups per compute unit.
 inline unsigned pad_grid(int64_t rows) {
   const int64_t need = (rows + kPadThreads / 64 - 1) / (kPadThreads / 64);
@@ -104,5 +137,11 @@ hipError_t mx_launch_unpad(const void* y_pad, int64_t rows_pad, int64_t row_byte
   hipLaunchKernelGGL(mx::k_unpad_rows, dim3(mx::pad_grid(rows)), dim3(mx::kPadThreads), 0, stream,
                      (const uint8_t*)y_pad, rows_pad, row_bytes, ld_pad_bytes, offs, groups, (uint8_t*)y,
                      (int32_t)rows, ld_y_bytes);
+  return hipGetLastError();
+}
+
+hipError_t mx_launch_check_offs(const int32_t* offs, int groups, int64_t m, int multiple, int32_t* result,
+                                hipStream_t stream) {
+  hipLaunchKernelGGL(mx::k_check_offs, dim3(1), dim3(mx::kPadThreads), 0, stream, offs, groups, m, multiple, result);
   return hipGetLastError();
 }

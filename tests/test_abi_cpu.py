@@ -216,3 +216,16 @@ def test_fused_padding_calls_validation(lib):
     d = lib.mx_grouped_mm_dgrad_padded
     assert d(P, P, P, P, P2, P2, 3, 256, 40, 64, 64, P2, 0, None) in (MX_E_DEVICE, 0)
     assert d(P, P, P, P, P2, P2, 3, 256, 40, 48, 64, P2, 0, None) == MX_E_SHAPE  # contraction n % 32
+
+
+def test_check_offs_validation(lib):
+    f = lib.mx_check_offs
+    assert f(P, 4, 1024, 32, P2, None) in (MX_E_DEVICE, 0)
+    assert f(P, 0, 1024, 32, P2, None) == MX_E_SHAPE  # groups
+    assert f(P, 4, -1, 32, P2, None) == MX_E_SHAPE  # m
+    assert f(P, 4, (1 << 31) + 1, 32, P2, None) == MX_E_SHAPE  # m above 2^31
+    assert f(P, 4, 1024, 0, P2, None) == MX_E_SHAPE  # multiple
+    assert f(None, 4, 1024, 32, P2, None) == MX_E_NULL
+    assert f(P, 4, 1024, 32, None, None) == MX_E_NULL
+    assert f(P + 2, 4, 1024, 32, P2, None) == MX_E_ALIGN
+    assert f(P, 4, 1024, 32, P2 + 1, None) == MX_E_ALIGN
