@@ -473,29 +473,33 @@ __global__ __launch_bounds__(64 * WGM * WGN) __attribute__((amdgpu_waves_per_eu(
     constexpr int ES = OUT_BF16 ? 2 : 4;
     constexpr int ROW_BYTES = C::WN * ES;
     constexpr int CPR = ROW_BYTES / 16;                      // 16-byte chunks per row
+    // rows of a power-of-two number of chunks are XOR-swizzled in place; others (96-
+    // column waves: 12 or 24 chunks) get one spare chunk per row, an odd pitch in
+    // chunks, so 32 rows at one column spread over the banks
+    constexpr bool POW2 = (CPR & (CPR - 1)) == 0;
+    constexpr int PITCH = POW2 ? ROW_BYTES : ROW_BYTES + 16;
     constexpr int EPI_BYTES = NST * C::STAGE_BYTES / C::WAVES;  // staging bytes per wave
-    constexpr int RP = epi_rows(C::WM, EPI_BYTES / ROW_BYTES);  // rows per pass
-    constexpr int RPI = 64 / CPR;                            // rows per 16-byte read / store
-    static_assert((CPR & (CPR - 1)) == 0 && CPR <= 64, "rows of whole power-of-two 16-byte chunks");
-    static_assert(RP * ROW_BYTES <= EPI_BYTES && RP % RPI == 0 && C::WM % RP == 0, "epilogue staging shape");
+    constexpr int RP = epi_rows(C::WM, EPI_BYTES / PITCH);   // rows per pass
+    constexpr int READS = RP * CPR / 64;                     // 16-byte reads / stores per lane and pass
+    static_assert(CPR <= 64 && RP * CPR % 64 == 0, "rows of whole 16-byte chunks");
+    static_assert(RP * PITCH <= EPI_BYTES && C::WM % RP == 0, "epilogue staging shape");
     const int64_t wrow0 = T.a_row0 + wm * C::WM;
     const int64_t wcol0 = T.col0 + wn * C::WN;
     if (((p.ldo * ES) & 15) == 0 && wcol0 + C::WN <= p.N) {
       uint8_t* stg = lds + wave * EPI_BYTES;
-      const int ch = l % CPR;
 #pragma unroll
       for (int pass = 0; pass < C::WM / RP; ++pass) {
 #pragma unroll
         for (int ii = 0; ii < RP / 32; ++ii) {
           const int i = pass * (RP / 32) + ii;
           const int r = 32 * ii + (l & 31);
-          uint8_t* srow = stg + r * ROW_BYTES;
+          uint8_t* srow = stg + r * PITCH;
 #pragma unroll
           for (int j = 0; j < C::TN; ++j)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
               const int lb = (32 * j + 8 * q + 4 * h) * ES;  // byte of the lane's first column
-              uint8_t* dst = srow + ((((lb >> 4) ^ r) & (CPR - 1)) << 4) + (lb & 15);
+              uint8_t* dst = srow + (POW2 ? ((((lb >> 4) ^ r) & (CPR - 1)) << 4) + (lb & 15) : lb);
               const v16f& c = acc[i][j];
               if (OUT_BF16)
                 *(u32x2*)dst = (u32x2){bf16x2_rne(c[4 * q], c[4 * q + 1]), bf16x2_rne(c[4 * q + 2], c[4 * q + 3])};
@@ -506,11 +510,12 @@ __global__ __launch_bounds__(64 * WGM * WGN) __attribute__((amdgpu_waves_per_eu(
 // bf16 rows: fully unrolled; fp32 (two staging passes): by 4, as the full
         // unroll keeps too many read-back loads in flight beside the accumulators
         // still live for the second pass and spills
-        constexpr int EPI_UNROLL = OUT_BF16 ? RP / RPI : 4;
+        constexpr int EPI_UNROLL = OUT_BF16 ? READS : 4;
 #pragma unroll EPI_UNROLL
-        for (int k = 0; k < RP / RPI; ++k) {
-          const int r = k * RPI + l / CPR;
-          const u32x4 d = *(const u32x4*)(stg + r * ROW_BYTES + (((ch ^ r) & (CPR - 1)) << 4));
+        for (int k = 0; k < READS; ++k) {
+          const int qi = 64 * k + l;  // chunk index in the pass: row qi / CPR, chunk qi % CPR
+          const int r = qi / CPR, ch = qi % CPR;
+          const u32x4 d = *(const u32x4*)(stg + r * PITCH + (POW2 ? (((ch ^ r) & (CPR - 1)) << 4) : ch * 16));
           const int64_t row = wrow0 + pass * RP + r;
           // Non-temporal: the output bypasses the caches, so a tile's stores drain
           // faster and no dirty lines are left for the kernels that follow to write
@@ -692,6 +697,7 @@ enum Tiling {
   TILE_128x256 = 2,  // 128x256, 2x2 waves of 64x128, 3-deep ring, 80 KB: two blocks per CU
   TILE_192x256 = 3,  // 192x256, 1x4 waves of 192x64, 4-deep ring, 120 KB: one block per CU
   TILE_256_8W = 4,   // 256x256, 2x4 waves of 128x64, 4-deep ring, 144 KB: one block, two waves per SIMD
+  TILE_256x192 = 5,  // 256x192, 2x2 waves of 128x96, 4-deep ring, 120 KB: one block per CU
 };
 
 template <int MODE, int EL>
@@ -701,6 +707,7 @@ hipError_t launch_tiling(int tiling, const mx::GemmArgs& p, int out_bf16, hipStr
     case TILE_128x256: return launch_cfg<128, 256, 2, 2, 3, 2, MODE, EL>(p, out_bf16, stream);
     case TILE_192x256: return launch_cfg<192, 256, 1, 4, 4, 1, MODE, EL>(p, out_bf16, stream);
     case TILE_256_8W: return launch_cfg<256, 256, 2, 4, 4, 2, MODE, EL>(p, out_bf16, stream);
+    case TILE_256x192: return launch_cfg<256, 192, 2, 2, 4, 1, MODE, EL>(p, out_bf16, stream);
     default: return launch_cfg<256, 256, 2, 2, 4, 1, MODE, EL>(p, out_bf16, stream);
   }
 }
@@ -719,6 +726,12 @@ int choose_tiling(const mx::GemmArgs& p, int out_bf16) {
   // blocks per compute unit overlap one block's stores with the other's loop
   // (16384x4096 output over K=576: 55 us against 69-75 us for 256x256 tiles)
   if (MODE == mx::MODE_MGROUP && p.K <= 1024) return TILE_128x256;
+  // M-grouped output columns that 192-column tiles cover with at least 1/8 less
+  // padding than 256-column ones, in 128 or more tiles (the 576-wide forward: 576
+  // against 768 columns, 44.5 against 48.3 us with eight-wave 256x256 tiles)
+  if (MODE == mx::MODE_MGROUP && (p.N + 191) / 192 * 192 * 8 <= (p.N + 255) / 256 * 256 * 7 &&
+      ((p.M + 255) / 256) * ((p.N + 191) / 192) >= 128)
+    return TILE_256x192;
   // K-grouped output rows that 192-row tiles cover with at least 1/8 less padding
   // than 256-row ones (576 rows: 576 against 768, 58-59 us against 68-72 us); a
   // smaller saving does not repay the lower operand reuse of 192-row tiles (4096 rows

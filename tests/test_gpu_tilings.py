@@ -10,7 +10,9 @@ partial tiles on both output edges:
   * 128x256 over a three-deep ring, two blocks per compute unit: M-grouped with a
     contraction of at most 1024 and >= 128 tiles;
   * 192x256: K-grouped outputs whose rows 192-row tiles cover with at least 1/8
-    less padding than 256-row ones, without and with split contractions.
+    less padding than 256-row ones, without and with split contractions;
+  * 256x192: M-grouped outputs whose columns 192-column tiles cover with at least
+    1/8 less padding (96-column waves: the epilogue's padded-pitch staging).
 The bit-exact sweep below also reaches 128x128 and the four-wave 256x256 (bf16
 output, 512 or more tiles), which the small-shape and full-size tests cover too.
 """
@@ -186,6 +188,8 @@ def sample_rows(rng, upto, count):
     (3104, 2336, 576, 3, "128x256"),        # K <= 1024
     (8192, 4128, 1088, 4, "256x256"),       # 32 x 17 = 544 tiles (bf16 out; fp32: 8-wave)
     (1000, 800, 320, 3, "128x128"),         # 4 x 4 tiles
+    (16384, 576, 1280, 2, "256x192"),       # 64 x 3 tiles of 256 x 192: 96-column waves
+    (16384, 352, 1088, 2, "256x192 ragged"),  # 64 x 2, the second column tile partial
 ])
 def test_exact_fwd_tilings(oracle, m, n, k, G, name):
     rng = np.random.default_rng(m + n + k)
