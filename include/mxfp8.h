@@ -314,6 +314,15 @@ mx_status mx_grouped_mm_bf16_wgrad(const uint16_t* dy_t, const uint16_t* x_t, co
 mx_status mx_check_offs(const int32_t* offs, int32_t groups, int64_t m, int32_t multiple, int32_t* result,
                         void* stream);
 
+/* Measurement aid, not part of the computation: a register-only loop of the
+ * block-scaled MFMA (v_mfma_scale_f32_32x32x64_f8f6f4, fixed pseudo-random E4M3
+ * operands, unit scales) on every SIMD, so a caller can time the MXFP8 rate this
+ * part sustains and report the GEMMs against it beside the nominal peak.
+ *   iters  loop trips, 1 <= iters < 2^31; one call performs iters * 2^30 flops
+ *   sink   device float[256] (written with checksums; keeps the loop)
+ * Errors: MX_E_SHAPE, MX_E_NULL, MX_E_ALIGN (sink not 4-byte aligned). */
+mx_status mx_probe_mfma(int64_t iters, float* sink, void* stream);
+
 /* Rows of the padded buffer for any split of `rows` rows into `groups` groups:
  * rows + 31 * groups rounded up to a multiple of 256 (a group grows by at most 31
  * rows; the rounding keeps the token axis, which is the row pitch of the dim1

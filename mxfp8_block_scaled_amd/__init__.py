@@ -278,6 +278,15 @@ def mx_check_offs(offs, m, multiple=32, result=None):
     return result
 
 
+def mx_probe_mfma(iters, sink=None, device="cuda:0"):
+    """Register-only loop of the block-scaled MFMA (iters * 2^30 flops), for timing the
+    MXFP8 rate the part sustains. Returns `sink` (device float32[256], written)."""
+    if sink is None:
+        sink = torch.empty(256, dtype=torch.float32, device=device)
+    _lib.call("mx_probe_mfma", int(iters), _ptr(sink), _stream(sink))
+    return sink
+
+
 def mx_padded_rows(rows, groups):
     """Rows of the padded buffer for `rows` token rows in `groups` groups."""
     n = _lib.load().mx_padded_rows(int(rows), int(groups))

@@ -31,6 +31,7 @@ SIGNATURES = {
     "mx_grouped_mm_bf16_wgrad": (_INT, [_P, _P, _P, _I32, _I64, _I64, _I64, _P, _INT, _P]),
     "mx_padded_rows": (_I64, [_I64, _I32]),
     "mx_check_offs": (_INT, [_P, _I32, _I64, _I32, _P, _P]),
+    "mx_probe_mfma": (_INT, [_I64, _P, _P]),
     "mx_pad_quantize_dim0_dim1": (_INT, [_P, _I64, _I64, _I64, _P, _I32, _I64, _P, _P, _P, _P, _P, _P]),
     "mx_grouped_mm_fwd_padded": (_INT, [_P, _P, _P, _P, _P, _P, _I32, _I64, _I64, _I64, _I64, _P, _INT, _P]),
     "mx_grouped_mm_dgrad_padded": (_INT, [_P, _P, _P, _P, _P, _P, _I32, _I64, _I64, _I64, _I64, _P, _INT, _P]),

@@ -13,7 +13,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmxfp8.so")
-SOURCES = ["abi.cpp", "cast.hip", "gemm.hip", "pad.hip", "convert.hip"]
+SOURCES = ["abi.cpp", "cast.hip", "gemm.hip", "pad.hip", "convert.hip", "probe.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

@@ -32,6 +32,7 @@ hipError_t mx_launch_gemm_bf16_kgroup(const uint16_t*, const uint16_t*, const in
 hipError_t mx_launch_gemm_mgroup(const uint8_t*, const uint8_t*, const uint8_t*, const uint8_t*, const int32_t*,
                                  const int32_t*, int, int64_t, int64_t, int64_t, int64_t, void*, int, hipStream_t);
 hipError_t mx_launch_check_offs(const int32_t*, int, int64_t, int, int32_t*, hipStream_t);
+hipError_t mx_launch_probe_mfma(int64_t, float*, hipStream_t);
 hipError_t mx_launch_pad_both(const uint16_t*, int64_t, int64_t, int64_t, const int32_t*, int, int64_t, uint8_t*,
                               uint8_t*, uint8_t*, uint8_t*, int32_t*, hipStream_t);
 hipError_t mx_launch_gemm_kgroup(const uint8_t*, const uint8_t*, const uint8_t*, const uint8_t*, const int32_t*, int,
@@ -468,6 +469,14 @@ mx_status mx_check_offs(const int32_t* offs, int32_t groups, int64_t m, int32_t 
   if ((uintptr_t)result & 3) return fail(MX_E_ALIGN, "result is not 4-byte aligned");
   TRY(check_device());
   return launched(mx_launch_check_offs(offs, groups, m, multiple, result, (hipStream_t)stream), "mx_check_offs");
+}
+
+mx_status mx_probe_mfma(int64_t iters, float* sink, void* stream) {
+  if (iters < 1 || iters > kInt32Max) return fail(MX_E_SHAPE, "iters = %lld must be in [1, 2^31)", (long long)iters);
+  if (!sink) return fail(MX_E_NULL, "sink is NULL");
+  if ((uintptr_t)sink & 3) return fail(MX_E_ALIGN, "sink is not 4-byte aligned");
+  TRY(check_device());
+  return launched(mx_launch_probe_mfma(iters, sink, (hipStream_t)stream), "mx_probe_mfma");
 }
 
 mx_status mx_pad_token_groups(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, const int32_t* offs,

@@ -229,3 +229,12 @@ def test_check_offs_validation(lib):
     assert f(P, 4, 1024, 32, None, None) == MX_E_NULL
     assert f(P + 2, 4, 1024, 32, P2, None) == MX_E_ALIGN
     assert f(P, 4, 1024, 32, P2 + 1, None) == MX_E_ALIGN
+
+
+def test_probe_mfma_validation(lib):
+    f = lib.mx_probe_mfma
+    assert f(16, P2, None) in (MX_E_DEVICE, 0)
+    assert f(0, P2, None) == MX_E_SHAPE
+    assert f(1 << 31, P2, None) == MX_E_SHAPE
+    assert f(16, None, None) == MX_E_NULL
+    assert f(16, P2 + 2, None) == MX_E_ALIGN

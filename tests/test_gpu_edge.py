@@ -127,3 +127,11 @@ def test_bf16_fwd_at_contraction_limit(oracle):
     got = host(mx.mx_grouped_mm_bf16_fwd(dev_bf16(a), dev_bf16(b), None, m, n, k, out_dtype=mx.MX_OUT_F32))
     fa, fb = oracle.bf16_to_f64(a), oracle.bf16_to_f64(b)
     check_f32(oracle, got, fa @ fb.T, "bf16 fwd k=2^21", np.abs(fa) @ np.abs(fb).T, k)
+
+
+def test_mfma_probe_runs():
+    """The measurement loop runs and leaves finite checksums (4 trips: 2^32 flops)."""
+    say("[edge] mfma probe")
+    sink = mx.mx_probe_mfma(4)
+    s = host(sink)
+    assert s.shape == (256,) and np.all(np.isfinite(s)) and np.any(s != 0)
