@@ -194,7 +194,6 @@ def main():
         # forward as MXFP8 (dim0 casts), backward from bf16 operands: transposes or
         # transposed dequantization (2 B written per element; 2 B read for bf16, 1 + 1/32
         # for codes) and bf16 grouped GEMMs
-        from mxfp8_block_scaled_amd import backward as bwd  # noqa: F401
         wt16, xt16, dyt16 = bf(G, K, N), bf(K, M), bf(N, M)
         tb = lambda n_elem: 4 * n_elem  # noqa: E731
         db = lambda n_elem: n_elem * (2 + 1 + 1 / 32)  # noqa: E731

@@ -1,7 +1,6 @@
 """The C-ABI library loads, exports every declared entry point and validates its
 arguments on the host (no GPU needed: nothing here launches a kernel)."""
 
-import ctypes
 import os
 import re
 

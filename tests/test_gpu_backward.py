@@ -9,13 +9,12 @@ compared with the oracle's arms.
 
 import numpy as np
 import pytest
-import torch
 
 import mxfp8_block_scaled_amd as mx
 from mxfp8_block_scaled_amd import backward, synth
 
 from gemm_check import check_bf16, check_f32
-from gpu_util import dev_bf16, dev_i32, dev_u8, host, require_gpu, say, stress_blocks
+from gpu_util import dev_bf16, dev_i32, host, require_gpu, say, stress_blocks
 
 pytestmark = pytest.mark.gpu
 

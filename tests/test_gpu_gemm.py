@@ -8,12 +8,11 @@ within one ulp of the correctly rounded value or inside the bound).
 
 import numpy as np
 import pytest
-import torch
 
 import mxfp8_block_scaled_amd as mx
 from mxfp8_block_scaled_amd import synth
 
-from gemm_check import REL_FRO_HW, check_bf16, check_f32  # noqa: F401
+from gemm_check import check_bf16, check_f32
 from gpu_util import dev_bf16, dev_i32, dev_u8, host, require_gpu, say
 
 pytestmark = pytest.mark.gpu
