@@ -29,6 +29,13 @@ arm ARM (ao fork PR 10, "Design notes"): "quantized" (the MXFP8 backward),
 "high_precision" (transposes of the saved bf16 W, X, dY and bf16 grouped GEMMs) or
 "dequantized" (the forward's codes of W and X dequantized transposed, dY
 transposed, bf16 grouped GEMMs); bf16 GEMMs are priced against the bf16 peak.
+
+--workload deepseek_share: one GPU's expert share of a DeepSeek-V3-like MoE layer
+(32 experts, hidden 7168, expert FFN 2048, 4096 tokens x top-8 = 32768 routed
+rows, Zipf(1.2) group sizes with 3 experts empty): one-pass casts of X, W1, H,
+W2, dY2, dY1 and the grouped fwd, dgrad and wgrad of the gate/up projection
+(W1 [32, 4096, 7168]) and the down projection (W2 [32, 7168, 2048]). No CPU
+baseline or traffic figure in this mode.
 """
 
 import argparse
@@ -72,6 +79,10 @@ def parse():
                          "group boundaries, runs the grouped passes on the padded offsets and unpads Y and dX")
     ap.add_argument("--backward", default=None, choices=["quantized", "high_precision", "dequantized"],
                     help="time the MoE grouped step (forward + the named backward override arm) instead")
+    ap.add_argument("--workload", default="moe_g8", choices=["moe_g8", "deepseek_share"],
+                    help="deepseek_share: one GPU's share of a DeepSeek-V3-like MoE layer (32 experts, hidden "
+                         "7168, FFN 2048, 32768 routed rows, Zipf group sizes, 3 experts empty), fwd+bwd of "
+                         "both expert projections, instead of the default MoE step")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a 1 GiB device-to-device copy instead (reference for HBM byte counters)")
     return ap.parse_args()
@@ -101,6 +112,64 @@ def load_traffic(kernel_key, units_per_launch):
     if not e or e.get("source_hash") != src_hash():
         return None
     return e.get("hbm_bytes_per_launch")
+
+
+def deepseek_share_ops(mx, synth, to_dev, dev):
+    """The expert share's training step: one-pass casts of X, W1, H, W2, dY2, dY1 and the
+    grouped fwd, dgrad and wgrad of the gate/up (X -> 4096) and down (H -> 7168)
+    projections; 8.659 TFLOP of GEMMs per step."""
+    import torch
+
+    d = synth.deepseek_share(0)
+    offs_np = d["offs"]
+    t = {k: to_dev(v) for k, v in d.items() if k != "offs"}
+    del d
+    offs = torch.from_numpy(offs_np).to(dev)
+    E, N1, H_ = t["w1"].shape  # 32, 4096, 7168
+    _, _, F = t["w2"].shape     # 2048
+    R = t["x"].shape[0]         # 32768 routed rows
+    u8 = lambda *s: torch.empty(s, dtype=torch.uint8, device=dev)  # noqa: E731
+    bf = lambda *s: torch.empty(s, dtype=torch.bfloat16, device=dev)  # noqa: E731
+    sb = mx.mx_scale_bytes
+    q = {}
+    for name, (rows, cols, batch) in {"x": (R, H_, 1), "w1": (N1, H_, E), "h": (R, F, 1), "w2": (H_, F, E),
+                                      "dy2": (R, H_, 1), "dy1": (R, N1, 1)}.items():
+        q[name] = (u8(batch * rows, cols), u8(sb(batch * rows, cols)),
+                   u8(cols, rows) if batch == 1 else u8(batch, cols, rows), u8(sb(batch * cols, rows)))
+    y1, y2, dh, dx = bf(R, N1), bf(R, H_), bf(R, F), bf(R, H_)
+    dw1, dw2 = bf(E, N1, H_), bf(E, H_, F)
+    both = lambda n_elem: n_elem * BOTH_BYTES_PER_ELEM  # noqa: E731
+
+    def cast(name):
+        return ("cast_dim0+dim1 " + name, "cast", both(t[name].numel()),
+                lambda: mx.mx_quantize_dim0_dim1(t[name], *q[name]))
+
+    ops = [
+        cast("x"), cast("w1"),
+        ("gemm_fwd gate/up", "gemm", 2 * R * N1 * H_,
+         lambda: mx.mx_grouped_mm_fwd(q["x"][0], q["x"][1], q["w1"][0], q["w1"][1], offs, R, N1, H_, out=y1)),
+        cast("h"), cast("w2"),
+        ("gemm_fwd down", "gemm", 2 * R * H_ * F,
+         lambda: mx.mx_grouped_mm_fwd(q["h"][0], q["h"][1], q["w2"][0], q["w2"][1], offs, R, H_, F, out=y2)),
+        cast("dy2"),
+        ("gemm_dgrad down", "gemm", 2 * R * H_ * F,
+         lambda: mx.mx_grouped_mm_dgrad(q["dy2"][0], q["dy2"][1], q["w2"][2], q["w2"][3], offs, R, H_, F, out=dh)),
+        ("gemm_wgrad down", "gemm", 2 * R * H_ * F,
+         lambda: mx.mx_grouped_mm_wgrad(q["dy2"][2], q["dy2"][3], q["h"][2], q["h"][3], offs, R, H_, F, out=dw2,
+                                        out_dtype=mx.MX_OUT_BF16)),
+        cast("dy1"),
+        ("gemm_dgrad gate/up", "gemm", 2 * R * N1 * H_,
+         lambda: mx.mx_grouped_mm_dgrad(q["dy1"][0], q["dy1"][1], q["w1"][2], q["w1"][3], offs, R, N1, H_, out=dx)),
+        ("gemm_wgrad gate/up", "gemm", 2 * R * N1 * H_,
+         lambda: mx.mx_grouped_mm_wgrad(q["dy1"][2], q["dy1"][3], q["x"][2], q["x"][3], offs, R, N1, H_, out=dw1,
+                                        out_dtype=mx.MX_OUT_BF16)),
+    ]
+    config = {"workload": "deepseek_share fwd+dgrad+wgrad: 32 experts, hidden 7168, FFN 2048 (gate/up N=4096, "
+                          "down N=7168 over K=2048), 32768 routed rows, Zipf(1.2) group sizes with 3 empty experts; "
+                          "one-pass casts of X, W1, H, W2, dY2, dY1",
+              "M": R, "K": H_, "N": N1, "G": E, "narrow": None, "offs": offs_np.tolist(), "rows_padded": None,
+              "parallelism": "none (1 GPU)"}
+    return ops, config
 
 
 def main():
@@ -288,6 +357,14 @@ def main():
             n_dgrad, n_wgrad,
         ]
 
+    share_config = None
+    if args.workload == "deepseek_share":
+        assert not (unaligned or args.backward or args.separate_casts), \
+            "--workload deepseek_share runs its own step; it takes none of the moe_g8 step's variants"
+        del buf, X, W, dY, Wn, dYn
+        torch.cuda.empty_cache()
+        ops, share_config = deepseek_share_ops(mx, synth, to_dev, dev)
+
     if args.only:
         # the casts an op depends on still run once, untimed, so its inputs exist
         for _, _, _, fn in ops:
@@ -401,7 +478,7 @@ def main():
     dom_name, dom_kind, dom_units, _ = ops[dom_i]
     dom = per_op[dom_name]
     achieved = dom_units / (dom["us"] * 1e-6) / 1e12
-    traffic = None if (unaligned or args.backward) else load_traffic(dom_name, dom_units)
+    traffic = None if (unaligned or args.backward or share_config) else load_traffic(dom_name, dom_units)
     dom_peak = PEAKS[dom_kind]
     roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": dom_peak, "unit": "TFLOP/s",
                 "frac": round(achieved / dom_peak, 4), "traffic": traffic, "kernel": dom_name,
@@ -412,7 +489,7 @@ def main():
     # the GEMMs' time at their own peaks over their measured time
     gemm_ideal_us = sum(u / (PEAKS[k] * 1e12) * 1e6 for _, k, u, _ in ops if k in PEAKS)
 
-    cpu = None if (args.no_cpu_baseline or unaligned or args.backward) else cpu_baseline()
+    cpu = None if (args.no_cpu_baseline or unaligned or args.backward or share_config) else cpu_baseline()
     workload = ("moe_g8 fwd+dgrad+wgrad: G=8 experts, M=16384 tokens, K=N=4096, "
                 "grad_out 16384x4096, plus dense 576x4096 layer (32x32 weight scales, "
                 "576-wide contraction in dgrad)")
@@ -433,11 +510,12 @@ def main():
         "vs_baseline": None,
         "dtype": "mxfp8 (e4m3 x e4m3, e8m0 block scales, fp32 accumulate)" + (
             "; bf16 backward GEMMs" if args.backward in ("high_precision", "dequantized") else ""),
-        "data": "synthetic (seeded N(0,sigma) bf16, multinomial group sizes)",
-        "config": {"workload": workload,
-                   "M": M, "K": K, "N": N, "G": G, "narrow": None if (unaligned or args.backward) else NARROW,
-                   "offs": offs_np.tolist(), "rows_padded": Mg if unaligned else None,
-                   "parallelism": "none (1 GPU)"},
+        "data": "synthetic (seeded N(0,sigma) bf16, " + ("Zipf" if share_config else "multinomial")
+                + " group sizes)",
+        "config": share_config or {
+            "workload": workload, "M": M, "K": K, "N": N, "G": G,
+            "narrow": None if (unaligned or args.backward) else NARROW,
+            "offs": offs_np.tolist(), "rows_padded": Mg if unaligned else None, "parallelism": "none (1 GPU)"},
         "gemm_tflops": round(gemm_flops / (gemm_us * 1e-6) / 1e12, 1),
         "gemm_frac_of_peak": round(gemm_ideal_us / gemm_us, 4),
         "cast_gbps": round(cast_bytes / (cast_us * 1e-6) / 1e9, 1),
