@@ -88,12 +88,16 @@ def parse():
     return ap.parse_args()
 
 
-def src_hash():
+HASHED_SOURCES = ("gemm.hip", "cast.hip", "common.h", "group_table.h")
+
+
+def src_hash(csrc=None):
     """Hash of the GEMM and cast kernel sources with comments and whitespace removed:
     the counters in profiles/traffic.json hold while it matches."""
+    csrc = csrc or os.path.join(ROOT, "mxfp8_block_scaled_amd", "csrc")
     h = hashlib.sha256()
-    for f in ("gemm.hip", "cast.hip", "common.h", "group_table.h"):
-        with open(os.path.join(ROOT, "mxfp8_block_scaled_amd", "csrc", f)) as fh:
+    for f in HASHED_SOURCES:
+        with open(os.path.join(csrc, f)) as fh:
             text = fh.read()
         text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
         text = re.sub(r"//[^\n]*", "", text)
