@@ -67,7 +67,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     # 100 untimed steps (~0.13 s): after 5 the timed steps still ran ~7% slower (1.366-1.371 against
-    # 1.274-1.283 ms, same box), the device still raising its clocks
+    # 1.274-1.283 ms, same device), the device still raising its clocks
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--separate-casts", action="store_true",

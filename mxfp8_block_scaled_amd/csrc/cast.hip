@@ -274,7 +274,7 @@ __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(2))) vo
         // lookup gives the run of source rows, and the lane's 16 loads issue back to
         // back through one stepped pointer (a pointer per load needed 301 VGPRs, one
         // workgroup per compute unit, 94 us; walking group edges row by row between
-        // loads, 78 us; this, 69 us, on the MoE tokens, same box).
+        // loads, 78 us; this, 69 us, on the MoE tokens, same device).
         const GroupTable& gt = s_grp;
         const int g = upper_index(gt.pad_end, gth.groups, base);
         int64_t src0 = 0, real = 0;  // source row of padded row `base`; real rows from it on

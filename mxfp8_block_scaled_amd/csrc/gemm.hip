@@ -522,7 +522,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) __attribute__((amdgpu_waves_per_eu(
           // faster and no dirty lines are left for the kernels that follow to write
           // back. Split partials too: re-read once by the reduction, they cost that
           // reduction a little but left dirty they slowed the casts that follow more
-          // (MoE step 1.42-1.45 -> 1.36-1.38 ms, against plain stores on one box).
+          // (MoE step 1.42-1.45 -> 1.36-1.38 ms, against plain stores on one device).
           if (row < row_limit)
             __builtin_nontemporal_store(d, (u32x4*)(T.out_base + ((row + row_shift) * p.ldo + wcol0) * ES + ch * 16));
         }
@@ -715,7 +715,7 @@ hipError_t launch_tiling(int tiling, const mx::GemmArgs& p, int out_bf16, hipStr
 
 // The tiling for a problem (p.splits set). Measured on the MoE training step's
 // GEMMs (G=8, M=16384, K=N=4096, and a dense 576-wide layer), A/B inside the step on
-// one box; every tiling gives bit-identical results, since each output element sums
+// one device; every tiling gives bit-identical results, since each output element sums
 // its k-steps in the same order.
 template <int MODE, int EL>
 int choose_tiling(const mx::GemmArgs& p, int out_bf16) {
