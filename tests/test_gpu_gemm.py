@@ -79,6 +79,37 @@ def test_wgrad_exact_integer(oracle, n, k, m, sizes):
                 assert np.all(got[g] == 0)
 
 
+@pytest.mark.parametrize("G,seed", [(96, 1), (300, 2)])
+def test_many_groups_exact(oracle, G, seed):
+    """Many small groups, about a third of them empty: the forward's group search and
+    the wgrad's slice-major order over G groups (each group's raster in several
+    slices of uneven length), full outputs bit-exact."""
+    rng = np.random.default_rng(1000 + seed)
+    units = rng.integers(0, 4, size=G) * (rng.random(G) > 0.35)
+    sizes = 32 * units
+    offs = np.cumsum(sizes).astype(np.int32)
+    m = int(offs[-1]) + 64  # rows past the last group: unwritten (fwd), unread (wgrad)
+    n, k = 96, 160
+    a_q, a_s = exact_operands(rng, m, k)
+    b_q, b_s = exact_operands(rng, G * n, k)
+    say(f"[gemm many groups] fwd G={G} m={m} n={n} k={k}")
+    got = host(mx.mx_grouped_mm_fwd(dev_u8(a_q), phys(oracle, a_s), dev_u8(b_q), phys(oracle, b_s), dev_i32(offs),
+                                    m, n, k, groups=G, out_dtype=mx.MX_OUT_F32))
+    ref = oracle.mx_grouped_mm_fwd(a_q, a_s, b_q, b_s, offs, G)
+    rows = int(offs[-1])
+    assert np.array_equal(got[:rows], ref[:rows].astype(np.float32))
+    # wgrad: dW_g = dY_g^T X_g over each group's token range; [G, 288, 96] outputs in 2 x 1 tiles per group
+    nw, kw = 288, 96
+    dy_t, dy_s = exact_operands(rng, nw, m)
+    x_t, x_s = exact_operands(rng, kw, m)
+    say(f"[gemm many groups] wgrad G={G} n={nw} k={kw} m={m}")
+    got = host(mx.mx_grouped_mm_wgrad(dev_u8(dy_t), phys(oracle, dy_s), dev_u8(x_t), phys(oracle, x_s), dev_i32(offs),
+                                      m, nw, kw, groups=G, out_dtype=mx.MX_OUT_F32))
+    ref = oracle.mx_grouped_mm_wgrad(dy_t, dy_s, x_t, x_s, offs, G)
+    assert np.array_equal(got, ref.astype(np.float32))
+    assert not got[sizes == 0].any()
+
+
 def test_dgrad_exact_integer(oracle):
     rng = np.random.default_rng(3)
     m, n, k, sizes = 320, 96, 128, [64, 0, 256]
