@@ -222,7 +222,10 @@ mx_status mx_grouped_mm_dgrad(const uint8_t* dy, const uint8_t* dy_s, const uint
  * boundaries into S parts (enough to fill the device once, at most 16); fp32
  * partials go to a per-device workspace of S * groups * n * k * 4 bytes (rounded
  * up to 16), allocated by the library on first need, and a second kernel sums
- * them in split order, so results are deterministic. */
+ * them in split order, so results are deterministic. Every split-contraction
+ * wgrad on one device uses that one workspace: two such calls whose work may
+ * overlap (different streams, no event between them) race on it, so the caller
+ * orders them (one stream, or an event). */
 mx_status mx_grouped_mm_wgrad(const uint8_t* dy_t, const uint8_t* dy_t_s, const uint8_t* x_t, const uint8_t* x_t_s,
                               const int32_t* offs, int32_t groups, int64_t m, int64_t n, int64_t k, void* dw,
                               int out_dtype, void* stream);
