@@ -35,7 +35,7 @@ transposed, bf16 grouped GEMMs); bf16 GEMMs are priced against the bf16 peak.
 rows, Zipf(1.2) group sizes with 3 experts empty): one-pass casts of X, W1, H,
 W2, dY2, dY1 and the grouped fwd, dgrad and wgrad of the gate/up projection
 (W1 [32, 4096, 7168]) and the down projection (W2 [32, 7168, 2048]). No CPU
-baseline or traffic figure in this mode.
+baseline in this mode; `traffic` is the committed counter figure of its gate/up wgrad.
 """
 
 import argparse
@@ -482,7 +482,8 @@ def main():
     dom_name, dom_kind, dom_units, _ = ops[dom_i]
     dom = per_op[dom_name]
     achieved = dom_units / (dom["us"] * 1e-6) / 1e12
-    traffic = None if (unaligned or args.backward or share_config) else load_traffic(dom_name, dom_units)
+    traffic = (None if (unaligned or args.backward) else
+               load_traffic(("deepseek_share: " if share_config else "") + dom_name, dom_units))
     dom_peak = PEAKS[dom_kind]
     roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": dom_peak, "unit": "TFLOP/s",
                 "frac": round(achieved / dom_peak, 4), "traffic": traffic, "kernel": dom_name,
