@@ -326,6 +326,26 @@ mx_status mx_check_offs(const int32_t* offs, int32_t groups, int64_t m, int32_t 
  * Errors: MX_E_SHAPE, MX_E_NULL, MX_E_ALIGN (sink not 4-byte aligned). */
 mx_status mx_probe_mfma(int64_t iters, float* sink, void* stream);
 
+/* Measurement aid, not part of the computation: ONE block-scaled MFMA of either
+ * full-rate form on caller-given operands, so tests can pin the instruction's
+ * arithmetic (which sets how closely the GEMMs can match an exact fp32 sum).
+ *   form     MX_PROBE_32X32X64 (v_mfma_scale_f32_32x32x64_f8f6f4: R = 32, K = 64)
+ *            or MX_PROBE_16X16X128 (v_mfma_scale_f32_16x16x128_f8f6f4: R = 16,
+ *            K = 128), optionally | MX_PROBE_SWAP (b is the instruction's first
+ *            operand, the order the GEMM kernels use)
+ *   a, b     device [R x K] E4M3 codes, row-major
+ *   a_scale, b_scale  device [R x K/32] E8M0 bytes, row-major (block kb of row r)
+ *   c        device [R x R] float32 accumulator input, row-major
+ *   d        device [R x R] float32 (written): d[i][j] = c[i][j] + the
+ *            instruction's dot product of row i of a with row j of b
+ * One wave; asynchronous on `stream`. Errors: MX_E_DTYPE (form), MX_E_NULL,
+ * MX_E_ALIGN (c or d not 4-byte aligned). */
+#define MX_PROBE_32X32X64 0
+#define MX_PROBE_16X16X128 1
+#define MX_PROBE_SWAP 2
+mx_status mx_probe_mfma_dot(int form, const uint8_t* a, const uint8_t* a_scale, const uint8_t* b,
+                            const uint8_t* b_scale, const float* c, float* d, void* stream);
+
 /* Rows of the padded buffer for any split of `rows` rows into `groups` groups:
  * rows + 31 * groups rounded up to a multiple of 256 (a group grows by at most 31
  * rows; the rounding keeps the token axis, which is the row pitch of the dim1

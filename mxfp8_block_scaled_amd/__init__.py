@@ -41,6 +41,11 @@ __all__ = [
     "mx_grouped_mm_fwd_padded",
     "mx_grouped_mm_dgrad_padded",
     "mx_unpad_token_groups",
+    "mx_probe_mfma",
+    "mx_probe_mfma_dot",
+    "MX_PROBE_32X32X64",
+    "MX_PROBE_16X16X128",
+    "MX_PROBE_SWAP",
     "MXError",
     "library_path",
 ]
@@ -285,6 +290,30 @@ def mx_probe_mfma(iters, sink=None, device="cuda:0"):
         sink = torch.empty(256, dtype=torch.float32, device=device)
     _lib.call("mx_probe_mfma", int(iters), _ptr(sink), _stream(sink))
     return sink
+
+
+MX_PROBE_32X32X64, MX_PROBE_16X16X128, MX_PROBE_SWAP = 0, 1, 2
+
+
+def mx_probe_mfma_dot(form, a, a_scale, b, b_scale, c=None):
+    """One block-scaled MFMA on logical operands (a numerics aid): a, b [R, K] uint8 E4M3
+    codes and a_scale, b_scale [R, K/32] uint8 E8M0 bytes on the device (R, K = 32, 64
+    for MX_PROBE_32X32X64, 16, 128 for MX_PROBE_16X16X128), c [R, R] float32 (zeros if
+    None). Returns d [R, R] float32: c + the instruction's dot of row i of a with row j
+    of b. form | MX_PROBE_SWAP passes b as the instruction's first operand."""
+    R, K = (16, 128) if form & 1 else (32, 64)
+    for name, t, shape in (("a", a, (R, K)), ("b", b, (R, K)), ("a_scale", a_scale, (R, K // 32)),
+                           ("b_scale", b_scale, (R, K // 32))):
+        if t.dtype != torch.uint8 or tuple(t.shape) != shape or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous uint8 device tensor of shape {shape}")
+    if c is None:
+        c = torch.zeros((R, R), dtype=torch.float32, device=a.device)
+    if c.dtype != torch.float32 or tuple(c.shape) != (R, R) or not c.is_cuda or not c.is_contiguous():
+        raise ValueError(f"c must be a contiguous float32 device tensor of shape {(R, R)}")
+    d = torch.empty_like(c)
+    _lib.call("mx_probe_mfma_dot", int(form), _ptr(a), _ptr(a_scale), _ptr(b), _ptr(b_scale), _ptr(c), _ptr(d),
+              _stream(a))
+    return d
 
 
 def mx_padded_rows(rows, groups):

@@ -33,6 +33,8 @@ hipError_t mx_launch_gemm_mgroup(const uint8_t*, const uint8_t*, const uint8_t*,
                                  const int32_t*, int, int64_t, int64_t, int64_t, int64_t, void*, int, hipStream_t);
 hipError_t mx_launch_check_offs(const int32_t*, int, int64_t, int, int32_t*, hipStream_t);
 hipError_t mx_launch_probe_mfma(int64_t, float*, hipStream_t);
+hipError_t mx_launch_probe_dot(int, const uint8_t*, const uint8_t*, const uint8_t*, const uint8_t*, const float*, float*,
+                               hipStream_t);
 hipError_t mx_launch_pad_both(const uint16_t*, int64_t, int64_t, int64_t, const int32_t*, int, int64_t, uint8_t*,
                               uint8_t*, uint8_t*, uint8_t*, int32_t*, hipStream_t);
 hipError_t mx_launch_gemm_kgroup(const uint8_t*, const uint8_t*, const uint8_t*, const uint8_t*, const int32_t*, int,
@@ -477,6 +479,15 @@ mx_status mx_probe_mfma(int64_t iters, float* sink, void* stream) {
   if ((uintptr_t)sink & 3) return fail(MX_E_ALIGN, "sink is not 4-byte aligned");
   TRY(check_device());
   return launched(mx_launch_probe_mfma(iters, sink, (hipStream_t)stream), "mx_probe_mfma");
+}
+
+mx_status mx_probe_mfma_dot(int form, const uint8_t* a, const uint8_t* a_scale, const uint8_t* b,
+                            const uint8_t* b_scale, const float* c, float* d, void* stream) {
+  if (form < 0 || form > 3) return fail(MX_E_DTYPE, "form = %d must be in [0, 3]", form);
+  if (!a || !a_scale || !b || !b_scale || !c || !d) return fail(MX_E_NULL, "a NULL operand, scale or accumulator");
+  if (((uintptr_t)c & 3) || ((uintptr_t)d & 3)) return fail(MX_E_ALIGN, "c and d must be 4-byte aligned");
+  TRY(check_device());
+  return launched(mx_launch_probe_dot(form, a, a_scale, b, b_scale, c, d, (hipStream_t)stream), "mx_probe_mfma_dot");
 }
 
 mx_status mx_pad_token_groups(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, const int32_t* offs,

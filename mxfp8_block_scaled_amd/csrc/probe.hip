@@ -43,3 +43,85 @@ hipError_t mx_launch_probe_mfma(int64_t iters, float* sink, hipStream_t stream) 
   hipLaunchKernelGGL(mx::k_mfma_probe, dim3(mx::kProbeBlocks), dim3(mx::kProbeThreads), 0, stream, iters, sink);
   return hipGetLastError();
 }
+
+// One block-scaled MFMA of either full-rate form on logical operands, for the
+// numerics tests: a and b are row-major [R x K] E4M3 codes with row-major [R x K/32]
+// E8M0 bytes; the single wave builds the instruction's register images from them
+// (layouts measured on gfx950):
+//   32x32x64: lane l holds row l % 32, contraction bytes [16h, 16h+16) and
+//             [32+16h, 32+16h+16), h = l / 32; the scale of row r, block b comes
+//             from lane r + 32b; output lane l, register v = row 8(v/4) + 4h + v%4
+//             of the first operand, column l % 32 of the second.
+//   16x16x128: lane l holds row l % 16, contraction bytes [16h, 16h+16) and
+//             [64+16h, 64+16h+16), h = l / 16; the scale of row r, block b comes
+//             from lane r + 16b; output lane l, register v = row 4h + v of the
+//             first operand, column l % 16 of the second.
+// `swap` passes b as the instruction's first operand (the order the GEMM uses) and
+// transposes the result back, so d[i][j] always pairs row i of a with row j of b.
+namespace mx {
+
+template <int R, int K>
+__device__ inline void probe_operand(const uint8_t* x, const uint8_t* xs, int l, v8i& reg, int& sc) {
+  const int r = l % R, h = l / R;
+  const uint8_t* row = x + r * K;
+#pragma unroll
+  for (int d = 0; d < 8; ++d) {
+    const int k0 = d < 4 ? 16 * h + 4 * d : K / 2 + 16 * h + 4 * (d - 4);
+    reg[d] = (int)((unsigned)row[k0] | (unsigned)row[k0 + 1] << 8 | (unsigned)row[k0 + 2] << 16 |
+                   (unsigned)row[k0 + 3] << 24);
+  }
+  sc = xs[r * (K / 32) + h];
+}
+
+__global__ __launch_bounds__(64) void k_probe_dot(int form, const uint8_t* __restrict__ a,
+                                                  const uint8_t* __restrict__ a_s, const uint8_t* __restrict__ b,
+                                                  const uint8_t* __restrict__ b_s, const float* __restrict__ c,
+                                                  float* __restrict__ d) {
+  const int l = threadIdx.x;
+  const bool swap = form & 2;
+  if ((form & 1) == 0) {
+    v8i ra, rb;
+    int sa, sb;
+    probe_operand<32, 64>(a, a_s, l, ra, sa);
+    probe_operand<32, 64>(b, b_s, l, rb, sb);
+    v16f acc;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int r = 8 * (v / 4) + 4 * (l / 32) + v % 4, col = l % 32;
+      acc[v] = swap ? c[col * 32 + r] : c[r * 32 + col];
+    }
+    acc = swap ? __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(rb, ra, acc, 0, 0, 0, sb, 0, sa)
+               : __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ra, rb, acc, 0, 0, 0, sa, 0, sb);
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int r = 8 * (v / 4) + 4 * (l / 32) + v % 4, col = l % 32;
+      d[swap ? col * 32 + r : r * 32 + col] = acc[v];
+    }
+  } else {
+    v8i ra, rb;
+    int sa, sb;
+    probe_operand<16, 128>(a, a_s, l, ra, sa);
+    probe_operand<16, 128>(b, b_s, l, rb, sb);
+    v4f acc;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int r = 4 * (l / 16) + v, col = l % 16;
+      acc[v] = swap ? c[col * 16 + r] : c[r * 16 + col];
+    }
+    acc = swap ? __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(rb, ra, acc, 0, 0, 0, sb, 0, sa)
+               : __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ra, rb, acc, 0, 0, 0, sa, 0, sb);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int r = 4 * (l / 16) + v, col = l % 16;
+      d[swap ? col * 16 + r : r * 16 + col] = acc[v];
+    }
+  }
+}
+
+}  // namespace mx
+
+hipError_t mx_launch_probe_dot(int form, const uint8_t* a, const uint8_t* a_s, const uint8_t* b, const uint8_t* b_s,
+                               const float* c, float* d, hipStream_t stream) {
+  hipLaunchKernelGGL(mx::k_probe_dot, dim3(1), dim3(64), 0, stream, form, a, a_s, b, b_s, c, d);
+  return hipGetLastError();
+}

@@ -9,7 +9,7 @@ import torch
 import mxfp8_block_scaled_amd as mx
 from mxfp8_block_scaled_amd import synth
 
-from gemm_check import check_f32
+from gemm_check import check_f32, check_mx_fwd, check_mx_wgrad
 from gpu_util import dev_bf16, dev_i32, dev_u8, host, require_gpu, say
 
 pytestmark = pytest.mark.gpu
@@ -95,8 +95,7 @@ def test_fwd_at_contraction_limit(oracle):
     say(f"[edge] fwd m={m} n={n} k=2^22")
     got = host(mx.mx_grouped_mm_fwd(dev_u8(a), phys(oracle, a_s), dev_u8(b), phys(oracle, b_s), None, m, n, k,
                                     out_dtype=mx.MX_OUT_F32))
-    da, db = oracle.dequantize(a, a_s), oracle.dequantize(b, b_s)
-    check_f32(oracle, got, da @ db.T, "fwd k=2^22", np.abs(da) @ np.abs(db).T, k)
+    check_mx_fwd(oracle, got, a, a_s, b, b_s, None, 1, "fwd k=2^22", model_rows=[0])
 
 
 def test_wgrad_at_contraction_limit(oracle):
@@ -111,10 +110,7 @@ def test_wgrad_at_contraction_limit(oracle):
     say(f"[edge] wgrad n={n} k={k} m=2^22 offs={offs.tolist()}")
     got = host(mx.mx_grouped_mm_wgrad(dev_u8(a), phys(oracle, a_s), dev_u8(b), phys(oracle, b_s), dev_i32(offs), m,
                                       n, k, out_dtype=mx.MX_OUT_F32))
-    da, db = oracle.dequantize(a, a_s), oracle.dequantize(b, b_s)
-    ref = oracle.grouped_mm_wgrad(da, db, offs, 2)
-    absw = oracle.grouped_mm_wgrad(np.abs(da), np.abs(db), offs, 2)
-    check_f32(oracle, got, ref, "wgrad m=2^22", absw, int(offs[1] - offs[0]))
+    check_mx_wgrad(oracle, got, a, a_s, b, b_s, offs, 2, "wgrad m=2^22", model_rows=[0])
 
 
 def test_bf16_fwd_at_contraction_limit(oracle):

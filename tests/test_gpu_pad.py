@@ -15,7 +15,8 @@ import torch
 import mxfp8_block_scaled_amd as mx
 from mxfp8_block_scaled_amd import synth
 
-from gemm_check import check_f32
+import mfma_model
+from gemm_check import check_mx, check_mx_fwd, check_mx_wgrad
 from gpu_util import dev_bf16, dev_i32, dev_u8, host, require_gpu, say
 
 pytestmark = pytest.mark.gpu
@@ -157,21 +158,17 @@ def test_padded_moe_path(oracle, M, N, K, sizes):
     parts = [oracle.quantize_dim1(w[g]) for g in range(G)]
     owt, owts = np.concatenate([p[0] for p in parts]), np.concatenate([p[1] for p in parts])
 
-    deq = oracle.dequantize
-    ref_y = oracle.unpad_token_groups(oracle.mx_grouped_mm_fwd(oxq, oxs, owq, ows, ooffs_pad, G), offs.tolist(), M)
-    abs_y = oracle.unpad_token_groups(oracle.grouped_mm(np.abs(deq(oxq, oxs)), np.abs(deq(owq, ows)), ooffs_pad, G),
-                                      offs.tolist(), M)
-    check_f32(oracle, host(y), ref_y, "padded fwd", abs_y, K)
-    ref_dx = oracle.unpad_token_groups(oracle.mx_grouped_mm_fwd(odyq, odys, owt, owts, ooffs_pad, G), offs.tolist(), M)
-    abs_dx = oracle.unpad_token_groups(
-        oracle.grouped_mm(np.abs(deq(odyq, odys)), np.abs(deq(owt, owts)), ooffs_pad, G), offs.tolist(), M)
-    check_f32(oracle, host(dx), ref_dx, "padded dgrad", abs_dx, N)
-    ref_dw = oracle.mx_grouped_mm_wgrad(odyt, odyts, oxt, oxts, ooffs_pad, G)
-    abs_dw = oracle.grouped_mm_wgrad(np.abs(deq(odyt, odyts)), np.abs(deq(oxt, oxts)), ooffs_pad, G)
-    check_f32(oracle, host(dw), ref_dw, "padded wgrad", abs_dw, rows_pad)
-    for g in range(G):
-        if sizes[g] == 0:
-            assert not host(dw)[g].any()
+    def unpadded_check(got, aq, as_, bq, bs, name, k_len):
+        # the padded GEMM, then the unpad gather, against the oracle and the MFMA model
+        unpad = lambda t: oracle.unpad_token_groups(t, offs.tolist(), M)  # noqa: E731
+        ref = unpad(oracle.mx_grouped_mm_fwd(aq, as_, bq, bs, ooffs_pad, G))
+        h, ab = mfma_model.grouped_fwd(aq, as_, bq, bs, ooffs_pad, G)
+        bound = mfma_model.grouped_fwd(aq, as_, bq, bs, ooffs_pad, G, fn=mfma_model.run_bound_mm)
+        check_mx(oracle, got, ref, unpad(ab), k_len, name, h=unpad(h), bound=unpad(bound))
+
+    unpadded_check(host(y), oxq, oxs, owq, ows, "padded fwd", K)
+    unpadded_check(host(dx), odyq, odys, owt, owts, "padded dgrad", N)
+    check_mx_wgrad(oracle, host(dw), odyt, odyts, oxt, oxts, ooffs_pad, G, "padded wgrad")
 
 
 def exact_operands(rng, rows, k):
@@ -268,14 +265,10 @@ def test_padded_gemm_outputs(oracle, M, N, K, sizes):
     grouped = int(offs[-1])
     oxq, oxs = oracle.quantize_dim0(x)
     owq, ows = oracle.quantize_dim0(w.reshape(G * N, K))
-    ref_y = oracle.mx_grouped_mm_fwd(oxq, oxs, owq, ows, offs, G)
-    abs_y = oracle.grouped_mm(np.abs(oracle.dequantize(oxq, oxs)), np.abs(oracle.dequantize(owq, ows)), offs, G)
     gy, gdx = host(y), host(dx)
-    check_f32(oracle, gy[:grouped], ref_y[:grouped], "fwd padded->unpadded", abs_y[:grouped], K)
+    check_mx_fwd(oracle, gy, oxq, oxs, owq, ows, offs, G, "fwd padded->unpadded")
     odyq, odys = oracle.quantize_dim0(dy)
     parts = [oracle.quantize_dim1(w[g]) for g in range(G)]
     owt, owts = np.concatenate([p[0] for p in parts]), np.concatenate([p[1] for p in parts])
-    ref_dx = oracle.mx_grouped_mm_fwd(odyq, odys, owt, owts, offs, G)
-    abs_dx = oracle.grouped_mm(np.abs(oracle.dequantize(odyq, odys)), np.abs(oracle.dequantize(owt, owts)), offs, G)
-    check_f32(oracle, gdx[:grouped], ref_dx[:grouped], "dgrad padded->unpadded", abs_dx[:grouped], N)
+    check_mx_fwd(oracle, gdx, odyq, odys, owt, owts, offs, G, "dgrad padded->unpadded")
     assert np.all(np.isnan(gy[grouped:])) and np.all(np.isnan(gdx[grouped:]))

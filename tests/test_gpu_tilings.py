@@ -23,7 +23,7 @@ import pytest
 import mxfp8_block_scaled_amd as mx
 from mxfp8_block_scaled_amd import synth
 
-from gemm_check import check_bf16, check_f32
+from gemm_check import check_bf16, check_f32, check_mx_fwd, check_mx_wgrad
 from gpu_util import dev_bf16, dev_i32, dev_u8, host, require_gpu, say
 
 pytestmark = pytest.mark.gpu
@@ -50,11 +50,11 @@ def fwd_case(oracle, m, n, k, sizes, seed, name):
     got16 = host(mx.mx_grouped_mm_fwd(xq, xs, wq, ws, doffs, m, n, k, out_dtype=mx.MX_OUT_BF16))
     oxq, oxs = oracle.quantize_dim0(x)
     owq, ows = oracle.quantize_dim0(w)
-    da, db = oracle.dequantize(oxq, oxs), oracle.dequantize(owq, ows)
-    ref = oracle.grouped_mm(da, db, offs, G)
-    absp = oracle.grouped_mm(np.abs(da), np.abs(db), offs, G)
-    check_f32(oracle, got, ref, f"{name} fwd f32", absp, k)
-    check_bf16(oracle, got16, ref, absp, k, f"{name} fwd bf16")
+    # the model on the rows at every group edge and a random sample
+    edges = np.concatenate([[0], offs[:-1], np.maximum(offs - 1, 0)])
+    mrows = np.unique(np.concatenate([edges, rng.integers(0, m, 40)]))
+    check_mx_fwd(oracle, got, oxq, oxs, owq, ows, offs, G, f"{name} fwd f32", model_rows=mrows)
+    check_mx_fwd(oracle, got16, oxq, oxs, owq, ows, offs, G, f"{name} fwd bf16", out_bf16=True, model_rows=mrows)
     return offs, rng
 
 
@@ -73,14 +73,10 @@ def wgrad_case(oracle, n, k, m, sizes, seed, name):
     got16 = host(mx.mx_grouped_mm_wgrad(dytq, dyts, xtq, xts, doffs, m, n, k, out_dtype=mx.MX_OUT_BF16))
     odyt, odyts = oracle.quantize_dim1(dy)
     oxt, oxts = oracle.quantize_dim1(x)
-    da, db = oracle.dequantize(odyt, odyts), oracle.dequantize(oxt, oxts)
-    ref = oracle.grouped_mm_wgrad(da, db, offs, G)
-    absw = oracle.grouped_mm_wgrad(np.abs(da), np.abs(db), offs, G)
-    kmax = int(np.max(sizes))
-    check_f32(oracle, got, ref, f"{name} wgrad f32", absw, kmax)
-    check_bf16(oracle, got16, ref, absw, kmax, f"{name} wgrad bf16")
-    for g in np.flatnonzero(np.array(sizes) == 0):
-        assert not got[g].any() and not got16[g].any(), f"empty group {g} must give zeros"
+    mrows = np.unique(np.concatenate([[0, n - 1], rng.integers(0, n, 14)]))
+    check_mx_wgrad(oracle, got, odyt, odyts, oxt, oxts, offs, G, f"{name} wgrad f32", model_rows=mrows)
+    check_mx_wgrad(oracle, got16, odyt, odyts, oxt, oxts, offs, G, f"{name} wgrad bf16", out_bf16=True,
+                   model_rows=mrows)
 
 
 def test_mgroup_eight_waves(oracle):
@@ -103,10 +99,11 @@ def test_mgroup_short_contraction(oracle):
     dyq, dys = mx.mx_quantize_dim0(dev_bf16(dy))
     wtq, wts = mx.mx_quantize_dim0(dev_bf16(w_t))
     got = host(mx.mx_grouped_mm_dgrad(dyq, dys, wtq, wts, dev_i32(offs), m, n, k, out_dtype=mx.MX_OUT_F32))
-    da = oracle.dequantize(*oracle.quantize_dim0(dy))
-    db = oracle.dequantize(*oracle.quantize_dim0(w_t))
-    ref = oracle.grouped_mm(da, db, offs, G)
-    check_f32(oracle, got, ref, "128x256 dgrad f32", oracle.grouped_mm(np.abs(da), np.abs(db), offs, G), n)
+    odyq, odys = oracle.quantize_dim0(dy)
+    owtq, owts = oracle.quantize_dim0(w_t)
+    edges = np.concatenate([[0], offs[:-1], np.maximum(offs - 1, 0)])
+    mrows = np.unique(np.concatenate([edges, rng.integers(0, m, 40)]))
+    check_mx_fwd(oracle, got, odyq, odys, owtq, owts, offs, G, "128x256 dgrad f32", model_rows=mrows)
 
 
 def test_kgroup_eight_waves(oracle):
