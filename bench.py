@@ -118,6 +118,15 @@ def load_traffic(kernel_key, units_per_launch):
     return e.get("hbm_bytes_per_launch")
 
 
+def wgrad_workspace(mx, dev, groups, m, n, k, bf16=False):
+    """The caller-owned split-contraction workspace of one wgrad call (None if it does
+    not split)."""
+    import torch
+
+    need = mx.mx_grouped_mm_wgrad_workspace_bytes(groups, m, n, k, bf16)
+    return torch.empty(need, dtype=torch.uint8, device=dev) if need else None
+
+
 def deepseek_share_ops(mx, synth, to_dev, dev):
     """The expert share's training step: one-pass casts of X, W1, H, W2, dY2, dY1 and the
     grouped fwd, dgrad and wgrad of the gate/up (X -> 4096) and down (H -> 7168)
@@ -143,6 +152,8 @@ def deepseek_share_ops(mx, synth, to_dev, dev):
     y1, y2, dh, dx = bf(R, N1), bf(R, H_), bf(R, F), bf(R, H_)
     dw1, dw2 = bf(E, N1, H_), bf(E, H_, F)
     both = lambda n_elem: n_elem * BOTH_BYTES_PER_ELEM  # noqa: E731
+    ws_down = wgrad_workspace(mx, dev, E, R, H_, F)
+    ws_gate = wgrad_workspace(mx, dev, E, R, N1, H_)
 
     def cast(name):
         return ("cast_dim0+dim1 " + name, "cast", both(t[name].numel()),
@@ -160,13 +171,13 @@ def deepseek_share_ops(mx, synth, to_dev, dev):
          lambda: mx.mx_grouped_mm_dgrad(q["dy2"][0], q["dy2"][1], q["w2"][2], q["w2"][3], offs, R, H_, F, out=dh)),
         ("gemm_wgrad down", "gemm", 2 * R * H_ * F,
          lambda: mx.mx_grouped_mm_wgrad(q["dy2"][2], q["dy2"][3], q["h"][2], q["h"][3], offs, R, H_, F, out=dw2,
-                                        out_dtype=mx.MX_OUT_BF16)),
+                                        out_dtype=mx.MX_OUT_BF16, workspace=ws_down)),
         cast("dy1"),
         ("gemm_dgrad gate/up", "gemm", 2 * R * N1 * H_,
          lambda: mx.mx_grouped_mm_dgrad(q["dy1"][0], q["dy1"][1], q["w1"][2], q["w1"][3], offs, R, N1, H_, out=dx)),
         ("gemm_wgrad gate/up", "gemm", 2 * R * N1 * H_,
          lambda: mx.mx_grouped_mm_wgrad(q["dy1"][2], q["dy1"][3], q["x"][2], q["x"][3], offs, R, N1, H_, out=dw1,
-                                        out_dtype=mx.MX_OUT_BF16)),
+                                        out_dtype=mx.MX_OUT_BF16, workspace=ws_gate)),
     ]
     config = {"workload": "deepseek_share fwd+dgrad+wgrad: 32 experts, hidden 7168, FFN 2048 (gate/up N=4096, "
                           "down N=7168 over K=2048), 32768 routed rows, Zipf(1.2) group sizes with 3 empty experts; "
@@ -233,6 +244,9 @@ def main():
         "yn": bf(M, NARROW), "dxn": bf(M, K), "dwn": bf(1, NARROW, K),
     }
     Wflat = W.view(G * N, K)
+    # split-contraction workspaces, allocated once outside the timed region
+    ws = {"g": wgrad_workspace(mx, dev, G, Mg, N, K), "n": wgrad_workspace(mx, dev, 1, M, NARROW, K),
+          "b": wgrad_workspace(mx, dev, G, M, N, K, bf16=True)}
 
     # (name, kind, work units, fn) ; kind "gemm" (MXFP8) / "gemm16" (bf16): units = flops,
     # "cast" / "pad": units = bytes
@@ -252,7 +266,7 @@ def main():
                                               out=buf["dx"]))
     g_wgrad = ("gemm_wgrad grouped", "gemm", 2 * M * N * K,
                lambda: mx.mx_grouped_mm_wgrad(buf["dytq"], buf["dyts"], buf["xtq"], buf["xts"], goffs, Mg, N, K,
-                                              out=buf["dw"], out_dtype=mx.MX_OUT_BF16))
+                                              out=buf["dw"], out_dtype=mx.MX_OUT_BF16, workspace=ws["g"]))
     n_w32 = ("cast_w32 W'", "cast", NARROW * K * W32_BYTES_PER_ELEM, cast_w32)
     n_fwd = ("gemm_fwd dense576", "gemm", 2 * M * NARROW * K,
              lambda: mx.mx_grouped_mm_fwd(buf["xq"], buf["xs"], w32["q"], w32["sr"], None, M, NARROW, K,
@@ -262,7 +276,7 @@ def main():
                                               out=buf["dxn"]))
     n_wgrad = ("gemm_wgrad dense576", "gemm", 2 * M * NARROW * K,
                lambda: mx.mx_grouped_mm_wgrad(buf["dyntq"], buf["dynts"], buf["xtq"], buf["xts"], None, M, NARROW,
-                                              K, out=buf["dwn"], out_dtype=mx.MX_OUT_BF16))
+                                              K, out=buf["dwn"], out_dtype=mx.MX_OUT_BF16, workspace=ws["n"]))
     if args.backward in ("high_precision", "dequantized"):
         # forward as MXFP8 (dim0 casts), backward from bf16 operands: transposes or
         # transposed dequantization (2 B written per element; 2 B read for bf16, 1 + 1/32
@@ -289,7 +303,7 @@ def main():
             x_src,
             ("bf16 wgrad grouped", "gemm16", 2 * M * N * K,
              lambda: mx.mx_grouped_mm_bf16_wgrad(dyt16, xt16, offs, M, N, K, out=buf["dw"],
-                                                 out_dtype=mx.MX_OUT_BF16)),
+                                                 out_dtype=mx.MX_OUT_BF16, workspace=ws["b"])),
         ]
     elif args.backward == "quantized":
         ops = [

@@ -24,17 +24,15 @@
  *
  * CONVENTIONS (every entry point)
  *   - Pointers are device pointers unless stated; the caller allocates and frees
- *     every buffer. The library keeps no state beyond a per-device architecture
- *     check and one exception: mx_grouped_mm_wgrad with few output tiles uses a
- *     per-device fp32 workspace for split contractions (see there), which the
- *     library allocates on first need and grows after synchronising the device.
+ *     every buffer, workspaces included. The library never allocates device
+ *     memory and keeps no state beyond a per-device architecture check and
+ *     per-process launch settings (both set up thread-safely).
  *   - bf16 data is passed as uint16_t bit patterns; E4M3 codes and E8M0 scales
  *     as uint8_t; `stream` is a hipStream_t (NULL = the default stream).
  *   - Work is enqueued asynchronously on `stream`. No call copies device memory
- *     to the host or reads `offs` on the host, and apart from the workspace
- *     growth above no call synchronises the host, so sequences of calls can be
- *     captured into a HIP graph once the largest split-contraction wgrad of the
- *     sequence has run once before the capture (the workspace then exists).
+ *     to the host, reads `offs` on the host or synchronises the host, and no call
+ *     records a memset, so sequences of calls can be captured into a HIP graph
+ *     as they are (no warm-up call needed).
  *   - Arguments are validated on the host before anything is launched. On any
  *     error nothing is launched, a negative status is returned and
  *     mx_last_error() describes the problem (thread-local string).
@@ -216,19 +214,28 @@ mx_status mx_grouped_mm_dgrad(const uint8_t* dy, const uint8_t* dy_s, const uint
  *                 one group over all m. Same caller preconditions as fwd; rows
  *                 past offs[G-1] are not read.
  *   dw            [groups x n x k] (written, every element)
+ *   workspace, workspace_bytes  caller memory (16-byte aligned; NULL, 0 allowed)
+ *                 for split contractions, below
  * m % 32 == 0 (the contraction), n >= 1, k >= 1.
- * When the output has fewer 256 x 256 tiles than the device has compute units
- * (narrow layers), each group's contraction is split at 256-token window
- * boundaries into S parts (enough to fill the device once, at most 16); fp32
- * partials go to a per-device workspace of S * groups * n * k * 4 bytes (rounded
- * up to 16), allocated by the library on first need, and a second kernel sums
- * them in split order, so results are deterministic. Every split-contraction
- * wgrad on one device uses that one workspace: two such calls whose work may
- * overlap (different streams, no event between them) race on it, so the caller
- * orders them (one stream, or an event). */
+ * Split contraction: when the output has fewer 256 x 256 tiles than the device
+ * has compute units (narrow layers), each group's contraction can be split at
+ * 256-token window boundaries into S parts (enough to fill the device once, at
+ * most 16): fp32 partials go to the workspace and a second kernel sums them in
+ * split order, so results are deterministic. It needs
+ * mx_grouped_mm_wgrad_workspace_bytes(groups, m, n, k, 0) bytes (S * groups * n
+ * * k * 4, rounded up to 16); with a smaller workspace, or none, the contraction
+ * runs unsplit (same sums up to the fp32 rounding of the partials; slower on
+ * narrow outputs). The workspace is in use until the call's work on `stream`
+ * has finished: calls that may overlap need workspaces of their own. */
 mx_status mx_grouped_mm_wgrad(const uint8_t* dy_t, const uint8_t* dy_t_s, const uint8_t* x_t, const uint8_t* x_t_s,
                               const int32_t* offs, int32_t groups, int64_t m, int64_t n, int64_t k, void* dw,
-                              int out_dtype, void* stream);
+                              int out_dtype, void* workspace, int64_t workspace_bytes, void* stream);
+
+/* Workspace bytes with which mx_grouped_mm_wgrad (bf16_operands = 0) or
+ * mx_grouped_mm_bf16_wgrad (bf16_operands = 1) splits its contraction; 0 when the
+ * call does not split (enough output tiles, or too short a contraction). Host
+ * function, no device access; -1 for arguments outside the calls' limits. */
+int64_t mx_grouped_mm_wgrad_workspace_bytes(int32_t groups, int64_t m, int64_t n, int64_t k, int bf16_operands);
 
 /* ---- Backward override arms ----
  * The backward of the MXFP8 grouped GEMM may take its gradients from elsewhere
@@ -272,14 +279,16 @@ mx_status mx_transpose_bf16(const uint16_t* x, int64_t batch, int64_t rows, int6
  * offs as for the MXFP8 calls but with no alignment: any non-decreasing ends with
  * offs[G-1] <= m (group edges inside a 16-byte chunk of the contraction are
  * masked element by element). The contraction (k, n, m respectively) is a
- * multiple of 8 and at most 2^21. The wgrad workspace rule of
- * mx_grouped_mm_wgrad applies here too. */
+ * multiple of 8 and at most 2^21. The wgrad takes a workspace as
+ * mx_grouped_mm_wgrad does (size from mx_grouped_mm_wgrad_workspace_bytes with
+ * bf16_operands = 1). */
 mx_status mx_grouped_mm_bf16_fwd(const uint16_t* a, const uint16_t* b, const int32_t* offs, int32_t groups, int64_t m,
                                  int64_t n, int64_t k, void* out, int out_dtype, void* stream);
 mx_status mx_grouped_mm_bf16_dgrad(const uint16_t* dy, const uint16_t* w_t, const int32_t* offs, int32_t groups,
                                    int64_t m, int64_t n, int64_t k, void* dx, int out_dtype, void* stream);
 mx_status mx_grouped_mm_bf16_wgrad(const uint16_t* dy_t, const uint16_t* x_t, const int32_t* offs, int32_t groups,
-                                   int64_t m, int64_t n, int64_t k, void* dw, int out_dtype, void* stream);
+                                   int64_t m, int64_t n, int64_t k, void* dw, int out_dtype, void* workspace,
+                                   int64_t workspace_bytes, void* stream);
 
 /* ---- Token-group padding (group sizes that are not multiples of 32) ----
  * The grouped GEMM needs every group to start on a 32-row boundary (its scales

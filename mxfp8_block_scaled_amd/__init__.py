@@ -29,6 +29,7 @@ __all__ = [
     "mx_grouped_mm_fwd",
     "mx_grouped_mm_dgrad",
     "mx_grouped_mm_wgrad",
+    "mx_grouped_mm_wgrad_workspace_bytes",
     "mx_dequantize",
     "mx_scales_to_logical",
     "mx_transpose_bf16",
@@ -93,6 +94,44 @@ def _pitch(x):
     return x.stride(-2)
 
 
+_U8 = (torch.uint8,)
+_I32 = (torch.int32,)
+_BF16 = (torch.bfloat16, torch.int16, torch.uint16)
+_OUT_DTYPES = {MX_OUT_F32: (torch.float32,), MX_OUT_BF16: _BF16}
+
+
+def _device_of(t, name):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} is on {t.device}; the library works on GPU memory")
+    return t.device
+
+
+def _buf(t, name, dtypes, numel, device):
+    """Checks a buffer the library reads or writes: a contiguous tensor of one of
+    `dtypes` on `device` with at least `numel` elements. The C library cannot see
+    buffer sizes, so this is where a short buffer, a host tensor or a wrong output
+    type is caught before a kernel would access memory outside it."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}; expected {' or '.join(str(d) for d in dtypes)}")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}; the call runs on {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.numel() < numel:
+        raise ValueError(f"{name} holds {t.numel()} elements; the call needs {numel}")
+    return t
+
+
+def _out_dtype(out_dtype):
+    if out_dtype not in _OUT_DTYPES:
+        raise ValueError(f"out_dtype must be MX_OUT_F32 or MX_OUT_BF16, got {out_dtype!r}")
+    return out_dtype
+
+
 def mx_quantize_dim0(x, q=None, scale=None):
     """1x32 rowwise cast of x [rows, cols] (row pitch x.stride(0)) -> (q [rows, cols], scale)."""
     x = _bf16_bits(x)
@@ -100,10 +139,13 @@ def mx_quantize_dim0(x, q=None, scale=None):
         raise ValueError("x must be a 2D tensor")
     rows, cols = x.shape
     ld = _pitch(x)
+    dev = _device_of(x, "x")
     if q is None:
         q = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
     if scale is None:
         scale = _u8(mx_scale_bytes(rows, cols), x.device)
+    _buf(q, "q", _U8, rows * cols, dev)
+    _buf(scale, "scale", _U8, mx_scale_bytes(rows, cols), dev)
     _lib.call("mx_quantize_dim0", _ptr(x), rows, cols, ld, _ptr(q), _ptr(scale), _stream(x))
     return q, scale
 
@@ -125,11 +167,14 @@ def mx_quantize_dim1(x, q_t=None, scale_t=None):
         raise ValueError("x must be 2D or 3D")
     if x.stride(-1) != 1:
         raise ValueError("x must have unit inner stride")
+    dev = _device_of(x, "x")
     if q_t is None:
         shape = (cols, rows) if x.dim() == 2 else (batch, cols, rows)
         q_t = torch.empty(shape, dtype=torch.uint8, device=x.device)
     if scale_t is None:
         scale_t = _u8(mx_scale_bytes(batch * cols, rows), x.device)
+    _buf(q_t, "q_t", _U8, batch * rows * cols, dev)
+    _buf(scale_t, "scale_t", _U8, mx_scale_bytes(batch * cols, rows), dev)
     _lib.call("mx_quantize_dim1", _ptr(x), batch, rows, cols, x.stride(-2), _ptr(q_t), _ptr(scale_t), _stream(x))
     return q_t, scale_t
 
@@ -158,6 +203,11 @@ def mx_quantize_dim0_dim1(x, q=None, scale=None, q_t=None, scale_t=None):
         q_t = torch.empty(shape, dtype=torch.uint8, device=x.device)
     if scale_t is None:
         scale_t = _u8(mx_scale_bytes(batch * cols, rows), x.device)
+    dev = _device_of(x, "x")
+    _buf(q, "q", _U8, batch * rows * cols, dev)
+    _buf(scale, "scale", _U8, mx_scale_bytes(batch * rows, cols), dev)
+    _buf(q_t, "q_t", _U8, batch * rows * cols, dev)
+    _buf(scale_t, "scale_t", _U8, mx_scale_bytes(batch * cols, rows), dev)
     _lib.call("mx_quantize_dim0_dim1", _ptr(x), batch, rows, cols, x.stride(-2), _ptr(q), _ptr(scale), _ptr(q_t),
               _ptr(scale_t), _stream(x))
     return q, scale, q_t, scale_t
@@ -224,24 +274,43 @@ def mx_quantize_weight_32x32(w, transposed=True):
 
 
 def _out(shape, out_dtype, device, out):
+    """The output buffer: `out` checked against the shape and out_dtype, or a new one."""
+    _out_dtype(out_dtype)
+    n = 1
+    for d in shape:
+        n *= d
     if out is not None:
-        return out
+        return _buf(out, "out", _OUT_DTYPES[out_dtype], n, device)
     dt = torch.float32 if out_dtype == MX_OUT_F32 else torch.bfloat16
     return torch.empty(shape, dtype=dt, device=device)
 
 
-def _groups(offs, groups):
+def _groups(offs, groups, device=None, name="offs"):
+    """Group count: offs.numel() unless `groups` is given; offs must hold that many
+    int32 ends on the call's device."""
     if offs is None:
         return 1 if groups is None else groups
     if offs.dtype != torch.int32:
-        raise TypeError("offs must be int32")
-    return offs.numel() if groups is None else groups
+        raise TypeError(f"{name} must be int32")
+    G = offs.numel() if groups is None else groups
+    if device is not None:
+        _buf(offs, name, _I32, G, device)
+    return G
+
+
+def _mx_operand(t, s, rows, cols, name, device):
+    """Codes [rows x cols] and their MFMA-blocked scales."""
+    _buf(t, name, _U8, rows * cols, device)
+    _buf(s, name + "_scale", _U8, mx_scale_bytes(rows, cols) if rows else 0, device)
 
 
 def mx_grouped_mm_fwd(a, a_s, b, b_s, offs, m, n, k, groups=None, out_dtype=MX_OUT_BF16, out=None):
     """out [m, n] = a [m, k] . b_g [n, k]^T per row group (offs None = dense)."""
-    G = _groups(offs, groups)
-    out = _out((m, n), out_dtype, a.device, out)
+    dev = _device_of(a, "a")
+    G = _groups(offs, groups, dev)
+    _mx_operand(a, a_s, m, k, "a", dev)
+    _mx_operand(b, b_s, G * n, k, "b", dev)
+    out = _out((m, n), out_dtype, dev, out)
     _lib.call("mx_grouped_mm_fwd", _ptr(a), _ptr(a_s), _ptr(b), _ptr(b_s), _ptr(offs), G, m, n, k, _ptr(out),
               out_dtype, _stream(a))
     return out
@@ -249,19 +318,58 @@ def mx_grouped_mm_fwd(a, a_s, b, b_s, offs, m, n, k, groups=None, out_dtype=MX_O
 
 def mx_grouped_mm_dgrad(dy, dy_s, w_t, w_t_s, offs, m, n, k, groups=None, out_dtype=MX_OUT_BF16, out=None):
     """dx [m, k] = dy [m, n] . W_g [n, k] per row group, with W_g^T given as w_t [G*k, n]."""
-    G = _groups(offs, groups)
-    out = _out((m, k), out_dtype, dy.device, out)
+    dev = _device_of(dy, "dy")
+    G = _groups(offs, groups, dev)
+    _mx_operand(dy, dy_s, m, n, "dy", dev)
+    _mx_operand(w_t, w_t_s, G * k, n, "w_t", dev)
+    out = _out((m, k), out_dtype, dev, out)
     _lib.call("mx_grouped_mm_dgrad", _ptr(dy), _ptr(dy_s), _ptr(w_t), _ptr(w_t_s), _ptr(offs), G, m, n, k, _ptr(out),
               out_dtype, _stream(dy))
     return out
 
 
-def mx_grouped_mm_wgrad(dy_t, dy_t_s, x_t, x_t_s, offs, m, n, k, groups=None, out_dtype=MX_OUT_F32, out=None):
-    """dw [G, n, k]: dw[g] = dy_t[:, rows_g] . x_t[:, rows_g]^T (empty group -> zeros)."""
-    G = _groups(offs, groups)
-    out = _out((G, n, k), out_dtype, dy_t.device, out)
+def mx_grouped_mm_wgrad_workspace_bytes(groups, m, n, k, bf16_operands=False):
+    """Workspace bytes with which the wgrad splits its contraction (0: no split)."""
+    b = _lib.load().mx_grouped_mm_wgrad_workspace_bytes(int(groups), int(m), int(n), int(k), int(bool(bf16_operands)))
+    if b < 0:
+        raise ValueError(f"wgrad workspace query: arguments outside the call's limits ({groups}, {m}, {n}, {k})")
+    return b
+
+
+def _workspace(workspace, need, device):
+    """(pointer, bytes) of the wgrad workspace: `workspace` as given (any dtype; its
+    bytes count; None or empty: the contraction runs unsplit), or, when workspace is
+    "auto", a new uint8 tensor of `need` bytes from torch's allocator (kept alive
+    by the caching allocator's stream semantics until the work has run)."""
+    if isinstance(workspace, str):
+        if workspace != "auto":
+            raise ValueError('workspace must be a tensor, None or "auto"')
+        if need == 0:
+            return None, 0, None
+        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+    if workspace is None:
+        return None, 0, None
+    if workspace.device != device or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on the call's device")
+    nbytes = workspace.numel() * workspace.element_size()
+    return _ptr(workspace) if nbytes else None, nbytes, workspace
+
+
+def mx_grouped_mm_wgrad(dy_t, dy_t_s, x_t, x_t_s, offs, m, n, k, groups=None, out_dtype=MX_OUT_F32, out=None,
+                        workspace="auto"):
+    """dw [G, n, k]: dw[g] = dy_t[:, rows_g] . x_t[:, rows_g]^T (empty group -> zeros).
+
+    workspace: "auto" (a torch allocation of mx_grouped_mm_wgrad_workspace_bytes when
+    the call splits its contraction), a caller tensor, or None (never split)."""
+    dev = _device_of(dy_t, "dy_t")
+    G = _groups(offs, groups, dev)
+    _mx_operand(dy_t, dy_t_s, n, m, "dy_t", dev)
+    _mx_operand(x_t, x_t_s, k, m, "x_t", dev)
+    out = _out((G, n, k), out_dtype, dev, out)
+    need = mx_grouped_mm_wgrad_workspace_bytes(G, m, n, k) if workspace == "auto" else 0
+    ws_ptr, ws_bytes, _keep = _workspace(workspace, need, dev)
     _lib.call("mx_grouped_mm_wgrad", _ptr(dy_t), _ptr(dy_t_s), _ptr(x_t), _ptr(x_t_s), _ptr(offs), G, m, n, k,
-              _ptr(out), out_dtype, _stream(dy_t))
+              _ptr(out), out_dtype, ws_ptr, ws_bytes, _stream(dy_t))
     return out
 
 
@@ -333,7 +441,8 @@ def mx_pad_token_groups(x, offs, rows_pad=None, x_pad=None, offs_pad=None):
     x = _bf16_bits(x)
     if x.dim() != 2 or (x.numel() and x.stride(1) != 1):
         raise ValueError("x must be a 2D tensor with unit inner stride")
-    G = _groups(offs, None)
+    dev = _device_of(x, "x")
+    G = _groups(offs, None, dev)
     rows, cols = x.shape
     ld = x.stride(0) if x.numel() else cols  # an empty tensor's strides are arbitrary
     if rows_pad is None:
@@ -342,6 +451,8 @@ def mx_pad_token_groups(x, offs, rows_pad=None, x_pad=None, offs_pad=None):
         x_pad = torch.empty((rows_pad, cols), dtype=x.dtype, device=x.device)
     if offs_pad is None:
         offs_pad = torch.empty(G, dtype=torch.int32, device=x.device)
+    _buf(x_pad, "x_pad", _BF16, rows_pad * cols, dev)
+    _buf(offs_pad, "offs_pad", _I32, G, dev)
     _lib.call("mx_pad_token_groups", _ptr(x), rows, cols, ld, _ptr(offs), G, _ptr(x_pad), rows_pad,
               _ptr(offs_pad), _stream(x))
     return x_pad, offs_pad
@@ -358,10 +469,14 @@ def mx_unpad_token_groups(y_pad, offs, rows, y=None):
         dt = MX_OUT_BF16
     else:
         raise TypeError(f"y_pad must be float32 or bf16, got {y_pad.dtype}")
-    G = _groups(offs, None)
+    dev = _device_of(y_pad, "y_pad")
+    G = _groups(offs, None, dev)
     rows_pad, cols = y_pad.shape
     if y is None:
         y = torch.empty((rows, cols), dtype=y_pad.dtype, device=y_pad.device)
+    if y.dtype != y_pad.dtype or y.device != dev or y.dim() != 2 or y.shape[1] != cols or y.shape[0] < rows or \
+            (y.numel() and y.stride(1) != 1):
+        raise ValueError("y must be a 2D tensor of y_pad's dtype and device, unit inner stride, [>= rows, cols]")
     _lib.call("mx_unpad_token_groups", _ptr(y_pad), rows_pad, cols, y_pad.stride(0), _ptr(offs), G, _ptr(y), rows,
               y.stride(0), dt, _stream(y_pad))
     return y
@@ -415,27 +530,40 @@ def mx_transpose_bf16(x, out=None):
 
 def mx_grouped_mm_bf16_fwd(a, b, offs, m, n, k, groups=None, out_dtype=MX_OUT_BF16, out=None):
     """out [m, n] = a [m, k] . b_g [n, k]^T per row group, bf16 operands."""
-    G = _groups(offs, groups)
-    out = _out((m, n), out_dtype, a.device, out)
+    dev = _device_of(a, "a")
+    G = _groups(offs, groups, dev)
+    _buf(a, "a", _BF16, m * k, dev)
+    _buf(b, "b", _BF16, G * n * k, dev)
+    out = _out((m, n), out_dtype, dev, out)
     _lib.call("mx_grouped_mm_bf16_fwd", _ptr(a), _ptr(b), _ptr(offs), G, m, n, k, _ptr(out), out_dtype, _stream(a))
     return out
 
 
 def mx_grouped_mm_bf16_dgrad(dy, w_t, offs, m, n, k, groups=None, out_dtype=MX_OUT_BF16, out=None):
     """dx [m, k] = dy [m, n] . W_g [n, k] per row group, with W_g^T given as w_t [G*k, n]."""
-    G = _groups(offs, groups)
-    out = _out((m, k), out_dtype, dy.device, out)
+    dev = _device_of(dy, "dy")
+    G = _groups(offs, groups, dev)
+    _buf(dy, "dy", _BF16, m * n, dev)
+    _buf(w_t, "w_t", _BF16, G * k * n, dev)
+    out = _out((m, k), out_dtype, dev, out)
     _lib.call("mx_grouped_mm_bf16_dgrad", _ptr(dy), _ptr(w_t), _ptr(offs), G, m, n, k, _ptr(out), out_dtype,
               _stream(dy))
     return out
 
 
-def mx_grouped_mm_bf16_wgrad(dy_t, x_t, offs, m, n, k, groups=None, out_dtype=MX_OUT_F32, out=None):
-    """dw [G, n, k]: dw[g] = dy_t[:, rows_g] . x_t[:, rows_g]^T, bf16 operands."""
-    G = _groups(offs, groups)
-    out = _out((G, n, k), out_dtype, dy_t.device, out)
+def mx_grouped_mm_bf16_wgrad(dy_t, x_t, offs, m, n, k, groups=None, out_dtype=MX_OUT_F32, out=None,
+                             workspace="auto"):
+    """dw [G, n, k]: dw[g] = dy_t[:, rows_g] . x_t[:, rows_g]^T, bf16 operands;
+    workspace as for mx_grouped_mm_wgrad."""
+    dev = _device_of(dy_t, "dy_t")
+    G = _groups(offs, groups, dev)
+    _buf(dy_t, "dy_t", _BF16, n * m, dev)
+    _buf(x_t, "x_t", _BF16, k * m, dev)
+    out = _out((G, n, k), out_dtype, dev, out)
+    need = mx_grouped_mm_wgrad_workspace_bytes(G, m, n, k, True) if workspace == "auto" else 0
+    ws_ptr, ws_bytes, _keep = _workspace(workspace, need, dev)
     _lib.call("mx_grouped_mm_bf16_wgrad", _ptr(dy_t), _ptr(x_t), _ptr(offs), G, m, n, k, _ptr(out), out_dtype,
-              _stream(dy_t))
+              ws_ptr, ws_bytes, _stream(dy_t))
     return out
 
 
@@ -446,12 +574,12 @@ def mx_pad_quantize_dim0_dim1(x, offs, rows_pad=None, q=None, scale=None, q_t=No
     x = _bf16_bits(x)
     if x.dim() != 2:
         raise ValueError("x must be a 2D tensor")
-    G = _groups(offs, None)
+    dev = _device_of(x, "x")
+    G = _groups(offs, None, dev)
     rows, cols = x.shape
     ld = _pitch(x)
     if rows_pad is None:
         rows_pad = mx_padded_rows(rows, G)
-    dev = x.device
     if q is None:
         q = torch.empty((rows_pad, cols), dtype=torch.uint8, device=dev)
     if scale is None:
@@ -462,6 +590,11 @@ def mx_pad_quantize_dim0_dim1(x, offs, rows_pad=None, q=None, scale=None, q_t=No
         scale_t = _u8(mx_scale_bytes(cols, rows_pad), dev)
     if offs_pad is None:
         offs_pad = torch.empty(G, dtype=torch.int32, device=dev)
+    _buf(q, "q", _U8, rows_pad * cols, dev)
+    _buf(scale, "scale", _U8, mx_scale_bytes(rows_pad, cols), dev)
+    _buf(q_t, "q_t", _U8, rows_pad * cols, dev)
+    _buf(scale_t, "scale_t", _U8, mx_scale_bytes(cols, rows_pad), dev)
+    _buf(offs_pad, "offs_pad", _I32, G, dev)
     _lib.call("mx_pad_quantize_dim0_dim1", _ptr(x), rows, cols, ld, _ptr(offs), G, rows_pad, _ptr(q), _ptr(scale),
               _ptr(q_t), _ptr(scale_t), _ptr(offs_pad), _stream(x))
     return q, scale, q_t, scale_t, offs_pad
@@ -469,8 +602,12 @@ def mx_pad_quantize_dim0_dim1(x, offs, rows_pad=None, q=None, scale=None, q_t=No
 
 def mx_grouped_mm_fwd_padded(a, a_s, b, b_s, offs_pad, offs, m_pad, m, n, k, out_dtype=MX_OUT_BF16, out=None):
     """Forward on padded token rows, output unpadded: out [m, n]."""
-    G = _groups(offs, None)
-    out = _out((m, n), out_dtype, a.device, out)
+    dev = _device_of(a, "a")
+    G = _groups(offs, None, dev)
+    _groups(offs_pad, G, dev, "offs_pad")
+    _mx_operand(a, a_s, m_pad, k, "a", dev)
+    _mx_operand(b, b_s, G * n, k, "b", dev)
+    out = _out((m, n), out_dtype, dev, out)
     _lib.call("mx_grouped_mm_fwd_padded", _ptr(a), _ptr(a_s), _ptr(b), _ptr(b_s), _ptr(offs_pad), _ptr(offs), G,
               m_pad, m, n, k, _ptr(out), out_dtype, _stream(a))
     return out
@@ -479,8 +616,12 @@ def mx_grouped_mm_fwd_padded(a, a_s, b, b_s, offs_pad, offs, m_pad, m, n, k, out
 def mx_grouped_mm_dgrad_padded(dy, dy_s, w_t, w_t_s, offs_pad, offs, m_pad, m, n, k, out_dtype=MX_OUT_BF16,
                                out=None):
     """dgrad on padded token rows, output unpadded: dx [m, k]."""
-    G = _groups(offs, None)
-    out = _out((m, k), out_dtype, dy.device, out)
+    dev = _device_of(dy, "dy")
+    G = _groups(offs, None, dev)
+    _groups(offs_pad, G, dev, "offs_pad")
+    _mx_operand(dy, dy_s, m_pad, n, "dy", dev)
+    _mx_operand(w_t, w_t_s, G * k, n, "w_t", dev)
+    out = _out((m, k), out_dtype, dev, out)
     _lib.call("mx_grouped_mm_dgrad_padded", _ptr(dy), _ptr(dy_s), _ptr(w_t), _ptr(w_t_s), _ptr(offs_pad), _ptr(offs),
               G, m_pad, m, n, k, _ptr(out), out_dtype, _stream(dy))
     return out

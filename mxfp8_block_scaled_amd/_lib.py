@@ -22,13 +22,14 @@ SIGNATURES = {
     "mx_quantize_weight_32x32": (_INT, [_P, _I64, _I64, _I64, _I64, _P, _P, _P, _P, _P]),
     "mx_grouped_mm_fwd": (_INT, [_P, _P, _P, _P, _P, _I32, _I64, _I64, _I64, _P, _INT, _P]),
     "mx_grouped_mm_dgrad": (_INT, [_P, _P, _P, _P, _P, _I32, _I64, _I64, _I64, _P, _INT, _P]),
-    "mx_grouped_mm_wgrad": (_INT, [_P, _P, _P, _P, _P, _I32, _I64, _I64, _I64, _P, _INT, _P]),
+    "mx_grouped_mm_wgrad": (_INT, [_P, _P, _P, _P, _P, _I32, _I64, _I64, _I64, _P, _INT, _P, _I64, _P]),
+    "mx_grouped_mm_wgrad_workspace_bytes": (_I64, [_I32, _I64, _I64, _I64, _INT]),
     "mx_dequantize": (_INT, [_P, _P, _I64, _I64, _I64, _INT, _P, _P]),
     "mx_scales_to_logical": (_INT, [_P, _I64, _I64, _P, _P]),
     "mx_transpose_bf16": (_INT, [_P, _I64, _I64, _I64, _I64, _P, _P]),
     "mx_grouped_mm_bf16_fwd": (_INT, [_P, _P, _P, _I32, _I64, _I64, _I64, _P, _INT, _P]),
     "mx_grouped_mm_bf16_dgrad": (_INT, [_P, _P, _P, _I32, _I64, _I64, _I64, _P, _INT, _P]),
-    "mx_grouped_mm_bf16_wgrad": (_INT, [_P, _P, _P, _I32, _I64, _I64, _I64, _P, _INT, _P]),
+    "mx_grouped_mm_bf16_wgrad": (_INT, [_P, _P, _P, _I32, _I64, _I64, _I64, _P, _INT, _P, _I64, _P]),
     "mx_padded_rows": (_I64, [_I64, _I32]),
     "mx_check_offs": (_INT, [_P, _I32, _I64, _I32, _P, _P]),
     "mx_probe_mfma": (_INT, [_I64, _P, _P]),

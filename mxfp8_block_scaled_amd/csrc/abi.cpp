@@ -28,7 +28,7 @@ hipError_t mx_launch_scales_logical(const uint8_t*, int64_t, int64_t, uint8_t*, 
 hipError_t mx_launch_gemm_bf16_mgroup(const uint16_t*, const uint16_t*, const int32_t*, int, int64_t, int64_t, int64_t,
                                       void*, int, hipStream_t);
 hipError_t mx_launch_gemm_bf16_kgroup(const uint16_t*, const uint16_t*, const int32_t*, int, int64_t, int64_t, int64_t,
-                                      void*, int, hipStream_t);
+                                      void*, int, void*, int64_t, hipStream_t);
 hipError_t mx_launch_gemm_mgroup(const uint8_t*, const uint8_t*, const uint8_t*, const uint8_t*, const int32_t*,
                                  const int32_t*, int, int64_t, int64_t, int64_t, int64_t, void*, int, hipStream_t);
 hipError_t mx_launch_check_offs(const int32_t*, int, int64_t, int, int32_t*, hipStream_t);
@@ -38,7 +38,8 @@ hipError_t mx_launch_probe_dot(int, const uint8_t*, const uint8_t*, const uint8_
 hipError_t mx_launch_pad_both(const uint16_t*, int64_t, int64_t, int64_t, const int32_t*, int, int64_t, uint8_t*,
                               uint8_t*, uint8_t*, uint8_t*, int32_t*, hipStream_t);
 hipError_t mx_launch_gemm_kgroup(const uint8_t*, const uint8_t*, const uint8_t*, const uint8_t*, const int32_t*, int,
-                                 int64_t, int64_t, int64_t, void*, int, hipStream_t);
+                                 int64_t, int64_t, int64_t, void*, int, void*, int64_t, hipStream_t);
+int64_t mx_kgroup_workspace_bytes(int, int64_t, int64_t, int64_t, int);
 
 namespace {
 
@@ -313,9 +314,16 @@ mx_status mx_grouped_mm_dgrad(const uint8_t* dy, const uint8_t* dy_s, const uint
                   "mx_grouped_mm_dgrad");
 }
 
-mx_status mx_grouped_mm_wgrad(const uint8_t* dy_t, const uint8_t* dy_t_s, const uint8_t* x_t, const uint8_t* x_t_s,
-                              const int32_t* offs, int32_t groups, int64_t m, int64_t n, int64_t k, void* dw,
-                              int out_dtype, void* stream) {
+namespace {
+
+mx_status check_workspace(const void* workspace, int64_t workspace_bytes) {
+  if (workspace_bytes < 0) return fail(MX_E_SHAPE, "workspace_bytes = %lld is negative", (long long)workspace_bytes);
+  if (workspace && !aligned16(workspace)) return fail(MX_E_ALIGN, "workspace is not 16-byte aligned");
+  return MX_OK;
+}
+
+mx_status check_wgrad(const uint8_t* dy_t, const uint8_t* dy_t_s, const uint8_t* x_t, const uint8_t* x_t_s,
+                      const int32_t* offs, int32_t groups, int64_t m, int64_t n, int64_t k, void* dw, int out_dtype) {
   TRY(check_gemm_common(dy_t, dy_t_s, x_t, x_t_s, dw, out_dtype, groups, offs, n * m, k * m, n * k));
   TRY(check_dim("m", m, 0));
   TRY(check_dim("n", n, 1));
@@ -323,9 +331,26 @@ mx_status mx_grouped_mm_wgrad(const uint8_t* dy_t, const uint8_t* dy_t_s, const 
   TRY(check_mul32("m", m));
   if ((int64_t)groups * n > kMaxDim) return fail(MX_E_SHAPE, "groups * n exceeds 2^31");
   TRY(check_gemm_extent("m", m, n, k));
+  return MX_OK;
+}
+
+}  // namespace
+
+int64_t mx_grouped_mm_wgrad_workspace_bytes(int32_t groups, int64_t m, int64_t n, int64_t k, int bf16_operands) {
+  if (groups < 1 || groups > 65536 || m < 0 || n < 1 || k < 1 || m > kMaxDim || n > kMaxDim || k > kMaxDim) return -1;
+  if ((int64_t)groups * n > kMaxDim) return -1;
+  return mx_kgroup_workspace_bytes(groups, m, n, k, bf16_operands ? 1 : 0);
+}
+
+mx_status mx_grouped_mm_wgrad(const uint8_t* dy_t, const uint8_t* dy_t_s, const uint8_t* x_t, const uint8_t* x_t_s,
+                              const int32_t* offs, int32_t groups, int64_t m, int64_t n, int64_t k, void* dw,
+                              int out_dtype, void* workspace, int64_t workspace_bytes, void* stream) {
+  TRY(check_wgrad(dy_t, dy_t_s, x_t, x_t_s, offs, groups, m, n, k, dw, out_dtype));
+  TRY(check_workspace(workspace, workspace_bytes));
   TRY(check_device());
   // dW_g[n x k] = dY^T[n x m] . (X^T[k x m])^T over group g's range of m
-  return launched(mx_launch_gemm_kgroup(dy_t, dy_t_s, x_t, x_t_s, offs, groups, n, k, m, dw, out_dtype, (hipStream_t)stream),
+  return launched(mx_launch_gemm_kgroup(dy_t, dy_t_s, x_t, x_t_s, offs, groups, n, k, m, dw, out_dtype,
+                                        workspace_bytes ? workspace : nullptr, workspace_bytes, (hipStream_t)stream),
                   "mx_grouped_mm_wgrad");
 }
 
@@ -421,14 +446,17 @@ mx_status mx_grouped_mm_bf16_dgrad(const uint16_t* dy, const uint16_t* w_t, cons
 }
 
 mx_status mx_grouped_mm_bf16_wgrad(const uint16_t* dy_t, const uint16_t* x_t, const int32_t* offs, int32_t groups,
-                                   int64_t m, int64_t n, int64_t k, void* dw, int out_dtype, void* stream) {
+                                   int64_t m, int64_t n, int64_t k, void* dw, int out_dtype, void* workspace,
+                                   int64_t workspace_bytes, void* stream) {
   TRY(check_dim("m", m, 0));
   TRY(check_dim("n", n, 1));
   TRY(check_dim("k", k, 1));
   TRY(check_bf16_gemm(dy_t, x_t, dw, out_dtype, groups, offs, "m", m, n, k, (int64_t)groups * n * k));
   if ((int64_t)groups * n > kMaxDim) return fail(MX_E_SHAPE, "groups * n exceeds 2^31");
+  TRY(check_workspace(workspace, workspace_bytes));
   TRY(check_device());
-  return launched(mx_launch_gemm_bf16_kgroup(dy_t, x_t, offs, groups, n, k, m, dw, out_dtype, (hipStream_t)stream),
+  return launched(mx_launch_gemm_bf16_kgroup(dy_t, x_t, offs, groups, n, k, m, dw, out_dtype,
+                                             workspace_bytes ? workspace : nullptr, workspace_bytes, (hipStream_t)stream),
                   "mx_grouped_mm_bf16_wgrad");
 }
 

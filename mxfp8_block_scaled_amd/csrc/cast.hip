@@ -496,8 +496,8 @@ hipError_t mx_launch_dim0(const uint16_t* x, int64_t rows, int64_t cols, int64_t
   const int64_t tiles = row_bands * ktiles;
   if (tiles == 0) return hipSuccess;
   // enough 4-wave blocks to fill the device once, each wave striding over the tiles
-  static int64_t fill = 0;  // per process; every gfx950 part has the same shape
-  if (fill == 0) fill = resident_blocks((const void*)mx::k_quant_dim0<false>, 256);
+  // per process (thread-safe static initialisation); every gfx950 part has the same shape
+  static const int64_t fill = resident_blocks((const void*)mx::k_quant_dim0<false>, 256);
   const int64_t blocks = std::min<int64_t>((tiles + 3) / 4, fill);
   if (floor_mode)
     hipLaunchKernelGGL(mx::k_quant_dim0<true>, dim3((unsigned)blocks), dim3(256), 0, stream, x, rows, cols, ld, q,
@@ -529,8 +529,7 @@ template <bool FLOOR, bool GATHER, int WV>
 hipError_t launch_both_wv(const uint16_t* x, int64_t batch, int64_t rows, int64_t cols, int64_t ld, uint8_t* q,
                           uint8_t* scale, uint8_t* q_t, uint8_t* scale_t, int64_t rtiles, int64_t ctiles,
                           mx::RowGather gth, hipStream_t stream) {
-  static int64_t fill = 0;
-  if (fill == 0) fill = resident_blocks((const void*)mx::k_quant_both<FLOOR, GATHER, WV>, 64 * WV);
+  static const int64_t fill = resident_blocks((const void*)mx::k_quant_both<FLOOR, GATHER, WV>, 64 * WV);
   const int64_t blocks = std::max<int64_t>(1, std::min<int64_t>(batch * rtiles * ctiles, fill));
   hipLaunchKernelGGL((mx::k_quant_both<FLOOR, GATHER, WV>), dim3((unsigned)blocks), dim3(64 * WV), 0, stream, x,
                      batch, rows, cols, ld, q, scale, q_t, scale_t, rtiles, ctiles, gth);
@@ -543,13 +542,13 @@ hipError_t launch_both_wv(const uint16_t* x, int64_t batch, int64_t rows, int64_
 // (one sub-tile each) finish a tile sooner (16384 x 576 grad_out: 14 against 18 us;
 // 16384 x 4096: 70 against 58 us).
 int both_waves(int64_t tiles) {
-  static int cus = 0;
-  if (cus == 0) {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        cus <= 0)
-      cus = 256;
-  }
+  static const int cus = [] {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+      n = 256;
+    return n;
+  }();
   return tiles <= cus ? 8 : 4;
 }
 }  // namespace

@@ -610,14 +610,17 @@ hipError_t launch_cfg(mx::GemmArgs p, int out_bf16, hipStream_t stream) {
   if (p.tiles == 0) return hipSuccess;
   const int64_t blocks = p.tiles;
   const size_t lds = (size_t)C::LDS_BYTES;
-  static bool attr_set[2] = {false, false};
-  const void* fn = out_bf16 ? (const void*)mx::k_gemm<BM, BN, WGM, WGN, NST, WPE, MODE, 1, EL>
-                            : (const void*)mx::k_gemm<BM, BN, WGM, WGN, NST, WPE, MODE, 0, EL>;
-  if (!attr_set[out_bf16 ? 1 : 0]) {
-    const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    attr_set[out_bf16 ? 1 : 0] = true;
-  }
+  // the dynamic LDS limit of both output-type instances, raised once per process
+  // (thread-safe static initialisation)
+  static const hipError_t attr = [] {
+    hipError_t e = hipFuncSetAttribute((const void*)mx::k_gemm<BM, BN, WGM, WGN, NST, WPE, MODE, 0, EL>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
+    if (e == hipSuccess)
+      e = hipFuncSetAttribute((const void*)mx::k_gemm<BM, BN, WGM, WGN, NST, WPE, MODE, 1, EL>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
+    return e;
+  }();
+  if (attr != hipSuccess) return attr;
   if (out_bf16)
     hipLaunchKernelGGL((mx::k_gemm<BM, BN, WGM, WGN, NST, WPE, MODE, 1, EL>), dim3((unsigned)blocks),
                        dim3(C::THREADS), lds, stream, p);
@@ -651,31 +654,6 @@ __global__ __launch_bounds__(256) void k_split_reduce(const float* __restrict__ 
       }
     }
   }
-}
-
-// Per-device fp32 workspace for split partials, grown on demand. Growing waits for
-// the device first, so no launched kernel still uses the old buffer.
-hipError_t split_workspace(size_t bytes, float** ptr) {
-  static std::mutex mu;
-  static void* buf[64] = {};
-  static size_t cap[64] = {};
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
-  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-  std::lock_guard<std::mutex> lock(mu);
-  if (cap[dev] < bytes) {
-    if (buf[dev]) {
-      if ((e = hipDeviceSynchronize()) != hipSuccess) return e;
-      if ((e = hipFree(buf[dev])) != hipSuccess) return e;
-      buf[dev] = nullptr;
-      cap[dev] = 0;
-    }
-    if ((e = hipMalloc(&buf[dev], bytes)) != hipSuccess) return e;
-    cap[dev] = bytes;
-  }
-  *ptr = (float*)buf[dev];
-  return hipSuccess;
 }
 
 // K-grouped outputs with fewer 256x256 tiles than compute units, over a long
@@ -751,26 +729,37 @@ int choose_tiling(const mx::GemmArgs& p, int out_bf16) {
   return TILE_256_8W;
 }
 
+// fp32 workspace bytes a K-grouped GEMM uses to split its contraction (0: no split).
+int64_t split_workspace_bytes(const mx::GemmArgs& p, int64_t elem_bytes, int* splits_out, int64_t* stride_out) {
+  const int splits = choose_splits(p, elem_bytes);
+  const int64_t n_out = (int64_t)p.groups * p.M * p.N;
+  const int64_t stride = (n_out + 3) / 4 * 4;  // keeps every partial 16-byte aligned
+  if (splits_out) *splits_out = splits;
+  if (stride_out) *stride_out = stride;
+  return splits > 1 ? stride * splits * (int64_t)sizeof(float) : 0;
+}
+
+// K-grouped: with a caller workspace of at least split_workspace_bytes, narrow outputs
+// split their contraction into fp32 partials that k_split_reduce sums in split order
+// (deterministic); with less (or none) the contraction runs unsplit.
 template <int MODE, int EL>
-hipError_t launch(mx::GemmArgs& p, int out_bf16, hipStream_t stream) {
+hipError_t launch(mx::GemmArgs& p, int out_bf16, void* ws, int64_t ws_bytes, hipStream_t stream) {
   p.splits = 1;
   if (MODE == mx::MODE_KGROUP) {
-    const int splits = choose_splits(p, EL == mx::EL_BF16 ? 2 : 1);
-    if (splits > 1) {
+    int splits = 1;
+    int64_t stride = 0;
+    const int64_t need = split_workspace_bytes(p, EL == mx::EL_BF16 ? 2 : 1, &splits, &stride);
+    if (need > 0 && ws && ws_bytes >= need) {
       const int64_t n_out = (int64_t)p.groups * p.M * p.N;
-      const int64_t stride = (n_out + 3) / 4 * 4;  // keeps every partial 16-byte aligned
-      float* ws = nullptr;
-      hipError_t e = split_workspace((size_t)stride * splits * sizeof(float), &ws);
-      if (e != hipSuccess) return e;
       mx::GemmArgs q = p;
       q.splits = splits;
       q.split_stride = stride;
       q.out = ws;
-      e = launch_tiling<MODE, EL>(choose_tiling<MODE, EL>(q, 0), q, 0, stream);
+      hipError_t e = launch_tiling<MODE, EL>(choose_tiling<MODE, EL>(q, 0), q, 0, stream);
       if (e != hipSuccess) return e;
       const int64_t blocks = std::min<int64_t>((n_out + 1023) / 1024, 4096);
-      hipLaunchKernelGGL(k_split_reduce, dim3((unsigned)std::max<int64_t>(blocks, 1)), dim3(256), 0, stream, ws,
-                         splits, stride, n_out, p.out, out_bf16);
+      hipLaunchKernelGGL(k_split_reduce, dim3((unsigned)std::max<int64_t>(blocks, 1)), dim3(256), 0, stream,
+                         (const float*)ws, splits, stride, n_out, p.out, out_bf16);
       return hipGetLastError();
     }
   }
@@ -790,13 +779,13 @@ hipError_t mx_launch_gemm_mgroup(const uint8_t* a, const uint8_t* a_s, const uin
   p.M = m; p.N = n; p.K = k; p.ldo = n;
   p.out_rows = offs_out ? out_rows : m;
   p.groups = groups;
-  return launch<mx::MODE_MGROUP, mx::EL_MXFP8>(p, out_bf16, stream);
+  return launch<mx::MODE_MGROUP, mx::EL_MXFP8>(p, out_bf16, nullptr, 0, stream);
 }
 
 // K-grouped: C_g[m x n] = A[m x K_g] . B[n x K_g]^T over each group's contraction range (wgrad).
 hipError_t mx_launch_gemm_kgroup(const uint8_t* a, const uint8_t* a_s, const uint8_t* b, const uint8_t* b_s,
                                  const int32_t* offs, int groups, int64_t m, int64_t n, int64_t k, void* out,
-                                 int out_bf16, hipStream_t stream) {
+                                 int out_bf16, void* ws, int64_t ws_bytes, hipStream_t stream) {
   mx::GemmArgs p{};
   p.a = a; p.a_s = a_s; p.b = b; p.b_s = b_s; p.offs = offs; p.out = out;
   p.lda = k; p.ldb = k;
@@ -804,7 +793,7 @@ hipError_t mx_launch_gemm_kgroup(const uint8_t* a, const uint8_t* a_s, const uin
   p.a_ktiles = p.b_ktiles = mx::scale_tiles_k(k / 32);
   p.M = m; p.N = n; p.K = k; p.ldo = n;
   p.groups = groups;
-  return launch<mx::MODE_KGROUP, mx::EL_MXFP8>(p, out_bf16, stream);
+  return launch<mx::MODE_KGROUP, mx::EL_MXFP8>(p, out_bf16, ws, ws_bytes, stream);
 }
 
 // bf16 operands, no scales: the same two cores with pitches of 2 bytes per element.
@@ -818,16 +807,28 @@ hipError_t mx_launch_gemm_bf16_mgroup(const uint16_t* a, const uint16_t* b, cons
   p.M = m; p.N = n; p.K = k; p.ldo = n;
   p.out_rows = m;
   p.groups = groups;
-  return launch<mx::MODE_MGROUP, mx::EL_BF16>(p, out_bf16, stream);
+  return launch<mx::MODE_MGROUP, mx::EL_BF16>(p, out_bf16, nullptr, 0, stream);
 }
 
 hipError_t mx_launch_gemm_bf16_kgroup(const uint16_t* a, const uint16_t* b, const int32_t* offs, int groups,
-                                      int64_t m, int64_t n, int64_t k, void* out, int out_bf16, hipStream_t stream) {
+                                      int64_t m, int64_t n, int64_t k, void* out, int out_bf16, void* ws,
+                                      int64_t ws_bytes, hipStream_t stream) {
   mx::GemmArgs p{};
   p.a = (const uint8_t*)a; p.b = (const uint8_t*)b; p.offs = offs; p.out = out;
   p.lda = 2 * k; p.ldb = 2 * k;
   p.a_rows = m; p.b_rows = n;
   p.M = m; p.N = n; p.K = k; p.ldo = n;
   p.groups = groups;
-  return launch<mx::MODE_KGROUP, mx::EL_BF16>(p, out_bf16, stream);
+  return launch<mx::MODE_KGROUP, mx::EL_BF16>(p, out_bf16, ws, ws_bytes, stream);
+}
+
+// Workspace bytes of a K-grouped call (dw [groups x n x k] over a contraction of m):
+// what it needs to split its contraction, 0 if it does not split.
+int64_t mx_kgroup_workspace_bytes(int groups, int64_t m, int64_t n, int64_t k, int bf16_operands) {
+  mx::GemmArgs p{};
+  p.groups = groups;
+  p.M = n;
+  p.N = k;
+  p.K = m;
+  return split_workspace_bytes(p, bf16_operands ? 2 : 1, nullptr, nullptr);
 }

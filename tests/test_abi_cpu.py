@@ -108,18 +108,52 @@ def test_gemm_validation(lib):
     assert f(P, P, P, P, None, 1, 64, 64, 64, P2, 7, None) == MX_E_DTYPE
     assert f(P, P, P, P, P + 2, 1, 64, 64, 64, P2, 0, None) == MX_E_ALIGN
     assert lib.mx_grouped_mm_dgrad(P, P, P, P, None, 1, 64, 40, 64, P2, 0, None) == MX_E_SHAPE  # n % 32
-    assert lib.mx_grouped_mm_wgrad(P, P, P, P, None, 1, 40, 64, 64, P2, 0, None) == MX_E_SHAPE  # m % 32
+    assert lib.mx_grouped_mm_wgrad(P, P, P, P, None, 1, 40, 64, 64, P2, 0, None, 0, None) == MX_E_SHAPE  # m % 32
     # extent limits: contraction above 2^22, or a scale buffer reaching 2^31 bytes
     big = (1 << 22) + 32
     assert f(P, P, P, P, None, 1, 64, 64, big, P2, 0, None) == MX_E_SHAPE
     assert b"2^22" in lib.mx_last_error()
     assert lib.mx_grouped_mm_dgrad(P, P, P, P, None, 1, 64, big, 64, P2, 0, None) == MX_E_SHAPE
-    assert lib.mx_grouped_mm_wgrad(P, P, P, P, None, 1, big, 64, 64, P2, 0, None) == MX_E_SHAPE
+    assert lib.mx_grouped_mm_wgrad(P, P, P, P, None, 1, big, 64, 64, P2, 0, None, 0, None) == MX_E_SHAPE
     assert f(P, P, P, P, None, 1, 1 << 30, 64, 1 << 22, P2, 0, None) == MX_E_SHAPE  # a's scales: 2^47 bytes
     assert b"2^31" in lib.mx_last_error()
-    assert lib.mx_grouped_mm_wgrad(P, P, P, P, None, 1, 1 << 22, 1 << 16, 64, P2, 0, None) == MX_E_SHAPE  # 2^33
+    assert lib.mx_grouped_mm_wgrad(P, P, P, P, None, 1, 1 << 22, 1 << 16, 64, P2, 0, None, 0, None) == MX_E_SHAPE  # 2^33
     # at the limit the shapes are accepted (no GPU here: the device check answers)
     assert f(P, P, P, P, None, 1, 64, 64, 1 << 22, P2, 0, None) in (MX_E_DEVICE, 0)
+
+
+def test_wgrad_workspace(lib):
+    """The split-contraction workspace is the caller's: its size comes from a host
+    query, bad workspace arguments are rejected before any launch."""
+    q = lib.mx_grouped_mm_wgrad_workspace_bytes
+    # the 576-wide dense wgrad over 16384 tokens: 3 x 16 = 48 tiles of 256x256, so
+    # 256 // 48 = 5 splits of fp32 partials, each 576 * 4096 floats
+    assert q(1, 16384, 576, 4096, 0) == 5 * 576 * 4096 * 4
+    # enough output tiles (8 x 16 x 16 = 2048): no split
+    assert q(8, 16384, 4096, 4096, 0) == 0
+    # too short a contraction to split (two 256-wide windows per split at least)
+    assert q(1, 256, 64, 64, 0) == 0
+    # the bf16 operands count 2 bytes per contraction element: more windows, same cap
+    assert q(1, 16384, 576, 4096, 1) == 5 * 576 * 4096 * 4
+    # a partial's length rounds up to a multiple of 4 floats (16-byte aligned partials)
+    assert q(1, 16384, 33, 33, 0) == 16 * ((33 * 33 + 3) // 4 * 4) * 4
+    assert q(0, 256, 64, 64, 0) == -1 and q(1, -1, 64, 64, 0) == -1 and q(1, 256, 0, 64, 0) == -1
+    w = lib.mx_grouped_mm_wgrad
+    assert w(P, P, P, P, None, 1, 256, 64, 64, P2, 0, P2, -16, None) == MX_E_SHAPE  # negative size
+    assert w(P, P, P, P, None, 1, 256, 64, 64, P2, 0, P2 + 8, 1024, None) == MX_E_ALIGN  # misaligned
+    assert w(P, P, P, P, None, 1, 256, 64, 64, P2, 0, P2, 1024, None) in (MX_E_DEVICE, 0)
+    assert w(P, P, P, P, None, 1, 256, 64, 64, P2, 0, None, 0, None) in (MX_E_DEVICE, 0)  # no workspace
+    assert lib.mx_grouped_mm_bf16_wgrad(P, P, P2, 3, 104, 36, 64, P2, 0, P2 + 4, 64, None) == MX_E_ALIGN
+
+
+def test_probe_mfma_dot_validation(lib):
+    f = lib.mx_probe_mfma_dot
+    assert f(0, P, P, P, P, P2, P2, None) in (MX_E_DEVICE, 0)
+    assert f(3, P, P, P, P, P2, P2, None) in (MX_E_DEVICE, 0)
+    assert f(4, P, P, P, P, P2, P2, None) == MX_E_DTYPE
+    assert f(-1, P, P, P, P, P2, P2, None) == MX_E_DTYPE
+    assert f(0, None, P, P, P, P2, P2, None) == MX_E_NULL
+    assert f(0, P, P, P, P, P2 + 2, P2, None) == MX_E_ALIGN
 
 
 def test_valid_arguments_without_a_gpu_report_device(lib):
@@ -195,8 +229,8 @@ def test_backward_arm_calls_validation(lib):
     assert f(P, P, None, 1, 100, 40, (1 << 21) + 8, P2, 0, None) == MX_E_SHAPE  # contraction limit
     assert f(P, P, P2, 1, 100, 40, 64, P2, 5, None) == MX_E_DTYPE
     assert lib.mx_grouped_mm_bf16_dgrad(P, P, P2, 3, 100, 36, 64, P2, 0, None) == MX_E_SHAPE  # n % 8
-    assert lib.mx_grouped_mm_bf16_wgrad(P, P, P2, 3, 100, 36, 64, P2, 0, None) == MX_E_SHAPE  # m % 8
-    assert lib.mx_grouped_mm_bf16_wgrad(P, P, P2, 3, 104, 36, 64, P2, 0, None) in (MX_E_DEVICE, 0)
+    assert lib.mx_grouped_mm_bf16_wgrad(P, P, P2, 3, 100, 36, 64, P2, 0, None, 0, None) == MX_E_SHAPE  # m % 8
+    assert lib.mx_grouped_mm_bf16_wgrad(P, P, P2, 3, 104, 36, 64, P2, 0, None, 0, None) in (MX_E_DEVICE, 0)
 
 
 def test_fused_padding_calls_validation(lib):

@@ -3,9 +3,11 @@ casts, the fused padded cast, grouped forward, dgrad, and a split-contraction
 wgrad) replayed several times, with other eager work and synchronisations between
 the replays; every replay must reproduce the eager results bit for bit.
 
-The calls enqueue kernels only (no memset nodes, no host synchronisation); the
-split-contraction wgrad's workspace must exist before the capture, so the
-sequence runs once eagerly first, as the header states.
+The calls enqueue kernels only (no memset nodes, no host synchronisation, no
+allocation by the library): the sequence is captured before it has ever run (no
+warm-up call); the split-contraction wgrad's workspace is the caller's (here a
+torch allocation from the graph's own memory pool). Between the replays a larger
+split wgrad runs eagerly with a workspace of its own, which must not disturb them.
 """
 
 import numpy as np
@@ -62,29 +64,34 @@ def test_captured_sequence_replays():
         mx.mx_grouped_mm_fwd_padded(b["pq"], b["ps"], b["wq"], b["ws"], b["poffs"], raw_offs, rows_pad, m, n, k,
                                     out=b["yp"])
 
-    say("[graph] eager reference")
-    sequence()
-    torch.cuda.synchronize()
     outs = ("xq", "xts", "dyq", "nqt", "nsc", "y", "dx", "dw", "pq", "pts", "poffs", "yp")
-    ref = {key: b[key].clone() for key in outs}
-    side = torch.cuda.Stream()
-    side.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(side):
-        sequence()  # warm-up on the capture's side stream, as torch's graph API expects
-    torch.cuda.current_stream().wait_stream(side)
-    torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
-    say("[graph] capture")
+    say("[graph] capture (no warm-up call)")
     with torch.cuda.graph(g):
         sequence()
     torch.cuda.synchronize()
-    other = dev_bf16(synth.normal_bf16(rng, (m, k), 3.0))
+    captured = {key: b[key] for key in outs}  # the 32x32 cast returns new tensors on every call
+    say("[graph] eager reference")
+    for key in outs:
+        b[key].zero_()
+    sequence()
+    torch.cuda.synchronize()
+    ref = {key: b[key].clone() for key in outs}
+    b.update(captured)
+    # a larger split wgrad between the replays: 576 x 1024 outputs over 16384 tokens
+    big_m, big_k = 16384, 1024
+    bx = dev_bf16(synth.normal_bf16(rng, (big_m, big_k), 1.0))
+    bdy = dev_bf16(synth.normal_bf16(rng, (big_m, n), 1e-2))
+    _, _, bxtq, bxts = mx.mx_quantize_dim0_dim1(bx)
+    _, _, bdytq, bdyts = mx.mx_quantize_dim0_dim1(bdy)
+    need = mx.mx_grouped_mm_wgrad_workspace_bytes(1, big_m, n, big_k)
+    assert need > mx.mx_grouped_mm_wgrad_workspace_bytes(G, m, n, k) > 0
+    big_ws = torch.empty(need, dtype=torch.uint8, device="cuda:0")
     for r in range(3):
         for key in outs:
             b[key].zero_()
-        # eager work between replays that reuses the library's split workspace
-        mx.mx_quantize_dim0_dim1(other)
-        mx.mx_grouped_mm_wgrad(b["dytq"], b["dyts"], b["xtq"], b["xts"], offs, m, n, k, out_dtype=mx.MX_OUT_F32)
+        mx.mx_grouped_mm_wgrad(bdytq, bdyts, bxtq, bxts, None, big_m, n, big_k, out_dtype=mx.MX_OUT_F32,
+                               workspace=big_ws)
         torch.cuda.synchronize()
         say(f"[graph] replay {r}")
         g.replay()
