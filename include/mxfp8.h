@@ -231,6 +231,23 @@ mx_status mx_grouped_mm_wgrad(const uint8_t* dy_t, const uint8_t* dy_t_s, const 
                               const int32_t* offs, int32_t groups, int64_t m, int64_t n, int64_t k, void* dw,
                               int out_dtype, void* workspace, int64_t workspace_bytes, void* stream);
 
+/* mx_grouped_mm_wgrad for callers that cannot allocate memory (code under HIP
+ * graph capture that must not allocate, tight serving loops, harnesses that forbid
+ * allocation): the same arguments without a workspace, the same results as
+ * mx_grouped_mm_wgrad with a workspace of mx_grouped_mm_wgrad_workspace_bytes
+ * (bit for bit). A split contraction keeps its fp32 partials in a fixed scratch
+ * array inside the library, MX_WGRAD_NOALLOC_SCRATCH_BYTES (64 MiB) per device,
+ * held until the process ends: the most any split can need (at most one round of
+ * 256 output tiles of 256 x 256 fp32 partials), so no valid call is refused; a
+ * call needing more would return MX_E_SHAPE. Every call on one device shares that
+ * device's scratch:
+ * calls whose work may overlap (different streams, no event between them) race, so
+ * the caller orders them. Nothing is allocated, synchronised or cleared. */
+#define MX_WGRAD_NOALLOC_SCRATCH_BYTES (64 * 1024 * 1024)
+mx_status mx_grouped_mm_wgrad_noalloc(const uint8_t* dy_t, const uint8_t* dy_t_s, const uint8_t* x_t,
+                                      const uint8_t* x_t_s, const int32_t* offs, int32_t groups, int64_t m, int64_t n,
+                                      int64_t k, void* dw, int out_dtype, void* stream);
+
 /* Workspace bytes with which mx_grouped_mm_wgrad (bf16_operands = 0) or
  * mx_grouped_mm_bf16_wgrad (bf16_operands = 1) splits its contraction; 0 when the
  * call does not split (enough output tiles, or too short a contraction). Host

@@ -30,6 +30,8 @@ __all__ = [
     "mx_grouped_mm_dgrad",
     "mx_grouped_mm_wgrad",
     "mx_grouped_mm_wgrad_workspace_bytes",
+    "mx_grouped_mm_wgrad_noalloc",
+    "MX_WGRAD_NOALLOC_SCRATCH_BYTES",
     "mx_dequantize",
     "mx_scales_to_logical",
     "mx_transpose_bf16",
@@ -370,6 +372,23 @@ def mx_grouped_mm_wgrad(dy_t, dy_t_s, x_t, x_t_s, offs, m, n, k, groups=None, ou
     ws_ptr, ws_bytes, _keep = _workspace(workspace, need, dev)
     _lib.call("mx_grouped_mm_wgrad", _ptr(dy_t), _ptr(dy_t_s), _ptr(x_t), _ptr(x_t_s), _ptr(offs), G, m, n, k,
               _ptr(out), out_dtype, ws_ptr, ws_bytes, _stream(dy_t))
+    return out
+
+
+MX_WGRAD_NOALLOC_SCRATCH_BYTES = 64 * 1024 * 1024
+
+
+def mx_grouped_mm_wgrad_noalloc(dy_t, dy_t_s, x_t, x_t_s, offs, m, n, k, groups=None, out_dtype=MX_OUT_F32, out=None):
+    """mx_grouped_mm_wgrad without a workspace: a split contraction uses the library's
+    fixed per-device scratch (MX_WGRAD_NOALLOC_SCRATCH_BYTES); overlapping calls on one
+    device race. `out` must be given by callers that cannot allocate."""
+    dev = _device_of(dy_t, "dy_t")
+    G = _groups(offs, groups, dev)
+    _mx_operand(dy_t, dy_t_s, n, m, "dy_t", dev)
+    _mx_operand(x_t, x_t_s, k, m, "x_t", dev)
+    out = _out((G, n, k), out_dtype, dev, out)
+    _lib.call("mx_grouped_mm_wgrad_noalloc", _ptr(dy_t), _ptr(dy_t_s), _ptr(x_t), _ptr(x_t_s), _ptr(offs), G, m, n,
+              k, _ptr(out), out_dtype, _stream(dy_t))
     return out
 
 

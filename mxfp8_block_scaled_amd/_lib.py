@@ -23,6 +23,7 @@ SIGNATURES = {
     "mx_grouped_mm_fwd": (_INT, [_P, _P, _P, _P, _P, _I32, _I64, _I64, _I64, _P, _INT, _P]),
     "mx_grouped_mm_dgrad": (_INT, [_P, _P, _P, _P, _P, _I32, _I64, _I64, _I64, _P, _INT, _P]),
     "mx_grouped_mm_wgrad": (_INT, [_P, _P, _P, _P, _P, _I32, _I64, _I64, _I64, _P, _INT, _P, _I64, _P]),
+    "mx_grouped_mm_wgrad_noalloc": (_INT, [_P, _P, _P, _P, _P, _I32, _I64, _I64, _I64, _P, _INT, _P]),
     "mx_grouped_mm_wgrad_workspace_bytes": (_I64, [_I32, _I64, _I64, _I64, _INT]),
     "mx_dequantize": (_INT, [_P, _P, _I64, _I64, _I64, _INT, _P, _P]),
     "mx_scales_to_logical": (_INT, [_P, _I64, _I64, _P, _P]),

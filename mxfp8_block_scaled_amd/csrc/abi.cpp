@@ -40,6 +40,8 @@ hipError_t mx_launch_pad_both(const uint16_t*, int64_t, int64_t, int64_t, const 
 hipError_t mx_launch_gemm_kgroup(const uint8_t*, const uint8_t*, const uint8_t*, const uint8_t*, const int32_t*, int,
                                  int64_t, int64_t, int64_t, void*, int, void*, int64_t, hipStream_t);
 int64_t mx_kgroup_workspace_bytes(int, int64_t, int64_t, int64_t, int);
+int64_t mx_noalloc_scratch_bytes();
+hipError_t mx_noalloc_scratch(void**);
 
 namespace {
 
@@ -352,6 +354,29 @@ mx_status mx_grouped_mm_wgrad(const uint8_t* dy_t, const uint8_t* dy_t_s, const 
   return launched(mx_launch_gemm_kgroup(dy_t, dy_t_s, x_t, x_t_s, offs, groups, n, k, m, dw, out_dtype,
                                         workspace_bytes ? workspace : nullptr, workspace_bytes, (hipStream_t)stream),
                   "mx_grouped_mm_wgrad");
+}
+
+mx_status mx_grouped_mm_wgrad_noalloc(const uint8_t* dy_t, const uint8_t* dy_t_s, const uint8_t* x_t,
+                                      const uint8_t* x_t_s, const int32_t* offs, int32_t groups, int64_t m, int64_t n,
+                                      int64_t k, void* dw, int out_dtype, void* stream) {
+  TRY(check_wgrad(dy_t, dy_t_s, x_t, x_t_s, offs, groups, m, n, k, dw, out_dtype));
+  const int64_t need = mx_kgroup_workspace_bytes(groups, m, n, k, 0);
+  const int64_t cap = mx_noalloc_scratch_bytes();
+  if (need > cap)
+    return fail(MX_E_SHAPE,
+                "this wgrad splits its contraction into %lld bytes of fp32 partials; the library's fixed scratch "
+                "holds %lld (use mx_grouped_mm_wgrad with a workspace)",
+                (long long)need, (long long)cap);
+  TRY(check_device());
+  void* ws = nullptr;
+  if (need > 0) {
+    const hipError_t e = mx_noalloc_scratch(&ws);
+    if (e != hipSuccess)
+      return fail(MX_E_LAUNCH, "mx_grouped_mm_wgrad_noalloc: scratch address: %s", hipGetErrorString(e));
+  }
+  return launched(mx_launch_gemm_kgroup(dy_t, dy_t_s, x_t, x_t_s, offs, groups, n, k, m, dw, out_dtype, ws, need,
+                                        (hipStream_t)stream),
+                  "mx_grouped_mm_wgrad_noalloc");
 }
 
 // ---- backward override arms: conversions and bf16 grouped GEMMs ----

@@ -822,6 +822,36 @@ hipError_t mx_launch_gemm_bf16_kgroup(const uint16_t* a, const uint16_t* b, cons
   return launch<mx::MODE_KGROUP, mx::EL_BF16>(p, out_bf16, ws, ws_bytes, stream);
 }
 
+// Scratch of mx_grouped_mm_wgrad_noalloc, for callers that cannot allocate: the
+// split partials live here instead of in a caller workspace. One copy per device,
+// held until the process ends; host code uses the address hipGetSymbolAddress gives
+// for the current device (the array's name is only a host-side stand-in). Every split
+// kernel writes all of its partial tiles, so nothing needs clearing between calls.
+// Size: a split fills at most one round of kComputeUnits output tiles of 256 x 256
+// fp32 partials (splits x tiles <= kComputeUnits), 64 MiB, so every call fits.
+constexpr int64_t kNoAllocScratchBytes = kComputeUnits * 256 * 256 * (int64_t)sizeof(float);
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+int64_t mx_noalloc_scratch_bytes() { return kNoAllocScratchBytes; }
+
+// Device address of `scratch` on the current device, looked up once per device.
+hipError_t mx_noalloc_scratch(void** ptr) {
+  static std::mutex mu;
+  static void* addr[64] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    if ((e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch))) != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
+}
+
 // Workspace bytes of a K-grouped call (dw [groups x n x k] over a contraction of m):
 // what it needs to split its contraction, 0 if it does not split.
 int64_t mx_kgroup_workspace_bytes(int groups, int64_t m, int64_t n, int64_t k, int bf16_operands) {

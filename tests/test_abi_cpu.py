@@ -146,6 +146,20 @@ def test_wgrad_workspace(lib):
     assert lib.mx_grouped_mm_bf16_wgrad(P, P, P2, 3, 104, 36, 64, P2, 0, P2 + 4, 64, None) == MX_E_ALIGN
 
 
+def test_wgrad_noalloc(lib):
+    """The no-allocation wgrad validates like mx_grouped_mm_wgrad; its fixed scratch is
+    the largest split any call can make (one round of 256 output tiles of 256 x 256
+    fp32 partials): the tightest case fills it exactly."""
+    f = lib.mx_grouped_mm_wgrad_noalloc
+    assert f(P, P, P, P, None, 1, 40, 64, 64, P2, 0, None) == MX_E_SHAPE  # m % 32
+    assert f(P, P, P, P, None, 1, 256, 64, 64, P2, 7, None) == MX_E_DTYPE
+    assert f(P, P, P, P, None, 1, 16384, 576, 4096, P2, 1, None) in (MX_E_DEVICE, 0)
+    q = lib.mx_grouped_mm_wgrad_workspace_bytes
+    assert q(1, 16384, 1024, 4096, 0) == 64 * 1024 * 1024  # 64 tiles, 4 splits of 1024 x 4096 fp32
+    for shape in [(1, 16384, 576, 4096), (4, 65536, 576, 4096), (3, 8192, 288, 520), (1, 1 << 22, 32, 64)]:
+        assert 0 <= q(*shape, 0) <= 64 * 1024 * 1024
+
+
 def test_probe_mfma_dot_validation(lib):
     f = lib.mx_probe_mfma_dot
     assert f(0, P, P, P, P, P2, P2, None) in (MX_E_DEVICE, 0)
