@@ -36,6 +36,18 @@ rows, Zipf(1.2) group sizes with 3 experts empty): one-pass casts of X, W1, H,
 W2, dY2, dY1 and the grouped fwd, dgrad and wgrad of the gate/up projection
 (W1 [32, 4096, 7168]) and the down projection (W2 [32, 7168, 2048]). No CPU
 baseline in this mode; `traffic` is the committed counter figure of its gate/up wgrad.
+
+--workload linear_4096: the dense MXFP8Linear step of the linear benchmark command on
+"Wire MoE and MXFP8Linear training paths to CuTeDSL by default" (M=N=4096, K=2048,
+CUDA-graph replay): one-pass casts of X [4096, 2048] and dY [4096, 4096], the 32x32
+cast of W [4096, 2048] (both orientations), then fwd Y = X W^T, dgrad dX = dY W (W^T
+from the 32x32 cast) and wgrad dW = dY^T X; 206.2 GFLOP per step. The step is captured
+into a HIP graph of `steps` steps (100 by default) and replayed once as the timed
+region; the dominant kernel is timed by events around its eager launches right after.
+The 256^3 small linear (dim0 casts of
+A and B with their planted zero and outlier blocks, fwd with fp32 output) is timed the
+same way and reported as a latency beside it. The CPU baseline is the oracle on the
+whole step.
 """
 
 import argparse
@@ -79,10 +91,12 @@ def parse():
                          "group boundaries, runs the grouped passes on the padded offsets and unpads Y and dX")
     ap.add_argument("--backward", default=None, choices=["quantized", "high_precision", "dequantized"],
                     help="time the MoE grouped step (forward + the named backward override arm) instead")
-    ap.add_argument("--workload", default="moe_g8", choices=["moe_g8", "deepseek_share"],
+    ap.add_argument("--workload", default="moe_g8", choices=["moe_g8", "deepseek_share", "linear_4096"],
                     help="deepseek_share: one GPU's share of a DeepSeek-V3-like MoE layer (32 experts, hidden "
                          "7168, FFN 2048, 32768 routed rows, Zipf group sizes, 3 experts empty), fwd+bwd of "
-                         "both expert projections, instead of the default MoE step")
+                         "both expert projections, instead of the default MoE step; linear_4096: the dense "
+                         "MXFP8Linear fwd+bwd at M=N=4096, K=2048 (32x32 weight scales) replayed as a HIP graph, "
+                         "with the 256^3 small linear's latency beside it")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a 1 GiB device-to-device copy instead (reference for HBM byte counters)")
     return ap.parse_args()
@@ -213,6 +227,11 @@ def main():
 
     def to_dev(bits):
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    if args.workload == "linear_4096":
+        assert not (args.unaligned_groups or args.backward or args.separate_casts or args.only), \
+            "--workload linear_4096 runs its own step"
+        return linear_4096_main(args, mx, synth, to_dev, dev)
 
     d = synth.moe_g8(0, with_backward=True)
     offs_np = d["offs"]
@@ -548,6 +567,183 @@ def main():
     print(json.dumps(line), flush=True)
 
 
+def host_facts():
+    """The host the CPU baseline ran on: affine cores and CPU model."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for ln in fh:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"affine_cores": len(os.sched_getaffinity(0)), "cpu_model": model}
+
+
+def blas_threads():
+    import threadpoolctl
+
+    return max([i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()] or [1])
+
+
+def linear_4096_main(args, mx, synth, to_dev, dev):
+    import torch
+
+    d = synth.linear_4096(0)
+    X, W, dY = to_dev(d["x"]), to_dev(d["w"]), to_dev(d["dy"])
+    Ml, Kl = X.shape
+    Nl = W.shape[0]
+    u8 = lambda *s: torch.empty(s, dtype=torch.uint8, device=dev)  # noqa: E731
+    bf = lambda *s: torch.empty(s, dtype=torch.bfloat16, device=dev)  # noqa: E731
+    sb = mx.mx_scale_bytes
+    b = {"xq": u8(Ml, Kl), "xs": u8(sb(Ml, Kl)), "xtq": u8(Kl, Ml), "xts": u8(sb(Kl, Ml)),
+         "wq": u8(Nl, Kl), "wqt": u8(Kl, Nl), "wsr": u8(sb(Nl, Kl)), "wsc": u8(sb(Kl, Nl)),
+         "dyq": u8(Ml, Nl), "dys": u8(sb(Ml, Nl)), "dytq": u8(Nl, Ml), "dyts": u8(sb(Nl, Ml)),
+         "y": bf(Ml, Nl), "dx": bf(Ml, Kl), "dw": bf(1, Nl, Kl)}
+    ws = wgrad_workspace(mx, dev, 1, Ml, Nl, Kl)
+    both = lambda n_elem: n_elem * BOTH_BYTES_PER_ELEM  # noqa: E731
+    ops = [
+        ("cast_dim0+dim1 X", "cast", both(Ml * Kl),
+         lambda: mx.mx_quantize_dim0_dim1(X, b["xq"], b["xs"], b["xtq"], b["xts"])),
+        ("cast_w32 W", "cast", Nl * Kl * W32_BYTES_PER_ELEM,
+         lambda: mx.mx_quantize_weight_32x32(W, True, b["wq"], b["wqt"], b["wsr"], b["wsc"])),
+        ("gemm_fwd dense", "gemm", 2 * Ml * Nl * Kl,
+         lambda: mx.mx_grouped_mm_fwd(b["xq"], b["xs"], b["wq"], b["wsr"], None, Ml, Nl, Kl, out=b["y"])),
+        ("cast_dim0+dim1 dY", "cast", both(Ml * Nl),
+         lambda: mx.mx_quantize_dim0_dim1(dY, b["dyq"], b["dys"], b["dytq"], b["dyts"])),
+        ("gemm_dgrad dense", "gemm", 2 * Ml * Nl * Kl,
+         lambda: mx.mx_grouped_mm_dgrad(b["dyq"], b["dys"], b["wqt"], b["wsc"], None, Ml, Nl, Kl, out=b["dx"])),
+        ("gemm_wgrad dense", "gemm", 2 * Ml * Nl * Kl,
+         lambda: mx.mx_grouped_mm_wgrad(b["dytq"], b["dyts"], b["xtq"], b["xts"], None, Ml, Nl, Kl, out=b["dw"],
+                                        out_dtype=mx.MX_OUT_BF16, workspace=ws)),
+    ]
+    stream = torch.cuda.current_stream()
+
+    def run(events=None):
+        for i, (_, _, _, fn) in enumerate(ops):
+            if events is not None:
+                events[i][0].record(stream)
+            fn()
+            if events is not None:
+                events[i][1].record(stream)
+
+    # eager warm-up with events around every launch: per-kernel table and the dominant kernel
+    ev_pairs = lambda: [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in ops]  # noqa: E731
+    eager = [ev_pairs() for _ in range(max(args.warmup, 1))]
+    for e in eager:
+        run(e)
+    torch.cuda.synchronize()
+    op_ms = [float(np.median([e[i][0].elapsed_time(e[i][1]) for e in eager[1:] or eager])) for i in range(len(ops))]
+    dom_i = max(range(len(ops)), key=lambda i: op_ms[i] if ops[i][1] in PEAKS else -1)
+
+    # the step as a HIP graph of `steps` steps (events recorded inside a capture give no
+    # timings, so the dominant kernel is timed by events around its eager launches
+    # in `steps` eager steps right after the timed replay)
+    reps = args.steps
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        for r in range(reps):
+            for _, _, _, fn in ops:
+                fn()
+    torch.cuda.synchronize()
+    graph.replay()  # warm-up replay
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    graph.replay()  # the timed region: `steps` steps, back to back
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / reps
+    after = [ev_pairs() for _ in range(reps)]
+    for e in after:
+        run(e)
+    torch.cuda.synchronize()
+    dom_ms = float(np.mean([e[dom_i][0].elapsed_time(e[dom_i][1]) for e in after]))
+
+    # the 256^3 small linear: its casts and fp32 forward, replayed the same way
+    sd = synth.linear_small(0)
+    A, B = to_dev(sd["a"]), to_dev(sd["b"])
+    sbuf = {"aq": u8(256, 256), "as": u8(sb(256, 256)), "bq": u8(256, 256), "bs": u8(sb(256, 256)),
+            "y": torch.empty(256, 256, dtype=torch.float32, device=dev)}
+
+    def small():
+        mx.mx_quantize_dim0(A, sbuf["aq"], sbuf["as"])
+        mx.mx_quantize_dim0(B, sbuf["bq"], sbuf["bs"])
+        mx.mx_grouped_mm_fwd(sbuf["aq"], sbuf["as"], sbuf["bq"], sbuf["bs"], None, 256, 256, 256,
+                             out_dtype=mx.MX_OUT_F32, out=sbuf["y"])
+
+    small()
+    torch.cuda.synchronize()
+    sgraph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(sgraph, stream=side):
+        for _ in range(100):
+            small()
+    sgraph.replay()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    sgraph.replay()
+    torch.cuda.synchronize()
+    small_us = (time.perf_counter() - t1) * 1e6 / 100
+
+    per_op = {}
+    for i, (name, kind, units, _) in enumerate(ops):
+        ms = dom_ms if i == dom_i else op_ms[i]
+        mm = kind in PEAKS
+        rate = units / (ms * 1e-3) / (1e12 if mm else 1e9)
+        per_op[name] = {"us": round(ms * 1e3, 2), ("tflops" if mm else "gbps"): round(rate, 1),
+                        "frac": round(rate / (PEAKS[kind] if mm else PEAK_HBM_GBPS), 4),
+                        "timed": ("events around its eager launches, `steps` steps after the timed replay (mean)"
+                                  if i == dom_i else "eager warm-up steps (median)")}
+    gemm_flops = sum(u for _, k, u, _ in ops if k in PEAKS)
+    dom_name, dom_kind, dom_units, _ = ops[dom_i]
+    achieved = dom_units / (dom_ms * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAKS[dom_kind], "unit": "TFLOP/s",
+                "frac": round(achieved / PEAKS[dom_kind], 4), "traffic": load_traffic("linear_4096: " + dom_name,
+                                                                                       dom_units),
+                "kernel": dom_name, "flops_per_launch": dom_units, "avg_launch_us": round(dom_ms * 1e3, 2)}
+    cpu = None if args.no_cpu_baseline else linear_cpu_baseline(synth)
+    line = {
+        "metric": METRIC, "value": round(gemm_flops / (ms_per_step * 1e-3) / 1e12, 1), "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": reps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "mxfp8 (e4m3 x e4m3, e8m0 block scales, fp32 accumulate)",
+        "data": "synthetic (seeded N(0,sigma) bf16)",
+        "config": {"workload": "linear_4096 MXFP8Linear fwd+dgrad+wgrad: X 4096x2048, W 4096x2048 (32x32 weight "
+                               "scales), dY 4096x4096; one HIP graph of `steps` steps, replayed",
+                   "M": Ml, "N": Nl, "K": Kl, "parallelism": "none (1 GPU)"},
+        "small_linear_256_us": round(small_us, 2),
+        "small_linear_256": "dim0 casts of A, B [256, 256] (1% zero, 1% outlier blocks) + fwd fp32 out, one "
+                            "iteration of a 100-iteration HIP graph",
+        "roofline": roofline, "cpu_baseline": cpu, "kernels": per_op, "source_hash": src_hash(),
+    }
+    print(json.dumps(line), flush=True)
+
+
+def linear_cpu_baseline(synth):
+    """The oracle on the whole linear_4096 step: casts of X, W (32x32), dY and the
+    float64 fwd, dgrad, wgrad."""
+    from oracle import mx as orc
+
+    d = synth.linear_4096(0)
+    t0 = time.perf_counter()
+    xq, xs = orc.quantize_dim0(d["x"])
+    wq, wqt, wsr, wsc = orc.quantize_weight_32x32(d["w"])
+    orc.mx_grouped_mm_fwd(xq, xs, wq, wsr, None, 1)
+    dyq, dys = orc.quantize_dim0(d["dy"])
+    orc.mx_grouped_mm_fwd(dyq, dys, wqt, wsc, None, 1)
+    dytq, dyts = orc.quantize_dim1(d["dy"])
+    xtq, xts = orc.quantize_dim1(d["x"])
+    orc.mx_grouped_mm_wgrad(dytq, dyts, xtq, xts, None, 1)
+    dt = time.perf_counter() - t0
+    flops = 3 * 2 * 4096 * 4096 * 2048
+    return dict({"value": round(flops / dt / 1e12, 5), "unit": "TFLOP/s", "cores": blas_threads(), "kind": "oracle",
+                 "seconds": round(dt, 2),
+                 "sample": "the whole step: oracle casts of X, W (32x32), dY and float64 fwd+dgrad+wgrad (numpy; "
+                           "casts single-threaded, BLAS matmul on `cores` threads)"}, **host_facts())
+
+
 def cpu_baseline():
     """The CPU oracle on a bounded slice of the same step, in the same unit.
 
@@ -556,8 +752,6 @@ def cpu_baseline():
     and dim1 casts of all three operands, then the float64 forward, dgrad and
     wgrad. About 10-15 s of host time. value = GEMM flops / total time.
     """
-    import threadpoolctl
-
     from mxfp8_block_scaled_amd import synth
     from oracle import mx as orc
 
@@ -578,11 +772,11 @@ def cpu_baseline():
         orc.mx_grouped_mm_wgrad(dytq, dyts, xtq, xts, None, 1)
     dt = time.perf_counter() - t0
     flops = experts * 3 * 2 * rows * N * K
-    threads = max([i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()] or [1])
-    return {"value": round(flops / dt / 1e12, 5), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "seconds": round(dt, 2),
-            "sample": f"{experts} expert slices, each {rows} token rows x W[{N},{K}]; oracle dim0+dim1 casts of X, W, "
-                      "dY and float64 fwd+dgrad+wgrad (numpy; casts single-threaded, BLAS matmul multi-threaded)"}
+    return dict({"value": round(flops / dt / 1e12, 5), "unit": "TFLOP/s", "cores": blas_threads(), "kind": "oracle",
+                 "seconds": round(dt, 2),
+                 "sample": f"{experts} expert slices, each {rows} token rows x W[{N},{K}]; oracle dim0+dim1 casts of "
+                           "X, W, dY and float64 fwd+dgrad+wgrad (numpy; casts single-threaded, BLAS matmul on "
+                           "`cores` threads)"}, **host_facts())
 
 
 if __name__ == "__main__":

@@ -247,11 +247,11 @@ def mx_quantize_ex(x, forms=MX_FORM_DIM0 | MX_FORM_DIM1, scale_mode=MX_SCALE_RCE
     return q, scale, q_t, scale_t
 
 
-def mx_quantize_weight_32x32(w, transposed=True):
+def mx_quantize_weight_32x32(w, transposed=True, q=None, q_t=None, scale_row=None, scale_col=None):
     """32x32 weight cast of w [n, k] or [batch, n, k] -> (q, q_t, scale_row, scale_col).
 
-    q_t and scale_col are None when transposed=False.
-    """
+    q_t and scale_col are None when transposed=False. Outputs may be given (fixed
+    buffers, e.g. for graph capture)."""
     w = _bf16_bits(w)
     if w.dim() == 2:
         batch, (n, k) = 1, w.shape
@@ -263,16 +263,26 @@ def mx_quantize_weight_32x32(w, transposed=True):
         raise ValueError("w must be 2D or 3D")
     if w.stride(-1) != 1:
         raise ValueError("w must have unit inner stride")
+    dev = _device_of(w, "w")
     lead = () if w.dim() == 2 else (batch,)
-    q = torch.empty(lead + (n, k), dtype=torch.uint8, device=w.device)
-    s_row = _u8(mx_scale_bytes(batch * n, k), w.device)
-    q_t = s_col = None
+    if q is None:
+        q = torch.empty(lead + (n, k), dtype=torch.uint8, device=w.device)
+    if scale_row is None:
+        scale_row = _u8(mx_scale_bytes(batch * n, k), w.device)
+    _buf(q, "q", _U8, batch * n * k, dev)
+    _buf(scale_row, "scale_row", _U8, mx_scale_bytes(batch * n, k), dev)
     if transposed:
-        q_t = torch.empty(lead + (k, n), dtype=torch.uint8, device=w.device)
-        s_col = _u8(mx_scale_bytes(batch * k, n), w.device)
-    _lib.call("mx_quantize_weight_32x32", _ptr(w), batch, n, k, w.stride(-2), _ptr(q), _ptr(q_t), _ptr(s_row),
-              _ptr(s_col), _stream(w))
-    return q, q_t, s_row, s_col
+        if q_t is None:
+            q_t = torch.empty(lead + (k, n), dtype=torch.uint8, device=w.device)
+        if scale_col is None:
+            scale_col = _u8(mx_scale_bytes(batch * k, n), w.device)
+        _buf(q_t, "q_t", _U8, batch * n * k, dev)
+        _buf(scale_col, "scale_col", _U8, mx_scale_bytes(batch * k, n), dev)
+    else:
+        q_t = scale_col = None
+    _lib.call("mx_quantize_weight_32x32", _ptr(w), batch, n, k, w.stride(-2), _ptr(q), _ptr(q_t), _ptr(scale_row),
+              _ptr(scale_col), _stream(w))
+    return q, q_t, scale_row, scale_col
 
 
 def _out(shape, out_dtype, device, out):

@@ -661,7 +661,9 @@ __global__ __launch_bounds__(256) void k_split_reduce(const float* __restrict__ 
 // so the splits fill about one round of the chip. Returns 1 for no split.
 int choose_splits(const mx::GemmArgs& p, int64_t elem_bytes) {
   const int64_t tiles = (int64_t)p.groups * ((p.M + 255) / 256) * ((p.N + 255) / 256);
-  if (tiles >= kComputeUnits || tiles == 0) return 1;
+  // half a round or more: 128x256 tiles fill the device without partials (a 4096 x
+  // 2048 output over 4096 tokens: 44 us against 61 us split two ways)
+  if (tiles >= kComputeUnits / 2 || tiles == 0) return 1;
   const int64_t wins_per_group = (p.K * elem_bytes + 255) / 256 / p.groups;  // 256-byte windows per group, on average
   int64_t s = kComputeUnits / tiles;
   s = std::min<int64_t>(s, wins_per_group / 2);  // at least two windows (8 k-steps) per split
@@ -716,6 +718,10 @@ int choose_tiling(const mx::GemmArgs& p, int out_bf16) {
   // smaller saving does not repay the lower operand reuse of 192-row tiles (4096 rows
   // ran 294 us against 263 us as 256x256)
   if (MODE == mx::MODE_KGROUP && (p.M + 191) / 192 * 192 * 8 <= (p.M + 255) / 256 * 256 * 7) return TILE_192x256;
+  // half a round to one round of 256x256 tiles: 128x256 tiles fill the device once
+  // (the 4096 x 4096 x 2048 linear's dgrad, 128 tiles: 44 against 52 us; its wgrad
+  // 44 against 61 us with the contraction split two ways)
+  if (big_tiles < kComputeUnits) return TILE_128x256;
   // many tiles, bf16 output: one wave per SIMD (grouped forward / dgrad 279-281 /
   // 269-272 us against 287-288 / 277-278 with two; MXFP8 wgrad 296-298 against
   // 301-304), except the bf16 K-grouped wgrad, where two waves per SIMD hide its

@@ -4,11 +4,12 @@ The library picks a tiling from the problem's shape; each case here is shaped to
 select one of them, with groups that end inside tiles (MXFP8 groups on 32-row
 boundaries, as the calls require; bf16 groups anywhere), one group empty, and
 partial tiles on both output edges:
-  * 256x256 with eight waves (two per SIMD): 128..511 tiles of 256x256 (M-grouped
+  * 256x256 with eight waves (two per SIMD): 256..511 tiles of 256x256 (M-grouped
     over a contraction above 1024, or K-grouped), and with more tiles for fp32
     outputs and the bf16 K-grouped wgrad;
   * 128x256 over a three-deep ring, two blocks per compute unit: M-grouped with a
-    contraction of at most 1024 and >= 128 tiles;
+    contraction of at most 1024 and >= 128 tiles, and either mode with 128..255
+    tiles of 256x256 (half a round to a round);
   * 192x256: K-grouped outputs whose rows 192-row tiles cover with at least 1/8
     less padding than 256-row ones, without and with split contractions;
   * 256x192: M-grouped outputs whose columns 192-column tiles cover with at least
@@ -80,8 +81,13 @@ def wgrad_case(oracle, n, k, m, sizes, seed, name):
 
 
 def test_mgroup_eight_waves(oracle):
-    """16 x 8 = 128 tiles of 256x256 over K = 1280: the eight-wave tiling."""
-    fwd_case(oracle, 4000, 2016, 1280, [992, 0, 1504, 1504], 61, "8-wave")
+    """16 x 16 = 256 tiles of 256x256 over K = 1280: the eight-wave tiling."""
+    fwd_case(oracle, 4000, 4064, 1280, [992, 0, 1504, 1504], 61, "8-wave")
+
+
+def test_mgroup_half_round(oracle):
+    """16 x 9 = 144 tiles of 256x256 over K = 1280 (less than a round): 128x256 tiles."""
+    fwd_case(oracle, 4000, 2080, 1280, [992, 0, 1504, 1504], 60, "128x256 half round")
 
 
 def test_mgroup_short_contraction(oracle):
@@ -107,8 +113,14 @@ def test_mgroup_short_contraction(oracle):
 
 
 def test_kgroup_eight_waves(oracle):
-    """992 x 1056 outputs per group, 8 groups (one empty): 4 x 5 x 8 = 160 tiles."""
-    wgrad_case(oracle, 992, 1056, 4096, [640, 512, 0, 736, 480, 576, 608, 544], 65, "8-wave")
+    """992 x 2080 outputs per group, 8 groups (one empty): 4 x 9 x 8 = 288 tiles."""
+    wgrad_case(oracle, 992, 2080, 4096, [640, 512, 0, 736, 480, 576, 608, 544], 65, "8-wave")
+
+
+def test_kgroup_half_round(oracle):
+    """992 x 1056 outputs per group, 8 groups (one empty): 4 x 5 x 8 = 160 tiles of
+    256x256, less than a round: 128x256 tiles, the contraction not split."""
+    wgrad_case(oracle, 992, 1056, 4096, [640, 512, 0, 736, 480, 576, 608, 544], 64, "128x256 half round")
 
 
 def test_kgroup_192_row_tiles(oracle):
@@ -132,7 +144,7 @@ def test_bf16_tilings(oracle, sizes):
     m = int(sum(sizes))
     offs = synth.offs_from_sizes(np.array(sizes))
     doffs = dev_i32(offs)
-    for n, k, name in ((2016, 1280, "8-wave"), (2016, 576, "128x256")):
+    for n, k, name in ((4064, 1280, "8-wave"), (2016, 576, "128x256")):
         a = synth.normal_bf16(rng, (m, k), 1.0)
         b = synth.normal_bf16(rng, (G * n, k), 0.02)
         say(f"[tiling bf16 {name}] fwd m={m} n={n} k={k} offs={offs.tolist()}")
@@ -181,7 +193,8 @@ def sample_rows(rng, upto, count):
 
 
 @pytest.mark.parametrize("m,n,k,G,name", [
-    (3104, 2336, 1280, 3, "8-wave"),        # 13 x 10 = 130 tiles, K > 1024
+    (4128, 4640, 1280, 3, "8-wave"),        # 17 x 19 = 323 tiles, K > 1024
+    (4096, 2080, 1280, 3, "128x256 half"),  # 16 x 9 = 144 tiles: less than a round
     (3104, 2336, 576, 3, "128x256"),        # K <= 1024
     (8192, 4128, 1088, 4, "256x256"),       # 32 x 17 = 544 tiles (bf16 out; fp32: 8-wave)
     (1000, 800, 320, 3, "128x128"),         # 4 x 4 tiles
@@ -208,7 +221,8 @@ def test_exact_fwd_tilings(oracle, m, n, k, G, name):
 
 @pytest.mark.parametrize("n,k,m,G,name", [
     (352, 2080, 4096, 8, "192x256"),        # 8 x 2 x 9 = 144 tiles, 352 rows in 192-row tiles
-    (1056, 1056, 4096, 8, "8-wave"),        # 8 x 5 x 5 = 200 tiles (1152 rows as 192s: too little saved)
+    (1056, 2080, 4096, 8, "8-wave"),        # 8 x 5 x 9 = 360 tiles (1152 rows as 192s: too little saved)
+    (1056, 1056, 4096, 8, "128x256 half"),  # 8 x 5 x 5 = 200 tiles: less than a round, no split
     (4128, 2080, 2048, 8, "256x256"),       # 8 x 17 x 9 = 1224 tiles (bf16 out; fp32: 8-wave)
     (576, 1056, 8192, 2, "192x256 split"),  # 2 x 3 x 5 = 30 tiles: contraction split 8 ways
 ])
