@@ -123,6 +123,67 @@ struct Tile {
   bool valid;
 };
 
+// The group owning m-tile `mt` of the concatenated per-group m-tile lists (M-grouped):
+// row range [s, e) of the group and, for padded outputs, its output range [so, eo).
+struct GroupHit {
+  int64_t s, e, so, eo, cum;  // cum: m-tiles of the groups before it
+  int g;                      // -1: no group owns mt
+};
+
+// Every wave scans the groups 64 at a time: the group ends as their running maximum
+// by a wave prefix scan, the m-tile counts' prefix sum, a ballot for the owner. That is
+// O(G / 64) steps of a few shuffles, so a thousand groups cost a few dozen steps where
+// a group-by-group walk would wait on one load per group; at eight groups it measured
+// the same as the walk. Each wave finds the same group on its own (no LDS, no
+// barrier). The ends are read as their running maximum clamped into [0, M] (the output
+// ends into [0, out_rows]): for valid offs this changes nothing; an out-of-contract
+// offs gives wrong rows but no access outside the operand and output buffers.
+template <int BM>
+__device__ inline GroupHit find_group(const GemmArgs& p, int64_t mt) {
+  const int l = threadIdx.x & 63;
+  int64_t carry_e = 0, carry_eo = 0, carry_cum = 0;
+  for (int g0 = 0; g0 < p.groups; g0 += 64) {
+    const int g = g0 + l;
+    const bool live = g < p.groups;
+    int64_t e = live ? (int64_t)p.offs[g] : 0, eo = live && p.offs_out ? (int64_t)p.offs_out[g] : 0;
+    e = e > carry_e ? e : carry_e;
+    eo = eo > carry_eo ? eo : carry_eo;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int64_t oe = __shfl_up(e, d, 64), oo = __shfl_up(eo, d, 64);
+      if (l >= d) {
+        e = oe > e ? oe : e;
+        eo = oo > eo ? oo : eo;
+      }
+    }
+    e = e < 0 ? 0 : (e > p.M ? p.M : e);
+    eo = eo < 0 ? 0 : (eo > p.out_rows ? p.out_rows : eo);
+    int64_t sp = __shfl_up(e, 1, 64), sop = __shfl_up(eo, 1, 64);
+    if (l == 0) {
+      sp = carry_e;
+      sop = carry_eo;
+    }
+    const int64_t tiles = live ? (e - sp + BM - 1) / BM : 0;
+    int64_t cum = tiles;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int64_t o = __shfl_up(cum, d, 64);
+      if (l >= d) cum += o;
+    }
+    cum += carry_cum;  // m-tiles up to and including this lane's group
+    const uint64_t own = __ballot(live && mt >= cum - tiles && mt < cum);
+    if (own) {
+      const int j = __ffsll((long long)own) - 1;
+      return GroupHit{__shfl(sp, j, 64), __shfl(e, j, 64), __shfl(sop, j, 64), __shfl(eo, j, 64),
+                      __shfl(cum - tiles, j, 64), g0 + j};
+    }
+    carry_e = __shfl(e, 63, 64);
+    carry_eo = __shfl(eo, 63, 64);
+    carry_cum = __shfl(cum, 63, 64);
+  }
+  return GroupHit{0, 0, 0, 0, 0, -1};
+}
+
 // Logical tile t -> its output tile and contraction range (one block per tile).
 // Blocks are dealt round-robin to the 8 XCDs and xcd_remap gives XCD x the
 // contiguous tile range [x * per_xcd, (x+1) * per_xcd), which its blocks take in
@@ -165,37 +226,19 @@ __device__ inline Tile tile_at(const GemmArgs& p, int64_t t) {
   const int64_t n_tile = in_band / gm;
   T.col0 = n_tile * BN;
   if (MODE == MODE_MGROUP) {
-    // find the group owning m-tile `mt` of the concatenated per-group tile lists. The
-    // group ends are read as the running maximum clamped into [0, M] (and the output
-    // ends into [0, out_rows]): identical for valid offs, and an out-of-contract offs
-    // gives wrong rows but no access outside the operand and output buffers.
-    int64_t cum = 0, s = 0, so = 0;
-    int found = -1;
-    const int G = p.offs ? p.groups : 1;
-    for (int gg = 0; gg < G; ++gg) {
-      int64_t e = p.offs ? p.offs[gg] : p.M;
-      e = e < s ? s : (e > p.M ? p.M : e);
-      int64_t eo = 0;
+    // the group owning m-tile `mt` (dense: the one group of all M rows)
+    GroupHit hit{0, p.M, 0, p.out_rows, 0, 0};
+    if (p.offs) hit = find_group<BM>(p, mt);
+    const int found = hit.g;
+    if (found >= 0) {
+      T.a_row0 = hit.s + (mt - hit.cum) * BM;
+      T.a_row_end = hit.e;
+      T.out_limit = hit.e;
       if (p.offs_out) {
-        eo = p.offs_out[gg];
-        eo = eo < so ? so : (eo > p.out_rows ? p.out_rows : eo);
+        const int64_t real_end = hit.s + (hit.eo - hit.so);  // the group's real rows, padded coordinates
+        T.out_shift = hit.so - hit.s;
+        T.out_limit = real_end < hit.e ? real_end : hit.e;
       }
-      const int64_t tiles = (e - s + BM - 1) / BM;
-      if (mt < cum + tiles) {
-        found = gg;
-        T.a_row0 = s + (mt - cum) * BM;
-        T.a_row_end = e;
-        T.out_limit = e;
-        if (p.offs_out) {
-          const int64_t real_end = s + (eo - so);  // the group's real rows, padded coordinates
-          T.out_shift = so - s;
-          T.out_limit = real_end < e ? real_end : e;
-        }
-        break;
-      }
-      cum += tiles;
-      s = e;
-      so = eo;
     }
     T.valid = found >= 0;
     g = found < 0 ? 0 : found;
@@ -599,9 +642,10 @@ namespace {
 
 constexpr int64_t kComputeUnits = 256;
 
-// Launches one tile configuration over the whole problem (p.splits already set).
-template <int BM, int BN, int WGM, int WGN, int NST, int WPE, int MODE, int EL>
-hipError_t launch_cfg(mx::GemmArgs p, int out_bf16, hipStream_t stream) {
+// Launches one tile configuration and output type over the whole problem (p.splits
+// already set).
+template <int BM, int BN, int WGM, int WGN, int NST, int WPE, int MODE, int EL, int OUT_BF16>
+hipError_t launch_cfg(mx::GemmArgs p, hipStream_t stream) {
   using C = mx::Cfg<BM, BN, WGM, WGN, NST>;
   const int64_t mt_extra = (MODE == mx::MODE_MGROUP && p.offs) ? p.groups : 0;
   p.mt_total = (p.M + BM - 1) / BM + mt_extra;
@@ -609,24 +653,13 @@ hipError_t launch_cfg(mx::GemmArgs p, int out_bf16, hipStream_t stream) {
   p.tiles = MODE == mx::MODE_MGROUP ? p.mt_total * p.nt : (int64_t)p.splits * p.groups * p.mt_total * p.nt;
   if (p.tiles == 0) return hipSuccess;
   const int64_t blocks = p.tiles;
-  const size_t lds = (size_t)C::LDS_BYTES;
-  // the dynamic LDS limit of both output-type instances, raised once per process
-  // (thread-safe static initialisation)
-  static const hipError_t attr = [] {
-    hipError_t e = hipFuncSetAttribute((const void*)mx::k_gemm<BM, BN, WGM, WGN, NST, WPE, MODE, 0, EL>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
-    if (e == hipSuccess)
-      e = hipFuncSetAttribute((const void*)mx::k_gemm<BM, BN, WGM, WGN, NST, WPE, MODE, 1, EL>,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
-    return e;
-  }();
+  // the dynamic LDS limit of this instance, raised once per process (thread-safe
+  // static initialisation)
+  static const hipError_t attr = hipFuncSetAttribute((const void*)mx::k_gemm<BM, BN, WGM, WGN, NST, WPE, MODE, OUT_BF16, EL>,
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
   if (attr != hipSuccess) return attr;
-  if (out_bf16)
-    hipLaunchKernelGGL((mx::k_gemm<BM, BN, WGM, WGN, NST, WPE, MODE, 1, EL>), dim3((unsigned)blocks),
-                       dim3(C::THREADS), lds, stream, p);
-  else
-    hipLaunchKernelGGL((mx::k_gemm<BM, BN, WGM, WGN, NST, WPE, MODE, 0, EL>), dim3((unsigned)blocks),
-                       dim3(C::THREADS), lds, stream, p);
+  hipLaunchKernelGGL((mx::k_gemm<BM, BN, WGM, WGN, NST, WPE, MODE, OUT_BF16, EL>), dim3((unsigned)blocks),
+                     dim3(C::THREADS), (size_t)C::LDS_BYTES, stream, p);
   return hipGetLastError();
 }
 
@@ -681,16 +714,26 @@ enum Tiling {
   TILE_256x192 = 5,  // 256x192, 2x2 waves of 128x96, 4-deep ring, 120 KB: one block per CU
 };
 
+template <int MODE, int EL, int OUT>
+hipError_t launch_tiling_out(int tiling, const mx::GemmArgs& p, hipStream_t stream) {
+  switch (tiling) {
+    case TILE_128: return launch_cfg<128, 128, 2, 2, 4, 2, MODE, EL, OUT>(p, stream);
+    case TILE_128x256: return launch_cfg<128, 256, 2, 2, 3, 2, MODE, EL, OUT>(p, stream);
+    case TILE_192x256: return launch_cfg<192, 256, 1, 4, 4, 1, MODE, EL, OUT>(p, stream);
+    case TILE_256_8W: return launch_cfg<256, 256, 2, 4, 4, 2, MODE, EL, OUT>(p, stream);
+    case TILE_256x192: return launch_cfg<256, 192, 2, 2, 4, 1, MODE, EL, OUT>(p, stream);
+    case TILE_256:
+      // one wave per SIMD holds 256 fp32 accumulators: bf16 output only (the fp32
+      // epilogue would spill), fp32 output takes the eight-wave tiling
+      if (OUT) return launch_cfg<256, 256, 2, 2, 4, 1, MODE, EL, 1>(p, stream);
+      return launch_cfg<256, 256, 2, 4, 4, 2, MODE, EL, OUT>(p, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 template <int MODE, int EL>
 hipError_t launch_tiling(int tiling, const mx::GemmArgs& p, int out_bf16, hipStream_t stream) {
-  switch (tiling) {
-    case TILE_128: return launch_cfg<128, 128, 2, 2, 4, 2, MODE, EL>(p, out_bf16, stream);
-    case TILE_128x256: return launch_cfg<128, 256, 2, 2, 3, 2, MODE, EL>(p, out_bf16, stream);
-    case TILE_192x256: return launch_cfg<192, 256, 1, 4, 4, 1, MODE, EL>(p, out_bf16, stream);
-    case TILE_256_8W: return launch_cfg<256, 256, 2, 4, 4, 2, MODE, EL>(p, out_bf16, stream);
-    case TILE_256x192: return launch_cfg<256, 192, 2, 2, 4, 1, MODE, EL>(p, out_bf16, stream);
-    default: return launch_cfg<256, 256, 2, 2, 4, 1, MODE, EL>(p, out_bf16, stream);
-  }
+  return out_bf16 ? launch_tiling_out<MODE, EL, 1>(tiling, p, stream) : launch_tiling_out<MODE, EL, 0>(tiling, p, stream);
 }
 
 // The tiling for a problem (p.splits set). Measured on the MoE training step's

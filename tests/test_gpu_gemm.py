@@ -80,11 +80,12 @@ def test_wgrad_exact_integer(oracle, n, k, m, sizes):
                 assert np.all(got[g] == 0)
 
 
-@pytest.mark.parametrize("G,seed", [(96, 1), (300, 2)])
-def test_many_groups_exact(oracle, G, seed):
-    """Many small groups, about a third of them empty: the forward's group search and
-    the wgrad's slice-major order over G groups (each group's raster in several
-    slices of uneven length), full outputs bit-exact."""
+@pytest.mark.parametrize("G,seed,nw", [(96, 1, 288), (300, 2, 288), (2000, 3, 64)])
+def test_many_groups_exact(oracle, G, seed, nw):
+    """Many small groups, about a third of them empty: the forward's group search (64
+    groups per wave-scan step, so 2, 5 and 32 steps here) and the wgrad's slice-major
+    order over G groups (each group's raster in several slices of uneven length),
+    full outputs bit-exact."""
     rng = np.random.default_rng(1000 + seed)
     units = rng.integers(0, 4, size=G) * (rng.random(G) > 0.35)
     sizes = 32 * units
@@ -99,8 +100,8 @@ def test_many_groups_exact(oracle, G, seed):
     ref = oracle.mx_grouped_mm_fwd(a_q, a_s, b_q, b_s, offs, G)
     rows = int(offs[-1])
     assert np.array_equal(got[:rows], ref[:rows].astype(np.float32))
-    # wgrad: dW_g = dY_g^T X_g over each group's token range; [G, 288, 96] outputs in 2 x 1 tiles per group
-    nw, kw = 288, 96
+    # wgrad: dW_g = dY_g^T X_g over each group's token range; [G, nw, 96] outputs
+    kw = 96
     dy_t, dy_s = exact_operands(rng, nw, m)
     x_t, x_s = exact_operands(rng, kw, m)
     say(f"[gemm many groups] wgrad G={G} n={nw} k={kw} m={m}")
