@@ -130,67 +130,97 @@ struct GroupHit {
   int g;                      // -1: no group owns mt
 };
 
-// Every wave scans the groups 64 at a time: the group ends as their running maximum
-// by a wave prefix scan, the m-tile counts' prefix sum, a ballot for the owner. That is
-// O(G / 64) steps of a few shuffles, so a thousand groups cost a few dozen steps where
-// a group-by-group walk would wait on one load per group; at eight groups it measured
-// the same as the walk. Each wave finds the same group on its own (no LDS, no
-// barrier). The ends are read as their running maximum clamped into [0, M] (the output
-// ends into [0, out_rows]): for valid offs this changes nothing; an out-of-contract
-// offs gives wrong rows but no access outside the operand and output buffers.
+// Groups g0 .. g0+63 of the M-grouped scan, lane l holding group g0 + l: its row
+// range [s, e), output range [so, eo), m-tiles, and the m-tiles of all groups up to
+// and including it. The ends are read as their running maximum clamped into [0, M]
+// (the output ends into [0, out_rows]): for valid offs this changes nothing; an
+// out-of-contract offs gives wrong rows but no access outside the operand and output
+// buffers. Lanes past the last group hold an empty range and the running totals.
+struct GroupChunk {
+  int64_t s, e, so, eo, tiles, cum;
+  bool live;
+};
+
 template <int BM>
-__device__ inline GroupHit find_group(const GemmArgs& p, int64_t mt) {
+__device__ inline GroupChunk scan_chunk(const GemmArgs& p, int g0, int64_t carry_e, int64_t carry_eo,
+                                        int64_t carry_cum) {
   const int l = threadIdx.x & 63;
-  int64_t carry_e = 0, carry_eo = 0, carry_cum = 0;
-  for (int g0 = 0; g0 < p.groups; g0 += 64) {
-    const int g = g0 + l;
-    const bool live = g < p.groups;
-    int64_t e = live ? (int64_t)p.offs[g] : 0, eo = live && p.offs_out ? (int64_t)p.offs_out[g] : 0;
-    e = e > carry_e ? e : carry_e;
-    eo = eo > carry_eo ? eo : carry_eo;
+  const int g = g0 + l;
+  GroupChunk c;
+  c.live = g < p.groups;
+  int64_t e = c.live ? (int64_t)p.offs[g] : 0, eo = c.live && p.offs_out ? (int64_t)p.offs_out[g] : 0;
+  e = e > carry_e ? e : carry_e;
+  eo = eo > carry_eo ? eo : carry_eo;
 #pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const int64_t oe = __shfl_up(e, d, 64), oo = __shfl_up(eo, d, 64);
-      if (l >= d) {
-        e = oe > e ? oe : e;
-        eo = oo > eo ? oo : eo;
-      }
+  for (int d = 1; d < 64; d <<= 1) {
+    const int64_t oe = __shfl_up(e, d, 64), oo = __shfl_up(eo, d, 64);
+    if (l >= d) {
+      e = oe > e ? oe : e;
+      eo = oo > eo ? oo : eo;
     }
-    e = e < 0 ? 0 : (e > p.M ? p.M : e);
-    eo = eo < 0 ? 0 : (eo > p.out_rows ? p.out_rows : eo);
-    int64_t sp = __shfl_up(e, 1, 64), sop = __shfl_up(eo, 1, 64);
-    if (l == 0) {
-      sp = carry_e;
-      sop = carry_eo;
-    }
-    const int64_t tiles = live ? (e - sp + BM - 1) / BM : 0;
-    int64_t cum = tiles;
+  }
+  e = e < 0 ? 0 : (e > p.M ? p.M : e);
+  eo = eo < 0 ? 0 : (eo > p.out_rows ? p.out_rows : eo);
+  c.s = __shfl_up(e, 1, 64);
+  c.so = __shfl_up(eo, 1, 64);
+  if (l == 0) {
+    c.s = carry_e;
+    c.so = carry_eo;
+  }
+  c.e = e;
+  c.eo = eo;
+  c.tiles = c.live ? (e - c.s + BM - 1) / BM : 0;
+  int64_t cum = c.tiles;
 #pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const int64_t o = __shfl_up(cum, d, 64);
-      if (l >= d) cum += o;
-    }
-    cum += carry_cum;  // m-tiles up to and including this lane's group
-    const uint64_t own = __ballot(live && mt >= cum - tiles && mt < cum);
+  for (int d = 1; d < 64; d <<= 1) {
+    const int64_t o = __shfl_up(cum, d, 64);
+    if (l >= d) cum += o;
+  }
+  c.cum = cum + carry_cum;
+  return c;
+}
+
+// The m-tiles of all groups (the first chunk's scan is kept in `first`). Every wave
+// scans on its own, 64 groups per step of a few shuffles: no LDS, no barrier, and a
+// thousand groups cost a few dozen steps where a group-by-group walk would wait on one
+// load per group (at eight groups the two measured the same).
+template <int BM>
+__device__ inline int64_t total_mtiles(const GemmArgs& p, GroupChunk& first) {
+  first = scan_chunk<BM>(p, 0, 0, 0, 0);
+  int64_t ce = __shfl(first.e, 63, 64), ceo = __shfl(first.eo, 63, 64), cc = __shfl(first.cum, 63, 64);
+  for (int g0 = 64; g0 < p.groups; g0 += 64) {
+    const GroupChunk c = scan_chunk<BM>(p, g0, ce, ceo, cc);
+    ce = __shfl(c.e, 63, 64);
+    ceo = __shfl(c.eo, 63, 64);
+    cc = __shfl(c.cum, 63, 64);
+  }
+  return cc;
+}
+
+// The group owning m-tile `mt`: a ballot over each chunk, starting from the first.
+template <int BM>
+__device__ inline GroupHit find_group(const GemmArgs& p, int64_t mt, const GroupChunk& first) {
+  GroupChunk c = first;
+  for (int g0 = 0;;) {
+    const uint64_t own = __ballot(c.live && mt >= c.cum - c.tiles && mt < c.cum);
     if (own) {
       const int j = __ffsll((long long)own) - 1;
-      return GroupHit{__shfl(sp, j, 64), __shfl(e, j, 64), __shfl(sop, j, 64), __shfl(eo, j, 64),
-                      __shfl(cum - tiles, j, 64), g0 + j};
+      return GroupHit{__shfl(c.s, j, 64), __shfl(c.e, j, 64), __shfl(c.so, j, 64), __shfl(c.eo, j, 64),
+                      __shfl(c.cum - c.tiles, j, 64), g0 + j};
     }
-    carry_e = __shfl(e, 63, 64);
-    carry_eo = __shfl(eo, 63, 64);
-    carry_cum = __shfl(cum, 63, 64);
+    g0 += 64;
+    if (g0 >= p.groups) return GroupHit{0, 0, 0, 0, 0, -1};
+    c = scan_chunk<BM>(p, g0, __shfl(c.e, 63, 64), __shfl(c.eo, 63, 64), __shfl(c.cum, 63, 64));
   }
-  return GroupHit{0, 0, 0, 0, 0, -1};
 }
 
 // Logical tile t -> its output tile and contraction range (one block per tile).
-// Blocks are dealt round-robin to the 8 XCDs and xcd_remap gives XCD x the
-// contiguous tile range [x * per_xcd, (x+1) * per_xcd), which its blocks take in
-// order; with a raster of GM m-tiles by all n-tiles, the ~32 tiles in flight on one
-// XCD share their A and B slices in its L2 (GM = 4 measured best among 1..16).
+// Each XCD takes a contiguous range of logical tiles in order (xcd_remap,
+// spread_tiles); with a raster, over `mt_count` m-tiles, of bands of GM m-tiles by all n-tiles,
+// the ~32 tiles in flight on one XCD share their A and B slices in its L2 (GM = 4
+// measured best among 1..16).
 template <int BM, int BN, int MODE, int OUT_BF16, int EL>
-__device__ inline Tile tile_at(const GemmArgs& p, int64_t t) {
+__device__ inline Tile tile_at(const GemmArgs& p, int64_t t, int64_t mt_count, const GroupChunk& first) {
   constexpr int64_t GM = 4;
   constexpr int64_t EB = EL == EL_BF16 ? 2 : 1;  // bytes per contraction element
   constexpr int out_es = OUT_BF16 ? 2 : 4;
@@ -220,7 +250,7 @@ __device__ inline Tile tile_at(const GemmArgs& p, int64_t t) {
   }
   const int64_t band = r / (GM * p.nt);
   const int64_t first_m = band * GM;
-  const int64_t gm = p.mt_total - first_m < GM ? p.mt_total - first_m : GM;
+  const int64_t gm = mt_count - first_m < GM ? mt_count - first_m : GM;
   const int64_t in_band = r % (GM * p.nt);
   const int64_t mt = first_m + in_band % gm;
   const int64_t n_tile = in_band / gm;
@@ -228,7 +258,7 @@ __device__ inline Tile tile_at(const GemmArgs& p, int64_t t) {
   if (MODE == MODE_MGROUP) {
     // the group owning m-tile `mt` (dense: the one group of all M rows)
     GroupHit hit{0, p.M, 0, p.out_rows, 0, 0};
-    if (p.offs) hit = find_group<BM>(p, mt);
+    if (p.offs) hit = find_group<BM>(p, mt, first);
     const int found = hit.g;
     if (found >= 0) {
       T.a_row0 = hit.s + (mt - hit.cum) * BM;
@@ -294,6 +324,23 @@ __device__ inline int64_t xcd_remap(int64_t bid, int64_t nblk) {
   return bid < per_xcd * 8 ? (bid % 8) * per_xcd + bid / 8 : bid;
 }
 
+// The same for `real` tiles on a grid of nblk >= real blocks (M-grouped with offs:
+// the grid is sized for the most m-tiles any group split can need, the real count is
+// known only on the device): XCD x takes [x * per, (x+1) * per) with per = real / 8
+// rounded up, so every XCD gets an eighth of the real work. Dividing the grid instead
+// left the unused blocks all at the end, on the last XCD: at the MoE step's 1088 real
+// tiles of 1152, XCDs 0-6 ran 144 tiles (4.5 rounds of 32 compute units) and XCD 7
+// ran 80. -1: the block has no tile.
+__device__ inline int64_t spread_tiles(int64_t bid, int64_t nblk, int64_t real) {
+  const int64_t nx = nblk / 8, per = (real + 7) / 8;
+  if (per <= nx) {
+    const int64_t j = bid / 8, t = (bid % 8) * per + j;
+    return bid < nx * 8 && j < per && t < real ? t : -1;
+  }
+  const int64_t t = xcd_remap(bid, nblk);
+  return t < real ? t : -1;
+}
+
 // WPE: waves per SIMD the register allocation must allow (2 where two blocks
 // share a compute unit).
 template <int BM, int BN, int WGM, int WGN, int NST_, int WPE, int MODE, int OUT_BF16, int EL>
@@ -310,7 +357,16 @@ __global__ __launch_bounds__(64 * WGM * WGN) __attribute__((amdgpu_waves_per_eu(
   const int tid = threadIdx.x, l = tid & 63, h = l >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int wm = wave / WGN, wn = wave % WGN;
-  Tile T = tile_at<BM, BN, MODE, OUT_BF16, EL>(p, xcd_remap(blockIdx.x, gridDim.x));
+  GroupChunk first{};
+  int64_t mt_count = p.mt_total, t;
+  if (MODE == MODE_MGROUP && p.offs) {
+    mt_count = uniform(total_mtiles<BM>(p, first));
+    t = uniform(spread_tiles(blockIdx.x, gridDim.x, mt_count * p.nt));
+    if (t < 0) return;
+  } else {
+    t = xcd_remap(blockIdx.x, gridDim.x);
+  }
+  Tile T = tile_at<BM, BN, MODE, OUT_BF16, EL>(p, t, mt_count, first);
   if (!__builtin_amdgcn_readfirstlane((int)T.valid)) return;
   T.a_row0 = uniform(T.a_row0); T.a_row_end = uniform(T.a_row_end);
   T.b_row0 = uniform(T.b_row0); T.b_row_end = uniform(T.b_row_end);
