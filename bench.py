@@ -497,6 +497,30 @@ def main():
         cps.append(c0.elapsed_time(c1))
     copy_gbps = round(2 * (1 << 30) / (min(cps) * 1e-3) / 1e9, 1)
     del src, dst
+    # the same copy at each cast's own traffic (reads + writes = the cast's bytes), each
+    # after a 512 MiB fill that leaves the caches holding dirty lines as the step's
+    # GEMM outputs do, best of five: a smaller copy pays its ramp and tail on fewer bytes
+    scrub = torch.empty(1 << 29, dtype=torch.uint8, device=dev)
+    copy_same = {}
+    for name, kind, units, _ in ops:
+        if kind != "cast":
+            continue
+        half = int(units // 2) // 16 * 16
+        src = torch.empty(half, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        cps = []
+        for r in range(5):
+            scrub.fill_(r)
+            c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            c0.record()
+            dst.copy_(src)
+            c1.record()
+            torch.cuda.synchronize()
+            cps.append(c0.elapsed_time(c1))
+        gbps = 2 * half / (min(cps) * 1e-3) / 1e9
+        copy_same[name] = {"copy_gbps": round(gbps, 1), "cast_frac_of_it": round(per_op[name]["gbps"] / gbps, 4)}
+        del src, dst
+    del scrub
     # practical MXFP8 ceiling, also after the timed region: the library's register-only
     # loop of the block-scaled MFMA on every SIMD (iters * 2^30 flops), best of three
     sink = mx.mx_probe_mfma(256)
@@ -561,6 +585,7 @@ def main():
         "hbm_copy_gbps": copy_gbps,
         "mfma_loop_tflops": mfma_loop_tflops,
         "cast_frac_of_copy": round(cast_bytes / (cast_us * 1e-6) / 1e9 / copy_gbps, 4),
+        "copy_same_bytes": copy_same,
         "step_gemm_gflop": round(gemm_flops / 1e9, 2), "step_cast_gb": round(cast_bytes / 1e9, 4),
         "roofline": roofline, "cpu_baseline": cpu, "kernels": per_op, "source_hash": src_hash(),
     }

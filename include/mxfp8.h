@@ -123,7 +123,8 @@ mx_status mx_quantize_dim1(const uint16_t* x, int64_t batch, int64_t rows, int64
  *   scale    mx_scale_bytes(batch*rows, cols) bytes (written)
  *   q_t      batch x [cols x rows] codes, transposed (written)
  *   scale_t  mx_scale_bytes(batch*cols, rows) bytes (written)
- * rows % 32 == 0, cols % 32 == 0, batch >= 1. */
+ * rows % 32 == 0, cols % 32 == 0, batch >= 1; ld_x < 2^25 and rows < 2^29 (the
+ * kernel addresses a 32-row sub-tile through 32-bit offsets), else MX_E_SHAPE. */
 mx_status mx_quantize_dim0_dim1(const uint16_t* x, int64_t batch, int64_t rows, int64_t cols, int64_t ld_x,
                                 uint8_t* q, uint8_t* scale, uint8_t* q_t, uint8_t* scale_t, void* stream);
 
@@ -139,7 +140,8 @@ mx_status mx_quantize_dim0_dim1(const uint16_t* x, int64_t batch, int64_t rows, 
  * (the one-pass cast); arguments as mx_quantize_dim0 (on the stacked
  * [batch*rows x cols] matrix), mx_quantize_dim1 and mx_quantize_dim0_dim1. Outputs
  * of a form not requested may be NULL. rows % 32 == 0 when MX_FORM_DIM1 is
- * requested; cols % 32 == 0 always. With MX_SCALE_RCEIL the results equal those of
+ * requested; cols % 32 == 0 always; both forms at once take the one-pass cast's
+ * limits (ld_x < 2^25, rows < 2^29). With MX_SCALE_RCEIL the results equal those of
  * the other entry points. An unknown forms or scale_mode value is MX_E_DTYPE. */
 mx_status mx_quantize_ex(const uint16_t* x, int64_t batch, int64_t rows, int64_t cols, int64_t ld_x, int forms,
                          int scale_mode, uint8_t* q, uint8_t* scale, uint8_t* q_t, uint8_t* scale_t, void* stream);
@@ -413,7 +415,8 @@ mx_status mx_unpad_token_groups(const void* y_pad, int64_t rows_pad, int64_t col
  *   x         [rows x cols] bf16 (pitch ld_x), offs the unpadded group ends
  *   q, scale  [rows_pad x cols] + mx_scale_bytes(rows_pad, cols) (written)
  *   q_t, scale_t  [cols x rows_pad] + mx_scale_bytes(cols, rows_pad) (written)
- * rows_pad >= mx_padded_rows(rows, groups), a multiple of 32; cols % 32 == 0. */
+ * rows_pad >= mx_padded_rows(rows, groups), a multiple of 32; cols % 32 == 0;
+ * ld_x < 2^25 and rows_pad < 2^29 as for mx_quantize_dim0_dim1. */
 mx_status mx_pad_quantize_dim0_dim1(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
                                     const int32_t* offs, int32_t groups, int64_t rows_pad, uint8_t* q,
                                     uint8_t* scale, uint8_t* q_t, uint8_t* scale_t, int32_t* offs_pad,

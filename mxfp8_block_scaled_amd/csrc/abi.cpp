@@ -116,6 +116,17 @@ mx_status check_pitch(const char* name, int64_t ld, int64_t cols) {
   return MX_OK;
 }
 
+// The one-pass cast reads a 32-row sub-tile and writes four q_t rows at a time through
+// 32-bit buffer offsets from a per-sub-tile base: the row pitch must stay below 2^25
+// elements and the rows (q_t's row length) below 2^29.
+mx_status check_one_pass(int64_t ld, int64_t rows) {
+  if (ld >= ((int64_t)1 << 25))
+    return fail(MX_E_SHAPE, "ld_x = %lld: the one-pass cast needs a row pitch below 2^25 elements", (long long)ld);
+  if (rows >= ((int64_t)1 << 29))
+    return fail(MX_E_SHAPE, "rows = %lld: the one-pass cast needs fewer than 2^29 rows", (long long)rows);
+  return MX_OK;
+}
+
 mx_status check_mul32(const char* name, int64_t v) {
   if (v % 32 != 0) return fail(MX_E_SHAPE, "%s = %lld must be a multiple of 32 (one MX block)", name, (long long)v);
   return MX_OK;
@@ -201,6 +212,7 @@ mx_status mx_quantize_dim0_dim1(const uint16_t* x, int64_t batch, int64_t rows, 
   TRY(check_mul32("rows", rows));
   TRY(check_mul32("cols", cols));
   TRY(check_pitch("ld_x", ld_x, cols));
+  TRY(check_one_pass(ld_x, rows));
   if (batch * rows > kMaxDim || batch * cols > kMaxDim) return fail(MX_E_SHAPE, "batch * rows or batch * cols exceeds 2^31");
   TRY(check_ptr("x", x));
   TRY(check_ptr("q", q));
@@ -225,6 +237,7 @@ mx_status mx_quantize_ex(const uint16_t* x, int64_t batch, int64_t rows, int64_t
   if (d1) TRY(check_mul32("rows", rows));
   TRY(check_mul32("cols", cols));
   TRY(check_pitch("ld_x", ld_x, cols));
+  if (d0 && d1) TRY(check_one_pass(ld_x, rows));
   if (batch * rows > kMaxDim || batch * cols > kMaxDim) return fail(MX_E_SHAPE, "batch * rows or batch * cols exceeds 2^31");
   TRY(check_rows_ptr("x", x, batch * rows));
   if (d0) {
@@ -593,6 +606,7 @@ mx_status mx_pad_quantize_dim0_dim1(const uint16_t* x, int64_t rows, int64_t col
   TRY(check_dim("cols", cols, 32));
   TRY(check_mul32("cols", cols));
   TRY(check_pitch("ld_x", ld_x, cols));
+  TRY(check_one_pass(ld_x, rows_pad));
   if (rows_pad * cols > ((int64_t)1 << 40)) return fail(MX_E_SHAPE, "rows_pad * cols is too large");
   TRY(check_rows_ptr("x", x, rows));
   TRY(check_ptr("q", q));

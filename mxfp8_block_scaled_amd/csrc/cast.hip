@@ -43,6 +43,20 @@ __device__ inline u32x2 encode8(u32x4 v, int byte, unsigned amax) {
   return out;
 }
 
+// The same for a block whose scale byte is at least 1 (or whose values are all
+// zero), given the scale operand: no doubling path.
+template <bool SAT>
+__device__ inline u32x2 encode8_plain(u32x4 v, float sc) {
+  u32x2 out;
+  out.x = cvt2(v.x, sc) | (cvt2(v.y, sc) << 16);
+  out.y = cvt2(v.z, sc) | (cvt2(v.w, sc) << 16);
+  if (SAT) {
+    out.x = sat_e4m3x4(out.x);
+    out.y = sat_e4m3x4(out.y);
+  }
+  return out;
+}
+
 __device__ inline unsigned amax8(u32x4 v) {
   unsigned a = amax_pair(0u, v.x);
   a = amax_pair(a, v.y);
@@ -224,6 +238,17 @@ __global__ __launch_bounds__(256) void k_quant_dim1(const uint16_t* __restrict__
 // padded row p holds row padded_source(p) of x, or zeros (ao fork PR 10, "Known
 // follow-ups": padded token groups), so the padded bf16 copy is never written.
 // ---------------------------------------------------------------------------------
+// A raw buffer from `base` for the one-pass cast's loads and stores: lanes outside
+// the tensor take the offset kOutside, which the range check drops (stores) or reads
+// as zeros (loads), so no lane needs a branch; the row-dependent part of an address
+// goes in the scalar offset, so a lane holds one 32-bit offset for all 16 rows
+// (64-bit addresses for 16 loads and 16 stores took 64 VGPRs). Every in-range offset
+// is below 2^31 for row strides up to 2^25 elements (checked on the host).
+constexpr uint32_t kOutside = 0x80000000u;
+__device__ inline __amdgpu_buffer_rsrc_t cast_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, 0x7fffffff, 0x00020000);
+}
+
 struct RowGather {
   const int32_t* offs;  // unpadded group ends (device)
   int groups;
@@ -242,7 +267,7 @@ __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(2))) vo
   __shared__ unsigned s_s0[WV][64];                                // dim0 scale tile per wave
   constexpr int SUBS = 8 / WV;  // 32-row sub-tiles per wave, one after the other
   __shared__ std::conditional_t<GATHER, GroupTable, char> s_grp;  // the group table (gather only)
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, h = l >> 5, c = l & 31;
+  const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, h = l >> 5, c = l & 31;
   if constexpr (GATHER) {
     build_table(s_grp, gth.offs, gth.groups, gth.src_rows);
     if (blockIdx.x == 0)
@@ -252,94 +277,143 @@ __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(2))) vo
   const int64_t tiles = batch * rtiles * ctiles;
   uint8_t* st0 = (uint8_t*)s_s0[w];
   uint8_t* ss1 = (uint8_t*)s_s1;
+
+  // The wave's sub-tile `sub` of tile t: its 16 loads (zeros outside the tensor or
+  // past the last tile).
+  auto load = [&](u32x4(&v)[16], int64_t t, int sub) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[i] = (u32x4){0, 0, 0, 0};
+    if (t >= tiles) return;
+    const int64_t b = t / (rtiles * ctiles), rem = t % (rtiles * ctiles);
+    const int64_t r0 = (rem % rtiles) * 256, col = (rem / rtiles) * 256 + 8 * c;
+    const int64_t base = r0 + 32 * (SUBS * w + sub);
+    if (base >= rows) return;  // rows % 32 == 0: the sub-tile is all in or all out
+    const uint32_t lane_off = col < cols ? (uint32_t)((16 * h * ld + col) * 2) : kOutside;
+    if constexpr (GATHER) {
+      // The sub-tile's 32 rows form one 32-row block of the padded rows, and padded
+      // group edges are multiples of 32, so they lie in one padded group: a single
+      // lookup gives the run of source rows, read as one run (a pointer per load needed
+      // 301 VGPRs, one workgroup per compute unit, 94 us; walking group edges row by
+      // row between loads, 78 us; one lookup, 69 us, on the MoE tokens, same device).
+      const GroupTable& gt = s_grp;
+      const int g = upper_index(gt.pad_end, gth.groups, base);
+      int64_t src0 = 0, real = 0;  // source row of padded row `base`; real rows from it on
+      if (g < gth.groups) {
+        src0 = (g ? gt.end[g - 1] : 0) + (base - (g ? gt.pad_end[g - 1] : 0));
+        real = gt.end[g] - src0;
+      }
+      if (real <= 0) src0 = 0;
+      src0 = __builtin_amdgcn_readfirstlane((int)src0);  // the same in every lane
+      const int nreal = real <= 16 * h ? 0 : (real - 16 * h < 16 ? (int)(real - 16 * h) : 16);  // the lane's real rows
+      const auto rx = cast_rsrc(x + src0 * ld);
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        v[i] = __builtin_amdgcn_raw_buffer_load_b128(rx, i < nreal ? lane_off : kOutside, (int)(i * ld * 2), 2);
+    } else {
+      const auto rx = cast_rsrc(x + (b * rows + base) * ld);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) v[i] = __builtin_amdgcn_raw_buffer_load_b128(rx, lane_off, (int)(i * ld * 2), 2);
+    }
+  };
+
+  // Each wave keeps its next sub-tile's loads in flight while it encodes the current
+  // one, and the first sub-tile of its next tile in flight across the barrier and the
+  // q_t stores that end a tile, so the bf16 reads never wait on the encode or the
+  // stores.
+  u32x4 v[16];
+  load(v, blockIdx.x, 0);
   for (int64_t t = blockIdx.x; t < tiles; t += gridDim.x) {
     const int64_t b = t / (rtiles * ctiles), rem = t % (rtiles * ctiles);
     const int64_t ct = rem / rtiles, rt = rem % rtiles;
     const int64_t r0 = rt * 256, c0 = ct * 256;
     const int64_t col = c0 + 8 * c;
     const bool col_ok = col < cols;  // cols % 32 == 0: a quad's 32 columns are all in or all out
-    const uint16_t* xb = x + b * rows * ld;
     const int64_t qrow0 = b * rows;  // dim0 rows of this batch in the stacked [batch*rows x cols]
     for (int i = tid; i < 8 * 64; i += 64 * WV) s_s1[i >> 6][i & 63] = 0x7f7f7f7fu;  // pad blocks past the last row
     __syncthreads();
-#pragma unroll 1
+#pragma unroll
     for (int sub = 0; sub < SUBS; ++sub) {
       const int kb = SUBS * w + sub;            // dim1 block (32 rows) within the tile
       const int64_t base = r0 + 32 * kb;        // first row of the sub-tile
       const bool rows_ok = base < rows;         // rows % 32 == 0: the sub-tile is all in or all out
-      u32x4 v[16];
-      if constexpr (GATHER) {
-        // The sub-tile's 32 rows form one 32-row block of the padded rows, and padded
-        // group edges are multiples of 32, so they lie in one padded group: a single
-        // lookup gives the run of source rows, and the lane's 16 loads issue back to
-        // back through one stepped pointer (a pointer per load needed 301 VGPRs, one
-        // workgroup per compute unit, 94 us; walking group edges row by row between
-        // loads, 78 us; this, 69 us, on the MoE tokens, same device).
-        const GroupTable& gt = s_grp;
-        const int g = upper_index(gt.pad_end, gth.groups, base);
-        int64_t src0 = 0, real = 0;  // source row of padded row `base`; real rows from it on
-        if (g < gth.groups) {
-          src0 = (g ? gt.end[g - 1] : 0) + (base - (g ? gt.pad_end[g - 1] : 0));
-          real = gt.end[g] - src0;
-        }
-        if (real <= 0) src0 = 0;
-        const int nreal = real <= 16 * h ? 0 : (real - 16 * h < 16 ? (int)(real - 16 * h) : 16);  // the lane's real rows
-        const u32x4* xr = (const u32x4*)(x + (src0 + 16 * h) * ld + col);
-        const int64_t step = ld / 8;
+      u32x4 nv[16];
+      if (sub + 1 < SUBS)
+        load(nv, t, sub + 1);
+      else
+        load(nv, t + gridDim.x, 0);
+      // the block amaxes of both casts from one pass over |v|: each row's 8 values
+      // (dim0, reduced over the quad below) and the lane's column pairs over its 16
+      // rows (dim1), so no |v| stays live between the two casts
+      unsigned a0[16], am[4] = {0, 0, 0, 0};
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          v[i] = (u32x4){0, 0, 0, 0};
-          if (col_ok && rows_ok && i < nreal) v[i] = __builtin_nontemporal_load(xr);
-          xr += step;
-        }
-      } else {
+      for (int i = 0; i < 16; ++i) {
+        unsigned r = 0;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          v[i] = (u32x4){0, 0, 0, 0};
-          if (col_ok && rows_ok) v[i] = __builtin_nontemporal_load((const u32x4*)(xb + (base + 16 * h + i) * ld + col));
+        for (int p = 0; p < 4; ++p) {
+          r = amax_pair(r, v[i][p]);
+          am[p] = amax_pair(am[p], v[i][p]);
         }
+        a0[i] = fold_pair(r);
       }
       // ---- dim0 ----
       s_s0[w][l] = 0x7f7f7f7fu;
+      const auto rq = cast_rsrc(q + (qrow0 + base) * cols);
+      const uint32_t q_off = col_ok ? (uint32_t)(16 * h * cols + col) : kOutside;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        unsigned a = amax8(v[i]);
+        unsigned a = a0[i];
         a = umax(a, dpp_xor1(a));
         a = umax(a, dpp_xor2(a));
         const int byte = scale_byte<FLOOR>(a);
-        const u32x2 codes = encode8<FLOOR>(v[i], byte, a);
-        if (col_ok && rows_ok) {
-          *(u32x2*)(q + (qrow0 + base + 16 * h + i) * cols + col) = codes;
-          if ((c & 3) == 0) st0[scale_in_tile(16 * h + i, c >> 2)] = (uint8_t)byte;
+        // a scale byte of 0 with a non-zero amax (tiny values) needs the doubling
+        // path; a wave that has none takes the short one
+        u32x2 codes;
+        if (__builtin_expect(__ballot(byte == 0 && a != 0) == 0, 1))
+          codes = encode8_plain<FLOOR>(v[i], scale_operand(byte == 0 ? 1 : byte));
+        else
+          codes = encode8<FLOOR>(v[i], byte, a);
+        if (rows_ok) {
+          __builtin_amdgcn_raw_buffer_store_b64(codes, rq, q_off, (int)(i * cols), 0);
+          if (col_ok && (c & 3) == 0) st0[scale_in_tile(16 * h + i, c >> 2)] = (uint8_t)byte;
         }
       }
       if (rows_ok && c0 < cols)
-        ((unsigned*)(scale + scale_tile_base((qrow0 + base) / 32, ct, kt0)))[l] = s_s0[w][l];
+        __builtin_amdgcn_raw_buffer_store_b32(s_s0[w][l], cast_rsrc(scale + scale_tile_base((qrow0 + base) / 32, ct, kt0)),
+                                              4 * l, 0, 0);
       // ---- dim1 ----
 #pragma unroll
       for (int p = 0; p < 4; ++p) {  // column pair (2p, 2p+1) of the lane's eight
-        unsigned am = 0;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) am = amax_pair(am, v[i][p]);
-        am = amax_pair(am, (unsigned)__shfl_xor((int)am, 32));
+        const unsigned a32 = amax_pair(am[p], (unsigned)__shfl_xor((int)am[p], 32));
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
-          const unsigned amax = e ? (am >> 16) : (am & 0xffff);
+          const unsigned amax = e ? (a32 >> 16) : (a32 & 0xffff);
           const int byte = scale_byte<FLOOR>(amax);
           const bool tiny = byte == 0 && amax != 0;
           const float sc = scale_operand(byte == 0 ? 1 : byte);
           const unsigned sel = e ? 0x07060302u : 0x05040100u;
           unsigned d[4];
+          if (__builtin_expect(__ballot(tiny) == 0, 1)) {
 #pragma unroll
-          for (int m = 0; m < 4; ++m) {
-            unsigned p01 = __builtin_amdgcn_perm(v[4 * m + 1][p], v[4 * m][p], sel);  // rows 4m, 4m+1
-            unsigned p23 = __builtin_amdgcn_perm(v[4 * m + 3][p], v[4 * m + 2][p], sel);
-            if (tiny) {
-              p01 = double_bf16x2(p01);
-              p23 = double_bf16x2(p23);
+            for (int m = 0; m < 4; ++m) {
+              const unsigned p01 = __builtin_amdgcn_perm(v[4 * m + 1][p], v[4 * m][p], sel);  // rows 4m, 4m+1
+              const unsigned p23 = __builtin_amdgcn_perm(v[4 * m + 3][p], v[4 * m + 2][p], sel);
+              d[m] = cvt2(p01, sc) | (cvt2(p23, sc) << 16);
             }
-            d[m] = cvt2(p01, sc) | (cvt2(p23, sc) << 16);
-            if (FLOOR) d[m] = sat_e4m3x4(d[m]);
+          } else {
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+              unsigned p01 = __builtin_amdgcn_perm(v[4 * m + 1][p], v[4 * m][p], sel);
+              unsigned p23 = __builtin_amdgcn_perm(v[4 * m + 3][p], v[4 * m + 2][p], sel);
+              if (tiny) {
+                p01 = double_bf16x2(p01);
+                p23 = double_bf16x2(p23);
+              }
+              d[m] = cvt2(p01, sc) | (cvt2(p23, sc) << 16);
+            }
+          }
+          if (FLOOR) {
+#pragma unroll
+            for (int m = 0; m < 4; ++m) d[m] = sat_e4m3x4(d[m]);
           }
           const int cc = 8 * c + 2 * p + e;      // column within the tile = row of s_t
           const int k = 2 * kb + h;  // 16-byte chunk: the lane's 16 rows
@@ -347,23 +421,31 @@ __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(2))) vo
           if (h == 0 && rows_ok) ss1[(cc >> 5) * 256 + scale_in_tile(cc & 31, kb)] = (uint8_t)byte;
         }
       }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) v[i] = nv[i];
     }
     __syncthreads();
-    // q_t rows c0 + (256/WV)w .. (columns of the tile), four per instruction, 256 bytes each
-    uint8_t* qtb = q_t + b * cols * rows;
+    // q_t rows c0 + (256/WV)w .. (columns of the tile), four per instruction, 256 bytes
+    // each: row c0 + orow0 + (l >> 4) from a per-instruction base, so a lane's offset
+    // stays below 4 * rows + 256
+    {
+      const int ch = l & 15;
+      const uint32_t lane_off = r0 + 16 * ch < rows ? (uint32_t)((l >> 4) * rows + 16 * ch) : kOutside;
 #pragma unroll
-    for (int k = 0; k < 64 / WV; ++k) {
-      const int orow = 256 / WV * w + 4 * k + (l >> 4), ch = l & 15;
-      const int64_t cidx = c0 + orow, rr = r0 + 16 * ch;
-      const u32x4 d = *(const u32x4*)(s_t + orow * 256 + ((ch ^ ((orow >> 3) & 15)) << 4));
-      if (cidx < cols && rr < rows) *(u32x4*)(qtb + cidx * rows + rr) = d;
+      for (int k = 0; k < 64 / WV; ++k) {
+        const int orow0 = 256 / WV * w + 4 * k, orow = orow0 + (l >> 4);
+        const u32x4 d = *(const u32x4*)(s_t + orow * 256 + ((ch ^ ((orow >> 3) & 15)) << 4));
+        if (c0 + orow0 < cols)  // cols % 32 == 0: the four rows are all in or all out
+          __builtin_amdgcn_raw_buffer_store_b128(d, cast_rsrc(q_t + (b * cols + c0 + orow0) * rows + r0), lane_off, 0, 0);
+      }
     }
 #pragma unroll
     for (int j = 0; j < 8 / WV; ++j) {
       const int tile = WV * j + w;  // dim1 scale tile (32 q_t rows) of this thread's dword
       const int64_t out_row0 = c0 + 32 * tile;
       if (out_row0 < cols)
-        ((unsigned*)(scale_t + scale_tile_base((b * cols + out_row0) / 32, rt, kt1)))[l] = s_s1[tile][l];
+        __builtin_amdgcn_raw_buffer_store_b32(s_s1[tile][l], cast_rsrc(scale_t + scale_tile_base((b * cols + out_row0) / 32, rt, kt1)),
+                                              4 * l, 0, 0);
     }
     __syncthreads();  // s_t and s_s1 are reused by the next tile
   }

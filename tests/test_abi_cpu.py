@@ -80,6 +80,11 @@ def test_dim0_dim1_validation(lib):
     assert f(P, 1, 64, 64, 64, P2, P2, None, P2, None) == MX_E_NULL  # q_t
     assert f(P, 1, 64, 64, 64, P2, P2, P2, None, None) == MX_E_NULL  # scale_t
     assert f(P, 1, 64, 64, 64, P2 + 4, P2, P2, P2, None) == MX_E_ALIGN
+    # the one-pass cast's 32-bit buffer offsets: row pitch below 2^25, rows below 2^29
+    assert f(P, 1, 64, 64, 1 << 25, P2, P2, P2, P2, None) == MX_E_SHAPE
+    assert f(P, 1, 1 << 29, 32, 32, P2, P2, P2, P2, None) == MX_E_SHAPE
+    assert lib.mx_quantize_ex(P, 1, 64, 64, 1 << 25, 3, 0, P2, P2, P2, P2, None) == MX_E_SHAPE
+    assert lib.mx_quantize_ex(P, 1, 64, 64, 1 << 25, 1, 0, P2, P2, None, None, None) in (MX_E_DEVICE, 0)
 
 
 def test_quantize_ex_validation(lib):
@@ -252,6 +257,7 @@ def test_fused_padding_calls_validation(lib):
     assert f(P, 40, 64, 64, P2, 3, 256, P2, P2, P2, P2, P2, None) in (MX_E_DEVICE, 0)
     assert f(P, 40, 48, 64, P2, 3, 256, P2, P2, P2, P2, P2, None) == MX_E_SHAPE  # cols % 32
     assert f(P, 40, 64, 64, P2, 3, 224, P2, P2, P2, P2, P2, None) == MX_E_SHAPE  # rows_pad below the bound
+    assert f(P, 40, 64, 1 << 25, P2, 3, 256, P2, P2, P2, P2, P2, None) == MX_E_SHAPE  # pitch >= 2^25
     assert f(P, 40, 64, 64, P2, 3, 256, P2, P2, None, P2, P2, None) == MX_E_NULL  # q_t
     assert f(P, 40, 64, 64, P2, 3, 256, P2, P2, P2, P2, None, None) == MX_E_NULL  # offs_pad
     g = lib.mx_grouped_mm_fwd_padded
