@@ -170,8 +170,11 @@ def deepseek_share_ops(mx, synth, to_dev, dev):
     ws_gate = wgrad_workspace(mx, dev, E, R, N1, H_)
 
     def cast(name):
+        # inputs' and weights' transposed codes are read late (wgrad, dgrad): streamed;
+        # the gradients' are read by the wgrad right after their dgrad: cached
+        st = name in ("x", "w1", "h", "w2")
         return ("cast_dim0+dim1 " + name, "cast", both(t[name].numel()),
-                lambda: mx.mx_quantize_dim0_dim1(t[name], *q[name]))
+                lambda: mx.mx_quantize_dim0_dim1(t[name], *q[name], stream_t=st))
 
     ops = [
         cast("x"), cast("w1"),
@@ -327,9 +330,9 @@ def main():
     elif args.backward == "quantized":
         ops = [
             ("cast_dim0+dim1 X", "cast", both(M * K),
-             lambda: mx.mx_quantize_dim0_dim1(X, buf["xq"], buf["xs"], buf["xtq"], buf["xts"])),
+             lambda: mx.mx_quantize_dim0_dim1(X, buf["xq"], buf["xs"], buf["xtq"], buf["xts"], stream_t=True)),
             ("cast_dim0+dim1 W", "cast", both(G * N * K),
-             lambda: mx.mx_quantize_dim0_dim1(W, buf["wq"], buf["ws"], buf["wtq"], buf["wts"])),
+             lambda: mx.mx_quantize_dim0_dim1(W, buf["wq"], buf["ws"], buf["wtq"], buf["wts"], stream_t=True)),
             g_fwd,
             ("cast_dim0+dim1 dY", "cast", both(M * N),
              lambda: mx.mx_quantize_dim0_dim1(dY, buf["dyq"], buf["dys"], buf["dytq"], buf["dyts"])),
@@ -378,12 +381,16 @@ def main():
             n_wgrad,
         ]
     else:
-        # every tensor here is needed in both orientations: one-pass casts
+        # every tensor here is needed in both orientations: one-pass casts. X's and W's
+        # transposed codes are read only by wgrad and dgrad, after the forward and the dY
+        # cast: they are streamed past the caches (MX_FORM_STREAM_T), which then still
+        # hold X's and W's row-wise codes when the forward reads them; dY's transposed
+        # codes are read by the wgrad right after dgrad and stay cached
         ops = [
             ("cast_dim0+dim1 X", "cast", both(M * K),
-             lambda: mx.mx_quantize_dim0_dim1(X, buf["xq"], buf["xs"], buf["xtq"], buf["xts"])),
+             lambda: mx.mx_quantize_dim0_dim1(X, buf["xq"], buf["xs"], buf["xtq"], buf["xts"], stream_t=True)),
             ("cast_dim0+dim1 W", "cast", both(G * N * K),
-             lambda: mx.mx_quantize_dim0_dim1(W, buf["wq"], buf["ws"], buf["wtq"], buf["wts"])),
+             lambda: mx.mx_quantize_dim0_dim1(W, buf["wq"], buf["ws"], buf["wtq"], buf["wts"], stream_t=True)),
             g_fwd,
             ("cast_dim0+dim1 dY", "cast", both(M * N),
              lambda: mx.mx_quantize_dim0_dim1(dY, buf["dyq"], buf["dys"], buf["dytq"], buf["dyts"])),

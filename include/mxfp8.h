@@ -131,18 +131,24 @@ mx_status mx_quantize_dim0_dim1(const uint16_t* x, int64_t batch, int64_t rows, 
 /* Forms and scale rules of mx_quantize_ex. */
 #define MX_FORM_DIM0 1
 #define MX_FORM_DIM1 2
+#define MX_FORM_STREAM_T 4 /* with both forms: write the transposed codes with non-temporal
+                              stores, for a q_t that is read only after much other traffic
+                              (a weight's q_t read by dgrad, the tokens' by wgrad): the
+                              caches then keep the row-wise codes the next GEMM reads.
+                              Results are identical; only where the bytes are cached differs */
 #define MX_SCALE_RCEIL 0 /* ceil(log2(amax / 448)): the rule of the other casts */
 #define MX_SCALE_FLOOR 1 /* floor(log2(amax)) - 8 (the OCP default): the block maximum
                             can exceed 448 after scaling and saturates to 448 */
 
 /* Casts with a choice of form and scale rule [ao fork PR 10, Known follow-ups:
  * FLOOR is reachable next to RCEIL]. forms = MX_FORM_DIM0, MX_FORM_DIM1 or both
- * (the one-pass cast); arguments as mx_quantize_dim0 (on the stacked
+ * (the one-pass cast), optionally with MX_FORM_STREAM_T; arguments as mx_quantize_dim0 (on the stacked
  * [batch*rows x cols] matrix), mx_quantize_dim1 and mx_quantize_dim0_dim1. Outputs
  * of a form not requested may be NULL. rows % 32 == 0 when MX_FORM_DIM1 is
  * requested; cols % 32 == 0 always; both forms at once take the one-pass cast's
  * limits (ld_x < 2^25, rows < 2^29). With MX_SCALE_RCEIL the results equal those of
- * the other entry points. An unknown forms or scale_mode value is MX_E_DTYPE. */
+ * the other entry points. An unknown forms or scale_mode value, or MX_FORM_STREAM_T
+ * without both forms, is MX_E_DTYPE. */
 mx_status mx_quantize_ex(const uint16_t* x, int64_t batch, int64_t rows, int64_t cols, int64_t ld_x, int forms,
                          int scale_mode, uint8_t* q, uint8_t* scale, uint8_t* q_t, uint8_t* scale_t, void* stream);
 

@@ -23,6 +23,7 @@ __all__ = [
     "mx_quantize_ex",
     "MX_FORM_DIM0",
     "MX_FORM_DIM1",
+    "MX_FORM_STREAM_T",
     "MX_SCALE_RCEIL",
     "MX_SCALE_FLOOR",
     "mx_quantize_weight_32x32",
@@ -181,10 +182,12 @@ def mx_quantize_dim1(x, q_t=None, scale_t=None):
     return q_t, scale_t
 
 
-def mx_quantize_dim0_dim1(x, q=None, scale=None, q_t=None, scale_t=None):
+def mx_quantize_dim0_dim1(x, q=None, scale=None, q_t=None, scale_t=None, stream_t=False):
     """Both casts in one pass: x [rows, cols] or [batch, rows, cols] (batches contiguous)
     -> (q [batch*rows, cols], scale, q_t [.., cols, rows], scale_t), the same as
-    mx_quantize_dim0 of the stacked rows plus mx_quantize_dim1."""
+    mx_quantize_dim0 of the stacked rows plus mx_quantize_dim1. stream_t: write q_t
+    with non-temporal stores (MX_FORM_STREAM_T), for a q_t read only after much other
+    traffic; the results are the same."""
     x = _bf16_bits(x)
     if x.dim() == 2:
         batch, (rows, cols) = 1, x.shape
@@ -210,12 +213,17 @@ def mx_quantize_dim0_dim1(x, q=None, scale=None, q_t=None, scale_t=None):
     _buf(scale, "scale", _U8, mx_scale_bytes(batch * rows, cols), dev)
     _buf(q_t, "q_t", _U8, batch * rows * cols, dev)
     _buf(scale_t, "scale_t", _U8, mx_scale_bytes(batch * cols, rows), dev)
-    _lib.call("mx_quantize_dim0_dim1", _ptr(x), batch, rows, cols, x.stride(-2), _ptr(q), _ptr(scale), _ptr(q_t),
-              _ptr(scale_t), _stream(x))
+    if stream_t:
+        _lib.call("mx_quantize_ex", _ptr(x), batch, rows, cols, x.stride(-2),
+                  MX_FORM_DIM0 | MX_FORM_DIM1 | MX_FORM_STREAM_T, MX_SCALE_RCEIL, _ptr(q), _ptr(scale), _ptr(q_t),
+                  _ptr(scale_t), _stream(x))
+    else:
+        _lib.call("mx_quantize_dim0_dim1", _ptr(x), batch, rows, cols, x.stride(-2), _ptr(q), _ptr(scale), _ptr(q_t),
+                  _ptr(scale_t), _stream(x))
     return q, scale, q_t, scale_t
 
 
-MX_FORM_DIM0, MX_FORM_DIM1 = 1, 2
+MX_FORM_DIM0, MX_FORM_DIM1, MX_FORM_STREAM_T = 1, 2, 4
 MX_SCALE_RCEIL, MX_SCALE_FLOOR = 0, 1
 
 

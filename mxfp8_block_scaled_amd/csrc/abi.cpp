@@ -15,7 +15,7 @@
 hipError_t mx_launch_dim0(const uint16_t*, int64_t, int64_t, int64_t, uint8_t*, uint8_t*, int, hipStream_t);
 hipError_t mx_launch_dim1(const uint16_t*, int64_t, int64_t, int64_t, int64_t, uint8_t*, uint8_t*, int, hipStream_t);
 hipError_t mx_launch_both(const uint16_t*, int64_t, int64_t, int64_t, int64_t, uint8_t*, uint8_t*, uint8_t*, uint8_t*,
-                          int, hipStream_t);
+                          int, int, hipStream_t);
 hipError_t mx_launch_w32(const uint16_t*, int64_t, int64_t, int64_t, int64_t, uint8_t*, uint8_t*, uint8_t*, uint8_t*,
                          hipStream_t);
 hipError_t mx_launch_pad(const uint16_t*, int64_t, int64_t, int64_t, const int32_t*, int, uint16_t*, int64_t, int32_t*,
@@ -220,14 +220,18 @@ mx_status mx_quantize_dim0_dim1(const uint16_t* x, int64_t batch, int64_t rows, 
   TRY(check_ptr("q_t", q_t));
   TRY(check_ptr("scale_t", scale_t));
   TRY(check_device());
-  return launched(mx_launch_both(x, batch, rows, cols, ld_x, q, scale, q_t, scale_t, 0, (hipStream_t)stream),
+  return launched(mx_launch_both(x, batch, rows, cols, ld_x, q, scale, q_t, scale_t, 0, 0, (hipStream_t)stream),
                   "mx_quantize_dim0_dim1");
 }
 
 mx_status mx_quantize_ex(const uint16_t* x, int64_t batch, int64_t rows, int64_t cols, int64_t ld_x, int forms,
                          int scale_mode, uint8_t* q, uint8_t* scale, uint8_t* q_t, uint8_t* scale_t, void* stream) {
+  const int stream_t = (forms & MX_FORM_STREAM_T) != 0;
+  if (stream_t) forms &= ~MX_FORM_STREAM_T;
   if (forms != MX_FORM_DIM0 && forms != MX_FORM_DIM1 && forms != (MX_FORM_DIM0 | MX_FORM_DIM1))
-    return fail(MX_E_DTYPE, "forms = %d must be MX_FORM_DIM0, MX_FORM_DIM1 or both", forms);
+    return fail(MX_E_DTYPE, "forms = %d must be MX_FORM_DIM0, MX_FORM_DIM1 or both (plus MX_FORM_STREAM_T)", forms);
+  if (stream_t && forms != (MX_FORM_DIM0 | MX_FORM_DIM1))
+    return fail(MX_E_DTYPE, "MX_FORM_STREAM_T applies to the one-pass cast (both forms) only");
   if (scale_mode != MX_SCALE_RCEIL && scale_mode != MX_SCALE_FLOOR)
     return fail(MX_E_DTYPE, "scale_mode = %d must be MX_SCALE_RCEIL or MX_SCALE_FLOOR", scale_mode);
   const bool d0 = forms & MX_FORM_DIM0, d1 = forms & MX_FORM_DIM1;
@@ -252,7 +256,7 @@ mx_status mx_quantize_ex(const uint16_t* x, int64_t batch, int64_t rows, int64_t
   const int fl = scale_mode == MX_SCALE_FLOOR;
   hipError_t e;
   if (d0 && d1)
-    e = mx_launch_both(x, batch, rows, cols, ld_x, q, scale, q_t, scale_t, fl, (hipStream_t)stream);
+    e = mx_launch_both(x, batch, rows, cols, ld_x, q, scale, q_t, scale_t, fl, stream_t, (hipStream_t)stream);
   else if (d0)  // batches are contiguous with the row pitch: one stacked matrix
     e = mx_launch_dim0(x, batch * rows, cols, ld_x, q, scale, fl, (hipStream_t)stream);
   else

@@ -261,7 +261,7 @@ __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(2))) vo
                                                     int64_t cols, int64_t ld, uint8_t* __restrict__ q,
                                                     uint8_t* __restrict__ scale, uint8_t* __restrict__ q_t,
                                                     uint8_t* __restrict__ scale_t, int64_t rtiles, int64_t ctiles,
-                                                    RowGather gth) {
+                                                    RowGather gth, int stream_t) {
   __shared__ __attribute__((aligned(16))) uint8_t s_t[256 * 256];  // transposed codes
   __shared__ unsigned s_s1[8][64];                                 // dim1 scale tiles
   __shared__ unsigned s_s0[WV][64];                                // dim0 scale tile per wave
@@ -435,8 +435,13 @@ __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(2))) vo
       for (int k = 0; k < 64 / WV; ++k) {
         const int orow0 = 256 / WV * w + 4 * k, orow = orow0 + (l >> 4);
         const u32x4 d = *(const u32x4*)(s_t + orow * 256 + ((ch ^ ((orow >> 3) & 15)) << 4));
-        if (c0 + orow0 < cols)  // cols % 32 == 0: the four rows are all in or all out
-          __builtin_amdgcn_raw_buffer_store_b128(d, cast_rsrc(q_t + (b * cols + c0 + orow0) * rows + r0), lane_off, 0, 0);
+        if (c0 + orow0 < cols) {  // cols % 32 == 0: the four rows are all in or all out
+          const auto rqt = cast_rsrc(q_t + (b * cols + c0 + orow0) * rows + r0);
+          if (stream_t)
+            __builtin_amdgcn_raw_buffer_store_b128(d, rqt, lane_off, 0, 2);  // non-temporal
+          else
+            __builtin_amdgcn_raw_buffer_store_b128(d, rqt, lane_off, 0, 0);
+        }
       }
     }
 #pragma unroll
@@ -610,11 +615,11 @@ namespace {
 template <bool FLOOR, bool GATHER, int WV>
 hipError_t launch_both_wv(const uint16_t* x, int64_t batch, int64_t rows, int64_t cols, int64_t ld, uint8_t* q,
                           uint8_t* scale, uint8_t* q_t, uint8_t* scale_t, int64_t rtiles, int64_t ctiles,
-                          mx::RowGather gth, hipStream_t stream) {
+                          mx::RowGather gth, int stream_t, hipStream_t stream) {
   static const int64_t fill = resident_blocks((const void*)mx::k_quant_both<FLOOR, GATHER, WV>, 64 * WV);
   const int64_t blocks = std::max<int64_t>(1, std::min<int64_t>(batch * rtiles * ctiles, fill));
   hipLaunchKernelGGL((mx::k_quant_both<FLOOR, GATHER, WV>), dim3((unsigned)blocks), dim3(64 * WV), 0, stream, x,
-                     batch, rows, cols, ld, q, scale, q_t, scale_t, rtiles, ctiles, gth);
+                     batch, rows, cols, ld, q, scale, q_t, scale_t, rtiles, ctiles, gth, stream_t);
   return hipGetLastError();
 }
 
@@ -636,17 +641,18 @@ int both_waves(int64_t tiles) {
 }  // namespace
 
 hipError_t mx_launch_both(const uint16_t* x, int64_t batch, int64_t rows, int64_t cols, int64_t ld, uint8_t* q,
-                          uint8_t* scale, uint8_t* q_t, uint8_t* scale_t, int floor_mode, hipStream_t stream) {
+                          uint8_t* scale, uint8_t* q_t, uint8_t* scale_t, int floor_mode, int stream_t,
+                          hipStream_t stream) {
   const int64_t rtiles = (rows + 255) / 256, ctiles = (cols + 255) / 256;
   const int64_t tiles = batch * rtiles * ctiles;
   if (tiles == 0) return hipSuccess;
   const mx::RowGather none{nullptr, 0, 0, nullptr};
   const bool eight = both_waves(tiles) == 8;
   if (floor_mode)
-    return eight ? launch_both_wv<true, false, 8>(x, batch, rows, cols, ld, q, scale, q_t, scale_t, rtiles, ctiles, none, stream)
-                 : launch_both_wv<true, false, 4>(x, batch, rows, cols, ld, q, scale, q_t, scale_t, rtiles, ctiles, none, stream);
-  return eight ? launch_both_wv<false, false, 8>(x, batch, rows, cols, ld, q, scale, q_t, scale_t, rtiles, ctiles, none, stream)
-               : launch_both_wv<false, false, 4>(x, batch, rows, cols, ld, q, scale, q_t, scale_t, rtiles, ctiles, none, stream);
+    return eight ? launch_both_wv<true, false, 8>(x, batch, rows, cols, ld, q, scale, q_t, scale_t, rtiles, ctiles, none, stream_t, stream)
+                 : launch_both_wv<true, false, 4>(x, batch, rows, cols, ld, q, scale, q_t, scale_t, rtiles, ctiles, none, stream_t, stream);
+  return eight ? launch_both_wv<false, false, 8>(x, batch, rows, cols, ld, q, scale, q_t, scale_t, rtiles, ctiles, none, stream_t, stream)
+               : launch_both_wv<false, false, 4>(x, batch, rows, cols, ld, q, scale, q_t, scale_t, rtiles, ctiles, none, stream_t, stream);
 }
 
 // Padded one-pass cast: x [rows x cols] with unpadded group ends offs -> codes of the
@@ -658,8 +664,8 @@ hipError_t mx_launch_pad_both(const uint16_t* x, int64_t rows, int64_t cols, int
   const int64_t rtiles = (rows_pad + 255) / 256, ctiles = (cols + 255) / 256;
   const mx::RowGather gth{offs, groups, (int32_t)rows, offs_pad};
   if (both_waves(rtiles * ctiles) == 8)
-    return launch_both_wv<false, true, 8>(x, 1, rows_pad, cols, ld, q, scale, q_t, scale_t, rtiles, ctiles, gth, stream);
-  return launch_both_wv<false, true, 4>(x, 1, rows_pad, cols, ld, q, scale, q_t, scale_t, rtiles, ctiles, gth, stream);
+    return launch_both_wv<false, true, 8>(x, 1, rows_pad, cols, ld, q, scale, q_t, scale_t, rtiles, ctiles, gth, 0, stream);
+  return launch_both_wv<false, true, 4>(x, 1, rows_pad, cols, ld, q, scale, q_t, scale_t, rtiles, ctiles, gth, 0, stream);
 }
 
 hipError_t mx_launch_w32(const uint16_t* w, int64_t batch, int64_t n, int64_t k, int64_t ld, uint8_t* q,

@@ -92,6 +92,9 @@ def test_quantize_ex_validation(lib):
     assert f(P, 1, 64, 64, 64, 0, 0, P2, P2, P2, P2, None) == MX_E_DTYPE  # no form
     assert f(P, 1, 64, 64, 64, 4, 0, P2, P2, P2, P2, None) == MX_E_DTYPE  # unknown form
     assert f(P, 1, 64, 64, 64, 3, 2, P2, P2, P2, P2, None) == MX_E_DTYPE  # unknown scale rule
+    assert f(P, 1, 64, 64, 64, 2 | 4, 0, None, None, P2, P2, None) == MX_E_DTYPE  # stream hint needs both forms
+    assert f(P, 1, 64, 64, 64, 8 | 3, 0, P2, P2, P2, P2, None) == MX_E_DTYPE  # unknown bit
+    assert f(P, 1, 64, 64, 64, 3 | 4, 0, P2, P2, P2, P2, None) in (MX_E_DEVICE, 0)  # one-pass with the hint
     assert f(P, 1, 48, 64, 64, 2, 1, None, None, P2, P2, None) == MX_E_SHAPE  # dim1 needs rows % 32
     assert f(P, 1, 48, 64, 64, 1, 1, P2, P2, None, None, None) in (MX_E_DEVICE, 0)  # dim0 alone: any rows
     assert f(P, 1, 64, 64, 64, 1, 1, None, P2, None, None, None) == MX_E_NULL  # dim0 output missing

@@ -54,10 +54,11 @@ def check_w32(oracle, bits, name):
     assert np.array_equal(host(s_col), oracle.scales_to_physical(osc)), name
 
 
-def check_both(oracle, bits, name):
-    """The one-pass cast must equal dim0 of the stacked rows and dim1, bit for bit."""
-    say(f"[cast dim0+dim1] {name} shape={bits.shape}")
-    q, s, q_t, s_t = mx.mx_quantize_dim0_dim1(dev_bf16(bits))
+def check_both(oracle, bits, name, stream_t=False):
+    """The one-pass cast must equal dim0 of the stacked rows and dim1, bit for bit
+    (stream_t: q_t written with non-temporal stores, same values)."""
+    say(f"[cast dim0+dim1] {name} shape={bits.shape} stream_t={stream_t}")
+    q, s, q_t, s_t = mx.mx_quantize_dim0_dim1(dev_bf16(bits), stream_t=stream_t)
     stacked = bits.reshape(-1, bits.shape[-1])
     oq, osl = oracle.quantize_dim0(stacked)
     gq = host(q)
@@ -180,6 +181,15 @@ def test_dim0_dim1_four_wave_path(oracle):
     rng = np.random.default_rng(7)
     check_both(oracle, synth.normal_bf16(rng, (4352, 4160), 1.0), "2D 289 tiles")
     check_both(oracle, synth.normal_bf16(rng, (5, 1056, 3328), 0.02), "batch5 325 tiles")
+
+
+@pytest.mark.parametrize("stream_t", [False, True])
+def test_dim0_dim1_stream_hint(oracle, stream_t):
+    """MX_FORM_STREAM_T changes only where q_t is cached: both paths bit-exact, on the
+    eight- and four-wave workgroups, 2D and batched."""
+    rng = np.random.default_rng(11)
+    check_both(oracle, synth.normal_bf16(rng, (300, 576), 1.0)[:288], "2D eight-wave", stream_t)
+    check_both(oracle, synth.normal_bf16(rng, (3, 2080, 1056), 0.02), "batch3 four-wave", stream_t)
 
 
 def test_dim0_dim1_full_size_sampled(oracle):
