@@ -457,106 +457,104 @@ __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(2))) vo
 }
 
 // ---------------------------------------------------------------------------------
-// 32x32 weight cast: one wave per 32-row x 256-column strip (eight 32x32 tiles),
-// one wave per workgroup so that the few strips of a narrow weight spread over all
-// compute units. The tile amax reduces over the lane's 16 rows, the quad (32
-// columns) and the two wave halves. Codes go out rowwise directly and, through
-// LDS, transposed.
+// 32x32 weight cast: one wave per 32-row x 64-column strip (two 32x32 tiles), four
+// independent waves per workgroup, so a narrow weight still spreads over every
+// compute unit (the 576 x 4096 weight: 1152 strips). Lane l holds 16-byte column
+// chunk l % 8 of rows l / 8 + 8i, i = 0..3. The tile amax reduces over the lane's 4
+// rows, the quad (the tile's 32 columns) and the 8 row groups. Codes go out rowwise
+// directly and, through the wave's LDS slice, transposed: each lane turns 8 rows x 4
+// columns into 8 bytes of 4 q_t rows with byte permutes.
 // ---------------------------------------------------------------------------------
-constexpr int kW32Waves = 1;  // waves per workgroup
+constexpr int kW32Waves = 4;  // waves per workgroup (independent strips)
 
 __global__ __launch_bounds__(64 * kW32Waves) void k_quant_w32(const uint16_t* __restrict__ w, int64_t batch, int64_t n,
                                                    int64_t k, int64_t ld, uint8_t* __restrict__ q,
                                                    uint8_t* __restrict__ q_t, uint8_t* __restrict__ s_row,
                                                    uint8_t* __restrict__ s_col, int64_t ktiles) {
-  __shared__ unsigned lds_q[kW32Waves][32 * 64];  // per wave: 32 rows x 256 bytes
-  __shared__ uint8_t lds_tb[kW32Waves][8];
-  const int wv = threadIdx.x >> 6, l = threadIdx.x & 63, h = l >> 5, c = l & 31;
-  const int64_t row_bands = batch * n / 32;
+  __shared__ unsigned lds_q[kW32Waves][32 * 16];  // per wave: 32 rows x 64 bytes of codes
+  const int wv = threadIdx.x >> 6, l = threadIdx.x & 63, c = l & 7, g = l >> 3;
+  const int64_t strips_k = (k + 63) / 64, row_bands = batch * n / 32;
   const int64_t t = (int64_t)blockIdx.x * kW32Waves + wv;
-  const bool active = t < row_bands * ktiles;
-  const int64_t rb = active ? t / ktiles : 0, kt = active ? t % ktiles : 0;
-  const int64_t col0 = kt * 256 + c * 8;
-  const bool col_ok = active && col0 < k;
-  const int64_t kb_total = k / 32;
+  const bool active = t < row_bands * strips_k;
+  const int64_t rb = active ? t / strips_k : 0, col0 = active ? (t % strips_k) * 64 : 0;
+  const int64_t col = col0 + 8 * c;
+  const bool col_ok = active && col < k;  // k % 32 == 0: a tile is all in or all out
+  const int kb_total = (int)(k / 32);
 
-  u32x4 v[16];
+  u32x4 v[4];
   unsigned a = 0;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    int64_t r = rb * 32 + 2 * i + h;
+  for (int i = 0; i < 4; ++i) {
     v[i] = (u32x4){0, 0, 0, 0};
-    if (col_ok) v[i] = __builtin_nontemporal_load((const u32x4*)(w + r * ld + col0));
+    if (col_ok) v[i] = __builtin_nontemporal_load((const u32x4*)(w + (rb * 32 + g + 8 * i) * ld + col));
+    a = umax(a, amax8(v[i]));
   }
-#pragma unroll
-  for (int i = 0; i < 16; ++i) a = umax(a, amax8(v[i]));
   a = umax(a, dpp_xor1(a));
   a = umax(a, dpp_xor2(a));
+  a = umax(a, (unsigned)__shfl_xor((int)a, 8));
+  a = umax(a, (unsigned)__shfl_xor((int)a, 16));
   a = umax(a, (unsigned)__shfl_xor((int)a, 32));
   const int byte = rceil_byte(a);
-  if (h == 0 && (c & 3) == 0) lds_tb[wv][c >> 2] = (uint8_t)byte;
+  const int tb0 = __shfl(byte, 0), tb1 = __shfl(byte, 4);  // the strip's two tile bytes
 
   uint8_t* lq = (uint8_t*)lds_q[wv];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    int64_t r = rb * 32 + 2 * i + h;
-    u32x2 codes = encode8<false>(v[i], byte, a);
-    if (col_ok) *(u32x2*)(q + r * k + col0) = codes;
-    *(u32x2*)(lq + (2 * i + h) * 256 + c * 8) = codes;
+  for (int i = 0; i < 4; ++i) {
+    const u32x2 codes = encode8<false>(v[i], byte, a);
+    if (col_ok) *(u32x2*)(q + (rb * 32 + g + 8 * i) * k + col) = codes;
+    *(u32x2*)(lq + (g + 8 * i) * 64 + c * 8) = codes;
   }
   __syncthreads();
   if (!active) return;
-  // rowwise scales: lane l's dword = tile bytes of blocks h, 2+h, 4+h, 6+h for row l%32
+  // rowwise scales: row l % 32 of the band, block col0/32 + l/32; the strip that ends
+  // the row also fills the layout's pad blocks up to a multiple of eight
   {
-    unsigned d = 0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      int kb = kt * 8 + 2 * j + h;
-      unsigned bj = kb < kb_total ? lds_tb[wv][2 * j + h] : 0x7fu;
-      d |= bj << (8 * j);
-    }
-    ((unsigned*)(s_row + scale_tile_base(rb, kt, ktiles)))[l] = d;
+    const int kb = (int)(col0 / 32) + (l >> 5);
+    if (kb < kb_total) s_row[scale_tile_base(rb, kb / 8, ktiles) + scale_in_tile(l & 31, kb & 7)] = (uint8_t)((l >> 5) ? tb1 : tb0);
+    if (col0 + 64 >= k)
+      for (int kp = kb_total + (l >> 5); kp < ktiles * 8; kp += 2)
+        s_row[scale_tile_base(rb, kp / 8, ktiles) + scale_in_tile(l & 31, kp & 7)] = 0x7f;
   }
   if (q_t == nullptr) return;
-  // transposed codes: lane l writes output rows kk = kt*256 + 4l + j (j = 0..3),
-  // columns rb_local*32 .. +31 of batch bi.
+  // transposed codes: lane l takes columns 4 (l % 16) .. +3 of rows 8 (l / 16) .. +7
+  // and writes 8 bytes of each of those 4 q_t rows
+  const int dc = l & 15, p8 = l >> 4;
+  unsigned outw[2][4];
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    const int r0 = 8 * p8 + 4 * half;
+    const unsigned d0 = lds_q[wv][(r0 + 0) * 16 + dc];
+    const unsigned d1 = lds_q[wv][(r0 + 1) * 16 + dc];
+    const unsigned d2 = lds_q[wv][(r0 + 2) * 16 + dc];
+    const unsigned d3 = lds_q[wv][(r0 + 3) * 16 + dc];
+    const unsigned t0 = __builtin_amdgcn_perm(d1, d0, 0x05010400u);
+    const unsigned t1 = __builtin_amdgcn_perm(d3, d2, 0x05010400u);
+    const unsigned t2 = __builtin_amdgcn_perm(d1, d0, 0x07030602u);
+    const unsigned t3 = __builtin_amdgcn_perm(d3, d2, 0x07030602u);
+    outw[half][0] = __builtin_amdgcn_perm(t1, t0, 0x05040100u);
+    outw[half][1] = __builtin_amdgcn_perm(t1, t0, 0x07060302u);
+    outw[half][2] = __builtin_amdgcn_perm(t3, t2, 0x05040100u);
+    outw[half][3] = __builtin_amdgcn_perm(t3, t2, 0x07060302u);
+  }
   const int64_t bi = (rb * 32) / n;
   const int64_t nb_local = (rb * 32 - bi * n) / 32;  // 32-column band of q_t within the batch
-  if (kt * 256 + 4 * l >= k) return;
-  unsigned outw[4][8];
-#pragma unroll
-  for (int a8 = 0; a8 < 8; ++a8) {
-    unsigned d0 = lds_q[wv][(4 * a8 + 0) * 64 + l];
-    unsigned d1 = lds_q[wv][(4 * a8 + 1) * 64 + l];
-    unsigned d2 = lds_q[wv][(4 * a8 + 2) * 64 + l];
-    unsigned d3 = lds_q[wv][(4 * a8 + 3) * 64 + l];
-    unsigned t0 = __builtin_amdgcn_perm(d1, d0, 0x05010400u);
-    unsigned t1 = __builtin_amdgcn_perm(d3, d2, 0x05010400u);
-    unsigned t2 = __builtin_amdgcn_perm(d1, d0, 0x07030602u);
-    unsigned t3 = __builtin_amdgcn_perm(d3, d2, 0x07030602u);
-    outw[0][a8] = __builtin_amdgcn_perm(t1, t0, 0x05040100u);
-    outw[1][a8] = __builtin_amdgcn_perm(t1, t0, 0x07060302u);
-    outw[2][a8] = __builtin_amdgcn_perm(t3, t2, 0x05040100u);
-    outw[3][a8] = __builtin_amdgcn_perm(t3, t2, 0x07060302u);
-  }
   uint8_t* qtb = q_t + bi * k * n;
-  const unsigned tb = lds_tb[wv][l >> 3];
-  const int64_t kt_col = nb_local / 8;
-  const int64_t ktiles_col = scale_tiles_k(n / 32);
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const int64_t kk = kt * 256 + 4 * l + j;
-    u32x4* dst = (u32x4*)(qtb + kk * n + nb_local * 32);
-    dst[0] = (u32x4){outw[j][0], outw[j][1], outw[j][2], outw[j][3]};
-    dst[1] = (u32x4){outw[j][4], outw[j][5], outw[j][6], outw[j][7]};
+    const int64_t kk = col0 + 4 * dc + j;
+    if (kk < k) *(u32x2*)(qtb + kk * n + nb_local * 32 + 8 * p8) = (u32x2){outw[0][j], outw[1][j]};
+  }
+  // column scales: q_t row col0 + l, block nb_local (the band's 32 columns); the last
+  // band of the batch also fills the layout's pad blocks
+  const int64_t kk = col0 + l;
+  if (kk < k) {
+    const int64_t ktiles_col = scale_tiles_k(n / 32);
     const int64_t band = (bi * k + kk) / 32;
-    uint8_t* sc = s_col + scale_tile_base(band, kt_col, ktiles_col);
-    sc[scale_in_tile((int)(kk & 31), (int)(nb_local & 7))] = (uint8_t)tb;
-    // the last column band of the batch also fills the layout's pad blocks
-    if (nb_local == n / 32 - 1) {
+    s_col[scale_tile_base(band, nb_local / 8, ktiles_col) + scale_in_tile((int)(kk & 31), (int)(nb_local & 7))] =
+        (uint8_t)((l >> 5) ? tb1 : tb0);
+    if (nb_local == n / 32 - 1)
       for (int64_t nb = n / 32; nb < ktiles_col * 8; ++nb)
         s_col[scale_tile_base(band, nb / 8, ktiles_col) + scale_in_tile((int)(kk & 31), (int)(nb & 7))] = 0x7f;
-    }
   }
 }
 
@@ -671,9 +669,9 @@ hipError_t mx_launch_pad_both(const uint16_t* x, int64_t rows, int64_t cols, int
 hipError_t mx_launch_w32(const uint16_t* w, int64_t batch, int64_t n, int64_t k, int64_t ld, uint8_t* q,
                          uint8_t* q_t, uint8_t* s_row, uint8_t* s_col, hipStream_t stream) {
   const int64_t ktiles = mx::scale_tiles_k(k / 32);
-  const int64_t tiles = batch * n / 32 * ktiles;
-  if (tiles == 0) return hipSuccess;
-  const int64_t blocks = (tiles + mx::kW32Waves - 1) / mx::kW32Waves;
+  const int64_t strips = batch * n / 32 * ((k + 63) / 64);
+  if (strips == 0) return hipSuccess;
+  const int64_t blocks = (strips + mx::kW32Waves - 1) / mx::kW32Waves;
   hipLaunchKernelGGL(mx::k_quant_w32, dim3((unsigned)blocks), dim3(64 * mx::kW32Waves), 0, stream, w, batch, n, k, ld,
                      q, q_t,
                      s_row, s_col, ktiles);
