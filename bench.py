@@ -346,11 +346,12 @@ def main():
         padded_both = lambda n_real, n_pad: 2 * n_real + n_pad * (2 + 2 / 32)  # noqa: E731
         y_u, dx_u = bf(M, N), bf(M, K)
         ops = [
+            # X's and W's transposed codes streamed past the caches, as in the aligned step
             ("cast_dim0+dim1 X (padded)", "cast", padded_both(M * K, Mg * K),
              lambda: mx.mx_pad_quantize_dim0_dim1(X, offs, Mg, buf["xq"], buf["xs"], buf["xtq"], buf["xts"],
-                                                  offs_pad)),
+                                                  offs_pad, stream_t=True)),
             ("cast_dim0+dim1 W", "cast", both(G * N * K),
-             lambda: mx.mx_quantize_dim0_dim1(W, buf["wq"], buf["ws"], buf["wtq"], buf["wts"])),
+             lambda: mx.mx_quantize_dim0_dim1(W, buf["wq"], buf["ws"], buf["wtq"], buf["wts"], stream_t=True)),
             ("gemm_fwd grouped", "gemm", 2 * M * N * K,
              lambda: mx.mx_grouped_mm_fwd_padded(buf["xq"], buf["xs"], buf["wq"], buf["ws"], offs_pad, offs, Mg, M,
                                                  N, K, out=y_u)),

@@ -428,6 +428,13 @@ mx_status mx_pad_quantize_dim0_dim1(const uint16_t* x, int64_t rows, int64_t col
                                     uint8_t* scale, uint8_t* q_t, uint8_t* scale_t, int32_t* offs_pad,
                                     void* stream);
 
+/* mx_pad_quantize_dim0_dim1 with flags: 0, or MX_FORM_STREAM_T to write the transposed
+ * codes with non-temporal stores (as for mx_quantize_ex; identical results). Any other
+ * flags value is MX_E_DTYPE. */
+mx_status mx_pad_quantize_ex(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, const int32_t* offs,
+                             int32_t groups, int64_t rows_pad, int flags, uint8_t* q, uint8_t* scale, uint8_t* q_t,
+                             uint8_t* scale_t, int32_t* offs_pad, void* stream);
+
 /* Forward / dgrad on padded token rows with unpadded outputs: the result equals
  * mx_unpad_token_groups of mx_grouped_mm_fwd(..., offs_pad, m = m_pad, ...) (resp.
  * dgrad): row offs_pad[g-1] + i of group g is written to row offs[g-1] + i of out

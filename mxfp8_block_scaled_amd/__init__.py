@@ -604,10 +604,12 @@ def mx_grouped_mm_bf16_wgrad(dy_t, x_t, offs, m, n, k, groups=None, out_dtype=MX
     return out
 
 
-def mx_pad_quantize_dim0_dim1(x, offs, rows_pad=None, q=None, scale=None, q_t=None, scale_t=None, offs_pad=None):
+def mx_pad_quantize_dim0_dim1(x, offs, rows_pad=None, q=None, scale=None, q_t=None, scale_t=None, offs_pad=None,
+                              stream_t=False):
     """Token-group padding fused into the one-pass cast: the casts of
     mx_pad_token_groups(x, offs) without writing the padded bf16 rows.
-    Returns (q, scale, q_t, scale_t, offs_pad)."""
+    Returns (q, scale, q_t, scale_t, offs_pad). stream_t: q_t written with
+    non-temporal stores (MX_FORM_STREAM_T), the same values."""
     x = _bf16_bits(x)
     if x.dim() != 2:
         raise ValueError("x must be a 2D tensor")
@@ -632,8 +634,9 @@ def mx_pad_quantize_dim0_dim1(x, offs, rows_pad=None, q=None, scale=None, q_t=No
     _buf(q_t, "q_t", _U8, rows_pad * cols, dev)
     _buf(scale_t, "scale_t", _U8, mx_scale_bytes(cols, rows_pad), dev)
     _buf(offs_pad, "offs_pad", _I32, G, dev)
-    _lib.call("mx_pad_quantize_dim0_dim1", _ptr(x), rows, cols, ld, _ptr(offs), G, rows_pad, _ptr(q), _ptr(scale),
-              _ptr(q_t), _ptr(scale_t), _ptr(offs_pad), _stream(x))
+    _lib.call("mx_pad_quantize_ex", _ptr(x), rows, cols, ld, _ptr(offs), G, rows_pad,
+              MX_FORM_STREAM_T if stream_t else 0, _ptr(q), _ptr(scale), _ptr(q_t), _ptr(scale_t), _ptr(offs_pad),
+              _stream(x))
     return q, scale, q_t, scale_t, offs_pad
 
 

@@ -36,6 +36,7 @@ SIGNATURES = {
     "mx_probe_mfma": (_INT, [_I64, _P, _P]),
     "mx_probe_mfma_dot": (_INT, [_INT, _P, _P, _P, _P, _P, _P, _P]),
     "mx_pad_quantize_dim0_dim1": (_INT, [_P, _I64, _I64, _I64, _P, _I32, _I64, _P, _P, _P, _P, _P, _P]),
+    "mx_pad_quantize_ex": (_INT, [_P, _I64, _I64, _I64, _P, _I32, _I64, _INT, _P, _P, _P, _P, _P, _P]),
     "mx_grouped_mm_fwd_padded": (_INT, [_P, _P, _P, _P, _P, _P, _I32, _I64, _I64, _I64, _I64, _P, _INT, _P]),
     "mx_grouped_mm_dgrad_padded": (_INT, [_P, _P, _P, _P, _P, _P, _I32, _I64, _I64, _I64, _I64, _P, _INT, _P]),
     "mx_pad_token_groups": (_INT, [_P, _I64, _I64, _I64, _P, _I32, _P, _I64, _P, _P]),

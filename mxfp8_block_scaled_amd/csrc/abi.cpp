@@ -36,7 +36,7 @@ hipError_t mx_launch_probe_mfma(int64_t, float*, hipStream_t);
 hipError_t mx_launch_probe_dot(int, const uint8_t*, const uint8_t*, const uint8_t*, const uint8_t*, const float*, float*,
                                hipStream_t);
 hipError_t mx_launch_pad_both(const uint16_t*, int64_t, int64_t, int64_t, const int32_t*, int, int64_t, uint8_t*,
-                              uint8_t*, uint8_t*, uint8_t*, int32_t*, hipStream_t);
+                              uint8_t*, uint8_t*, uint8_t*, int32_t*, int, hipStream_t);
 hipError_t mx_launch_gemm_kgroup(const uint8_t*, const uint8_t*, const uint8_t*, const uint8_t*, const int32_t*, int,
                                  int64_t, int64_t, int64_t, void*, int, void*, int64_t, hipStream_t);
 int64_t mx_kgroup_workspace_bytes(int, int64_t, int64_t, int64_t, int);
@@ -601,10 +601,11 @@ mx_status mx_unpad_token_groups(const void* y_pad, int64_t rows_pad, int64_t col
 
 // ---- token-group padding fused into the cast and the GEMM outputs ----
 
-mx_status mx_pad_quantize_dim0_dim1(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
-                                    const int32_t* offs, int32_t groups, int64_t rows_pad, uint8_t* q,
-                                    uint8_t* scale, uint8_t* q_t, uint8_t* scale_t, int32_t* offs_pad,
-                                    void* stream) {
+mx_status mx_pad_quantize_ex(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, const int32_t* offs,
+                             int32_t groups, int64_t rows_pad, int flags, uint8_t* q, uint8_t* scale, uint8_t* q_t,
+                             uint8_t* scale_t, int32_t* offs_pad, void* stream) {
+  if (flags != 0 && flags != MX_FORM_STREAM_T)
+    return fail(MX_E_DTYPE, "flags = %d must be 0 or MX_FORM_STREAM_T", flags);
   TRY(check_pad_common(rows, groups, rows_pad, offs));
   if (rows_pad % 32 != 0) return fail(MX_E_SHAPE, "rows_pad = %lld must be a multiple of 32", (long long)rows_pad);
   TRY(check_dim("cols", cols, 32));
@@ -621,8 +622,15 @@ mx_status mx_pad_quantize_dim0_dim1(const uint16_t* x, int64_t rows, int64_t col
   if ((uintptr_t)offs_pad & 3) return fail(MX_E_ALIGN, "offs_pad is not 4-byte aligned");
   TRY(check_device());
   return launched(mx_launch_pad_both(x, rows, cols, ld_x, offs, groups, rows_pad, q, scale, q_t, scale_t, offs_pad,
-                                     (hipStream_t)stream),
-                  "mx_pad_quantize_dim0_dim1");
+                                     flags == MX_FORM_STREAM_T, (hipStream_t)stream),
+                  "mx_pad_quantize_ex");
+}
+
+mx_status mx_pad_quantize_dim0_dim1(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
+                                    const int32_t* offs, int32_t groups, int64_t rows_pad, uint8_t* q,
+                                    uint8_t* scale, uint8_t* q_t, uint8_t* scale_t, int32_t* offs_pad,
+                                    void* stream) {
+  return mx_pad_quantize_ex(x, rows, cols, ld_x, offs, groups, rows_pad, 0, q, scale, q_t, scale_t, offs_pad, stream);
 }
 
 namespace {

@@ -658,12 +658,12 @@ hipError_t mx_launch_both(const uint16_t* x, int64_t batch, int64_t rows, int64_
 // launched even for no tiles, to write offs_pad).
 hipError_t mx_launch_pad_both(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, const int32_t* offs,
                               int groups, int64_t rows_pad, uint8_t* q, uint8_t* scale, uint8_t* q_t,
-                              uint8_t* scale_t, int32_t* offs_pad, hipStream_t stream) {
+                              uint8_t* scale_t, int32_t* offs_pad, int stream_t, hipStream_t stream) {
   const int64_t rtiles = (rows_pad + 255) / 256, ctiles = (cols + 255) / 256;
   const mx::RowGather gth{offs, groups, (int32_t)rows, offs_pad};
   if (both_waves(rtiles * ctiles) == 8)
-    return launch_both_wv<false, true, 8>(x, 1, rows_pad, cols, ld, q, scale, q_t, scale_t, rtiles, ctiles, gth, 0, stream);
-  return launch_both_wv<false, true, 4>(x, 1, rows_pad, cols, ld, q, scale, q_t, scale_t, rtiles, ctiles, gth, 0, stream);
+    return launch_both_wv<false, true, 8>(x, 1, rows_pad, cols, ld, q, scale, q_t, scale_t, rtiles, ctiles, gth, stream_t, stream);
+  return launch_both_wv<false, true, 4>(x, 1, rows_pad, cols, ld, q, scale, q_t, scale_t, rtiles, ctiles, gth, stream_t, stream);
 }
 
 hipError_t mx_launch_w32(const uint16_t* w, int64_t batch, int64_t n, int64_t k, int64_t ld, uint8_t* q,

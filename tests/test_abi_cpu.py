@@ -256,6 +256,11 @@ def test_backward_arm_calls_validation(lib):
 
 
 def test_fused_padding_calls_validation(lib):
+    e = lib.mx_pad_quantize_ex
+    assert e(P, 40, 64, 64, P2, 3, 256, 4, P2, P2, P2, P2, P2, None) in (MX_E_DEVICE, 0)  # MX_FORM_STREAM_T
+    assert e(P, 40, 64, 64, P2, 3, 256, 0, P2, P2, P2, P2, P2, None) in (MX_E_DEVICE, 0)
+    assert e(P, 40, 64, 64, P2, 3, 256, 1, P2, P2, P2, P2, P2, None) == MX_E_DTYPE  # not a flag here
+    assert e(P, 40, 64, 64, P2, 3, 256, 4 | 8, P2, P2, P2, P2, P2, None) == MX_E_DTYPE
     f = lib.mx_pad_quantize_dim0_dim1
     assert f(P, 40, 64, 64, P2, 3, 256, P2, P2, P2, P2, P2, None) in (MX_E_DEVICE, 0)
     assert f(P, 40, 48, 64, P2, 3, 256, P2, P2, P2, P2, P2, None) == MX_E_SHAPE  # cols % 32

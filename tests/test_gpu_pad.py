@@ -214,18 +214,20 @@ FUSED_CASES = [
 ]
 
 
+@pytest.mark.parametrize("stream_t", [False, True], ids=["cached", "stream_t"])
 @pytest.mark.parametrize("rows,cols,ld,sizes", FUSED_CASES, ids=[f"r{c[0]}c{c[1]}g{len(c[3])}" for c in FUSED_CASES])
-def test_pad_quantize_matches_oracle(oracle, rows, cols, ld, sizes):
+def test_pad_quantize_matches_oracle(oracle, rows, cols, ld, sizes, stream_t):
     """The padded one-pass cast equals the oracle's padding followed by its casts:
-    codes, physical scale bytes (pads included) and padded offsets, bit for bit."""
+    codes, physical scale bytes (pads included) and padded offsets, bit for bit; with
+    MX_FORM_STREAM_T (q_t stored past the caches) the same."""
     rng = np.random.default_rng(rows + cols + 11)
     offs = offs_of(sizes)
     G = len(sizes)
     x_full = synth.normal_bf16(rng, (rows, ld), 1.0) if rows else np.zeros((0, ld), np.uint16)
     x = x_full[:, :cols]
     rows_pad = mx.mx_padded_rows(rows, G)
-    say(f"[pad+cast] rows={rows} cols={cols} G={G} rows_pad={rows_pad}")
-    q, s, qt, st, offs_pad = mx.mx_pad_quantize_dim0_dim1(dev_bf16(x_full)[:, :cols], dev_i32(offs))
+    say(f"[pad+cast] rows={rows} cols={cols} G={G} rows_pad={rows_pad} stream_t={stream_t}")
+    q, s, qt, st, offs_pad = mx.mx_pad_quantize_dim0_dim1(dev_bf16(x_full)[:, :cols], dev_i32(offs), stream_t=stream_t)
     x_pad, ref_offs = oracle.pad_token_groups(x, offs.tolist(), rows_pad)
     assert host(offs_pad).tolist() == ref_offs
     oq, os_ = oracle.quantize_dim0(x_pad)
