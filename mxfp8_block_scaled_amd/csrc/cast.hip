@@ -13,7 +13,9 @@
 // follows (torchtitan PR 5334, body: blocked E8M0 scales emitted directly).
 // The bf16 input is read once, with non-temporal loads (keeping it out of the caches
 // sped the one-pass cast of the weights from 111 to 103 us inside the MoE step); the
-// codes are stored normally: the GEMMs read them next.
+// codes are stored normally, as a GEMM reads them next, except the one-pass cast's
+// transposed codes on request (stream_t): those a caller reads only much later are
+// stored non-temporally, so the row-wise codes stay cached.
 
 #include <algorithm>
 #include <type_traits>
