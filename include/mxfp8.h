@@ -25,8 +25,9 @@
  * CONVENTIONS (every entry point)
  *   - Pointers are device pointers unless stated; the caller allocates and frees
  *     every buffer, workspaces included. The library never allocates device
- *     memory and keeps no state beyond a per-device architecture check and
- *     per-process launch settings (both set up thread-safely).
+ *     memory and keeps no state beyond a per-device architecture check,
+ *     per-process launch settings (both set up thread-safely) and the fixed
+ *     per-device scratch of mx_grouped_mm_wgrad_noalloc (part of the code object).
  *   - bf16 data is passed as uint16_t bit patterns; E4M3 codes and E8M0 scales
  *     as uint8_t; `stream` is a hipStream_t (NULL = the default stream).
  *   - Work is enqueued asynchronously on `stream`. No call copies device memory
