@@ -42,6 +42,9 @@ __all__ = [
     "mx_padded_rows",
     "mx_pad_token_groups",
     "mx_pad_quantize_dim0_dim1",
+    "mx_pad_quantize_ex",
+    "mx_status_string",
+    "mx_last_error",
     "mx_grouped_mm_fwd_padded",
     "mx_grouped_mm_dgrad_padded",
     "mx_unpad_token_groups",
@@ -73,6 +76,16 @@ def _bf16_bits(x):
     if x.dtype in (torch.int16, torch.uint16):
         return x
     raise TypeError(f"expected bf16 data (torch.bfloat16 or 16-bit bit patterns), got {x.dtype}")
+
+
+def mx_status_string(status):
+    """Name of a status code ("MX_OK", "MX_E_SHAPE", ...)."""
+    return _lib.load().mx_status_string(int(status)).decode()
+
+
+def mx_last_error():
+    """This thread's message for its last failed call."""
+    return _lib.load().mx_last_error().decode()
 
 
 def mx_scale_bytes(rows, cols):
@@ -638,6 +651,14 @@ def mx_pad_quantize_dim0_dim1(x, offs, rows_pad=None, q=None, scale=None, q_t=No
               MX_FORM_STREAM_T if stream_t else 0, _ptr(q), _ptr(scale), _ptr(q_t), _ptr(scale_t), _ptr(offs_pad),
               _stream(x))
     return q, scale, q_t, scale_t, offs_pad
+
+
+def mx_pad_quantize_ex(x, offs, flags=0, rows_pad=None, q=None, scale=None, q_t=None, scale_t=None, offs_pad=None):
+    """mx_pad_quantize_dim0_dim1 with the C call's flags: 0 or MX_FORM_STREAM_T."""
+    if flags not in (0, MX_FORM_STREAM_T):
+        raise ValueError(f"flags = {flags} must be 0 or MX_FORM_STREAM_T")
+    return mx_pad_quantize_dim0_dim1(x, offs, rows_pad, q, scale, q_t, scale_t, offs_pad,
+                                     stream_t=flags == MX_FORM_STREAM_T)
 
 
 def mx_grouped_mm_fwd_padded(a, a_s, b, b_s, offs_pad, offs, m_pad, m, n, k, out_dtype=MX_OUT_BF16, out=None):

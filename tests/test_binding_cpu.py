@@ -61,3 +61,21 @@ def test_workspace_query():
     assert mx.mx_grouped_mm_wgrad_workspace_bytes(8, 16384, 4096, 4096) == 0
     with pytest.raises(ValueError):
         mx.mx_grouped_mm_wgrad_workspace_bytes(0, 16384, 4096, 4096)
+
+
+def test_binding_has_every_entry_point():
+    """The binding carries the C ABI's names: every function the header declares."""
+    import re
+    import os
+    here = os.path.dirname(os.path.abspath(__file__))
+    text = open(os.path.join(here, "..", "include", "mxfp8.h")).read()
+    names = sorted(set(re.findall(r"\b(mx_[a-z0-9_]+)\s*\(", text)))
+    assert names and not [n for n in names if not hasattr(mx, n)]
+    assert mx.mx_status_string(0) == "MX_OK"
+    assert mx.mx_status_string(-2) == "MX_E_SHAPE"
+
+
+def test_pad_quantize_ex_flags():
+    x = torch.zeros(64, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        mx.mx_pad_quantize_ex(x, torch.tensor([64], dtype=torch.int32), flags=1)
