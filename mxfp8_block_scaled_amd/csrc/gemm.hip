@@ -90,7 +90,11 @@ struct Cfg {
   static constexpr int A_LOADS = A_ROWS_W / 16, B_LOADS = B_ROWS_W / 16;
   static constexpr int AB_LOADS = A_LOADS + B_LOADS;
   static constexpr int SC_WAVES = BANDS / 4;
-  static constexpr int HALF_MFMAS = TM / 2 * TN;
+  // rows of a wave's 32x32 tiles whose MFMAs run before the pipeline's wait and
+  // barrier: three quarters where the rows split so (more matrix work in flight
+  // while the wave waits), else half; the rest run beside the next step's LDS reads
+  static constexpr int HEAD_ROWS = TM % 4 == 0 ? TM * 3 / 4 : TM / 2;
+  static constexpr int TAIL_MFMAS = (TM - HEAD_ROWS) * TN;
   static_assert(SC_WAVES <= WAVES && A_ROWS_W % 16 == 0 && B_ROWS_W % 16 == 0, "tile shape");
   static_assert(TM % 2 == 0 && 2 * AB_LOADS + 2 < 64 && NST >= 2 && NST <= 4, "");
 };
@@ -350,8 +354,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) __attribute__((amdgpu_waves_per_eu(
   constexpr bool SCALED = EL == EL_MXFP8;
   constexpr int MPK = SCALED ? 1 : 2;  // MFMAs per 32x32 tile and 64-byte k-step
   // LDS reads per k-step (two 16-byte fragment halves per tile, plus one scale dword
-  // per tile when scaled) spread over the second half's MFMAs
-  constexpr int DS_PER_MFMA = ((SCALED ? 3 : 2) * (C::TM + C::TN) + C::HALF_MFMAS - 1) / C::HALF_MFMAS;
+  // per tile when scaled) spread over the tail MFMAs
+  constexpr int DS_PER_MFMA = ((SCALED ? 3 : 2) * (C::TM + C::TN) + C::TAIL_MFMAS - 1) / C::TAIL_MFMAS;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
 
   const int tid = threadIdx.x, l = tid & 63, h = l >> 5;
@@ -526,19 +530,19 @@ __global__ __launch_bounds__(64 * WGM * WGN) __attribute__((amdgpu_waves_per_eu(
   };
 
   // One pipeline step over an NST-deep LDS ring. Step `it` issues stage it+NST-1,
-  // runs the first half of stage it's MFMAs, waits for its own loads of stage it+1
+  // runs the MFMAs of stage it's first HEAD_ROWS tile rows, waits for its own loads of stage it+1
   // (at most NST-2 later stages stay in flight), meets the other waves at a barrier
   // (so stage it+1 is complete in LDS and every wave is past stage it-1, whose slot
   // the next issue overwrites), then reads stage it+1's fragments interleaved with
-  // the second half of stage it's MFMAs. `s4` is it % 4 (a constant in the unrolled
+  // the remaining rows' MFMAs. `s4` is it % 4 (a constant in the unrolled
   // loop): it places the scale windows, and the ring slots for NST 2 and 4.
   auto step = [&](int64_t it, int s4, const Frag& cur, Frag& nxt, auto masked) {
     const int slot = s4;
     issue_stage(it + NST - 1, (slot + NST - 1) & 3, it + NST - 1 < n_iter);
-    mfma_rows(cur, 0, C::TM / 2);
+    mfma_rows(cur, 0, C::HEAD_ROWS);
     // spread the loads over the MFMAs so no load waits in front of an idle matrix core
 #pragma unroll
-    for (int q = 0; q < C::TM / 2 * C::TN; ++q) {
+    for (int q = 0; q < C::HEAD_ROWS * C::TN; ++q) {
       __builtin_amdgcn_sched_group_barrier(0x008, MPK, 0);  // MFMA
       __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // VALU (load offsets)
       __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read
@@ -548,10 +552,10 @@ __global__ __launch_bounds__(64 * WGM * WGN) __attribute__((amdgpu_waves_per_eu(
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
     read_frags(nxt, NST == 3 ? (int)(it + 1) % 3 : (slot + 1) % NST, k_first + (it + 1) * BK, masked);
-    mfma_rows(cur, C::TM / 2, C::TM);
+    mfma_rows(cur, C::HEAD_ROWS, C::TM);
     // interleave: one MFMA, then a share of the LDS reads
 #pragma unroll
-    for (int q = 0; q < C::HALF_MFMAS; ++q) {
+    for (int q = 0; q < C::TAIL_MFMAS; ++q) {
       __builtin_amdgcn_sched_group_barrier(0x008, MPK, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, DS_PER_MFMA, 0);
     }
