@@ -60,7 +60,16 @@ struct GemmArgs {
   int groups;
   int splits;            // K-grouped: contraction splits (1 = none), partials in fp32 at out
   int64_t split_stride;  // elements between the partial outputs of consecutive splits
+  int tail;              // M-grouped with offs: TAIL_NONE, TAIL_MAIN or TAIL_SUB (below)
 };
+
+// The last, partial round of an M-grouped launch with offs. The real tile count is
+// known only on the device, so the split is decided there: with TAIL_MAIN the
+// 256x256 launch runs only each XCD's whole rounds (one tile per compute unit each)
+// when at most half a round is left over, and a second launch of 128x128 tiles
+// (TAIL_SUB) runs each XCD's left-over tiles as four quarters each, on the same XCD
+// and on four times as many compute units.
+enum { TAIL_NONE = 0, TAIL_MAIN = 1, TAIL_SUB = 2 };
 
 // Block tile BM x BN over a WGM x WGN grid of waves, each wave (BM/WGM) x (BN/WGN)
 // in 32x32 MFMA tiles; the contraction advances 64 elements (one MFMA k-step) per
@@ -345,6 +354,30 @@ __device__ inline int64_t spread_tiles(int64_t bid, int64_t nblk, int64_t real) 
   return t < real ? t : -1;
 }
 
+// The XCD shares of `real` 256x256 tiles with a TAIL_MAIN / TAIL_SUB pair: XCD x
+// owns tiles [x * per, (x+1) * per), per = real / 8 rounded up (as spread_tiles deals
+// them); TAIL_MAIN runs the first `mainp` of them (whole rounds of the XCD's 32
+// compute units) and TAIL_SUB the `restp` after them as quarters, when 1..16 are left
+// (two quarters per compute unit at most); otherwise restp = 0 and TAIL_MAIN runs all.
+// Keeping every tile on the XCD that spread_tiles gives it keeps the XCDs at different
+// places of the raster at once: a split that gave each XCD whole bands (all of them
+// starting on the same columns of their groups' B) ran the dgrad inside the training
+// step 3 us slower, not faster.
+struct TailSplit {
+  int64_t per, mainp, restp;
+};
+__device__ inline TailSplit tail_split(int64_t real) {
+  TailSplit s;
+  s.per = (real + 7) / 8;
+  s.mainp = s.per / 32 * 32;
+  s.restp = s.per - s.mainp;
+  if (!(s.mainp > 0 && s.restp > 0 && s.restp <= 16)) {
+    s.mainp = s.per;
+    s.restp = 0;
+  }
+  return s;
+}
+
 // WPE: waves per SIMD the register allocation must allow (2 where two blocks
 // share a compute unit).
 template <int BM, int BN, int WGM, int WGN, int NST_, int WPE, int MODE, int OUT_BF16, int EL>
@@ -363,14 +396,47 @@ __global__ __launch_bounds__(64 * WGM * WGN) __attribute__((amdgpu_waves_per_eu(
   const int wm = wave / WGN, wn = wave % WGN;
   GroupChunk first{};
   int64_t mt_count = p.mt_total, t;
-  if (MODE == MODE_MGROUP && p.offs) {
-    mt_count = uniform(total_mtiles<BM>(p, first));
-    t = uniform(spread_tiles(blockIdx.x, gridDim.x, mt_count * p.nt));
-    if (t < 0) return;
+  Tile T;
+  constexpr bool QUARTERS = MODE == MODE_MGROUP && BM == 128 && BN == 128;
+  if (QUARTERS && p.offs && p.tail == TAIL_SUB) {
+    if constexpr (QUARTERS) {
+      // block j of XCD x (blocks reach XCDs round-robin): quarter j % 4 (row half,
+      // column half) of the XCD's left-over tile j / 4 in the 256x256 geometry
+      mt_count = uniform(total_mtiles<2 * BM>(p, first));
+      GemmArgs pp = p;
+      pp.nt = (p.N + 2 * BN - 1) / (2 * BN);
+      const int64_t real = mt_count * pp.nt;
+      const TailSplit sp = tail_split(real);
+      const int64_t x = blockIdx.x % 8, j = blockIdx.x / 8;
+      if (sp.restp == 0 || j >= sp.restp * 4) return;
+      const int64_t tt = x * sp.per + sp.mainp + j / 4;
+      if (tt >= real) return;
+      T = tile_at<2 * BM, 2 * BN, MODE, OUT_BF16, EL>(pp, tt, mt_count, first);
+      const int q = (int)(j & 3);
+      T.a_row0 += (q >> 1) * BM;
+      T.col0 += (q & 1) * BN;
+      T.b_row0 += (q & 1) * BN;
+      if (T.a_row0 >= T.a_row_end || T.col0 >= p.N) T.valid = false;
+    }
   } else {
-    t = xcd_remap(blockIdx.x, gridDim.x);
+    if (MODE == MODE_MGROUP && p.offs) {
+      mt_count = uniform(total_mtiles<BM>(p, first));
+      const int64_t real = mt_count * p.nt;
+      const TailSplit sp = tail_split(real);
+      if (p.tail == TAIL_MAIN && sp.restp > 0) {
+        // the first mainp tiles of each XCD's share (mainp <= real / 8 <= grid / 8)
+        const int64_t x = blockIdx.x % 8, j = blockIdx.x / 8;
+        t = j < sp.mainp && x * sp.per + j < real ? x * sp.per + j : -1;
+      } else {
+        t = spread_tiles(blockIdx.x, gridDim.x, real);
+      }
+      t = uniform(t);
+      if (t < 0) return;
+    } else {
+      t = xcd_remap(blockIdx.x, gridDim.x);
+    }
+    T = tile_at<BM, BN, MODE, OUT_BF16, EL>(p, t, mt_count, first);
   }
-  Tile T = tile_at<BM, BN, MODE, OUT_BF16, EL>(p, t, mt_count, first);
   if (!__builtin_amdgcn_readfirstlane((int)T.valid)) return;
   T.a_row0 = uniform(T.a_row0); T.a_row_end = uniform(T.a_row_end);
   T.b_row0 = uniform(T.b_row0); T.b_row_end = uniform(T.b_row_end);
@@ -703,16 +769,16 @@ namespace {
 constexpr int64_t kComputeUnits = 256;
 
 // Launches one tile configuration and output type over the whole problem (p.splits
-// already set).
+// already set), one block per tile or `grid` blocks.
 template <int BM, int BN, int WGM, int WGN, int NST, int WPE, int MODE, int EL, int OUT_BF16>
-hipError_t launch_cfg(mx::GemmArgs p, hipStream_t stream) {
+hipError_t launch_cfg(mx::GemmArgs p, hipStream_t stream, int64_t grid = 0) {
   using C = mx::Cfg<BM, BN, WGM, WGN, NST>;
   const int64_t mt_extra = (MODE == mx::MODE_MGROUP && p.offs) ? p.groups : 0;
   p.mt_total = (p.M + BM - 1) / BM + mt_extra;
   p.nt = (p.N + BN - 1) / BN;
   p.tiles = MODE == mx::MODE_MGROUP ? p.mt_total * p.nt : (int64_t)p.splits * p.groups * p.mt_total * p.nt;
   if (p.tiles == 0) return hipSuccess;
-  const int64_t blocks = p.tiles;
+  const int64_t blocks = grid > 0 ? grid : p.tiles;
   // the dynamic LDS limit of this instance, raised once per process (thread-safe
   // static initialisation)
   static const hipError_t attr = hipFuncSetAttribute((const void*)mx::k_gemm<BM, BN, WGM, WGN, NST, WPE, MODE, OUT_BF16, EL>,
@@ -872,7 +938,21 @@ hipError_t launch(mx::GemmArgs& p, int out_bf16, void* ws, int64_t ws_bytes, hip
       return hipGetLastError();
     }
   }
-  return launch_tiling<MODE, EL>(choose_tiling<MODE, EL>(p, out_bf16), p, out_bf16, stream);
+  const int tiling = choose_tiling<MODE, EL>(p, out_bf16);
+  if (MODE == mx::MODE_MGROUP && p.offs && tiling == TILE_256 && out_bf16) {
+    // whole rounds of 256x256 tiles, then the quarters of a short last round (the
+    // MoE step's 1088 tiles: four rounds and 8 tiles per XCD as 256 quarters; inside
+    // the step fwd 272 -> 263 us, dgrad 271-272 -> 265 us); when the device finds no
+    // such round the second launch's blocks exit at once
+    mx::GemmArgs main = p;
+    main.tail = mx::TAIL_MAIN;
+    hipError_t e = launch_tiling<MODE, EL>(tiling, main, out_bf16, stream);
+    if (e != hipSuccess) return e;
+    mx::GemmArgs rest = p;
+    rest.tail = mx::TAIL_SUB;
+    return launch_cfg<128, 128, 2, 2, 4, 2, MODE, EL, 1>(rest, stream, 2 * kComputeUnits);
+  }
+  return launch_tiling<MODE, EL>(tiling, p, out_bf16, stream);
 }
 }  // namespace
 

@@ -15,7 +15,8 @@ partial tiles on both output edges:
   * 256x192: M-grouped outputs whose columns 192-column tiles cover with at least
     1/8 less padding (96-column waves: the epilogue's padded-pitch staging).
 The bit-exact sweep below also reaches 128x128 and the four-wave 256x256 (bf16
-output, 512 or more tiles), which the small-shape and full-size tests cover too.
+output, 512 or more tiles), which the small-shape and full-size tests cover too, and
+the split of a short last round of 256x256 tiles into 128x128 quarters.
 """
 
 import numpy as np
@@ -242,6 +243,35 @@ def test_exact_wgrad_tilings(oracle, n, k, m, G, name):
     assert np.array_equal(got16[:, rows], oracle.round_to_bf16_bits(ref)), f"{name}: bf16 wgrad is not the rounded exact result"
     for g in np.flatnonzero(sizes == 0):
         assert not got[g].any() and not got16[g].any()
+
+
+@pytest.mark.parametrize("sizes,n,rest", [
+    ([3008, 2912, 2720], 4096, 6),       # 35 x 16 = 560 tiles, 70 per XCD: 64 + 6 left, one quarter per unit
+    ([3008, 0, 2912, 2720], 4128, 11),   # 35 x 17 = 595, 75 per XCD (70 on the last): 64 + 11, two quarters
+                                         # on some units; ragged last column, an empty group
+    ([2560, 2560, 2560, 2560], 4096, 16),  # 40 x 16 = 640, 80 per XCD: 64 + 16, the largest rest split
+    ([2048, 2048, 2048, 2048], 4096, 0),   # 32 x 16 = 512: whole rounds, the quarter launch does nothing
+    ([2592, 2592, 2592, 2304], 4096, 20),  # 42 x 16 = 672, 84 per XCD: 20 left, more than half a round: no split
+])
+def test_exact_fwd_last_round_quarters(oracle, sizes, n, rest):
+    """M-grouped forward with bf16 output over 256x256 tiles: each XCD's whole rounds
+    (32 compute units) run as 256x256 tiles, a short rest as 128x128 quarters in a
+    second launch. Every output row is compared with the exact sum, fp32 and bf16."""
+    rng = np.random.default_rng(len(sizes) * 1000 + n + rest)
+    sizes = np.array(sizes)
+    G, m, k = len(sizes), int(sizes.sum()), 1088
+    per = (int(np.sum((sizes + 255) // 256)) * ((n + 255) // 256) + 7) // 8
+    assert per % 32 == rest
+    offs = np.cumsum(sizes).astype(np.int32)
+    a, a_s = exact_codes(rng, m, k)
+    b, b_s = exact_codes(rng, G * n, k)
+    say(f"[exact quarters] fwd m={m} n={n} k={k} offs={offs.tolist()} rest per XCD={rest}")
+    args = (dev_u8(a), phys(oracle, a_s), dev_u8(b), phys(oracle, b_s), dev_i32(offs), m, n, k)
+    got16 = host(mx.mx_grouped_mm_fwd(*args, out_dtype=mx.MX_OUT_BF16))
+    got = host(mx.mx_grouped_mm_fwd(*args, out_dtype=mx.MX_OUT_F32))
+    ref = oracle.grouped_mm(oracle.dequantize(a, a_s), oracle.dequantize(b, b_s), offs, G)
+    assert np.array_equal(got16, oracle.round_to_bf16_bits(ref)), "bf16 fwd is not the rounded exact result"
+    assert np.array_equal(got, ref.astype(np.float32)), "fp32 fwd differs from the exact result"
 
 
 def test_exact_dgrad_short_contraction(oracle):
