@@ -22,6 +22,7 @@
 // C[row l % 32][col 8*(v/4) + 4*h + v%4], which it stores directly.
 
 #include <algorithm>
+#include <cstdint>
 #include <mutex>
 #include <type_traits>
 
@@ -143,69 +144,76 @@ struct GroupHit {
   int g;                      // -1: no group owns mt
 };
 
+// Inclusive scans over the 64 lanes of a wave of values >= 0 (0 is the identity of
+// both), in DPP moves between lanes: four row shifts give the scan inside each row of
+// 16 lanes, then the last lane of row 0 (of row 2) is added into row 1 (row 3) and the
+// last lane of row 1 into rows 2 and 3. Each step is one ALU operation on a
+// neighbour's register, where a shuffle through LDS costs a round trip per step.
+__device__ inline int32_t dpp_max_step(int32_t v, int32_t w) { return w > v ? w : v; }
+template <bool MAX>
+__device__ inline int32_t wave_incl_scan(int32_t v) {
+  auto op = [](int32_t a, int32_t b) { return MAX ? dpp_max_step(a, b) : a + b; };
+  v = op(v, __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false));  // row_shr:1
+  v = op(v, __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false));  // row_shr:2
+  v = op(v, __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false));  // row_shr:4
+  v = op(v, __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false));  // row_shr:8
+  v = op(v, __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false));  // row_bcast:15 into rows 1, 3
+  v = op(v, __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false));  // row_bcast:31 into rows 2, 3
+  return v;
+}
+// The value of the previous lane (lane 0: `first`).
+__device__ inline int32_t wave_prev(int32_t v, int32_t first) {
+  return __builtin_amdgcn_update_dpp(first, v, 0x138, 0xf, 0xf, false);  // wave_shr:1
+}
+
 // Groups g0 .. g0+63 of the M-grouped scan, lane l holding group g0 + l: its row
 // range [s, e), output range [so, eo), m-tiles, and the m-tiles of all groups up to
-// and including it. The ends are read as their running maximum clamped into [0, M]
-// (the output ends into [0, out_rows]): for valid offs this changes nothing; an
+// and including it. The ends are read clamped into [0, M] (the output ends into
+// [0, out_rows]) as their running maximum: for valid offs this changes nothing; an
 // out-of-contract offs gives wrong rows but no access outside the operand and output
 // buffers. Lanes past the last group hold an empty range and the running totals.
+// Everything fits 32 bits: offs are int32 and the m-tile counts are below 2^27.
 struct GroupChunk {
-  int64_t s, e, so, eo, tiles, cum;
+  int32_t s, e, so, eo, tiles, cum;
   bool live;
 };
 
 template <int BM>
-__device__ inline GroupChunk scan_chunk(const GemmArgs& p, int g0, int64_t carry_e, int64_t carry_eo,
-                                        int64_t carry_cum) {
+__device__ inline GroupChunk scan_chunk(const GemmArgs& p, int g0, int32_t carry_e, int32_t carry_eo,
+                                        int32_t carry_cum) {
   const int l = threadIdx.x & 63;
   const int g = g0 + l;
+  const int32_t m32 = p.M < INT32_MAX ? (int32_t)p.M : INT32_MAX;
+  const int32_t o32 = p.out_rows < INT32_MAX ? (int32_t)p.out_rows : INT32_MAX;
   GroupChunk c;
   c.live = g < p.groups;
-  int64_t e = c.live ? (int64_t)p.offs[g] : 0, eo = c.live && p.offs_out ? (int64_t)p.offs_out[g] : 0;
-  e = e > carry_e ? e : carry_e;
-  eo = eo > carry_eo ? eo : carry_eo;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int64_t oe = __shfl_up(e, d, 64), oo = __shfl_up(eo, d, 64);
-    if (l >= d) {
-      e = oe > e ? oe : e;
-      eo = oo > eo ? oo : eo;
-    }
-  }
-  e = e < 0 ? 0 : (e > p.M ? p.M : e);
-  eo = eo < 0 ? 0 : (eo > p.out_rows ? p.out_rows : eo);
-  c.s = __shfl_up(e, 1, 64);
-  c.so = __shfl_up(eo, 1, 64);
-  if (l == 0) {
-    c.s = carry_e;
-    c.so = carry_eo;
-  }
+  int32_t e = c.live ? p.offs[g] : 0, eo = c.live && p.offs_out ? p.offs_out[g] : 0;
+  e = e < 0 ? 0 : (e > m32 ? m32 : e);
+  eo = eo < 0 ? 0 : (eo > o32 ? o32 : eo);
+  e = wave_incl_scan<true>(e > carry_e ? e : carry_e);
+  eo = wave_incl_scan<true>(eo > carry_eo ? eo : carry_eo);
+  c.s = wave_prev(e, carry_e);
+  c.so = wave_prev(eo, carry_eo);
   c.e = e;
   c.eo = eo;
   c.tiles = c.live ? (e - c.s + BM - 1) / BM : 0;
-  int64_t cum = c.tiles;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int64_t o = __shfl_up(cum, d, 64);
-    if (l >= d) cum += o;
-  }
-  c.cum = cum + carry_cum;
+  c.cum = wave_incl_scan<false>(c.tiles) + carry_cum;
   return c;
 }
 
 // The m-tiles of all groups (the first chunk's scan is kept in `first`). Every wave
-// scans on its own, 64 groups per step of a few shuffles: no LDS, no barrier, and a
-// thousand groups cost a few dozen steps where a group-by-group walk would wait on one
-// load per group (at eight groups the two measured the same).
+// scans on its own, 64 groups per step: no LDS, no barrier, and a thousand groups
+// cost a few dozen steps where a group-by-group walk would wait on one load per group.
 template <int BM>
 __device__ inline int64_t total_mtiles(const GemmArgs& p, GroupChunk& first) {
   first = scan_chunk<BM>(p, 0, 0, 0, 0);
-  int64_t ce = __shfl(first.e, 63, 64), ceo = __shfl(first.eo, 63, 64), cc = __shfl(first.cum, 63, 64);
+  int32_t ce = __builtin_amdgcn_readlane(first.e, 63), ceo = __builtin_amdgcn_readlane(first.eo, 63);
+  int32_t cc = __builtin_amdgcn_readlane(first.cum, 63);
   for (int g0 = 64; g0 < p.groups; g0 += 64) {
     const GroupChunk c = scan_chunk<BM>(p, g0, ce, ceo, cc);
-    ce = __shfl(c.e, 63, 64);
-    ceo = __shfl(c.eo, 63, 64);
-    cc = __shfl(c.cum, 63, 64);
+    ce = __builtin_amdgcn_readlane(c.e, 63);
+    ceo = __builtin_amdgcn_readlane(c.eo, 63);
+    cc = __builtin_amdgcn_readlane(c.cum, 63);
   }
   return cc;
 }
@@ -217,15 +225,24 @@ __device__ inline GroupHit find_group(const GemmArgs& p, int64_t mt, const Group
   for (int g0 = 0;;) {
     const uint64_t own = __ballot(c.live && mt >= c.cum - c.tiles && mt < c.cum);
     if (own) {
-      const int j = __ffsll((long long)own) - 1;
-      return GroupHit{__shfl(c.s, j, 64), __shfl(c.e, j, 64), __shfl(c.so, j, 64), __shfl(c.eo, j, 64),
-                      __shfl(c.cum - c.tiles, j, 64), g0 + j};
+      const int j = __builtin_amdgcn_readfirstlane(__ffsll((long long)own) - 1);
+      return GroupHit{__builtin_amdgcn_readlane(c.s, j), __builtin_amdgcn_readlane(c.e, j),
+                      __builtin_amdgcn_readlane(c.so, j), __builtin_amdgcn_readlane(c.eo, j),
+                      __builtin_amdgcn_readlane(c.cum - c.tiles, j), g0 + j};
     }
     g0 += 64;
     if (g0 >= p.groups) return GroupHit{0, 0, 0, 0, 0, -1};
-    c = scan_chunk<BM>(p, g0, __shfl(c.e, 63, 64), __shfl(c.eo, 63, 64), __shfl(c.cum, 63, 64));
+    c = scan_chunk<BM>(p, g0, __builtin_amdgcn_readlane(c.e, 63), __builtin_amdgcn_readlane(c.eo, 63),
+                       __builtin_amdgcn_readlane(c.cum, 63));
   }
 }
+
+// a / b and a % b for a, b >= 0: a 32-bit division when both fit (a few instructions
+// where a 64-bit one is a long expansion), else the 64-bit one.
+__device__ inline int64_t udiv(int64_t a, int64_t b) {
+  return ((a | b) >> 32) == 0 ? (int64_t)((uint32_t)a / (uint32_t)b) : a / b;
+}
+__device__ inline int64_t umod(int64_t a, int64_t b) { return a - udiv(a, b) * b; }
 
 // Logical tile t -> its output tile and contraction range (one block per tile).
 // Each XCD takes a contiguous range of logical tiles in order (xcd_remap,
@@ -261,12 +278,12 @@ __device__ inline Tile tile_at(const GemmArgs& p, int64_t t, int64_t mt_count, c
     g = (int)(rem / n_s);
     r = sl * S + rem % n_s;
   }
-  const int64_t band = r / (GM * p.nt);
+  const int64_t band = udiv(r, GM * p.nt);
   const int64_t first_m = band * GM;
   const int64_t gm = mt_count - first_m < GM ? mt_count - first_m : GM;
-  const int64_t in_band = r % (GM * p.nt);
-  const int64_t mt = first_m + in_band % gm;
-  const int64_t n_tile = in_band / gm;
+  const int64_t in_band = r - band * GM * p.nt;
+  const int64_t mt = first_m + (gm == GM ? in_band % GM : umod(in_band, gm));
+  const int64_t n_tile = gm == GM ? in_band / GM : udiv(in_band, gm);
   T.col0 = n_tile * BN;
   if (MODE == MODE_MGROUP) {
     // the group owning m-tile `mt` (dense: the one group of all M rows)
