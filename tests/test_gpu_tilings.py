@@ -274,6 +274,22 @@ def test_exact_fwd_last_round_quarters(oracle, sizes, n, rest):
     assert np.array_equal(got, ref.astype(np.float32)), "fp32 fwd differs from the exact result"
 
 
+def test_exact_bf16_fwd_last_round_quarters(oracle):
+    """bf16 operands, bf16 output over 256x256 tiles with a short last round (70 tiles per
+    XCD: 64 + 6, run as 128x128 quarters): values in {0, +-0.5, +-1, +-2}, so every sum is
+    exact in fp32 and the output must be the correctly rounded exact sum, every row."""
+    rng = np.random.default_rng(77)
+    sizes = np.array([3008, 2912, 2720])
+    G, m, n, k = len(sizes), int(sizes.sum()), 4096, 1088
+    offs = np.cumsum(sizes).astype(np.int32)
+    pats = np.array([0x0000, 0x3F00, 0xBF00, 0x3F80, 0xBF80, 0x4000, 0xC000], np.uint16)
+    a, b = rng.choice(pats, size=(m, k)), rng.choice(pats, size=(G * n, k))
+    say(f"[exact quarters bf16] fwd m={m} n={n} k={k} offs={offs.tolist()}")
+    got = host(mx.mx_grouped_mm_bf16_fwd(dev_bf16(a), dev_bf16(b), dev_i32(offs), m, n, k, out_dtype=mx.MX_OUT_BF16))
+    ref = oracle.grouped_mm(oracle.bf16_to_f64(a), oracle.bf16_to_f64(b), offs, G)
+    assert np.array_equal(got, oracle.round_to_bf16_bits(ref)), "bf16 fwd is not the rounded exact result"
+
+
 def test_exact_dgrad_short_contraction(oracle):
     """dgrad over a 576-wide contraction, 13 x 10 tiles: 128x256 tiles, two blocks per CU."""
     rng = np.random.default_rng(81)
