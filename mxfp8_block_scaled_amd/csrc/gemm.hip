@@ -849,7 +849,7 @@ int choose_splits(const mx::GemmArgs& p, int64_t elem_bytes) {
 
 // Tile configurations (block tile, wave grid, ring depth, blocks per compute unit):
 enum Tiling {
-  TILE_256 = 0,      // 256x256, 2x2 waves of 128x128, 4-deep ring, 136 KB LDS: one block per CU (bf16 out)
+  TILE_256 = 0,      // 256x256, 2x2 waves of 128x128, 4-deep ring, 136 KB LDS: one block per CU (M-grouped, bf16 out)
   TILE_128 = 1,      // 128x128, 2x2 waves of 64x64, 4-deep ring, 68 KB: two blocks per CU
   TILE_128x256 = 2,  // 128x256, 2x2 waves of 64x128, 3-deep ring, 80 KB: two blocks per CU
   TILE_192x256 = 3,  // 192x256, 1x4 waves of 192x64, 4-deep ring, 120 KB: one block per CU
@@ -866,9 +866,9 @@ hipError_t launch_tiling_out(int tiling, const mx::GemmArgs& p, hipStream_t stre
     case TILE_256_8W: return launch_cfg<256, 256, 2, 4, 4, 2, MODE, EL, OUT>(p, stream);
     case TILE_256x192: return launch_cfg<256, 192, 2, 2, 4, 1, MODE, EL, OUT>(p, stream);
     case TILE_256:
-      // one wave per SIMD holds 256 fp32 accumulators: bf16 output only (the fp32
-      // epilogue would spill), fp32 output takes the eight-wave tiling
-      if (OUT) return launch_cfg<256, 256, 2, 2, 4, 1, MODE, EL, 1>(p, stream);
+      // one wave per SIMD holds 256 fp32 accumulators: M-grouped bf16 output only (the
+      // fp32 epilogue would spill; choose_tiling gives K-grouped tiles two waves per SIMD)
+      if (OUT && MODE == mx::MODE_MGROUP) return launch_cfg<256, 256, 2, 2, 4, 1, MODE, EL, 1>(p, stream);
       return launch_cfg<256, 256, 2, 4, 4, 2, MODE, EL, OUT>(p, stream);
     default: return hipErrorInvalidValue;
   }
@@ -908,13 +908,15 @@ int choose_tiling(const mx::GemmArgs& p, int out_bf16) {
   // (the 4096 x 4096 x 2048 linear's dgrad, 128 tiles: 44 against 52 us; its wgrad
   // 44 against 61 us with the contraction split two ways)
   if (big_tiles < kComputeUnits) return TILE_128x256;
-  // many tiles, bf16 output: one wave per SIMD (grouped forward / dgrad 279-281 /
-  // 269-272 us against 287-288 / 277-278 with two; MXFP8 wgrad 296-298 against
-  // 301-304), except the bf16 K-grouped wgrad, where two waves per SIMD hide its
-  // masked, longer steps better (540 against 564 us). fp32 output keeps two waves per
-  // SIMD: 128 accumulators per wave leave room for the fp32 epilogue, which with 256
-  // spills (forward 286 against 287 us, wgrad 292 against 310 us)
-  if (big_tiles >= 512 && out_bf16 && !(EL == mx::EL_BF16 && MODE == mx::MODE_KGROUP)) return TILE_256;
+  // many tiles, bf16 output, M-grouped: one wave per SIMD (grouped forward / dgrad
+  // 279-281 / 269-272 us against 287-288 / 277-278 with two). K-grouped wgrads take two
+  // waves per SIMD: the bf16 one hides its masked, longer steps better (540 against
+  // 564 us), and since the MFMAs split 3:1 around the k-step's wait the MXFP8 ones run
+  // faster so too (inside the steps: MoE 286-287 against 290-291 us, 32-expert share
+  // gate/up 1277 against 1296 us, down 611-612 against 633-636 us). fp32 output keeps
+  // two waves per SIMD: 128 accumulators per wave leave room for the fp32 epilogue,
+  // which with 256 spills (forward 286 against 287 us, wgrad 292 against 310 us)
+  if (big_tiles >= 512 && out_bf16 && MODE == mx::MODE_MGROUP) return TILE_256;
   // otherwise (128-511 tiles: one round or two) two waves per SIMD hide each tile's
   // prologue and epilogue better (the 576-wide forward's single round of 192 tiles:
   // 53-54 us against 63-68 us)

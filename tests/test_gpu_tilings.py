@@ -5,8 +5,8 @@ select one of them, with groups that end inside tiles (MXFP8 groups on 32-row
 boundaries, as the calls require; bf16 groups anywhere), one group empty, and
 partial tiles on both output edges:
   * 256x256 with eight waves (two per SIMD): 256..511 tiles of 256x256 (M-grouped
-    over a contraction above 1024, or K-grouped), and with more tiles for fp32
-    outputs and the bf16 K-grouped wgrad;
+    over a contraction above 1024), K-grouped wgrads of 256 or more such tiles, and
+    M-grouped fp32 outputs with more tiles;
   * 128x256 over a three-deep ring, two blocks per compute unit: M-grouped with a
     contraction of at most 1024 and >= 128 tiles, and either mode with 128..255
     tiles of 256x256 (half a round to a round);
@@ -14,8 +14,8 @@ partial tiles on both output edges:
     less padding than 256-row ones, without and with split contractions;
   * 256x192: M-grouped outputs whose columns 192-column tiles cover with at least
     1/8 less padding (96-column waves: the epilogue's padded-pitch staging).
-The bit-exact sweep below also reaches 128x128 and the four-wave 256x256 (bf16
-output, 512 or more tiles), which the small-shape and full-size tests cover too, and
+The bit-exact sweep below also reaches 128x128 and the four-wave 256x256 (M-grouped
+bf16 output, 512 or more tiles), which the small-shape and full-size tests cover too, and
 the split of a short last round of 256x256 tiles into 128x128 quarters.
 """
 
@@ -224,7 +224,7 @@ def test_exact_fwd_tilings(oracle, m, n, k, G, name):
     (352, 2080, 4096, 8, "192x256"),        # 8 x 2 x 9 = 144 tiles, 352 rows in 192-row tiles
     (1056, 2080, 4096, 8, "8-wave"),        # 8 x 5 x 9 = 360 tiles (1152 rows as 192s: too little saved)
     (1056, 1056, 4096, 8, "128x256 half"),  # 8 x 5 x 5 = 200 tiles: less than a round, no split
-    (4128, 2080, 2048, 8, "256x256"),       # 8 x 17 x 9 = 1224 tiles (bf16 out; fp32: 8-wave)
+    (4128, 2080, 2048, 8, "256x256"),       # 8 x 17 x 9 = 1224 tiles, eight waves
     (576, 1056, 8192, 2, "192x256 split"),  # 2 x 3 x 5 = 30 tiles: contraction split 8 ways
 ])
 def test_exact_wgrad_tilings(oracle, n, k, m, G, name):
