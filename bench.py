@@ -99,6 +99,9 @@ def parse():
                          "with the 256^3 small linear's latency beside it")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a 1 GiB device-to-device copy instead (reference for HBM byte counters)")
+    ap.add_argument("--cycle-stamps", action="store_true",
+                    help="load the instrumented library (libmxfp8_stamps.so), run the step, then each GEMM of "
+                         "the step once more alone and print its per-block cycle breakdown as one JSON line")
     return ap.parse_args()
 
 
@@ -106,13 +109,15 @@ HASHED_SOURCES = ("gemm.hip", "cast.hip", "common.h", "group_table.h")
 
 
 def src_hash(csrc=None):
-    """Hash of the GEMM and cast kernel sources with comments and whitespace removed:
-    the counters in profiles/traffic.json hold while it matches."""
+    """Hash of the GEMM and cast kernel sources with comments and whitespace removed,
+    and without the blocks that only the instrumented build (MX_CYCLE_STAMPS)
+    compiles: the counters in profiles/traffic.json hold while it matches."""
     csrc = csrc or os.path.join(ROOT, "mxfp8_block_scaled_amd", "csrc")
     h = hashlib.sha256()
     for f in HASHED_SOURCES:
         with open(os.path.join(csrc, f)) as fh:
             text = fh.read()
+        text = re.sub(r"#ifdef MX_CYCLE_STAMPS\n.*?#endif\n", "", text, flags=re.S)
         text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
         text = re.sub(r"//[^\n]*", "", text)
         h.update("".join(text.split()).encode())
@@ -216,6 +221,13 @@ def main():
     import mxfp8_block_scaled_amd as mx
     from mxfp8_block_scaled_amd import synth
 
+    if args.cycle_stamps:
+        # the instrumented build of the same sources; loaded before any library call
+        from mxfp8_block_scaled_amd import _lib, build as _build
+
+        assert os.path.exists(_build.STAMPS_LIB), "build it: python -m mxfp8_block_scaled_amd.build --stamps"
+        _lib.LIB_PATH = _build.STAMPS_LIB
+
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
 
@@ -232,7 +244,7 @@ def main():
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
 
     if args.workload == "linear_4096":
-        assert not (args.unaligned_groups or args.backward or args.separate_casts or args.only), \
+        assert not (args.unaligned_groups or args.backward or args.separate_casts or args.only or args.cycle_stamps), \
             "--workload linear_4096 runs its own step"
         return linear_4096_main(args, mx, synth, to_dev, dev)
 
@@ -409,6 +421,9 @@ def main():
         del buf, X, W, dY, Wn, dYn
         torch.cuda.empty_cache()
         ops, share_config = deepseek_share_ops(mx, synth, to_dev, dev)
+
+    if args.cycle_stamps:
+        return cycle_stamps_main(args, ops, share_config)
 
     if args.only:
         # the casts an op depends on still run once, untimed, so its inputs exist
@@ -598,6 +613,93 @@ def main():
         "roofline": roofline, "cpu_baseline": cpu, "kernels": per_op, "source_hash": src_hash(),
     }
     print(json.dumps(line), flush=True)
+
+
+def stamp_summary(rec):
+    """Per-block cycle records of one launch (rows of 8 words, see gemm.hip) -> summary.
+    Cycles are shader-clock cycles (s_memtime) of each block's own compute unit."""
+    rec = rec[rec[:, 7] == 1]
+    if len(rec) == 0:
+        return None
+    t0, t1, t2, t3 = (rec[:, i].astype(np.float64) for i in range(4))
+    hw = rec[:, 5].astype(np.uint64)
+    n_iter = rec[:, 6].astype(np.float64)
+    loop_ok = (t1 > 0) & (t2 >= t1) & (n_iter > 0)
+    xcc = (hw >> np.uint64(32)).astype(np.int64)
+    # compute unit: XCC, shader engine, shader array, CU (fields of HW_ID)
+    cu = (xcc << 16) | (((hw >> np.uint64(13)) & np.uint64(7)).astype(np.int64) << 8) | \
+         (((hw >> np.uint64(12)) & np.uint64(1)).astype(np.int64) << 4) | ((hw >> np.uint64(8)) & np.uint64(15)).astype(np.int64)
+    spans, gaps, busy, by_xcd = [], [], 0.0, {}
+    for c in np.unique(cu):
+        idx = np.where(cu == c)[0]
+        idx = idx[np.argsort(t0[idx])]
+        span = t3[idx].max() - t0[idx].min()
+        spans.append(span)
+        busy += float(np.sum(t3[idx] - t0[idx]))
+        gaps.extend((t0[idx][1:] - t3[idx][:-1]).tolist())
+        by_xcd.setdefault(int(c >> 16), []).append(span)
+    spans = np.array(spans)
+    # tilings with two blocks per compute unit: blocks overlap, so neither the gap
+    # between consecutive blocks nor a busy fraction is defined
+    overlap = bool(gaps) and min(gaps) < 0
+    per_step = (t2 - t1)[loop_ok] / n_iter[loop_ok]
+    out = {
+        "blocks": int(len(rec)), "compute_units": int(len(spans)), "k_steps_mean": round(float(n_iter.mean()), 2),
+        "setup_cycles": round(float(np.mean((t1 - t0)[loop_ok])), 0) if loop_ok.any() else None,
+        "loop_cycles": round(float(np.mean((t2 - t1)[loop_ok])), 0) if loop_ok.any() else None,
+        "loop_cycles_per_k_step": round(float(per_step.mean()), 0) if loop_ok.any() else None,
+        "epilogue_cycles": round(float(np.mean((t3 - t2)[loop_ok])), 0) if loop_ok.any() else None,
+        "block_cycles": round(float(np.mean(t3 - t0)), 0),
+        "gap_between_blocks_cycles": round(float(np.mean(gaps)), 0) if gaps and not overlap else None,
+        "blocks_overlap_on_a_cu": overlap,
+        "cu_span_cycles": {"mean": round(float(spans.mean()), 0), "min": round(float(spans.min()), 0),
+                           "max": round(float(spans.max()), 0)},
+        "busy_frac": None if overlap else round(busy / float(spans.sum()), 3),
+        "per_xcd_span_mean_max": {str(x): [round(float(np.mean(v)), 0), round(float(np.max(v)), 0)]
+                                  for x, v in sorted(by_xcd.items())},
+    }
+    if loop_ok.any():
+        out["per_xcd_loop_cycles_per_k_step"] = {
+            str(x): round(float(np.mean(per_step[xcc[loop_ok] == x])), 0) for x in sorted(set(xcc[loop_ok].tolist()))}
+    return out
+
+
+def cycle_stamps_main(args, ops, share_config):
+    """Runs the step `warmup` times, then, in step order, every op once more, each GEMM
+    alone between synchronisations, and prints each GEMM launch's per-block cycle
+    breakdown (instrumented build: libmxfp8_stamps.so)."""
+    import ctypes
+
+    import torch
+
+    from mxfp8_block_scaled_amd import _lib
+
+    lib = _lib.load()
+    lib.mx_cycle_stamps_blocks.restype = ctypes.c_int64
+    lib.mx_cycle_stamps_read.argtypes = [ctypes.c_void_p]
+    lib.mx_cycle_stamps_read.restype = ctypes.c_int
+    lib.mx_cycle_stamps_clear.restype = ctypes.c_int
+    nb = int(lib.mx_cycle_stamps_blocks())
+    buf = np.zeros(nb * 8, dtype=np.uint64)
+    for _ in range(args.warmup):
+        for _, _, _, fn in ops:
+            fn()
+    torch.cuda.synchronize()
+    res = {}
+    for name, kind, _, fn in ops:
+        if kind not in PEAKS:
+            fn()
+            continue
+        torch.cuda.synchronize()
+        assert lib.mx_cycle_stamps_clear() == 0
+        fn()
+        torch.cuda.synchronize()
+        assert lib.mx_cycle_stamps_read(buf.ctypes.data) == 0
+        rec = buf.reshape(nb, 8)
+        launches = {"main": stamp_summary(rec[: nb // 2]), "quarter_tiles": stamp_summary(rec[nb // 2:])}
+        res[name] = {k: v for k, v in launches.items() if v is not None}
+    print(json.dumps({"cycle_stamps": res, "workload": share_config["workload"] if share_config else "moe_g8",
+                      "warmup_steps": args.warmup, "source_hash": src_hash()}))
 
 
 def host_facts():

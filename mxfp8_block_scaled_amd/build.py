@@ -13,6 +13,9 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmxfp8.so")
+# the same sources built with MX_CYCLE_STAMPS: the GEMM kernels also record per-block
+# cycle stamps (bench.py --cycle-stamps); never loaded by the library's own callers
+STAMPS_LIB = os.path.join(HERE, "libmxfp8_stamps.so")
 SOURCES = ["abi.cpp", "cast.hip", "gemm.hip", "pad.hip", "convert.hip", "probe.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -30,9 +33,11 @@ FLAGS = [
 ]
 
 
-def build(verbose=False):
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC] + FLAGS + [os.path.join(CSRC, s) for s in SOURCES] + ["-o", tmp]
+def build(verbose=False, stamps=False):
+    """Builds libmxfp8.so, or with stamps=True the instrumented libmxfp8_stamps.so."""
+    lib = STAMPS_LIB if stamps else LIB
+    tmp = lib + ".tmp"
+    cmd = [HIPCC] + FLAGS + (["-DMX_CYCLE_STAMPS"] if stamps else []) + [os.path.join(CSRC, s) for s in SOURCES] + ["-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -47,9 +52,9 @@ def build(verbose=False):
     missing = [ln.split()[-1] for ln in nm.stdout.splitlines() if "_ZN2mx" in ln]
     if missing:
         raise RuntimeError("libmxfp8.so would have undefined kernel symbols: " + ", ".join(missing))
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    print(build(verbose="-v" in sys.argv, stamps="--stamps" in sys.argv))

@@ -397,6 +397,16 @@ __device__ inline TailSplit tail_split(int64_t real) {
 
 // WPE: waves per SIMD the register allocation must allow (2 where two blocks
 // share a compute unit).
+#ifdef MX_CYCLE_STAMPS
+// Instrumented build only (libmxfp8_stamps.so): wave 0 of every block records the
+// shader clock (s_memtime) at its start, when the first stage has landed, when the
+// last k-step is done and after the epilogue's stores are issued, with the hardware
+// ids of its compute unit and the tile's k-steps. 8 words per block; the second
+// launch of a split last round (128x128 quarters) records at kStampBlocks / 2 on.
+constexpr int64_t kStampBlocks = 32768;
+__device__ unsigned long long g_cycle_stamps[kStampBlocks * 8];
+#endif
+
 template <int BM, int BN, int WGM, int WGN, int NST_, int WPE, int MODE, int OUT_BF16, int EL>
 __global__ __launch_bounds__(64 * WGM * WGN) __attribute__((amdgpu_waves_per_eu(WPE))) void k_gemm(GemmArgs p) {
   using C = Cfg<BM, BN, WGM, WGN, NST_>;
@@ -407,6 +417,10 @@ __global__ __launch_bounds__(64 * WGM * WGN) __attribute__((amdgpu_waves_per_eu(
   // per tile when scaled) spread over the tail MFMAs
   constexpr int DS_PER_MFMA = ((SCALED ? 3 : 2) * (C::TM + C::TN) + C::TAIL_MFMAS - 1) / C::TAIL_MFMAS;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+#ifdef MX_CYCLE_STAMPS
+  const unsigned long long st_t0 = __builtin_amdgcn_s_memtime(), st_rt = __builtin_amdgcn_s_memrealtime();
+  unsigned long long st_t1 = 0, st_t2 = 0;
+#endif
 
   const int tid = threadIdx.x, l = tid & 63, h = l >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
@@ -748,6 +762,9 @@ __global__ __launch_bounds__(64 * WGM * WGN) __attribute__((amdgpu_waves_per_eu(
     for (int s = 0; s < NST - 1; ++s) issue_stage(s, s & 3, s < n_iter);
     wait_n(loads_after(0, NST - 2));
     __builtin_amdgcn_s_barrier();
+#ifdef MX_CYCLE_STAMPS
+    st_t1 = __builtin_amdgcn_s_memtime();
+#endif
     // The main loop is unrolled by four (one 256-wide scale window), so window
     // boundaries, and the ring slots of a 2- or 4-deep ring, are compile-time
     // constants, and alternates two register sets, so no fragment is ever copied.
@@ -766,6 +783,9 @@ __global__ __launch_bounds__(64 * WGM * WGN) __attribute__((amdgpu_waves_per_eu(
     }
     MX_WAIT_VMCNT(0);  // every load has landed
     __builtin_amdgcn_s_barrier();  // every wave is done with the ring
+#ifdef MX_CYCLE_STAMPS
+    st_t2 = __builtin_amdgcn_s_memtime();
+#endif
   };
   // bf16 K-grouped tiles whose range cuts a 16-byte chunk take the masked copy of
   // the loop; every other tile runs the loop without the per-step edge test (a
@@ -777,6 +797,19 @@ __global__ __launch_bounds__(64 * WGM * WGN) __attribute__((amdgpu_waves_per_eu(
     main_loop(std::false_type{});
   }
   epilogue();
+#ifdef MX_CYCLE_STAMPS
+  const unsigned long long st_t3 = __builtin_amdgcn_s_memtime();
+  const int64_t st_idx = (int64_t)blockIdx.x + (p.tail == TAIL_SUB ? kStampBlocks / 2 : 0);
+  if (tid == 0 && st_idx < kStampBlocks) {
+    const unsigned hw = __builtin_amdgcn_s_getreg(4 | (31 << 11));    // HW_ID: wave, SIMD, CU, SH, SE
+    const unsigned xcc = __builtin_amdgcn_s_getreg(20 | (31 << 11));  // XCC_ID
+    unsigned long long* o = g_cycle_stamps + st_idx * 8;
+    o[0] = st_t0; o[1] = st_t1; o[2] = st_t2; o[3] = st_t3; o[4] = st_rt;
+    o[5] = ((unsigned long long)xcc << 32) | hw;
+    o[6] = (unsigned long long)n_iter;
+    o[7] = 1;
+  }
+#endif
 }
 
 }  // namespace mx
@@ -1070,3 +1103,17 @@ int64_t mx_kgroup_workspace_bytes(int groups, int64_t m, int64_t n, int64_t k, i
   p.K = m;
   return split_workspace_bytes(p, bf16_operands ? 2 : 1, nullptr, nullptr);
 }
+
+#ifdef MX_CYCLE_STAMPS
+// Instrumented build only: copy out / clear the per-block records (8 x uint64 each,
+// kStampBlocks blocks). Synchronous; for profiling runs, one call at a time.
+extern "C" int64_t mx_cycle_stamps_blocks() { return mx::kStampBlocks; }
+extern "C" int mx_cycle_stamps_read(void* host) {
+  return (int)hipMemcpyFromSymbol(host, HIP_SYMBOL(mx::g_cycle_stamps), sizeof(mx::g_cycle_stamps), 0,
+                                  hipMemcpyDeviceToHost);
+}
+extern "C" int mx_cycle_stamps_clear() {
+  static unsigned long long zeros[mx::kStampBlocks * 8];
+  return (int)hipMemcpyToSymbol(HIP_SYMBOL(mx::g_cycle_stamps), zeros, sizeof(zeros), 0, hipMemcpyHostToDevice);
+}
+#endif

@@ -33,6 +33,23 @@ def test_exports_every_declared_symbol(lib):
         assert n in _lib.SIGNATURES, n
 
 
+def test_instrumented_build_is_separate(lib):
+    # the product library carries no cycle-stamp code; the instrumented copy exports
+    # the same entry points plus its record reader
+    import ctypes
+
+    from mxfp8_block_scaled_amd import build
+
+    assert not hasattr(lib, "mx_cycle_stamps_read")
+    if not os.path.exists(build.STAMPS_LIB):
+        pytest.skip("instrumented library not built")
+    st = ctypes.CDLL(build.STAMPS_LIB)
+    for n in declared_functions() + ["mx_cycle_stamps_blocks", "mx_cycle_stamps_read", "mx_cycle_stamps_clear"]:
+        assert hasattr(st, n), n
+    st.mx_cycle_stamps_blocks.restype = ctypes.c_int64
+    assert st.mx_cycle_stamps_blocks() == 32768
+
+
 def test_scale_bytes(lib):
     assert lib.mx_scale_bytes(32, 256) == 256
     assert lib.mx_scale_bytes(33, 256) == 512

@@ -37,6 +37,53 @@ def test_source_hash_ignores_comments_and_whitespace(tmp_path):
     assert bench.src_hash(str(tmp_path)) != h0
 
 
+def test_source_hash_ignores_the_instrumented_blocks(tmp_path):
+    # the blocks only the cycle-stamp build compiles do not change the product kernels
+    src = os.path.join(ROOT, "mxfp8_block_scaled_amd", "csrc")
+    for f in bench.HASHED_SOURCES:
+        shutil.copy(os.path.join(src, f), tmp_path / f)
+    g = tmp_path / "gemm.hip"
+    text = g.read_text()
+    assert text.count("#ifdef MX_CYCLE_STAMPS") >= 5
+    h0 = bench.src_hash(str(tmp_path))
+    out, rest = [], text
+    while "#ifdef MX_CYCLE_STAMPS\n" in rest:
+        pre, post = rest.split("#ifdef MX_CYCLE_STAMPS\n", 1)
+        out.append(pre)
+        rest = post.split("#endif\n", 1)[1]
+    g.write_text("".join(out) + rest)
+    assert "MX_CYCLE_STAMPS" not in g.read_text()
+    assert bench.src_hash(str(tmp_path)) == h0
+    # code outside such a block still counts
+    g.write_text(text.replace("#ifdef MX_CYCLE_STAMPS\n", "#if 1\n", 1))
+    assert bench.src_hash(str(tmp_path)) != h0
+
+
+def test_stamp_summary():
+    import numpy as np
+
+    # two compute units of XCC 3, two blocks each: start, loop start, loop end, end
+    def row(t0, t1, t2, t3, cu, n_iter):
+        return [t0, t1, t2, t3, 0, (3 << 32) | (cu << 8), n_iter, 1]
+
+    rec = np.array([row(0, 100, 1100, 1300, 1, 10), row(1400, 1500, 2500, 2700, 1, 10),
+                    row(0, 200, 1200, 1400, 2, 10), row(1500, 1600, 2600, 2800, 2, 10),
+                    [0] * 8], dtype=np.uint64)
+    s = bench.stamp_summary(rec)
+    assert s["blocks"] == 4 and s["compute_units"] == 2
+    assert s["setup_cycles"] == 125 and s["loop_cycles"] == 1000 and s["loop_cycles_per_k_step"] == 100
+    assert s["epilogue_cycles"] == 200 and s["gap_between_blocks_cycles"] == 100
+    assert s["cu_span_cycles"] == {"mean": 2750, "min": 2700, "max": 2800}
+    assert s["busy_frac"] == round((1300 + 1300 + 1400 + 1300) / (2700 + 2800), 3)
+    assert s["per_xcd_span_mean_max"] == {"3": [2750, 2800]}
+    assert not s["blocks_overlap_on_a_cu"]
+    assert bench.stamp_summary(np.zeros((4, 8), dtype=np.uint64)) is None
+    # two blocks at once on one compute unit: no gap, no busy fraction
+    o = bench.stamp_summary(np.array([row(0, 100, 1100, 1300, 1, 10), row(50, 150, 1150, 1350, 1, 10)],
+                                     dtype=np.uint64))
+    assert o["blocks_overlap_on_a_cu"] and o["gap_between_blocks_cycles"] is None and o["busy_frac"] is None
+
+
 def test_traffic_table_is_consistent():
     with open(os.path.join(ROOT, "profiles", "traffic.json")) as fh:
         d = json.load(fh)
