@@ -37,6 +37,14 @@ W2, dY2, dY1 and the grouped fwd, dgrad and wgrad of the gate/up projection
 (W1 [32, 4096, 7168]) and the down projection (W2 [32, 7168, 2048]). No CPU
 baseline in this mode; `traffic` is the committed counter figure of its gate/up wgrad.
 
+--precise: the default step with its six GEMMs computed from the same codes on the
+bf16 MFMA (both operands dequantized to bf16 inside each op, then the bf16 grouped
+GEMM): the route whose fp32 outputs meet the IEEE-fp32 figure, priced against the
+bf16 peak.
+
+--cycle-stamps: loads the instrumented build (libmxfp8_stamps.so) and prints each GEMM
+launch's per-block cycle breakdown instead of a timing line.
+
 --workload linear_4096: the dense MXFP8Linear step of the linear benchmark command on
 "Wire MoE and MXFP8Linear training paths to CuTeDSL by default" (M=N=4096, K=2048,
 CUDA-graph replay): one-pass casts of X [4096, 2048] and dY [4096, 4096], the 32x32
@@ -99,6 +107,10 @@ def parse():
                          "with the 256^3 small linear's latency beside it")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a 1 GiB device-to-device copy instead (reference for HBM byte counters)")
+    ap.add_argument("--precise", action="store_true",
+                    help="the default step with its six GEMMs computed from the same codes on the bf16 MFMA "
+                         "(mxfp8_block_scaled_amd.precise: dequantize both operands, bf16 grouped GEMM), the "
+                         "path that meets the IEEE-fp32 figure; priced against the bf16 peak")
     ap.add_argument("--cycle-stamps", action="store_true",
                     help="load the instrumented library (libmxfp8_stamps.so), run the step, then each GEMM of "
                          "the step once more alone and print its per-block cycle breakdown as one JSON line")
@@ -244,7 +256,8 @@ def main():
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
 
     if args.workload == "linear_4096":
-        assert not (args.unaligned_groups or args.backward or args.separate_casts or args.only or args.cycle_stamps), \
+        assert not (args.unaligned_groups or args.backward or args.separate_casts or args.only or args.cycle_stamps
+                    or args.precise), \
             "--workload linear_4096 runs its own step"
         return linear_4096_main(args, mx, synth, to_dev, dev)
 
@@ -311,6 +324,30 @@ def main():
     n_wgrad = ("gemm_wgrad dense576", "gemm", 2 * M * NARROW * K,
                lambda: mx.mx_grouped_mm_wgrad(buf["dyntq"], buf["dynts"], buf["xtq"], buf["xts"], None, M, NARROW,
                                               K, out=buf["dwn"], out_dtype=mx.MX_OUT_BF16, workspace=ws["n"]))
+    if args.precise:
+        assert not (args.backward or unaligned or args.separate_casts or args.workload != "moe_g8"), \
+            "--precise replaces the default MoE step's GEMMs only"
+        from mxfp8_block_scaled_amd import precise
+
+        # the same calls and operands; each op now also dequantizes its two operands
+        g_fwd = ("precise fwd grouped", "gemm16", g_fwd[2],
+                 lambda: precise.grouped_mm_fwd(buf["xq"], buf["xs"], buf["wq"], buf["ws"], goffs, Mg, N, K,
+                                                out=buf["y"]))
+        g_dgrad = ("precise dgrad grouped", "gemm16", g_dgrad[2],
+                   lambda: precise.grouped_mm_dgrad(buf["dyq"], buf["dys"], buf["wtq"], buf["wts"], goffs, Mg, N, K,
+                                                    out=buf["dx"]))
+        g_wgrad = ("precise wgrad grouped", "gemm16", g_wgrad[2],
+                   lambda: precise.grouped_mm_wgrad(buf["dytq"], buf["dyts"], buf["xtq"], buf["xts"], goffs, Mg, N,
+                                                    K, out=buf["dw"], out_dtype=mx.MX_OUT_BF16))
+        n_fwd = ("precise fwd dense576", "gemm16", n_fwd[2],
+                 lambda: precise.grouped_mm_fwd(buf["xq"], buf["xs"], w32["q"], w32["sr"], None, M, NARROW, K,
+                                                out=buf["yn"]))
+        n_dgrad = ("precise dgrad dense576", "gemm16", n_dgrad[2],
+                   lambda: precise.grouped_mm_dgrad(buf["dynq"], buf["dyns"], w32["qt"], w32["sc"], None, M, NARROW,
+                                                    K, out=buf["dxn"]))
+        n_wgrad = ("precise wgrad dense576", "gemm16", n_wgrad[2],
+                   lambda: precise.grouped_mm_wgrad(buf["dyntq"], buf["dynts"], buf["xtq"], buf["xts"], None, M,
+                                                    NARROW, K, out=buf["dwn"], out_dtype=mx.MX_OUT_BF16))
     if args.backward in ("high_precision", "dequantized"):
         # forward as MXFP8 (dim0 casts), backward from bf16 operands: transposes or
         # transposed dequantization (2 B written per element; 2 B read for bf16, 1 + 1/32
@@ -562,7 +599,7 @@ def main():
     dom_name, dom_kind, dom_units, _ = ops[dom_i]
     dom = per_op[dom_name]
     achieved = dom_units / (dom["us"] * 1e-6) / 1e12
-    traffic = (None if (unaligned or args.backward) else
+    traffic = (None if (unaligned or args.backward or args.precise) else
                load_traffic(("deepseek_share: " if share_config else "") + dom_name, dom_units))
     dom_peak = PEAKS[dom_kind]
     roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": dom_peak, "unit": "TFLOP/s",
@@ -574,7 +611,8 @@ def main():
     # the GEMMs' time at their own peaks over their measured time
     gemm_ideal_us = sum(u / (PEAKS[k] * 1e12) * 1e6 for _, k, u, _ in ops if k in PEAKS)
 
-    cpu = None if (args.no_cpu_baseline or unaligned or args.backward or share_config) else cpu_baseline()
+    cpu = None if (args.no_cpu_baseline or unaligned or args.backward or share_config or args.precise) \
+        else cpu_baseline()
     workload = ("moe_g8 fwd+dgrad+wgrad: G=8 experts, M=16384 tokens, K=N=4096, "
                 "grad_out 16384x4096, plus dense 576x4096 layer (32x32 weight scales, "
                 "576-wide contraction in dgrad)")
@@ -584,6 +622,9 @@ def main():
                                                   ", bf16 grouped dgrad and wgrad from "
                                                   + ("the saved bf16 operands" if args.backward == "high_precision"
                                                      else "the dequantized forward codes")) + " (no dense layer)")
+    if args.precise:
+        workload += ("; every GEMM from the same codes on the bf16 MFMA (both operands dequantized to bf16 "
+                     "inside each op)")
     if unaligned:
         workload = (f"moe_g8 unaligned groups: G=8 experts, M=16384 tokens (per-row group sizes), K=N=4096; "
                     f"casts of X and dY padded to {Mg} rows in one pass, grouped fwd/dgrad/wgrad on padded "
@@ -593,8 +634,9 @@ def main():
         "metric": METRIC, "value": round(value, 1), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "mxfp8 (e4m3 x e4m3, e8m0 block scales, fp32 accumulate)" + (
-            "; bf16 backward GEMMs" if args.backward in ("high_precision", "dequantized") else ""),
+        "dtype": ("bf16 (MXFP8 codes dequantized to bf16, bf16 MFMA, fp32 accumulate)" if args.precise else
+                  "mxfp8 (e4m3 x e4m3, e8m0 block scales, fp32 accumulate)" + (
+                      "; bf16 backward GEMMs" if args.backward in ("high_precision", "dequantized") else "")),
         "data": "synthetic (seeded N(0,sigma) bf16, " + ("Zipf" if share_config else "multinomial")
                 + " group sizes)",
         "config": share_config or {
