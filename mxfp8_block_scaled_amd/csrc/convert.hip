@@ -4,6 +4,7 @@
 // high-precision arm runs the same GEMMs on the saved bf16 operands).
 //
 //   k_dequant      E4M3 codes + MFMA-blocked E8M0 scales -> bf16, same orientation
+//                  (also the first step of the GEMMs computed from codes on the bf16 MFMA)
 //   k_tile_t<IN>   transposes [rows x cols] tiles of bf16 (IN_BF16) or of codes
 //                  dequantized on the way (IN_MXFP8) into bf16 [cols x rows], so
 //                  the GEMM reads every operand contraction-contiguous
@@ -13,6 +14,8 @@
 // bf16's fields with integer operations: it is exact unless it falls below 2^-126
 // (rounded to nearest even on bf16's 2^-133 grid) or reaches 2^128 (infinity), so no
 // fp32 flush-to-zero mode can change a result.
+
+#include <type_traits>
 
 #include "common.h"
 
@@ -90,18 +93,43 @@ __device__ inline void deq16(u32x4 c, int byte, unsigned out[8]) {
   }
 }
 
-// q [rows x cols] (pitch cols) -> out [rows x cols] bf16 (pitch cols); one thread per 16 codes.
+// q [rows x cols] (pitch cols) -> out [rows x cols] bf16 (pitch cols). Each thread takes
+// four chunks of 16 codes per pass, 256 chunks apart, so each load instruction of a wave
+// reads 1 KB of consecutive codes and a thread has four loads in flight before it converts;
+// chunk indexes are 32-bit below 2^31 chunks (WIDE: 64-bit beyond).
+template <bool WIDE>
 __global__ __launch_bounds__(256) void k_dequant(const uint8_t* __restrict__ q, const uint8_t* __restrict__ scale,
                                                  int64_t rows, int64_t cols, uint16_t* __restrict__ out) {
-  const int64_t per_row = cols / 16, n = rows * per_row, kt = scale_tiles_k(cols / 32);
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
-    const int64_t r = i / per_row, c = (i - r * per_row) * 16;
-    const u32x4 codes = __builtin_nontemporal_load((const u32x4*)(q + r * cols + c));
-    unsigned o[8];
-    deq16(codes, scale_at(scale, r, c / 32, kt), o);
-    u32x4* dst = (u32x4*)(out + r * cols + c);
-    dst[0] = (u32x4){o[0], o[1], o[2], o[3]};
-    dst[1] = (u32x4){o[4], o[5], o[6], o[7]};
+  using I = std::conditional_t<WIDE, int64_t, uint32_t>;
+  constexpr int U = 4;
+  const I per_row = (I)(cols / 16), n = (I)(rows * (cols / 16));
+  const int64_t kt = scale_tiles_k(cols / 32);
+  const I step = (I)gridDim.x * (256 * U);
+  for (I i0 = (I)blockIdx.x * (256 * U) + (I)threadIdx.x; i0 < n; i0 += step) {
+    u32x4 codes[U];
+    int byte[U];
+#pragma unroll
+    for (int k = 0; k < U; ++k) {
+      const I i = i0 + (I)(256 * k);
+      codes[k] = (u32x4){0, 0, 0, 0};
+      byte[k] = 127;
+      if (i < n) {
+        const I r = i / per_row;
+        codes[k] = __builtin_nontemporal_load((const u32x4*)(q + (int64_t)i * 16));
+        byte[k] = scale_at(scale, (int64_t)r, (int64_t)((i - r * per_row) / 2), kt);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < U; ++k) {
+      const I i = i0 + (I)(256 * k);
+      if (i < n) {
+        unsigned o[8];
+        deq16(codes[k], byte[k], o);
+        u32x4* dst = (u32x4*)(out + (int64_t)i * 16);
+        dst[0] = (u32x4){o[0], o[1], o[2], o[3]};
+        dst[1] = (u32x4){o[4], o[5], o[6], o[7]};
+      }
+    }
   }
 }
 
@@ -199,8 +227,12 @@ hipError_t mx_launch_dequant(const uint8_t* q, const uint8_t* scale, int64_t bat
                              int transpose, uint16_t* out, hipStream_t stream) {
   if (batch * rows == 0) return hipSuccess;
   if (!transpose) {
-    hipLaunchKernelGGL(mx::k_dequant, dim3(mx::grid_for(batch * rows * cols / 16)), dim3(256), 0, stream, q, scale,
-                       batch * rows, cols, out);
+    const int64_t chunks = batch * rows * cols / 16;
+    const dim3 grid(mx::grid_for((chunks + 3) / 4));  // four chunks per thread and pass
+    if (chunks < ((int64_t)1 << 31))
+      hipLaunchKernelGGL(mx::k_dequant<false>, grid, dim3(256), 0, stream, q, scale, batch * rows, cols, out);
+    else
+      hipLaunchKernelGGL(mx::k_dequant<true>, grid, dim3(256), 0, stream, q, scale, batch * rows, cols, out);
   } else {
     constexpr int TC = mx::tile_cols<mx::IN_MXFP8>();
     const int64_t tr = (rows + mx::kT - 1) / mx::kT, tc = (cols + TC - 1) / TC;
