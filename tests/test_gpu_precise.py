@@ -84,3 +84,44 @@ def test_precise_meets_fp32_figure(oracle, data, which):
     check_bf16(oracle, got16, ref, absp, klen, f"precise {which} bf16")
     if which == "wgrad":
         assert not got[1].any(), "the empty group's gradient must be zero"
+
+
+def test_precise_dense_576_layer(oracle):
+    """The dense 576-wide layer (offs=None, 32x32 weight scales; dgrad contracts over 576)."""
+    require_gpu()
+    rng = np.random.default_rng(33)
+    m, n, k = 1024, 576, 1024
+    x = synth.normal_bf16(rng, (m, k), 1.0)
+    w = synth.normal_bf16(rng, (n, k), 0.02)
+    dy = synth.normal_bf16(rng, (m, n), 1e-2)
+    xq, xs, xtq, xts = mx.mx_quantize_dim0_dim1(dev_bf16(x))
+    wq, wqt, wsr, wsc = mx.mx_quantize_weight_32x32(dev_bf16(w))
+    dyq, dys, dytq, dyts = mx.mx_quantize_dim0_dim1(dev_bf16(dy))
+    oxq, oxs = oracle.quantize_dim0(x)
+    oxt, oxts = oracle.quantize_dim1(x)
+    owq, owqt, owsr, owsc = oracle.quantize_weight_32x32(w)
+    odq, ods = oracle.quantize_dim0(dy)
+    odt, odts = oracle.quantize_dim1(dy)
+    cases = {
+        "fwd": (lambda: precise.grouped_mm_fwd(xq, xs, wq, wsr, None, m, n, k, out_dtype=mx.MX_OUT_F32),
+                oracle.mx_grouped_mm_fwd(oxq, oxs, owq, owsr, None, 1),
+                oracle.grouped_mm(np.abs(oracle.dequantize(oxq, oxs)), np.abs(oracle.dequantize(owq, owsr)), None, 1),
+                k),
+        "dgrad": (lambda: precise.grouped_mm_dgrad(dyq, dys, wqt, wsc, None, m, n, k, out_dtype=mx.MX_OUT_F32),
+                  oracle.mx_grouped_mm_fwd(odq, ods, owqt, owsc, None, 1),
+                  oracle.grouped_mm(np.abs(oracle.dequantize(odq, ods)), np.abs(oracle.dequantize(owqt, owsc)), None,
+                                    1),
+                  n),
+        "wgrad": (lambda: precise.grouped_mm_wgrad(dytq, dyts, xtq, xts, None, m, n, k, out_dtype=mx.MX_OUT_F32),
+                  oracle.mx_grouped_mm_wgrad(odt, odts, oxt, oxts, None, 1),
+                  oracle.grouped_mm_wgrad(np.abs(oracle.dequantize(odt, odts)), np.abs(oracle.dequantize(oxt, oxts)),
+                                          None, 1),
+                  m),
+    }
+    for name, (call, ref, absp, klen) in cases.items():
+        got = host(call())
+        err = oracle.rel_frobenius(got, ref)
+        say(f"[precise dense576 {name}] rel. Frobenius {err:.3e}")
+        assert err <= REL_FRO
+        check_f32(oracle, got, ref, f"precise dense576 {name} f32", absp, klen)
+
